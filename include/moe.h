@@ -1,0 +1,155 @@
+/*
+ * moe.h -- C ABI of the GPT-OSS mixture-of-experts feed-forward block for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the block computes, per token t with hidden vector x[t] (D values):
+ *
+ *   1. router logits    l[t,e] = sum_d x[t,d] * Wr[e,d] + br[e]          (E experts)
+ *      The router is a Linear layer with a bias (torchtitan GPT-OSS guide,
+ *      section "StateDict adapter": router.gate weight and bias).  The sum is
+ *      exact up to float64 rounding and is rounded once to fp32.
+ *   2. top-k            the k experts with the largest logits; slot j holds the
+ *      j-th largest; equal logits go to the lower expert index first
+ *      ("gptoss" re-implementation page, section "basic parameters": top-4 of 32).
+ *   3. gate weights     g[t,j] = softmax over the k selected logits.
+ *   4. grouping         assignment a = t*k + j; counts[e] = #{a : idx[a] = e};
+ *      offsets = exclusive prefix sum of counts (offsets[1..E] is the int32
+ *      cumulative sum of the torchtitan guide, section "Grouped matrix
+ *      multiplication"); perm lists assignments grouped by expert, ascending a
+ *      inside each group.
+ *   5. mlp1             u = x[t] . W1[e]^T + b1[e], G = 2F outputs; W1 is stored
+ *      (experts, out, in) as in the same section; u[0:F] is the gate half and
+ *      u[F:2F] the linear half.
+ *   6. SwiGLU (GPT-OSS variant, same section): gate clamped from above at LIMIT,
+ *      times sigmoid(ALPHA * gate); linear clamped to [-LIMIT, LIMIT], plus 1;
+ *      h = gate_c * sigmoid(ALPHA * gate_c) * (lin_c + 1).
+ *   7. mlp2 + gate      y[a] = g[a] * (h . W2[e]^T + b2[e]).
+ *   8. combine          out[t] = sum_j y[t*k + j]   ("gptoss" page, section
+ *      "model run flow": weighted combination of the experts' outputs).
+ *
+ * Expert weights are bf16 or MXFP4 (GPT-OSS-in-Transformers blog, MXFP4
+ * paragraph: 4-bit E2M1 values, 1 sign / 2 exponent / 1 mantissa bit, one scale
+ * per 32-element block).  MXFP4 storage used here: one uint8 buffer per matrix,
+ * first the codes [E][rows][K/2] (element 2i in the low nibble of byte i, 2i+1
+ * in the high nibble), then the E8M0 scale bytes [E][rows][K/32]; scale byte s
+ * multiplies its 32 consecutive K elements by 2^(s-127).  K is the reduction
+ * dimension: D for W1 (rows = 2F), F for W2 (rows = D).  Scale bytes must lie in
+ * [2, 252] so every decoded weight is an exact normal bf16 value; other bytes
+ * are outside the contract (not checked on the device).
+ *
+ * Numerics: every product is accumulated in fp32 on the matrix cores except the
+ * router (fp64).  The bf16 path rounds h to bf16 once; the MXFP4 path carries h
+ * as a bf16 pair (hi + lo, 16 significant bits) into mlp2.  The output is fp32
+ * and deterministic: no float atomics, fixed summation orders, bitwise equal
+ * from run to run.
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller; the library keeps
+ *     none of them after the call returns.  Every pointer must be 16-byte
+ *     aligned and non-null whenever T > 0 (logits may be null).
+ *   - Shapes: 1 <= k <= E <= 256; D and F positive multiples of 64;
+ *     0 <= T and T*k < 2^31.  T == 0 returns MOE_OK and launches nothing.
+ *   - Calls are asynchronous on the calling thread's stream (moe_set_stream)
+ *     and return after enqueueing; device faults surface at the caller's next
+ *     synchronisation.  Outputs are fully overwritten and must not alias inputs.
+ *   - Return value: MOE_OK (0) or a negative MOE_E* status; on failure nothing
+ *     has been launched and moe_last_error() describes the problem.
+ *   - The library-owned workspace is shared by all calls of the process and is
+ *     reused between calls: calls that run concurrently on different streams
+ *     race on it.  Serialise them, or give each stream its own workspace with
+ *     moe_set_workspace.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_FMT_BF16 0
+#define MOE_FMT_MXFP4 1
+
+/* GPT-OSS SwiGLU constants: the torchtitan guide names alpha and limit but prints no
+ * value; these are the published GPT-OSS defaults (alpha = 1.702 is the sigmoid
+ * approximation of GELU, Hendrycks & Gimpel 2016). */
+#define MOE_SWIGLU_ALPHA 1.702f
+#define MOE_SWIGLU_LIMIT 7.0f
+
+#define MOE_OK 0
+#define MOE_EINVAL -1   /* bad shape, k, E, null pointer, or T*k overflow */
+#define MOE_EFMT -2     /* unknown weight format */
+#define MOE_EALIGN -3   /* a pointer is not 16-byte aligned */
+#define MOE_ENOMEM -4   /* workspace allocation failed, or the caller's workspace is too small */
+#define MOE_EHIP -5     /* a HIP runtime call failed (launch, event, device query) */
+
+/* Whole block (steps 1-8).
+ *   x        bf16 [T][D]
+ *   router_w bf16 [E][D]             router_b bf16 [E]
+ *   w1       fmt 0: bf16 [E][2F][D]; fmt 1: MXFP4 buffer (codes [E][2F][D/2], scales [E][2F][D/32])
+ *   b1       bf16 [E][2F]            ([0,F) gate half, [F,2F) linear half)
+ *   w2       fmt 0: bf16 [E][D][F];  fmt 1: MXFP4 buffer (codes [E][D][F/2],  scales [E][D][F/32])
+ *   b2       bf16 [E][D]
+ *   out      fp32 [T][D] (written)
+ */
+int moe_forward(const void* x, const void* router_w, const void* router_b,
+                const void* w1, const void* b1, const void* w2, const void* b2,
+                int64_t T, int64_t D, int64_t E, int64_t k, int64_t F,
+                int fmt, float* out);
+
+/* Steps 1-4 only (routing stage; its integer outputs are exact).
+ *   logits   fp32 [T][E] or NULL     topk_idx int32 [T][k]    gates fp32 [T][k]
+ *   counts   int32 [E]               offsets  int32 [E+1]     perm  int32 [T*k]
+ */
+int moe_route(const void* x, const void* router_w, const void* router_b,
+              int64_t T, int64_t D, int64_t E, int64_t k,
+              float* logits, int32_t* topk_idx, float* gates,
+              int32_t* counts, int32_t* offsets, int32_t* perm);
+
+/* Steps 5-8 on a given routing (expert stage), e.g. the routing of moe_route or of a
+ * reference.  gates fp32 [T][k], offsets int32 [E+1] and perm int32 [T*k] must be
+ * consistent (as moe_route produces them: perm[offsets[e] .. offsets[e+1]) lists the
+ * assignments t*k+j routed to expert e); inconsistent routing is outside the contract.
+ * The token and slot of a row come from its assignment id, so top-k indices are not
+ * needed.  Other arguments as in moe_forward. */
+int moe_experts(const void* x, const void* w1, const void* b1, const void* w2, const void* b2,
+                const float* gates, const int32_t* offsets, const int32_t* perm,
+                int64_t T, int64_t D, int64_t E, int64_t k, int64_t F,
+                int fmt, float* out);
+
+/* Stream for the calling thread's subsequent calls (a hipStream_t; NULL = default stream). */
+int moe_set_stream(void* hip_stream);
+
+/* Device bytes of workspace a moe_forward call of this shape needs (0 for T == 0). */
+size_t moe_workspace_bytes(int64_t T, int64_t D, int64_t E, int64_t k, int64_t F, int fmt);
+
+/* Use caller-owned device memory as the workspace (256-byte aligned).  Calls whose need
+ * exceeds `bytes` fail with MOE_ENOMEM.  Passing NULL returns to the library-owned
+ * workspace, which grows on demand with hipMalloc and is kept until moe_release. */
+int moe_set_workspace(void* dev_ptr, size_t bytes);
+
+/* Message for the calling thread's last failing call ("" if none). */
+const char* moe_last_error(void);
+
+/* Free the library-owned workspace and profiling events. */
+void moe_release(void);
+
+/* Kernel timing (tracing): while enabled, every launch is bracketed by HIP events on the
+ * call's stream, and each kernel's summed device time and launch count accumulate per
+ * stage.  Stages: 0 router, 1 top-k, 2 permute, 3 mlp1, 4 mlp2, 5 combine.
+ * moe_profile_read synchronises on the recorded events; it fills ms[6] and launches[6]
+ * (either may be NULL) and resets the counters. */
+#define MOE_NUM_STAGES 6
+int moe_profile_enable(int on);
+int moe_profile_read(double* ms, int64_t* launches);
+
+/* Library build string (architecture and tile configuration). */
+const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,22 @@
+"""GPT-OSS mixture-of-experts feed-forward block on AMD Instinct MI355X (gfx950).
+
+The compute lives in ``libmoe.so`` (hand-written HIP kernels behind the C ABI of
+``include/moe.h``); ``moe`` is its ctypes binding.
+"""
+from .moe import (  # noqa: F401
+    FMT,
+    LIB_PATH,
+    STAGES,
+    MoEError,
+    experts,
+    forward,
+    lib,
+    mxfp4_bytes,
+    profile_enable,
+    profile_read,
+    release,
+    route,
+    set_workspace,
+    version,
+    workspace_bytes,
+)

@@ -1,0 +1,53 @@
+// Internal declarations shared by the kernel sources and the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+enum Stage { ST_ROUTER = 0, ST_TOPK = 1, ST_PERMUTE = 2, ST_MLP1 = 3, ST_MLP2 = 4, ST_COMBINE = 5 };
+
+// ---------------------------------------------------------------- routing
+// Number of K splits the router uses for T tokens of width D (>= 1).
+int router_ksplit(int64_t T, int64_t D);
+
+// fp64 partial dot products partial[s][t][e] over the s-th K range.
+hipError_t launch_router_partial(const uint16_t* x, const uint16_t* wr, int T, int D, int E,
+                                 int ksplit, double* partial, hipStream_t st);
+// Sum of partials + bias -> fp32 logits, top-k (ties to lower index), softmax gates.
+hipError_t launch_topk(const double* partial, int ksplit, const uint16_t* br, int T, int E, int k,
+                       float* logits, int32_t* idx, float* gates, hipStream_t st);
+// counts, exclusive offsets and the stable per-expert permutation of the T*k assignments.
+hipError_t launch_permute(const int32_t* idx, int A, int E, int32_t* counts, int32_t* offsets,
+                          int32_t* perm, hipStream_t st);
+
+// ---------------------------------------------------------------- experts
+struct ExpertArgs {
+  const uint16_t* x;        // [T][D] bf16
+  const void* w1;           // bf16 [E][2F][D] or MXFP4 buffer
+  const uint16_t* b1;       // [E][2F]
+  const void* w2;           // bf16 [E][D][F] or MXFP4 buffer
+  const uint16_t* b2;       // [E][D]
+  const float* gates;       // [A]
+  const int32_t* offsets;   // [E+1]
+  const int32_t* perm;      // [A]
+  uint16_t* h;              // [A][F] bf16 (hi part for MXFP4)
+  uint16_t* h_lo;           // [A][F] bf16 low part (MXFP4 only)
+  float* y;                 // [A][D] fp32, row a = assignment id
+  float* out;               // [T][D] fp32
+  int T, D, E, k, F, fmt;
+};
+
+// Tile configuration chosen for a routed-row count (the same choice for every stage).
+int expert_tile_config(int64_t A, int64_t E);
+hipError_t launch_mlp1(const ExpertArgs& a, int cfg, hipStream_t st);
+hipError_t launch_mlp2(const ExpertArgs& a, int cfg, hipStream_t st);
+hipError_t launch_combine(const float* y, int T, int D, int k, float* out, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,295 @@
+// Routing stage of the GPT-OSS MoE block on gfx950: router logits, top-k with softmax
+// gates, and the stable grouping of assignments by expert.
+//
+// Router: a Linear with a bias (torchtitan GPT-OSS guide, section "StateDict adapter").
+// The logits decide integer outputs, so they are computed as the exact dot product of
+// the bf16 inputs up to float64 rounding, then rounded once to fp32.  The products of
+// two bf16 values are exact in fp64, so the only rounding is the fp64 accumulation.
+// The dot products run on the fp64 matrix cores (v_mfma_f64_16x16x4f64): a wave owns
+// 16 tokens x 16 experts per instruction, converting bf16 operands to fp64 in registers.
+// K is split across the grid so small token counts still occupy the chip; the partial
+// sums are added in a fixed order by the top-k kernel (deterministic).
+//
+// Top-k ("gptoss" re-implementation page, basic parameters: top-4 of 32 experts): one
+// wave per token, lanes own experts, k rounds of a wave-wide (value desc, index asc)
+// argmax.  Gates: softmax over the k selected logits, in fp64, stored as fp32.
+//
+// Grouping (torchtitan guide, grouped GEMM section: per-expert counts and their int32
+// cumulative sum as group offsets): one workgroup of 16 waves.  Each wave owns a
+// contiguous range of assignments, counts them per expert in LDS, and after a scan
+// places each assignment at offsets[e] + (earlier assignments of e), computing ranks
+// inside a 64-assignment step with ballots over the bits of the expert index.  The
+// result is the stable counting sort, independent of any atomic arrival order.
+#include "moe_internal.h"
+
+namespace moe {
+
+static __device__ __forceinline__ double bf16_bits_to_f64(uint32_t b) {
+  return (double)__uint_as_float(b << 16);
+}
+
+// ------------------------------------------------------------------------------ router
+constexpr int RT_WAVES = 4;           // waves per workgroup, each owns 16 tokens
+constexpr int RT_CHUNK = 32;          // K elements per MFMA group (8 steps of K=4)
+
+int router_ksplit(int64_t T, int64_t D) {
+  const int64_t chunks = D / RT_CHUNK;
+  const int64_t tiles = (T + 15) / 16;
+  // aim at ~2048 waves in flight; keep >= 2 chunks per split
+  int64_t ks = (2048 + tiles - 1) / tiles;
+  int64_t maxks = chunks / 2 > 0 ? chunks / 2 : 1;
+  if (ks > maxks) ks = maxks;
+  if (ks < 1) ks = 1;
+  return (int)ks;
+}
+
+// v_mfma_f64_16x16x4f64 lane layout (measured on gfx950): A lane l supplies A[l & 15][l >> 4],
+// B lane l supplies B[l >> 4][l & 15], and output register r of lane l holds C[m][n] with
+// m = (l >> 4) + 4 r, n = l & 15.
+template <int NEB>
+__global__ __launch_bounds__(64 * RT_WAVES) void router_partial_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int D, int E,
+    int ksplit, double* __restrict__ partial) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int t0 = (blockIdx.x * RT_WAVES + wave) * 16;
+  if (t0 >= T) return;
+  const int s = blockIdx.y;
+  const int nchunks = D / RT_CHUNK;
+  const int c_begin = (int)((int64_t)nchunks * s / ksplit);
+  const int c_end = (int)((int64_t)nchunks * (s + 1) / ksplit);
+
+  const int row = lane & 15;   // token (A) / expert-in-block (B)
+  const int kg = lane >> 4;    // which 8-element run of the 32-element chunk
+  const int t = min(t0 + row, T - 1);
+  const uint16_t* xrow = x + (size_t)t * D + kg * 8;
+  const uint16_t* wrow[NEB];
+#pragma unroll
+  for (int b = 0; b < NEB; ++b) {
+    const int e = min(b * 16 + row, E - 1);
+    wrow[b] = wr + (size_t)e * D + kg * 8;
+  }
+
+  f64x4 acc[NEB];
+#pragma unroll
+  for (int b = 0; b < NEB; ++b) acc[b] = f64x4{0.0, 0.0, 0.0, 0.0};
+
+  uint4 xa = {0, 0, 0, 0};
+  uint4 wa[NEB];
+  if (c_begin < c_end) {
+    xa = *(const uint4*)(xrow + c_begin * RT_CHUNK);
+#pragma unroll
+    for (int b = 0; b < NEB; ++b) wa[b] = *(const uint4*)(wrow[b] + c_begin * RT_CHUNK);
+  }
+  for (int c = c_begin; c < c_end; ++c) {
+    const uint4 xc = xa;
+    uint4 wc[NEB];
+#pragma unroll
+    for (int b = 0; b < NEB; ++b) wc[b] = wa[b];
+    if (c + 1 < c_end) {   // prefetch the next chunk
+      xa = *(const uint4*)(xrow + (c + 1) * RT_CHUNK);
+#pragma unroll
+      for (int b = 0; b < NEB; ++b) wa[b] = *(const uint4*)(wrow[b] + (c + 1) * RT_CHUNK);
+    }
+    const uint32_t xw[4] = {xc.x, xc.y, xc.z, xc.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t xb = (i & 1) ? (xw[i >> 1] >> 16) : (xw[i >> 1] & 0xFFFFu);
+      const double a = bf16_bits_to_f64(xb);
+#pragma unroll
+      for (int b = 0; b < NEB; ++b) {
+        const uint32_t ww[4] = {wc[b].x, wc[b].y, wc[b].z, wc[b].w};
+        const uint32_t wb = (i & 1) ? (ww[i >> 1] >> 16) : (ww[i >> 1] & 0xFFFFu);
+        acc[b] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bf16_bits_to_f64(wb), acc[b], 0, 0, 0);
+      }
+    }
+  }
+  // partial[s][t][e]: token t0 + kg + 4r, expert b*16 + row
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int tt = t0 + kg + 4 * r;
+    if (tt < T) {
+      double* dst = partial + ((size_t)s * T + tt) * E;
+#pragma unroll
+      for (int b = 0; b < NEB; ++b) {
+        const int e = b * 16 + row;
+        if (e < E) dst[e] = acc[b][r];
+      }
+    }
+  }
+}
+
+hipError_t launch_router_partial(const uint16_t* x, const uint16_t* wr, int T, int D, int E,
+                                 int ksplit, double* partial, hipStream_t st) {
+  const dim3 grid((T + 16 * RT_WAVES - 1) / (16 * RT_WAVES), ksplit);
+  const dim3 block(64 * RT_WAVES);
+  const int neb = (E + 15) / 16;
+  if (neb <= 1)
+    hipLaunchKernelGGL(router_partial_kernel<1>, grid, block, 0, st, x, wr, T, D, E, ksplit, partial);
+  else if (neb <= 2)
+    hipLaunchKernelGGL(router_partial_kernel<2>, grid, block, 0, st, x, wr, T, D, E, ksplit, partial);
+  else if (neb <= 4)
+    hipLaunchKernelGGL(router_partial_kernel<4>, grid, block, 0, st, x, wr, T, D, E, ksplit, partial);
+  else if (neb <= 8)
+    hipLaunchKernelGGL(router_partial_kernel<8>, grid, block, 0, st, x, wr, T, D, E, ksplit, partial);
+  else
+    hipLaunchKernelGGL(router_partial_kernel<16>, grid, block, 0, st, x, wr, T, D, E, ksplit, partial);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------ top-k
+constexpr int TK_WAVES = 4;
+
+// (v, e) beats (v2, e2): larger value, or equal value and lower index.
+static __device__ __forceinline__ bool beats(float v, int e, float v2, int e2) {
+  return v > v2 || (v == v2 && e < e2);
+}
+
+__global__ __launch_bounds__(64 * TK_WAVES) void topk_kernel(
+    const double* __restrict__ partial, int ksplit, const uint16_t* __restrict__ br, int T, int E,
+    int k, float* __restrict__ logits, int32_t* __restrict__ idx, float* __restrict__ gates) {
+  __shared__ float sel_v[TK_WAVES][256];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * TK_WAVES + wave;
+  if (t >= T) return;
+  constexpr int PER = 4;   // E <= 256 = 4 * 64
+  float v[PER];
+  bool live[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = lane + 64 * i;
+    live[i] = e < E;
+    v[i] = -INFINITY;
+    if (live[i]) {
+      double s = 0.0;
+      for (int q = 0; q < ksplit; ++q) s += partial[((size_t)q * T + t) * E + e];
+      s += bf16_bits_to_f64(br[e]);
+      v[i] = (float)s;   // round to nearest even
+      if (logits) logits[(size_t)t * E + e] = v[i];
+    }
+  }
+  for (int j = 0; j < k; ++j) {
+    // lane-local best among live entries; any live entry beats "none" (NONE), so the
+    // winner is always a valid expert index even for NaN logits (outside the contract)
+    constexpr int NONE = 0x7fffffff;
+    float bv = -INFINITY;
+    int be = NONE;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = lane + 64 * i;
+      if (live[i] && (be == NONE || beats(v[i], e, bv, be))) { bv = v[i]; be = e; }
+    }
+    // wave argmax (butterfly: every lane ends with the same winner)
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oe = __shfl_xor(be, off);
+      if (oe != NONE && (be == NONE || beats(ov, oe, bv, be))) { bv = ov; be = oe; }
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (lane + 64 * i == be) live[i] = false;
+    if (lane == 0) {
+      idx[(size_t)t * k + j] = be;
+      sel_v[wave][j] = bv;
+    }
+  }
+  // gates: softmax over the k selected logits, in fp64
+  const double top = (double)sel_v[wave][0];
+  double part = 0.0;
+  for (int j = lane; j < k; j += 64) part += exp((double)sel_v[wave][j] - top);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+  for (int j = lane; j < k; j += 64)
+    gates[(size_t)t * k + j] = (float)(exp((double)sel_v[wave][j] - top) / part);
+}
+
+hipError_t launch_topk(const double* partial, int ksplit, const uint16_t* br, int T, int E, int k,
+                       float* logits, int32_t* idx, float* gates, hipStream_t st) {
+  const dim3 grid((T + TK_WAVES - 1) / TK_WAVES);
+  hipLaunchKernelGGL(topk_kernel, grid, dim3(64 * TK_WAVES), 0, st, partial, ksplit, br, T, E, k,
+                     logits, idx, gates);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------ grouping
+constexpr int PM_WAVES = 16;
+
+__global__ __launch_bounds__(64 * PM_WAVES) void permute_kernel(
+    const int32_t* __restrict__ idx, int A, int E, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm) {
+  __shared__ int cnt[PM_WAVES][256];
+  __shared__ int base[PM_WAVES][256];
+  __shared__ int tot[256];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  for (int i = tid; i < PM_WAVES * 256; i += blockDim.x) (&cnt[0][0])[i] = 0;
+  __syncthreads();
+  // contiguous range per wave, a multiple of 64 long
+  const int per = ((A + PM_WAVES - 1) / PM_WAVES + 63) & ~63;
+  const int lo = min(A, wave * per);
+  const int hi = min(A, lo + per);
+  for (int a = lo + lane; a < hi; a += 64) atomicAdd(&cnt[wave][idx[a]], 1);
+  __syncthreads();
+  // exclusive scan of the totals over experts (threads 0..255)
+  if (tid < 256) {
+    int s = 0;
+    if (tid < E)
+      for (int w = 0; w < PM_WAVES; ++w) s += cnt[w][tid];
+    tot[tid] = s;
+    if (tid < E) counts[tid] = s;
+  }
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    int v = 0;
+    if (tid < 256 && tid >= off) v = tot[tid - off];
+    __syncthreads();
+    if (tid < 256) tot[tid] += v;
+    __syncthreads();
+  }
+  if (tid < E) {
+    int b = (tid == 0) ? 0 : tot[tid - 1];   // exclusive prefix
+    offsets[tid] = b;
+    for (int w = 0; w < PM_WAVES; ++w) {
+      base[w][tid] = b;
+      b += cnt[w][tid];
+    }
+    if (tid == E - 1) offsets[E] = b;
+  }
+  __syncthreads();
+  // place assignments: rank among equal experts inside each 64-wide step by ballots
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  for (int a0 = lo; a0 < hi; a0 += 64) {
+    const int a = a0 + lane;
+    const bool valid = a < hi;
+    const int e = valid ? idx[a] : 0;
+    uint64_t match = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const uint64_t on = __ballot(valid && ((e >> b) & 1));
+      match &= ((e >> b) & 1) ? on : ~on;
+    }
+    if (valid) {
+      const uint64_t below = match & ((1ull << lane) - 1ull);
+      const int rank = __popcll(below);
+      const int pos = base[wave][e] + rank;
+      perm[pos] = a;
+      const int leader = 63 - __clzll(match);
+      // every lane has read base[wave][e] above; the group's highest lane advances it
+      __builtin_amdgcn_wave_barrier();
+      if (lane == leader) base[wave][e] = pos + 1;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+hipError_t launch_permute(const int32_t* idx, int A, int E, int32_t* counts, int32_t* offsets,
+                          int32_t* perm, hipStream_t st) {
+  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(64 * PM_WAVES), 0, st, idx, A, E, counts,
+                     offsets, perm);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -59,12 +59,13 @@ def mxfp4_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """
     codes = np.asarray(codes, dtype=np.uint8)
     rows, half = codes.shape
-    q = np.empty((rows, 2 * half), dtype=np.float64)
-    q[:, 0::2] = e2m1_value(codes & 15)
-    q[:, 1::2] = e2m1_value(codes >> 4)
+    # value pair of every byte: (low-nibble element, high-nibble element)
+    b = np.arange(256)
+    pair = np.stack([e2m1_value(b & 15), e2m1_value(b >> 4)], axis=1)
+    q = pair[codes].reshape(rows, (2 * half) // 32, 32)
     s = np.asarray(scales, dtype=np.int64)
     factor = np.where(s == 255, np.nan, np.ldexp(1.0, s - 127))
-    return q * np.repeat(factor, 32, axis=1)
+    return (q * factor[:, :, None]).reshape(rows, 2 * half)
 
 
 def expert_weight(w: np.ndarray, fmt: str, E: int, rows: int, K: int, e: int) -> np.ndarray:

@@ -11,6 +11,7 @@ from .generate import (  # noqa: F401
     f32_to_bf16_bits,
     make_inputs,
     make_router_inputs,
+    make_routing_inputs,
     zipf_plan,
     router_bias_path,
 )

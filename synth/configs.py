@@ -69,9 +69,9 @@ CONFIGS = {
 }
 
 
-def get_config(name: str, **overrides) -> Config:
-    """Look up a named workload; keyword overrides give a variant (e.g. T=...)."""
-    base = CONFIGS[name]
+def get_config(base_name: str, **overrides) -> Config:
+    """Look up a named workload; keyword overrides give a variant (e.g. T=..., name=...)."""
+    base = CONFIGS[base_name]
     if not overrides:
         return base
     d = dict(base.__dict__)

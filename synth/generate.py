@@ -160,6 +160,25 @@ def make_router_inputs(cfg) -> tuple:
     return x, wr
 
 
+def make_routing_inputs(cfg) -> tuple:
+    """(x, router weight, router bias) as bf16 bits, identical to ``make_inputs``'s draws."""
+    if isinstance(cfg, str):
+        cfg = get_config(cfg)
+    x, wr = make_router_inputs(cfg)
+    return x, wr, _router_bias(cfg, _streams(cfg))
+
+
+def _router_bias(cfg: Config, st) -> np.ndarray:
+    if cfg.router_bias == "zero":
+        return np.zeros(cfg.E, dtype=np.uint16)
+    if cfg.router_bias == "normal":
+        return f32_to_bf16_bits(np.random.default_rng(st["br"]).standard_normal(cfg.E, dtype=np.float32)
+                                * np.float32(cfg.bias_std))
+    if cfg.router_bias == "zipf":
+        return _read_router_bias(cfg)
+    raise ValueError(cfg.router_bias)
+
+
 @dataclass
 class MoEInputs:
     """Host copies of one layer's inputs, as raw storage bits.
@@ -182,17 +201,7 @@ def _build(cfg: Config, router_bias: Optional[np.ndarray]) -> MoEInputs:
     st = _streams(cfg)
     T, D, E, F = cfg.T, cfg.D, cfg.E, cfg.F
     x, wr = make_router_inputs(cfg)
-    if router_bias is not None:
-        br = np.asarray(router_bias, dtype=np.uint16)
-    elif cfg.router_bias == "zero":
-        br = np.zeros(E, dtype=np.uint16)
-    elif cfg.router_bias == "normal":
-        br = f32_to_bf16_bits(np.random.default_rng(st["br"]).standard_normal(E, dtype=np.float32)
-                              * np.float32(cfg.bias_std))
-    elif cfg.router_bias == "zipf":
-        br = _read_router_bias(cfg)
-    else:
-        raise ValueError(cfg.router_bias)
+    br = np.asarray(router_bias, dtype=np.uint16) if router_bias is not None else _router_bias(cfg, st)
     if cfg.fmt == "bf16":
         w1 = _normal_bf16_rows(st["w1"], E, (2 * F, D), cfg.weight_std)
         w2 = _normal_bf16_rows(st["w2"], E, (D, F), cfg.weight_std)

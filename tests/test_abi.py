@@ -1,0 +1,108 @@
+"""The C ABI without a GPU: the library loads, exports every function the header declares,
+and rejects invalid arguments in host code before any HIP call (no compute call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_transformer_amd as moe
+from mixture_experts_transformer_amd.moe import _SIGNATURES
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+MOE_OK, MOE_EINVAL, MOE_EFMT, MOE_EALIGN = 0, -1, -2, -3
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = moe.lib()
+    names = declared_functions()
+    assert {"moe_forward", "moe_route", "moe_experts"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in moe.h but not exported"
+    assert set(names) == set(_SIGNATURES), "binding signatures and header disagree"
+
+
+def test_header_constants_match_binding():
+    src = open(HEADER).read()
+    assert re.search(r"#define MOE_FMT_BF16 0\b", src) and re.search(r"#define MOE_FMT_MXFP4 1\b", src)
+    assert moe.FMT == {"bf16": 0, "mxfp4": 1}
+    assert "#define MOE_SWIGLU_ALPHA 1.702f" in src and "#define MOE_SWIGLU_LIMIT 7.0f" in src
+    assert re.search(r"#define MOE_NUM_STAGES 6\b", src) and len(moe.STAGES) == 6
+
+
+def test_version_string():
+    assert "gfx950" in moe.version()
+
+
+# fake, 16-byte aligned device addresses: only ever passed to calls that must fail validation
+P = 0x10000
+BAD = 0x10008
+
+
+def fwd(T=8, D=64, E=4, k=2, F=64, fmt=0, ptrs=None):
+    p = ptrs or [P] * 8
+    return moe.lib().moe_forward(p[0], p[1], p[2], p[3], p[4], p[5], p[6], T, D, E, k, F, fmt, p[7])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), MOE_EINVAL), (dict(D=0), MOE_EINVAL), (dict(D=96), MOE_EINVAL), (dict(F=32), MOE_EINVAL),
+    (dict(E=0), MOE_EINVAL), (dict(E=257, k=2), MOE_EINVAL), (dict(k=0), MOE_EINVAL), (dict(k=5, E=4), MOE_EINVAL),
+    (dict(T=2**30, k=2), MOE_EINVAL), (dict(fmt=2), MOE_EFMT), (dict(fmt=-1), MOE_EFMT),
+])
+def test_forward_rejects_bad_shapes(kw, code):
+    assert fwd(**kw) == code
+    assert moe.lib().moe_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("which", range(8))
+def test_forward_rejects_null_and_misaligned_pointers(which):
+    ptrs = [P] * 8
+    ptrs[which] = None
+    assert fwd(ptrs=ptrs) == MOE_EINVAL
+    assert "NULL" in moe.lib().moe_last_error().decode()
+    ptrs[which] = BAD
+    assert fwd(ptrs=ptrs) == MOE_EALIGN
+    assert "aligned" in moe.lib().moe_last_error().decode()
+
+
+def test_zero_tokens_is_a_no_op():
+    # T = 0 returns before any pointer is looked at or any launch is made
+    assert fwd(T=0, ptrs=[None] * 8) == MOE_OK
+    assert moe.lib().moe_route(None, None, None, 0, 64, 4, 2, None, None, None, None, None, None) == MOE_OK
+    assert moe.lib().moe_experts(None, None, None, None, None, None, None, None, 0, 64, 4, 2, 64, 0, None) == MOE_OK
+
+
+def test_route_and_experts_validate():
+    lib = moe.lib()
+    # logits may be NULL; other outputs may not
+    assert lib.moe_route(P, P, P, 8, 64, 4, 2, None, None, P, P, P, P) == MOE_EINVAL
+    assert lib.moe_route(P, P, P, 8, 64, 4, 5, None, P, P, P, P, P) == MOE_EINVAL
+    assert lib.moe_route(P, P, P, 8, 64, 4, 2, BAD, P, P, P, P, P) == MOE_EALIGN
+    assert lib.moe_experts(P, P, P, P, P, P, P, None, 8, 64, 4, 2, 64, 0, P) == MOE_EINVAL
+    assert lib.moe_experts(P, P, P, P, P, P, P, P, 8, 64, 4, 2, 64, 7, P) == MOE_EFMT
+
+
+def test_workspace_bytes():
+    wb = moe.lib().moe_workspace_bytes
+    assert wb(0, 2880, 32, 4, 2880, 0) == 0
+    assert wb(8, 100, 4, 2, 64, 0) == 0        # invalid shape
+    b16 = wb(8192, 2880, 32, 4, 2880, 0)
+    b4 = wb(8192, 2880, 32, 4, 2880, 1)
+    A = 8192 * 4
+    # h (bf16) + y (fp32) dominate; MXFP4 adds the low half of h
+    assert b16 >= A * 2880 * 2 + A * 2880 * 4
+    assert b4 - b16 >= A * 2880 * 2 and b4 - b16 < A * 2880 * 2 + 4096
+    assert b16 % 256 == 0
+
+
+def test_set_workspace_rejects_misaligned():
+    assert moe.lib().moe_set_workspace(0x1010, 4096) == MOE_EALIGN
+    assert moe.lib().moe_set_workspace(None, 0) == MOE_OK

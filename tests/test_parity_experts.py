@@ -1,0 +1,77 @@
+"""GPU expert stage (mlp1 + SwiGLU, mlp2 + bias + gate, combine) on the oracle's routing.
+
+Isolating the grouped GEMMs from the router follows the stage-by-stage verification of
+the "gptoss" re-implementation page (section on testing: each layer is fed the reference
+output of the previous one)."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_transformer_amd as moe
+import oracle
+from synth import f32_to_bf16_bits, get_config, make_inputs
+from _gpu import assert_close, note, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def experts_vs_oracle(inp, label):
+    cfg = inp.cfg
+    note(f"experts {label}: T={cfg.T} D={cfg.D} E={cfg.E} k={cfg.k} F={cfg.F} fmt={cfg.fmt}")
+    ref, r = oracle.moe_forward(inp.x, inp.wr, inp.br, inp.w1, inp.b1, inp.w2, inp.b2,
+                                k=cfg.k, F=cfg.F, fmt=cfg.fmt, return_routing=True)
+    d = upload(inp)
+    gates = torch.from_numpy(r["gates"].astype(np.float32)).cuda()
+    offsets = torch.from_numpy(r["offsets"]).cuda()
+    perm = torch.from_numpy(r["perm"]).cuda()
+    out = moe.experts(d["x"], d["w1"], d["b1"], d["w2"], d["b2"], gates, offsets, perm, cfg.k, cfg.fmt)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), ref, label)
+    return r
+
+
+@pytest.mark.parametrize("name", ["C1", "C2", "X1"])
+def test_experts_workloads(name):
+    experts_vs_oracle(make_inputs(name), name)
+
+
+# shapes chosen to cover both tile configurations, row tails inside a tile, column tails of
+# mlp1 (F not a multiple of the tile's pair count) and of mlp2 (D not a multiple of the tile
+# width), single-K-step and multi-step reductions
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp4"])
+@pytest.mark.parametrize("T,D,E,k,F", [
+    (37, 128, 5, 2, 192),       # small tiles, ragged groups
+    (300, 64, 3, 3, 64),        # k = E
+    (1000, 192, 4, 2, 320),     # large tiles: mlp1 pair tail (320 = 3*96 + 32)
+    (700, 256, 2, 1, 128),      # large tiles: mlp2 column tail (256 = 192 + 64), k = 1
+    (2500, 384, 8, 4, 448),     # large tiles, many row tiles per expert
+])
+def test_experts_ragged_shapes(fmt, T, D, E, k, F):
+    base = "C4" if fmt == "mxfp4" else "C2"
+    cfg = get_config(base, name=f"rag{T}", T=T, D=D, E=E, k=k, F=F, seed=1000 + T)
+    experts_vs_oracle(make_inputs(cfg), f"ragged {fmt} T={T} D={D} E={E} k={k} F={F}")
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp4"])
+def test_experts_with_empty_experts(fmt):
+    base = "C4" if fmt == "mxfp4" else "C2"
+    cfg = get_config(base, name="empty", T=600, D=128, E=16, k=2, F=128, seed=77)
+    inp = make_inputs(cfg)
+    neg = f32_to_bf16_bits(np.float32([-64.0]))[0]
+    br = inp.br.copy()
+    br[[0, 1, 7, 15]] = neg
+    inp2 = make_inputs(cfg, router_bias=br)
+    r = experts_vs_oracle(inp2, f"empty experts {fmt}")
+    assert all(r["counts"][e] == 0 for e in (0, 1, 7, 15))
+
+
+def test_experts_with_clamped_swiglu():
+    """Large mlp1 weights push its outputs far past the SwiGLU limit on both sides; W2 is
+    scaled by 2^-6 (exponent field - 6, exact) so the output keeps a moderate size."""
+    cfg = get_config("C2", name="clamp", T=200, D=256, E=4, k=2, F=128, seed=5, weight_std=0.5)
+    inp = make_inputs(cfg)
+    u = oracle.bf16_to_f64(inp.x) @ oracle.expert_weight(inp.w1, "bf16", 4, 256, 256, 0).T
+    assert (u[:, :128] > 7).mean() > 0.1 and (u[:, 128:] < -7).mean() > 0.1
+    nz = (inp.w2 & 0x7FFF) != 0
+    inp.w2 = np.where(nz, inp.w2 - np.uint16(6 << 7), inp.w2).astype(np.uint16)
+    experts_vs_oracle(inp, "clamped SwiGLU")

@@ -1,0 +1,108 @@
+"""GPU moe_forward end to end vs the oracle, at every workload's full size.
+
+Small workloads are compared on every output.  At the large ones the integer routing is
+compared in full (through moe_route, same kernels as moe_forward) and the fp32 output on a
+sample of tokens the oracle evaluates on its own: a token's output depends only on its
+own row, so the oracle runs the block on the sampled rows alone.  The C5 sample is drawn
+from tokens whose experts lie in a bounded set (the most loaded experts plus some of the
+least loaded) to keep the oracle's MXFP4 decoding to a few experts."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_transformer_amd as moe
+import oracle
+from synth import get_config, make_inputs
+from _gpu import assert_close, note, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def forward(inp, d=None):
+    cfg = inp.cfg
+    d = d or upload(inp)
+    out = moe.forward(d["x"], d["router_w"], d["router_b"], d["w1"], d["b1"], d["w2"], d["b2"], cfg.k, cfg.fmt)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("name", ["C1", "C2", "X1"])
+def test_forward_full(name):
+    inp = make_inputs(name)
+    cfg = inp.cfg
+    note(f"forward {name} full: T={cfg.T} E={cfg.E} fmt={cfg.fmt}")
+    out = forward(inp).cpu().numpy()
+    ref = oracle.moe_forward(inp.x, inp.wr, inp.br, inp.w1, inp.b1, inp.w2, inp.b2, k=cfg.k, F=cfg.F, fmt=cfg.fmt)
+    assert_close(out, ref, f"forward {name}")
+
+
+def pick_sample(name, idx, E, n):
+    g = np.random.default_rng(123)
+    T = idx.shape[0]
+    if name != "C5":
+        return np.sort(g.choice(T, size=n, replace=False))
+    counts = np.bincount(idx.reshape(-1), minlength=E)
+    live = np.flatnonzero(counts)
+    order = live[np.argsort(-counts[live], kind="stable")]
+    allowed = set(order[:10].tolist()) | set(order[-4:].tolist())
+    ok = np.array([set(row.tolist()) <= allowed for row in idx])
+    cand = np.flatnonzero(ok)
+    # every allowed tail expert appears in the sample when some token reaches it
+    tail = [np.flatnonzero(ok & (idx == e).any(axis=1))[:2] for e in order[-4:]]
+    return np.unique(np.concatenate([g.choice(cand, size=min(n, cand.size), replace=False)] + tail))
+
+
+@pytest.mark.parametrize("name,n", [("C3", 256), ("C4", 256), ("X2", 256), ("C5", 128)])
+def test_forward_large_sampled(name, n):
+    inp = make_inputs(name)
+    cfg = inp.cfg
+    d = upload(inp)
+    note(f"forward {name}: T={cfg.T} E={cfg.E} fmt={cfg.fmt}")
+    out = forward(inp, d)
+    r = moe.route(d["x"], d["router_w"], d["router_b"], cfg.k, want_logits=False)
+    torch.cuda.synchronize()
+    idx_ref = oracle.select_experts(oracle.router_logits(inp.x, inp.wr, inp.br), cfg.k)
+    assert np.array_equal(r["idx"].cpu().numpy(), idx_ref), f"{name}: top-k indices differ"
+    counts_ref, offsets_ref, perm_ref, _ = oracle.route_assignments(idx_ref, cfg.E)
+    assert np.array_equal(r["offsets"].cpu().numpy(), offsets_ref)
+    assert np.array_equal(r["perm"].cpu().numpy(), perm_ref)
+    sample = pick_sample(name, idx_ref, cfg.E, n)
+    ref = oracle.moe_forward(inp.x[sample], inp.wr, inp.br, inp.w1, inp.b1, inp.w2, inp.b2,
+                             k=cfg.k, F=cfg.F, fmt=cfg.fmt)
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    assert_close(got[sample], ref, f"forward {name} ({sample.size} sampled tokens)")
+
+
+@pytest.mark.parametrize("name", ["C3", "C4"])
+def test_forward_is_bitwise_deterministic(name):
+    inp = make_inputs(name)
+    d = upload(inp)
+    note(f"determinism {name}")
+    a = forward(inp, d)
+    b = forward(inp, d)
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp4"])
+def test_forward_power_of_two_scaling_is_exact(fmt):
+    """W2, b2 doubled (bf16: exponent + 1; MXFP4: every W2 scale byte + 1, b2 doubled) doubles
+    the output bit for bit: scaling by 2 commutes with every rounding on the path."""
+    base = "C4" if fmt == "mxfp4" else "C2"
+    cfg = get_config(base, name="scale", T=1024, E=8, seed=31)
+    inp = make_inputs(cfg)
+    d = upload(inp)
+    note(f"power-of-two scaling {fmt}")
+    out = forward(inp, d)
+    nz = (inp.b2 & 0x7FFF) != 0
+    b2s = np.where(nz, inp.b2 + np.uint16(1 << 7), inp.b2).astype(np.uint16)
+    if fmt == "bf16":
+        nzw = (inp.w2 & 0x7FFF) != 0
+        w2s = np.where(nzw, inp.w2 + np.uint16(1 << 7), inp.w2).astype(np.uint16)
+    else:
+        w2s = inp.w2.copy()
+        w2s[cfg.E * cfg.D * cfg.F // 2:] += 1
+    from _gpu import u16, weights
+    d2 = dict(d, w2=weights(w2s, fmt), b2=u16(b2s))
+    out2 = forward(inp, d2)
+    assert torch.equal(out2, 2 * out)
