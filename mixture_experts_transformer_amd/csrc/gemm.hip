@@ -125,28 +125,35 @@ static __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ off
   return true;
 }
 
-// LDS byte offset of 16-byte chunk c (0..7) of row r in a [rows][64 bf16] tile.
-static __device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
+// LDS byte offset of 16-byte chunk c (0..7) of row r in a [rows][64 bf16] tile.  The chunk
+// index is XOR-swizzled with (r & 7) ^ (r >> 3 & 1): the 16 rows that 16 lanes read with the
+// same chunk index then occupy 16 distinct 16-byte bank groups whether the LDS serves 8 or
+// 16 lanes of a 128-bit read per cycle.
+static __device__ __forceinline__ int swz(int r, int c) {
+  return r * 128 + ((c ^ (r & 7) ^ ((r >> 3) & 1)) << 4);
+}
 
 // Decode 32 MXFP4 codes (16 bytes) with E8M0 byte s into 32 bf16 (four 16-byte chunks).
-static __device__ __forceinline__ void decode_fp4x32(const uint4 q, uint32_t s, uint4 out[4]) {
+static __device__ __forceinline__ void decode_fp4x32(const u32x4 q, uint32_t s, u32x4 out[4]) {
   const float scale = __uint_as_float(s << 23);   // 2^(s-127), s in [1, 254]
-  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scale, 0);
-    bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scale, 1);
-    bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scale, 2);
-    bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scale, 3);
-    out[i].x = __builtin_bit_cast(uint32_t, p0);
-    out[i].y = __builtin_bit_cast(uint32_t, p1);
-    out[i].z = __builtin_bit_cast(uint32_t, p2);
-    out[i].w = __builtin_bit_cast(uint32_t, p3);
+    const uint32_t w = q[i];
+    out[i] = u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3))};
   }
 }
 
 // ------------------------------------------------------------------------------ kernel
 // MODE 1: mlp1 (+SwiGLU), MODE 2: mlp2 (+bias, gate).  FMT 0: bf16 weights, 1: MXFP4.
+//
+// Per-thread load assignment is fixed for the whole K loop: thread t moves 16-byte chunk
+// t + i * THREADS of the A tile (row = chunk / 8, column chunk = chunk % 8) and likewise of
+// the B tile, so a wave moves eight whole 128-byte row segments per instruction.  Sources
+// are kept as 32-bit element offsets (or -1 for rows outside the group / columns outside
+// the matrix, which load zeros) so nothing leaves registers.
 template <int MODE, int FMT, class C>
 __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, TH = C::THREADS;
@@ -160,6 +167,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
   constexpr int B_CH = (FMT == 0) ? BN * 8 : BN * 2;        // bf16: 8 chunks/row; fp4: 2 x 16 B codes/row
   constexpr int B_IT = (B_CH + TH - 1) / TH;
   constexpr int PN = BN / 2;                                // mlp1: pairs per tile
+  constexpr int WP = PN / C::WAVES_N;                       // mlp1: pairs per wave
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
 
@@ -191,111 +199,67 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
   const int K = p.K;
   const int nk = K / BK;
 
-  // ---- per-thread global sources (fixed across K steps)
-  const uint16_t* a_src[A_IT];
-  const uint16_t* a_lo_src[A_IT];
+  // ---- per-thread sources: element offsets (A: from p.a / p.a_lo; B: from the expert's
+  // weight block), -1 = zero fill
+  int a_off[A_IT];
 #pragma unroll
   for (int i = 0; i < A_IT; ++i) {
     const int ch = tid + i * TH;
     const int r = ch >> 3, c = ch & 7;
-    a_src[i] = nullptr;
-    a_lo_src[i] = nullptr;
+    a_off[i] = -1;
     if (r < rows) {
       if (MODE == 1) {
         const int asg = p.perm[gbase + r];
-        if ((unsigned)asg < (unsigned)p.A) a_src[i] = p.a + (size_t)(asg / p.k) * K + c * 8;
+        if ((unsigned)asg < (unsigned)p.A) a_off[i] = (asg / p.k) * K + c * 8;
       } else {
-        a_src[i] = p.a + (size_t)(gbase + r) * K + c * 8;
-        if (AP == 2) a_lo_src[i] = p.a_lo + (size_t)(gbase + r) * K + c * 8;
+        a_off[i] = (gbase + r) * K + c * 8;
       }
     }
   }
-  // weight row of tile row rr
-  auto wrow_of = [&](int rr, bool& ok) -> int {
+  int b_off[B_IT];   // bf16: element offset within the expert; fp4: byte offset of the codes
+  int s_off[B_IT];   // fp4: byte offset of the scale byte within the expert's scales
+#pragma unroll
+  for (int i = 0; i < B_IT; ++i) {
+    const int ch = tid + i * TH;
+    b_off[i] = -1;
+    s_off[i] = 0;
+    const int rr = (FMT == 0) ? (ch >> 3) : (ch >> 1);
+    const int c = (FMT == 0) ? (ch & 7) : (ch & 1);
+    int wrow;
+    bool ok;
     if (MODE == 1) {
       const int q = rr < PN ? rr : rr - PN;
       const int f = n_tile * PN + q;
       ok = f < p.F;
-      return rr < PN ? f : p.F + f;
+      wrow = rr < PN ? f : p.F + f;
     } else {
-      const int o = n_tile * BN + rr;
-      ok = o < p.N;
-      return o;
+      wrow = n_tile * BN + rr;
+      ok = wrow < p.N;
     }
-  };
-  const uint8_t* b_src[B_IT];
-  const uint8_t* b_scale[B_IT];
-#pragma unroll
-  for (int i = 0; i < B_IT; ++i) {
-    const int ch = tid + i * TH;
-    b_src[i] = nullptr;
-    b_scale[i] = nullptr;
-    if (ch < B_CH) {
+    if (ch < B_CH && ok) {
       if (FMT == 0) {
-        const int rr = ch >> 3, c = ch & 7;
-        bool ok;
-        const int wrow = wrow_of(rr, ok);
-        if (ok) b_src[i] = p.w + ((size_t)e * p.N + wrow) * K * 2 + c * 16;
+        b_off[i] = wrow * K + c * 8;
       } else {
-        const int rr = ch >> 1, c = ch & 1;
-        bool ok;
-        const int wrow = wrow_of(rr, ok);
-        if (ok) {
-          const size_t row = (size_t)e * p.N + wrow;
-          b_src[i] = p.w + row * (K / 2) + c * 16;
-          b_scale[i] = p.w + (size_t)p.E * p.N * (K / 2) + row * (K / 32) + c;
-        }
+        b_off[i] = wrow * (K / 2) + c * 16;
+        s_off[i] = wrow * (K / 32) + c;
       }
     }
   }
+  const uint16_t* a_base = p.a;
+  const uint16_t* a_lo_base = p.a_lo;
+  const uint8_t* w_e;        // expert e's weight block (bf16: [N][K]; fp4: codes [N][K/2])
+  const uint8_t* s_e = nullptr;
+  if (FMT == 0) {
+    w_e = p.w + (size_t)e * p.N * K * 2;
+  } else {
+    w_e = p.w + (size_t)e * p.N * (K / 2);
+    s_e = p.w + (size_t)p.E * p.N * (K / 2) + (size_t)e * p.N * (K / 32);
+  }
 
-  uint4 ra[AP][A_IT];
-  uint4 rb[B_IT];
+  u32x4 ra[AP][A_IT];
+  u32x4 rb[B_IT];
   uint32_t rs[B_IT];
-  const uint4 zero4 = {0u, 0u, 0u, 0u};
-
-  auto load_global = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < A_IT; ++i) {
-      ra[0][i] = a_src[i] ? *(const uint4*)(a_src[i] + kt * BK) : zero4;
-      if (AP == 2) ra[AP - 1][i] = a_lo_src[i] ? *(const uint4*)(a_lo_src[i] + kt * BK) : zero4;
-    }
-#pragma unroll
-    for (int i = 0; i < B_IT; ++i) {
-      if (FMT == 0) {
-        rb[i] = b_src[i] ? *(const uint4*)(b_src[i] + kt * BK * 2) : zero4;
-      } else {
-        rb[i] = b_src[i] ? *(const uint4*)(b_src[i] + kt * (BK / 2)) : zero4;
-        rs[i] = b_scale[i] ? (uint32_t)b_scale[i][kt * (BK / 32)] : 127u;
-      }
-    }
-  };
-  auto store_lds = [&](int stage) {
-    uint8_t* sa = smem + stage * STAGE;
-    uint8_t* sb = sa + AP * A_TILE;
-#pragma unroll
-    for (int pa = 0; pa < AP; ++pa)
-#pragma unroll
-      for (int i = 0; i < A_IT; ++i) {
-        const int ch = tid + i * TH;
-        *(uint4*)(sa + pa * A_TILE + swz(ch >> 3, ch & 7)) = ra[pa][i];
-      }
-#pragma unroll
-    for (int i = 0; i < B_IT; ++i) {
-      const int ch = tid + i * TH;
-      if (ch < B_CH) {
-        if (FMT == 0) {
-          *(uint4*)(sb + swz(ch >> 3, ch & 7)) = rb[i];
-        } else {
-          uint4 d[4];
-          decode_fp4x32(rb[i], rs[i], d);
-          const int rr = ch >> 1, c = ch & 1;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) *(uint4*)(sb + swz(rr, c * 4 + j)) = d[j];
-        }
-      }
-    }
-  };
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
   f32x4 acc[FM][FN];
 #pragma unroll
@@ -304,22 +268,65 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // B-tile row of this wave's fragment j
-  auto b_row = [&](int j) -> int {
-    if (MODE == 1) {
-      constexpr int WP = PN / C::WAVES_N;          // pairs per wave
-      return (j < FN / 2) ? wn * WP + j * 16 : PN + wn * WP + (j - FN / 2) * 16;
-    } else {
-      return wn * C::WTN + j * 16;
-    }
-  };
+  int brow[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    if (MODE == 1)
+      brow[j] = (j < FN / 2) ? wn * WP + j * 16 : PN + wn * WP + (j - FN / 2) * 16;
+    else
+      brow[j] = wn * C::WTN + j * 16;
+    brow[j] += lane & 15;
+  }
+  const int arow0 = wm * C::WTM + (lane & 15);
 
-  load_global(0);
-  store_lds(0);
+#define MOE_LOAD_GLOBAL(kt)                                                                      \
+  do {                                                                                           \
+    _Pragma("unroll") for (int i = 0; i < A_IT; ++i) {                                           \
+      ra[0][i] = a_off[i] >= 0 ? *(const u32x4*)(a_base + a_off[i] + (kt) * BK) : zero4;        \
+      if (AP == 2)                                                                               \
+        ra[AP - 1][i] = a_off[i] >= 0 ? *(const u32x4*)(a_lo_base + a_off[i] + (kt) * BK) : zero4; \
+    }                                                                                            \
+    _Pragma("unroll") for (int i = 0; i < B_IT; ++i) {                                           \
+      if (FMT == 0) {                                                                            \
+        rb[i] = b_off[i] >= 0 ? *(const u32x4*)(w_e + 2 * (b_off[i] + (kt) * BK)) : zero4;       \
+      } else {                                                                                   \
+        rb[i] = b_off[i] >= 0 ? *(const u32x4*)(w_e + b_off[i] + (kt) * (BK / 2)) : zero4;       \
+        rs[i] = b_off[i] >= 0 ? (uint32_t)s_e[s_off[i] + (kt) * (BK / 32)] : 127u;              \
+      }                                                                                          \
+    }                                                                                            \
+  } while (0)
+
+#define MOE_STORE_LDS(stage)                                                                     \
+  do {                                                                                           \
+    uint8_t* sa_ = smem + (stage) * STAGE;                                                       \
+    uint8_t* sb_ = sa_ + AP * A_TILE;                                                            \
+    _Pragma("unroll") for (int pa = 0; pa < AP; ++pa)                                            \
+    _Pragma("unroll") for (int i = 0; i < A_IT; ++i) {                                           \
+      const int ch = tid + i * TH;                                                               \
+      *(u32x4*)(sa_ + pa * A_TILE + swz(ch >> 3, ch & 7)) = ra[pa][i];                           \
+    }                                                                                            \
+    _Pragma("unroll") for (int i = 0; i < B_IT; ++i) {                                           \
+      const int ch = tid + i * TH;                                                               \
+      if (ch < B_CH) {                                                                           \
+        if (FMT == 0) {                                                                          \
+          *(u32x4*)(sb_ + swz(ch >> 3, ch & 7)) = rb[i];                                         \
+        } else {                                                                                 \
+          u32x4 d_[4];                                                                           \
+          decode_fp4x32(rb[i], rs[i], d_);                                                       \
+          _Pragma("unroll") for (int j = 0; j < 4; ++j)                                          \
+            *(u32x4*)(sb_ + swz(ch >> 1, (ch & 1) * 4 + j)) = d_[j];                             \
+        }                                                                                        \
+      }                                                                                          \
+    }                                                                                            \
+  } while (0)
+
+  MOE_LOAD_GLOBAL(0);
+  MOE_STORE_LDS(0);
   __syncthreads();
 
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) load_global(kt + 1);
+    if (kt + 1 < nk) MOE_LOAD_GLOBAL(kt + 1);
     const uint8_t* sa = smem + cur * STAGE;
     const uint8_t* sb = sa + AP * A_TILE;
 #pragma unroll
@@ -330,15 +337,9 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int pa = 0; pa < AP; ++pa)
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const int r = wm * C::WTM + i * 16 + (lane & 15);
-          fa[pa][i] = *(const bf16x8*)(sa + pa * A_TILE + swz(r, cc));
-        }
+        for (int i = 0; i < FM; ++i) fa[pa][i] = *(const bf16x8*)(sa + pa * A_TILE + swz(arow0 + i * 16, cc));
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int r = b_row(j) + (lane & 15);
-        fb[j] = *(const bf16x8*)(sb + swz(r, cc));
-      }
+      for (int j = 0; j < FN; ++j) fb[j] = *(const bf16x8*)(sb + swz(brow[j], cc));
 #pragma unroll
       for (int pa = 0; pa < AP; ++pa)
 #pragma unroll
@@ -347,14 +348,15 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
           for (int j = 0; j < FN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[pa][i], fb[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) store_lds(cur ^ 1);
+    if (kt + 1 < nk) MOE_STORE_LDS(cur ^ 1);
     __syncthreads();
   }
+#undef MOE_LOAD_GLOBAL
+#undef MOE_STORE_LDS
 
   // ---- epilogue
   const uint16_t* bias = p.bias + (size_t)e * p.N;
   if (MODE == 1) {
-    constexpr int WP = PN / C::WAVES_N;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll

@@ -10,6 +10,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 enum Stage { ST_ROUTER = 0, ST_TOPK = 1, ST_PERMUTE = 2, ST_MLP1 = 3, ST_MLP2 = 4, ST_COMBINE = 5 };
 
