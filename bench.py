@@ -201,6 +201,8 @@ def main():
     ap.add_argument("--workload", default="C2", help="C2 (default), C3, C4, C5, X1, X2")
     ap.add_argument("--all", action="store_true", help="one line per target workload: C2 C3 X1 X2")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 3 plain device copies of MIB MiB (reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the MoE block is built and timed on a single MI355X; "
@@ -210,6 +212,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
+        return
     names = ["C2", "C3", "X1", "X2"] if args.all else [args.workload]
     for i, name in enumerate(names):
         res = bench_workload(name, args.steps, args.warmup, with_cpu=(not args.no_cpu) and i == 0)

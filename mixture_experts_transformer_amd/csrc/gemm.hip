@@ -41,25 +41,83 @@ namespace moe {
 constexpr float SWIGLU_ALPHA = 1.702f;
 constexpr float SWIGLU_LIMIT = 7.0f;
 
-template <int BM_, int BN_, int WM_, int WN_>
+template <int BM_, int BN_, int WM_, int WN_, int NS_, int BK_>
 struct Tile {
   static constexpr int BM = BM_;      // routed rows per tile
   static constexpr int BN = BN_;      // weight rows per tile (mlp1: gate + linear halves)
-  static constexpr int BK = 64;       // K per pipeline step (2 MFMA K-steps of 32)
+  static constexpr int BK = BK_;      // K per pipeline stage (32 or 64)
+  static constexpr int CPR = BK_ / 8; // 16-byte chunks per bf16 row segment
+  static constexpr int NS = NS_;      // LDS stages; NS - 1 K steps are in flight
   static constexpr int WAVES_M = WM_;
   static constexpr int WAVES_N = WN_;
-  static constexpr int THREADS = 64 * WM_ * WN_;
+  static constexpr int NW = WM_ * WN_;
+  static constexpr int THREADS = 64 * NW;
   static constexpr int WTM = BM / WM_;
   static constexpr int WTN = BN / WN_;
-  static constexpr int FM = WTM / 16;
-  static constexpr int FN = WTN / 16;
-  static_assert(BM % (16 * WM_) == 0 && BN % (16 * WN_) == 0, "tile/wave mismatch");
+  static constexpr int FM = WTM / 32;  // 32x32 output blocks per wave
+  static constexpr int FN = WTN / 32;
+  static_assert(BM % (32 * WM_) == 0 && BN % (32 * WN_) == 0, "tile/wave mismatch");
+  static_assert(BK == 32 || BK == 64, "K step");
+  static_assert((BM * CPR) % 64 == 0 && (BN * CPR) % 64 == 0, "copy granularity");
 };
 
-// Configuration 0: few rows per expert (weight streaming); 1: many rows (matrix-core bound).
-using SmallTile = Tile<32, 64, 1, 2>;
-using LargeTile = Tile<256, 192, 2, 2>;
-using LargeTileHiLo = Tile<128, 192, 2, 2>;   // mlp2 with the two h parts
+// Tile shapes.  Few rows per expert (weight streaming, full 128-byte row segments per
+// stage) and many rows (matrix-core bound).  The defaults below are the tuned shapes; the
+// macros let a build try others without touching the kernel.
+#ifndef MOE_S_BM
+#define MOE_S_BM 64
+#endif
+#ifndef MOE_S_BN1
+#define MOE_S_BN1 128
+#endif
+#ifndef MOE_S_BN2
+#define MOE_S_BN2 128
+#endif
+#ifndef MOE_S_WM
+#define MOE_S_WM 1
+#endif
+#ifndef MOE_S_WN
+#define MOE_S_WN 4
+#endif
+#ifndef MOE_S_NS
+#define MOE_S_NS 3
+#endif
+#ifndef MOE_S_NS4
+#define MOE_S_NS4 4
+#endif
+#ifndef MOE_L_BM
+#define MOE_L_BM 192
+#endif
+#ifndef MOE_L_BN
+#define MOE_L_BN 192
+#endif
+#ifndef MOE_L_WM
+#define MOE_L_WM 2
+#endif
+#ifndef MOE_L_WN
+#define MOE_L_WN 2
+#endif
+#ifndef MOE_L_NS
+#define MOE_L_NS 3
+#endif
+#ifndef MOE_L_NS4
+#define MOE_L_NS4 3
+#endif
+#ifndef MOE_L_NSH
+#define MOE_L_NSH 2                 // mlp2 with MXFP4 weights (two A parts per stage)
+#endif
+#ifndef MOE_S_NSH
+#define MOE_S_NSH 3
+#endif
+#ifndef MOE_L_BK
+#define MOE_L_BK 64
+#endif
+template <int MODE, int FMT> using SmallTile =
+    Tile<MOE_S_BM, (MODE == 1 ? MOE_S_BN1 : MOE_S_BN2), MOE_S_WM, MOE_S_WN,
+         (FMT == 0 ? MOE_S_NS : (MODE == 1 ? MOE_S_NS4 : MOE_S_NSH)), 64>;
+template <int MODE, int FMT> using LargeTile =
+    Tile<MOE_L_BM, MOE_L_BN, MOE_L_WM, MOE_L_WN, (FMT == 0 ? MOE_L_NS : (MODE == 1 ? MOE_L_NS4 : MOE_L_NSH)),
+         MOE_L_BK>;
 
 struct GemmArgs {
   const uint16_t* a;        // mlp1: x [T][K]; mlp2: h (hi) [A][K]
@@ -125,51 +183,99 @@ static __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ off
   return true;
 }
 
-// LDS byte offset of 16-byte chunk c (0..7) of row r in a [rows][64 bf16] tile.  The chunk
-// index is XOR-swizzled with (r & 7) ^ (r >> 3 & 1): the 16 rows that 16 lanes read with the
-// same chunk index then occupy 16 distinct 16-byte bank groups whether the LDS serves 8 or
-// 16 lanes of a 128-bit read per cycle.
-static __device__ __forceinline__ int swz(int r, int c) {
-  return r * 128 + ((c ^ (r & 7) ^ ((r >> 3) & 1)) << 4);
+// LDS layout of a bf16 operand stage: [rows][BK] with the 16-byte chunks of a row
+// XOR-swizzled by row bits, which spreads the rows one chunk index touches over the banks.
+template <int CPR>
+static __device__ __forceinline__ int swz_pos(int r, int c) {
+  if (CPR == 8) return c ^ (r & 7) ^ ((r >> 3) & 1);
+  return c ^ ((r >> 1) & 3) ^ ((r >> 3) & 1);
+}
+template <int CPR>
+static __device__ __forceinline__ int swz(int r, int c) { return r * (CPR * 16) + (swz_pos<CPR>(r, c) << 4); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct global -> LDS copy of 16 bytes per lane: lane L fills LDS bytes [dst + 16 L, +16).
+static __device__ __forceinline__ void dma16(const void* src, uint8_t* dst_wave) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst_wave, 16, 0, 0);
+}
+// Direct global -> LDS copy of one dword per lane: lane L fills LDS bytes [dst + 4 L, +4).
+static __device__ __forceinline__ void dma4(const void* src, uint8_t* dst_wave) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst_wave, 4, 0, 0);
 }
 
-// Decode 32 MXFP4 codes (16 bytes) with E8M0 byte s into 32 bf16 (four 16-byte chunks).
-static __device__ __forceinline__ void decode_fp4x32(const u32x4 q, uint32_t s, u32x4 out[4]) {
-  const float scale = __uint_as_float(s << 23);   // 2^(s-127), s in [1, 254]
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t w = q[i];
-    out[i] = u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0)),
-                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1)),
-                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2)),
-                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3))};
-  }
+// s_waitcnt vmcnt(N) with the LDS/export counters left alone (gfx9 encoding).
+template <int N>
+static __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+static __device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (0x7 << 4) | (0 << 8));
+}
+// Workgroup barrier without a memory fence: the waits above say what must have landed.
+// The empty asm statements keep the compiler from moving memory accesses across it.
+static __device__ __forceinline__ void barrier_nofence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Decode 8 MXFP4 codes (one dword: element 2i in the low nibble of byte i) times the
+// power-of-two scale into one bf16x8 matrix-core operand.
+static __device__ __forceinline__ bf16x8 decode_fp4x8(uint32_t codes, float scale) {
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
+  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
 // ------------------------------------------------------------------------------ kernel
 // MODE 1: mlp1 (+SwiGLU), MODE 2: mlp2 (+bias, gate).  FMT 0: bf16 weights, 1: MXFP4.
 //
-// Per-thread load assignment is fixed for the whole K loop: thread t moves 16-byte chunk
-// t + i * THREADS of the A tile (row = chunk / 8, column chunk = chunk % 8) and likewise of
-// the B tile, so a wave moves eight whole 128-byte row segments per instruction.  Sources
-// are kept as 32-bit element offsets (or -1 for rows outside the group / columns outside
-// the matrix, which load zeros) so nothing leaves registers.
+// Matrix-core mapping: v_mfma_f32_32x32x16_bf16 (measured on gfx950 at about twice the
+// sustained rate of the 16x16x32 form).  Lane l feeds row l & 31 and K elements
+// 8 (l >> 5) .. +7 of each operand; output register r of lane l is
+// C[8 (r >> 2) + 4 (l >> 5) + (r & 3)][l & 31].
+//
+// Pipeline: K advances BK at a time through an NS-stage ring in LDS.  Each stage is filled
+// by direct global->LDS copies (no registers), issued NS-1 steps before it is consumed;
+// before consuming a stage every wave waits until its own copies for that stage have
+// landed (vmcnt) and the workgroup meets at a fence-free barrier, which also frees the
+// stage consumed in the previous step for the next copy.
+//
+// Copy assignment: a bf16 stage is rows x BK with 16-byte chunks; copy instruction i fills
+// LDS bytes [1024 i, 1024 i + 1024), lane L landing at row 1024 i / (16 CPR) + L / CPR,
+// swizzle position L % CPR, i.e. it fetches the logical chunk stored at that position.
+// Instructions are dealt to waves round robin.  Rows past the group's end or the matrix
+// edge copy a valid row (their results are never stored).  An MXFP4 B stage holds BK/2 code
+// bytes per row and, per row, the aligned dword holding the stage's scale byte(s).
 template <int MODE, int FMT, class C>
 __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
-  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, TH = C::THREADS;
+  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, CPR = C::CPR, NS = C::NS, NW = C::NW;
   constexpr int FM = C::FM, FN = C::FN;
+  constexpr int KS = BK / 16;                               // MFMA K steps per stage
   constexpr int AP = (MODE == 2 && FMT == 1) ? 2 : 1;      // A parts (h hi, h lo)
-  constexpr int A_TILE = BM * BK * 2;                       // bytes per A part
-  constexpr int B_TILE = BN * BK * 2;
-  constexpr int STAGE = AP * A_TILE + B_TILE;
-  constexpr int A_IT = BM * 8 / TH;                         // 16-byte chunks per thread per part
-  static_assert(BM * 8 % TH == 0, "A chunks must divide evenly");
-  constexpr int B_CH = (FMT == 0) ? BN * 8 : BN * 2;        // bf16: 8 chunks/row; fp4: 2 x 16 B codes/row
-  constexpr int B_IT = (B_CH + TH - 1) / TH;
+  constexpr int ROWB = CPR * 16;                            // bytes per bf16 row segment
+  constexpr int A_BYTES = BM * ROWB;                        // per A part per stage
+  constexpr int CODEB = BK / 2;                             // MXFP4 code bytes per row per stage
+  constexpr int B_CODE_BYTES = (FMT == 0) ? BN * ROWB : BN * CODEB;
+  constexpr int B_SCALE_BYTES = (FMT == 0) ? 0 : BN * 4;
+  constexpr int STAGE = AP * A_BYTES + B_CODE_BYTES + B_SCALE_BYTES;
+  constexpr int ROWS_PER_CP = 1024 / ROWB;                  // bf16 rows per copy instruction
+  constexpr int NA = AP * (BM / ROWS_PER_CP);               // copy instructions per stage: A
+  constexpr int NB = (FMT == 0) ? BN / ROWS_PER_CP : BN * CODEB / 1024;   //   B codes
+  constexpr int NSC = (FMT == 0) ? 0 : BN / 64;             //   B scales
+  constexpr int NI = NA + NB + NSC;
+  constexpr int PER_WAVE = (NI + NW - 1) / NW;              // copy slots per wave per stage
+  constexpr int CNT_HI = (NI + NW - 1) / NW;                // copies per stage of waves w < NI % NW
+  constexpr int CNT_LO = NI / NW;                           // ... of the others
   constexpr int PN = BN / 2;                                // mlp1: pairs per tile
-  constexpr int WP = PN / C::WAVES_N;                       // mlp1: pairs per wave
+  static_assert(BN % 32 == 0, "mlp1 pairs gate and linear rows inside 32-row groups");
+  static_assert(FMT == 0 || (BN * CODEB) % 1024 == 0, "MXFP4 copy granularity");
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -199,183 +305,191 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
   const int K = p.K;
   const int nk = K / BK;
 
-  // ---- per-thread sources: element offsets (A: from p.a / p.a_lo; B: from the expert's
-  // weight block), -1 = zero fill
-  int a_off[A_IT];
-#pragma unroll
-  for (int i = 0; i < A_IT; ++i) {
-    const int ch = tid + i * TH;
-    const int r = ch >> 3, c = ch & 7;
-    a_off[i] = -1;
-    if (r < rows) {
-      if (MODE == 1) {
-        const int asg = p.perm[gbase + r];
-        if ((unsigned)asg < (unsigned)p.A) a_off[i] = (asg / p.k) * K + c * 8;
-      } else {
-        a_off[i] = (gbase + r) * K + c * 8;
-      }
-    }
-  }
-  int b_off[B_IT];   // bf16: element offset within the expert; fp4: byte offset of the codes
-  int s_off[B_IT];   // fp4: byte offset of the scale byte within the expert's scales
-#pragma unroll
-  for (int i = 0; i < B_IT; ++i) {
-    const int ch = tid + i * TH;
-    b_off[i] = -1;
-    s_off[i] = 0;
-    const int rr = (FMT == 0) ? (ch >> 3) : (ch >> 1);
-    const int c = (FMT == 0) ? (ch & 7) : (ch & 1);
-    int wrow;
-    bool ok;
-    if (MODE == 1) {
-      const int q = rr < PN ? rr : rr - PN;
-      const int f = n_tile * PN + q;
-      ok = f < p.F;
-      wrow = rr < PN ? f : p.F + f;
-    } else {
-      wrow = n_tile * BN + rr;
-      ok = wrow < p.N;
-    }
-    if (ch < B_CH && ok) {
-      if (FMT == 0) {
-        b_off[i] = wrow * K + c * 8;
-      } else {
-        b_off[i] = wrow * (K / 2) + c * 16;
-        s_off[i] = wrow * (K / 32) + c;
-      }
-    }
-  }
-  const uint16_t* a_base = p.a;
-  const uint16_t* a_lo_base = p.a_lo;
-  const uint8_t* w_e;        // expert e's weight block (bf16: [N][K]; fp4: codes [N][K/2])
+  const uint8_t* w_e;
   const uint8_t* s_e = nullptr;
+  size_t s_e_off = 0;                       // byte offset of expert e's scales in p.w
   if (FMT == 0) {
     w_e = p.w + (size_t)e * p.N * K * 2;
   } else {
     w_e = p.w + (size_t)e * p.N * (K / 2);
-    s_e = p.w + (size_t)p.E * p.N * (K / 2) + (size_t)e * p.N * (K / 32);
+    s_e_off = (size_t)p.E * p.N * (K / 2) + (size_t)e * p.N * (K / 32);
+    s_e = p.w + s_e_off;
+  }
+  // tile row -> weight row, clamped into the matrix.  mlp1 tiles interleave the halves in
+  // 16-row groups: rows 32 j .. 32 j + 15 are gate rows of pairs 16 j .. 16 j + 15 and rows
+  // 32 j + 16 .. 32 j + 31 the linear rows of the same pairs, so every 32-column output
+  // fragment holds matching gate and linear columns in lanes n and n + 16.
+#define MOE_WROW(rr)                                                                             \
+  (MODE == 1 ? ((((rr) & 16) ? p.F : 0) + min(n_tile * PN + ((rr) >> 5) * 16 + ((rr) & 15), p.F - 1)) \
+             : min(n_tile * BN + (rr), p.N - 1))
+
+  // ---- this wave's copy slots: global byte source for K step 0 and LDS offset in a stage
+  const uint8_t* src[PER_WAVE];
+  int dst[PER_WAVE];
+#pragma unroll
+  for (int j = 0; j < PER_WAVE; ++j) {
+    const int i = wave + j * NW;
+    src[j] = p.w;
+    dst[j] = 0;
+    if (i < NA) {
+      const int part = i / (BM / ROWS_PER_CP);
+      const int ii = i % (BM / ROWS_PER_CP);
+      const int r = ii * ROWS_PER_CP + lane / CPR;
+      const int c = swz_pos<CPR>(r, lane % CPR);           // logical chunk at this position
+      const int rc = min(r, rows - 1);
+      size_t elem;
+      if (MODE == 1) {
+        int asg = p.perm[gbase + rc];
+        asg = ((unsigned)asg < (unsigned)p.A) ? asg : 0;
+        elem = (size_t)(asg / p.k) * K;
+      } else {
+        elem = (size_t)(gbase + rc) * K;
+      }
+      const uint16_t* base = part == 0 ? p.a : p.a_lo;
+      src[j] = (const uint8_t*)(base + elem + c * 8);
+      dst[j] = part * A_BYTES + ii * 1024;
+    } else if (i < NA + NB) {
+      const int ii = i - NA;
+      if (FMT == 0) {
+        const int r = ii * ROWS_PER_CP + lane / CPR;
+        const int c = swz_pos<CPR>(r, lane % CPR);
+        src[j] = w_e + ((size_t)MOE_WROW(r) * K + c * 8) * 2;
+      } else {
+        constexpr int LPR = CODEB / 16;                    // lanes per row (1 or 2)
+        const int r = ii * (64 / LPR) + lane / LPR;
+        src[j] = w_e + (size_t)MOE_WROW(r) * (K / 2) + (lane % LPR) * 16;
+      }
+      dst[j] = AP * A_BYTES + ii * 1024;
+    } else if (i < NI) {
+      const int ii = i - NA - NB;
+      const int r = ii * 64 + lane;
+      src[j] = s_e + (size_t)MOE_WROW(r) * (K / 32);      // scale byte (r, block 0)
+      dst[j] = AP * A_BYTES + B_CODE_BYTES + ii * 256;
+    }
   }
 
-  u32x4 ra[AP][A_IT];
-  u32x4 rb[B_IT];
-  uint32_t rs[B_IT];
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-
-  f32x4 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // B-tile row of this wave's fragment j
-  int brow[FN];
-#pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    if (MODE == 1)
-      brow[j] = (j < FN / 2) ? wn * WP + j * 16 : PN + wn * WP + (j - FN / 2) * 16;
-    else
-      brow[j] = wn * C::WTN + j * 16;
-    brow[j] += lane & 15;
-  }
-  const int arow0 = wm * C::WTM + (lane & 15);
-
-#define MOE_LOAD_GLOBAL(kt)                                                                      \
+  // issue the copies of K step kt into stage slot
+#define MOE_ISSUE(kt, slot)                                                                      \
   do {                                                                                           \
-    _Pragma("unroll") for (int i = 0; i < A_IT; ++i) {                                           \
-      ra[0][i] = a_off[i] >= 0 ? *(const u32x4*)(a_base + a_off[i] + (kt) * BK) : zero4;        \
-      if (AP == 2)                                                                               \
-        ra[AP - 1][i] = a_off[i] >= 0 ? *(const u32x4*)(a_lo_base + a_off[i] + (kt) * BK) : zero4; \
-    }                                                                                            \
-    _Pragma("unroll") for (int i = 0; i < B_IT; ++i) {                                           \
-      if (FMT == 0) {                                                                            \
-        rb[i] = b_off[i] >= 0 ? *(const u32x4*)(w_e + 2 * (b_off[i] + (kt) * BK)) : zero4;       \
-      } else {                                                                                   \
-        rb[i] = b_off[i] >= 0 ? *(const u32x4*)(w_e + b_off[i] + (kt) * (BK / 2)) : zero4;       \
-        rs[i] = b_off[i] >= 0 ? (uint32_t)s_e[s_off[i] + (kt) * (BK / 32)] : 127u;              \
-      }                                                                                          \
-    }                                                                                            \
-  } while (0)
-
-#define MOE_STORE_LDS(stage)                                                                     \
-  do {                                                                                           \
-    uint8_t* sa_ = smem + (stage) * STAGE;                                                       \
-    uint8_t* sb_ = sa_ + AP * A_TILE;                                                            \
-    _Pragma("unroll") for (int pa = 0; pa < AP; ++pa)                                            \
-    _Pragma("unroll") for (int i = 0; i < A_IT; ++i) {                                           \
-      const int ch = tid + i * TH;                                                               \
-      *(u32x4*)(sa_ + pa * A_TILE + swz(ch >> 3, ch & 7)) = ra[pa][i];                           \
-    }                                                                                            \
-    _Pragma("unroll") for (int i = 0; i < B_IT; ++i) {                                           \
-      const int ch = tid + i * TH;                                                               \
-      if (ch < B_CH) {                                                                           \
-        if (FMT == 0) {                                                                          \
-          *(u32x4*)(sb_ + swz(ch >> 3, ch & 7)) = rb[i];                                         \
+    _Pragma("unroll") for (int j = 0; j < PER_WAVE; ++j) {                                       \
+      const int i_ = wave + j * NW;                                                              \
+      if (i_ < NI) {                                                                             \
+        uint8_t* d_ = smem + (slot) * STAGE + dst[j];                                            \
+        if (FMT == 1 && i_ >= NA + NB) {                                                         \
+          const uintptr_t sp_ = (uintptr_t)(src[j] + (kt) * (BK / 32));                          \
+          dma4((const void*)(sp_ & ~(uintptr_t)3), d_);                                          \
+        } else if (FMT == 1 && i_ >= NA) {                                                       \
+          dma16(src[j] + (size_t)(kt) * CODEB, d_);                                              \
         } else {                                                                                 \
-          u32x4 d_[4];                                                                           \
-          decode_fp4x32(rb[i], rs[i], d_);                                                       \
-          _Pragma("unroll") for (int j = 0; j < 4; ++j)                                          \
-            *(u32x4*)(sb_ + swz(ch >> 1, (ch & 1) * 4 + j)) = d_[j];                             \
+          dma16(src[j] + (size_t)(kt) * ROWB, d_);                                               \
         }                                                                                        \
       }                                                                                          \
     }                                                                                            \
   } while (0)
 
-  MOE_LOAD_GLOBAL(0);
-  MOE_STORE_LDS(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) MOE_LOAD_GLOBAL(kt + 1);
-    const uint8_t* sa = smem + cur * STAGE;
-    const uint8_t* sb = sa + AP * A_TILE;
+  f32x16 acc[FM][FN];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int cc = ks * 4 + (lane >> 4);
-      bf16x8 fa[AP][FM];
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  // B-tile row of this lane for fragment j; byte of its scale dword for K step 0
+  int brow[FN];
+  int sbyte[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    brow[j] = wn * C::WTN + j * 32 + (lane & 31);
+    sbyte[j] = 0;
+    if (FMT == 1) sbyte[j] = (int)((s_e_off + (size_t)MOE_WROW(brow[j]) * (K / 32)) & 3);
+  }
+  const int arow0 = wm * C::WTM + (lane & 31);
+  const int kg = lane >> 5;                 // which 8-element half of a 16-wide K step
+
+  // prologue: NS - 1 stages in flight
+#pragma unroll
+  for (int s0 = 0; s0 < NS - 1; ++s0)
+    if (s0 < nk) MOE_ISSUE(s0, s0);
+
+  const bool hi_cnt = (NI % NW == 0) || wave < (NI % NW);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int slot = kt % NS;
+    // this wave's copies for step kt have landed: at most (NS - 2) later steps outstanding
+    if (kt + NS - 2 < nk) {
+      if (hi_cnt) wait_vmcnt<CNT_HI * (NS - 2)>();
+      else wait_vmcnt<CNT_LO * (NS - 2)>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    wait_lgkmcnt0();
+    barrier_nofence();
+    if (kt + NS - 1 < nk) MOE_ISSUE(kt + NS - 1, (kt + NS - 1) % NS);
+
+    const uint8_t* sa = smem + slot * STAGE;
+    const uint8_t* sb = sa + AP * A_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int cc = ks * 2 + kg;           // chunk (8 K elements) this lane feeds
       bf16x8 fb[FN];
 #pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        if (FMT == 0) {
+          fb[j] = *(const bf16x8*)(sb + swz<CPR>(brow[j], cc));
+        } else {
+          const uint32_t codes = *(const uint32_t*)(sb + brow[j] * CODEB + cc * 4);
+          const uint32_t sc = sb[B_CODE_BYTES + brow[j] * 4 + ((sbyte[j] + kt * (BK / 32) + (ks * 16) / 32) & 3)];
+          fb[j] = decode_fp4x8(codes, __uint_as_float(sc << 23));
+        }
+      }
+      bf16x8 fa[AP][FM];
+#pragma unroll
       for (int pa = 0; pa < AP; ++pa)
 #pragma unroll
-        for (int i = 0; i < FM; ++i) fa[pa][i] = *(const bf16x8*)(sa + pa * A_TILE + swz(arow0 + i * 16, cc));
+        for (int i = 0; i < FM; ++i) fa[pa][i] = *(const bf16x8*)(sa + pa * A_BYTES + swz<CPR>(arow0 + i * 32, cc));
 #pragma unroll
-      for (int j = 0; j < FN; ++j) fb[j] = *(const bf16x8*)(sb + swz(brow[j], cc));
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int pa = 0; pa < AP; ++pa)
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
+        for (int pa = 0; pa < AP; ++pa)
 #pragma unroll
           for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[pa][i], fb[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[pa][i], fb[j], acc[i][j], 0, 0, 0);
+      // every LDS read of the step ahead of its matrix instructions: the reads overlap and
+      // the waits before the MFMAs can be partial
+      __builtin_amdgcn_sched_group_barrier(0x100, (FMT == 0 ? FN : 2 * FN) + AP * FM, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, AP * FM * FN, 0);
     }
-    if (kt + 1 < nk) MOE_STORE_LDS(cur ^ 1);
-    __syncthreads();
   }
-#undef MOE_LOAD_GLOBAL
-#undef MOE_STORE_LDS
+#undef MOE_ISSUE
+#undef MOE_WROW
 
-  // ---- epilogue
+  // ---- epilogue: output register q of fragment (i, j) is row 8 (q >> 2) + 4 kg + (q & 3)
   const uint16_t* bias = p.bias + (size_t)e * p.N;
   if (MODE == 1) {
+    // lane n < 16 of a fragment holds the gate column of pair 16 j' + n, lane n + 16 the
+    // linear column of the same pair: one lane exchange pairs them
+    const bool gate_lane = (lane & 16) == 0;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+    for (int j = 0; j < FN; ++j) {
+      const int f = n_tile * PN + (wn * C::WTN + j * 32) / 2 + (lane & 15);
+      const float bg = (f < p.F) ? bf16_to_f32(bias[f]) : 0.f;
+      const float bl = (f < p.F) ? bf16_to_f32(bias[p.F + f]) : 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rl = wm * C::WTM + i * 16 + 4 * (lane >> 4) + r;
-        if (rl >= rows) continue;
-        const size_t prow = (size_t)(gbase + rl) * p.F;
+      for (int i = 0; i < FM; ++i) {
 #pragma unroll
-        for (int j = 0; j < FN / 2; ++j) {
-          const int f = n_tile * PN + wn * WP + j * 16 + (lane & 15);
-          if (f >= p.F) continue;
-          const float ug = acc[i][j][r] + bf16_to_f32(bias[f]);
-          const float ul = acc[i][j + FN / 2][r] + bf16_to_f32(bias[p.F + f]);
+        for (int q = 0; q < 16; ++q) {
+          const float other = __shfl_xor(acc[i][j][q], 16);
+          const int rl = wm * C::WTM + i * 32 + 8 * (q >> 2) + 4 * kg + (q & 3);
+          if (!gate_lane || rl >= rows || f >= p.F) continue;
+          const float ug = acc[i][j][q] + bg;
+          const float ul = other + bl;
           const float gc = fminf(ug, SWIGLU_LIMIT);
           const float lc = fminf(fmaxf(ul, -SWIGLU_LIMIT), SWIGLU_LIMIT);
           const float hv = gc / (1.0f + __expf(-SWIGLU_ALPHA * gc)) * (lc + 1.0f);
           const uint32_t hi = f32_to_bf16_rne(hv);
-          p.h[prow + f] = (uint16_t)hi;
-          if (FMT == 1) p.h_lo[prow + f] = (uint16_t)f32_to_bf16_rne(hv - bf16_to_f32(hi));
+          const size_t at = (size_t)(gbase + rl) * p.F + f;
+          p.h[at] = (uint16_t)hi;
+          if (FMT == 1) p.h_lo[at] = (uint16_t)f32_to_bf16_rne(hv - bf16_to_f32(hi));
         }
       }
     }
@@ -383,8 +497,8 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rl = wm * C::WTM + i * 16 + 4 * (lane >> 4) + r;
+      for (int q = 0; q < 16; ++q) {
+        const int rl = wm * C::WTM + i * 32 + 8 * (q >> 2) + 4 * kg + (q & 3);
         if (rl >= rows) continue;
         const int a = p.perm[gbase + rl];
         if ((unsigned)a >= (unsigned)p.A) continue;
@@ -392,8 +506,8 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
         float* yrow = p.y + (size_t)a * p.N;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-          const int o = n_tile * BN + wn * C::WTN + j * 16 + (lane & 15);
-          if (o < p.N) yrow[o] = gw * (acc[i][j][r] + bf16_to_f32(bias[o]));
+          const int o = n_tile * BN + wn * C::WTN + j * 32 + (lane & 31);
+          if (o < p.N) yrow[o] = gw * (acc[i][j][q] + bf16_to_f32(bias[o]));
         }
       }
     }
@@ -416,10 +530,19 @@ static int max_m_tiles(int64_t A, int E) {
 template <int MODE, int FMT, class C>
 static hipError_t launch_gemm(GemmArgs g, int64_t A, hipStream_t st) {
   g.max_m_tiles = max_m_tiles<C>(A, g.E);
+  g.n_tiles = MODE == 1 ? (g.F + C::BN / 2 - 1) / (C::BN / 2) : (g.N + C::BN - 1) / C::BN;
   const int64_t total = (int64_t)g.max_m_tiles * g.n_tiles;
   const int64_t blocks = (total + 7) / 8 * 8;
   hipLaunchKernelGGL((grouped_gemm_kernel<MODE, FMT, C>), dim3((unsigned)blocks), dim3(C::THREADS), 0, st, g);
   return hipGetLastError();
+}
+
+template <int MODE>
+static hipError_t launch_any(const GemmArgs& g, int fmt, int cfg, int64_t A, hipStream_t st) {
+  if (fmt == 0)
+    return cfg == 0 ? launch_gemm<MODE, 0, SmallTile<MODE, 0>>(g, A, st) : launch_gemm<MODE, 0, LargeTile<MODE, 0>>(g, A, st);
+  return cfg == 0 ? launch_gemm<MODE, 1, SmallTile<MODE, 1>>(g, A, st)
+                  : launch_gemm<MODE, 1, LargeTile<MODE, 1>>(g, A, st);
 }
 
 hipError_t launch_mlp1(const ExpertArgs& a, int cfg, hipStream_t st) {
@@ -429,12 +552,7 @@ hipError_t launch_mlp1(const ExpertArgs& a, int cfg, hipStream_t st) {
   g.E = a.E; g.k = a.k; g.K = a.D; g.N = 2 * a.F; g.F = a.F;
   const int64_t A = (int64_t)a.T * a.k;
   g.A = (int)A;
-  if (cfg == 0) {
-    g.n_tiles = (a.F + SmallTile::BN / 2 - 1) / (SmallTile::BN / 2);
-    return a.fmt == 0 ? launch_gemm<1, 0, SmallTile>(g, A, st) : launch_gemm<1, 1, SmallTile>(g, A, st);
-  }
-  g.n_tiles = (a.F + LargeTile::BN / 2 - 1) / (LargeTile::BN / 2);
-  return a.fmt == 0 ? launch_gemm<1, 0, LargeTile>(g, A, st) : launch_gemm<1, 1, LargeTile>(g, A, st);
+  return launch_any<1>(g, a.fmt, cfg, A, st);
 }
 
 hipError_t launch_mlp2(const ExpertArgs& a, int cfg, hipStream_t st) {
@@ -444,16 +562,7 @@ hipError_t launch_mlp2(const ExpertArgs& a, int cfg, hipStream_t st) {
   g.E = a.E; g.k = a.k; g.K = a.F; g.N = a.D; g.F = a.F;
   const int64_t A = (int64_t)a.T * a.k;
   g.A = (int)A;
-  if (cfg == 0) {
-    g.n_tiles = (a.D + SmallTile::BN - 1) / SmallTile::BN;
-    return a.fmt == 0 ? launch_gemm<2, 0, SmallTile>(g, A, st) : launch_gemm<2, 1, SmallTile>(g, A, st);
-  }
-  if (a.fmt == 0) {
-    g.n_tiles = (a.D + LargeTile::BN - 1) / LargeTile::BN;
-    return launch_gemm<2, 0, LargeTile>(g, A, st);
-  }
-  g.n_tiles = (a.D + LargeTileHiLo::BN - 1) / LargeTileHiLo::BN;
-  return launch_gemm<2, 1, LargeTileHiLo>(g, A, st);
+  return launch_any<2>(g, a.fmt, cfg, A, st);
 }
 
 // ------------------------------------------------------------------------------ combine

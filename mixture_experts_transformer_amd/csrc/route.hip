@@ -163,6 +163,7 @@ __global__ __launch_bounds__(64 * TK_WAVES) void topk_kernel(
     v[i] = -INFINITY;
     if (live[i]) {
       double s = 0.0;
+#pragma unroll 8
       for (int q = 0; q < ksplit; ++q) s += partial[((size_t)q * T + t) * E + e];
       s += bf16_bits_to_f64(br[e]);
       v[i] = (float)s;   // round to nearest even
