@@ -41,8 +41,9 @@ namespace moe {
 constexpr float SWIGLU_ALPHA = 1.702f;
 constexpr float SWIGLU_LIMIT = 7.0f;
 
-template <int BM_, int BN_, int WM_, int WN_, int NS_, int BK_>
+template <int BM_, int BN_, int WM_, int WN_, int NS_, int BK_, bool STREAM_ = false>
 struct Tile {
+  static constexpr bool STREAM = STREAM_;   // weight-streaming tile order
   static constexpr int BM = BM_;      // routed rows per tile
   static constexpr int BN = BN_;      // weight rows per tile (mlp1: gate + linear halves)
   static constexpr int BK = BK_;      // K per pipeline stage (32 or 64)
@@ -85,6 +86,9 @@ struct Tile {
 #ifndef MOE_S_NS4
 #define MOE_S_NS4 4
 #endif
+#ifndef MOE_S_STREAM
+#define MOE_S_STREAM 1
+#endif
 #ifndef MOE_L_BM
 #define MOE_L_BM 192
 #endif
@@ -114,7 +118,7 @@ struct Tile {
 #endif
 template <int MODE, int FMT> using SmallTile =
     Tile<MOE_S_BM, (MODE == 1 ? MOE_S_BN1 : MOE_S_BN2), MOE_S_WM, MOE_S_WN,
-         (FMT == 0 ? MOE_S_NS : (MODE == 1 ? MOE_S_NS4 : MOE_S_NSH)), 64>;
+         (FMT == 0 ? MOE_S_NS : (MODE == 1 ? MOE_S_NS4 : MOE_S_NSH)), 64, MOE_S_STREAM != 0>;
 template <int MODE, int FMT> using LargeTile =
     Tile<MOE_L_BM, MOE_L_BN, MOE_L_WM, MOE_L_WN, (FMT == 0 ? MOE_L_NS : (MODE == 1 ? MOE_L_NS4 : MOE_L_NSH)),
          MOE_L_BK>;
@@ -283,18 +287,29 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
   const int wm = wave / C::WAVES_N;
   const int wn = wave % C::WAVES_N;
 
-  // ---- tile order: XCD-contiguous ranges of the linear id, then groups of GM row tiles
-  const int nb = gridDim.x;                 // multiple of 8
-  const int lin = (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3);
+  // ---- tile order.  Streaming tiles (few rows per expert): column tiles fastest, so
+  // workgroups launched together read neighbouring rows of one expert's weights.  Large
+  // tiles: XCD-contiguous ranges of the linear id, then groups of GM row tiles, so the
+  // workgroups sharing an XCD's L2 share operand tiles.
   const int total = p.max_m_tiles * p.n_tiles;
-  if (lin >= total) return;
-  constexpr int GM = 4;
-  const int gsize = GM * p.n_tiles;
-  const int g = lin / gsize;
-  const int first_m = g * GM;
-  const int gm = min(p.max_m_tiles - first_m, GM);
-  const int m_tile = first_m + (lin % gsize) % gm;
-  const int n_tile = (lin % gsize) / gm;
+  int m_tile, n_tile;
+  if (C::STREAM) {
+    const int lin = blockIdx.x;
+    if (lin >= total) return;
+    m_tile = lin / p.n_tiles;
+    n_tile = lin % p.n_tiles;
+  } else {
+    const int nb = gridDim.x;               // multiple of 8
+    const int lin = (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3);
+    if (lin >= total) return;
+    constexpr int GM = 4;
+    const int gsize = GM * p.n_tiles;
+    const int g = lin / gsize;
+    const int first_m = g * GM;
+    const int gm = min(p.max_m_tiles - first_m, GM);
+    m_tile = first_m + (lin % gsize) % gm;
+    n_tile = (lin % gsize) / gm;
+  }
 
   int e, row0, cnt;
   if (!find_tile<BM>(p.offsets, p.E, m_tile, e, row0, cnt)) return;
