@@ -236,25 +236,46 @@ static __device__ __forceinline__ bf16x8 decode_fp4x8(uint32_t codes, float scal
 }
 
 // ------------------------------------------------------------------------------ kernel
+// s_waitcnt needs an immediate: dispatch a wave-uniform count to the matching wait.
+static __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
+  switch (n) {
+#define MOE_W(k) case k: wait_vmcnt<k>(); break;
+    MOE_W(0) MOE_W(1) MOE_W(2) MOE_W(3) MOE_W(4) MOE_W(5) MOE_W(6) MOE_W(7)
+    MOE_W(8) MOE_W(9) MOE_W(10) MOE_W(11) MOE_W(12) MOE_W(13) MOE_W(14) MOE_W(15)
+    MOE_W(16) MOE_W(17) MOE_W(18) MOE_W(19) MOE_W(20) MOE_W(21) MOE_W(22) MOE_W(23)
+    MOE_W(24) MOE_W(25) MOE_W(26) MOE_W(27) MOE_W(28) MOE_W(29) MOE_W(30) MOE_W(31)
+    MOE_W(32) MOE_W(33) MOE_W(34) MOE_W(35) MOE_W(36) MOE_W(37) MOE_W(38) MOE_W(39)
+    MOE_W(40) MOE_W(41) MOE_W(42) MOE_W(43) MOE_W(44) MOE_W(45) MOE_W(46) MOE_W(47)
+#undef MOE_W
+    default: wait_vmcnt<0>(); break;
+  }
+}
+
 // MODE 1: mlp1 (+SwiGLU), MODE 2: mlp2 (+bias, gate).  FMT 0: bf16 weights, 1: MXFP4.
 //
 // Matrix-core mapping: v_mfma_f32_32x32x16_bf16 (measured on gfx950 at about twice the
-// sustained rate of the 16x16x32 form).  Lane l feeds row l & 31 and K elements
-// 8 (l >> 5) .. +7 of each operand; output register r of lane l is
-// C[8 (r >> 2) + 4 (l >> 5) + (r & 3)][l & 31].
+// sustained rate of the 16x16x32 form).  In MFMA step ks of a stage, lane l feeds row
+// l & 31 and the 8 K elements  g BK/2 + 8 ks .. +7  (g = l >> 5) of each operand: each lane
+// half covers one contiguous half of the stage's K range.  Output register r of lane l is
+// C[8 (r >> 2) + 4 g + (r & 3)][l & 31].
 //
-// Pipeline: K advances BK at a time through an NS-stage ring in LDS.  Each stage is filled
-// by direct global->LDS copies (no registers), issued NS-1 steps before it is consumed;
-// before consuming a stage every wave waits until its own copies for that stage have
-// landed (vmcnt) and the workgroup meets at a fence-free barrier, which also frees the
-// stage consumed in the previous step for the next copy.
+// Pipeline: K advances BK at a time through an NS-stage ring in LDS, filled by direct
+// global->LDS copies (no registers) issued NS-1 steps before use.  Before consuming a stage
+// every wave waits until its own copies for it have landed (vmcnt counts, in issue order,
+// exactly the copies issued after them) and the workgroup meets at a fence-free barrier,
+// which also frees the stage consumed in the previous step.
 //
-// Copy assignment: a bf16 stage is rows x BK with 16-byte chunks; copy instruction i fills
-// LDS bytes [1024 i, 1024 i + 1024), lane L landing at row 1024 i / (16 CPR) + L / CPR,
-// swizzle position L % CPR, i.e. it fetches the logical chunk stored at that position.
-// Instructions are dealt to waves round robin.  Rows past the group's end or the matrix
-// edge copy a valid row (their results are never stored).  An MXFP4 B stage holds BK/2 code
-// bytes per row and, per row, the aligned dword holding the stage's scale byte(s).
+// bf16 stage: rows x BK with 16-byte chunks; copy instruction i fills LDS bytes
+// [1024 i, +1024), lane L landing at row 1024 i / (16 CPR) + L / CPR, swizzle position
+// L % CPR.  Rows past the group's end or the matrix edge copy a valid row (their results
+// are never stored).
+//
+// MXFP4 B: full 128-byte row segments are what HBM serves efficiently, and one stage's
+// codes are only 32 bytes per row, so the codes have their own ring of two super-stages of
+// four stages (128 code bytes = 256 K elements per row, 16-byte chunks XOR-swizzled by
+// row & 7).  A super-stage's copies are issued just before the group of its first stage,
+// so that group's completion implies the codes'.  Each stage also copies, per row, the
+// aligned dword holding the stage's two scale bytes.
 template <int MODE, int FMT, class C>
 __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, CPR = C::CPR, NS = C::NS, NW = C::NW;
@@ -263,23 +284,27 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
   constexpr int AP = (MODE == 2 && FMT == 1) ? 2 : 1;      // A parts (h hi, h lo)
   constexpr int ROWB = CPR * 16;                            // bytes per bf16 row segment
   constexpr int A_BYTES = BM * ROWB;                        // per A part per stage
-  constexpr int CODEB = BK / 2;                             // MXFP4 code bytes per row per stage
-  constexpr int B_CODE_BYTES = (FMT == 0) ? BN * ROWB : BN * CODEB;
-  constexpr int B_SCALE_BYTES = (FMT == 0) ? 0 : BN * 4;
-  constexpr int STAGE = AP * A_BYTES + B_CODE_BYTES + B_SCALE_BYTES;
+  static_assert(FMT == 0 || BK == 64, "MXFP4 staging assumes 64-wide K steps");
+  constexpr int SUPER = 4;                                  // stages per MXFP4 code super-stage
+  constexpr int NSB = 2;                                    // code super-stage slots
+  static_assert(FMT == 0 || 4 * NSB > NS + 2, "code ring too short for the stage ring");
+  constexpr int B_STAGE_BYTES = (FMT == 0) ? BN * ROWB : BN * 4;   // bf16 B tile, or scale dwords
+  constexpr int STAGE = AP * A_BYTES + B_STAGE_BYTES;
+  constexpr int CODE_SLOT = BN * 128;
+  constexpr int CODE_BYTES = (FMT == 1) ? NSB * CODE_SLOT : 0;
   constexpr int ROWS_PER_CP = 1024 / ROWB;                  // bf16 rows per copy instruction
-  constexpr int NA = AP * (BM / ROWS_PER_CP);               // copy instructions per stage: A
-  constexpr int NB = (FMT == 0) ? BN / ROWS_PER_CP : BN * CODEB / 1024;   //   B codes
-  constexpr int NSC = (FMT == 0) ? 0 : BN / 64;             //   B scales
-  constexpr int NI = NA + NB + NSC;
-  constexpr int PER_WAVE = (NI + NW - 1) / NW;              // copy slots per wave per stage
-  constexpr int CNT_HI = (NI + NW - 1) / NW;                // copies per stage of waves w < NI % NW
-  constexpr int CNT_LO = NI / NW;                           // ... of the others
+  constexpr int NA = AP * (BM / ROWS_PER_CP);               // per stage: A copies
+  constexpr int NBS = (FMT == 0) ? BN / ROWS_PER_CP : BN / 64;   // per stage: B copies / scale copies
+  constexpr int NG = NA + NBS;                              // copies per stage group
+  constexpr int NC = (FMT == 1) ? BN * 128 / 1024 : 0;      // copies per code super-stage
+  constexpr int PW_G = (NG + NW - 1) / NW;
+  constexpr int PW_C = (NC + NW - 1) / NW + (NC == 0 ? 1 : 0);
   constexpr int PN = BN / 2;                                // mlp1: pairs per tile
-  static_assert(BN % 32 == 0, "mlp1 pairs gate and linear rows inside 32-row groups");
-  static_assert(FMT == 0 || (BN * CODEB) % 1024 == 0, "MXFP4 copy granularity");
+  static_assert(BN % 32 == 0 && (BM * CPR) % 64 == 0 && (BN * CPR) % 64 == 0, "copy granularity");
+  static_assert(FMT == 0 || BN % 64 == 0, "scale copies cover 64 rows");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE + CODE_BYTES];
+  uint8_t* const codes_lds = smem + NS * STAGE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -338,14 +363,14 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
   (MODE == 1 ? ((((rr) & 16) ? p.F : 0) + min(n_tile * PN + ((rr) >> 5) * 16 + ((rr) & 15), p.F - 1)) \
              : min(n_tile * BN + (rr), p.N - 1))
 
-  // ---- this wave's copy slots: global byte source for K step 0 and LDS offset in a stage
-  const uint8_t* src[PER_WAVE];
-  int dst[PER_WAVE];
+  // ---- this wave's copy slots: global byte source for K step 0 and LDS offset
+  const uint8_t* gsrc[PW_G];
+  int gdst[PW_G];
 #pragma unroll
-  for (int j = 0; j < PER_WAVE; ++j) {
+  for (int j = 0; j < PW_G; ++j) {
     const int i = wave + j * NW;
-    src[j] = p.w;
-    dst[j] = 0;
+    gsrc[j] = p.w;
+    gdst[j] = 0;
     if (i < NA) {
       const int part = i / (BM / ROWS_PER_CP);
       const int ii = i % (BM / ROWS_PER_CP);
@@ -361,45 +386,67 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
         elem = (size_t)(gbase + rc) * K;
       }
       const uint16_t* base = part == 0 ? p.a : p.a_lo;
-      src[j] = (const uint8_t*)(base + elem + c * 8);
-      dst[j] = part * A_BYTES + ii * 1024;
-    } else if (i < NA + NB) {
+      gsrc[j] = (const uint8_t*)(base + elem + c * 8);
+      gdst[j] = part * A_BYTES + ii * 1024;
+    } else if (i < NG) {
       const int ii = i - NA;
       if (FMT == 0) {
         const int r = ii * ROWS_PER_CP + lane / CPR;
         const int c = swz_pos<CPR>(r, lane % CPR);
-        src[j] = w_e + ((size_t)MOE_WROW(r) * K + c * 8) * 2;
+        gsrc[j] = w_e + ((size_t)MOE_WROW(r) * K + c * 8) * 2;
+        gdst[j] = AP * A_BYTES + ii * 1024;
       } else {
-        constexpr int LPR = CODEB / 16;                    // lanes per row (1 or 2)
-        const int r = ii * (64 / LPR) + lane / LPR;
-        src[j] = w_e + (size_t)MOE_WROW(r) * (K / 2) + (lane % LPR) * 16;
+        const int r = ii * 64 + lane;
+        gsrc[j] = s_e + (size_t)MOE_WROW(r) * (K / 32);   // scale byte (r, block 0)
+        gdst[j] = AP * A_BYTES + ii * 256;
       }
-      dst[j] = AP * A_BYTES + ii * 1024;
-    } else if (i < NI) {
-      const int ii = i - NA - NB;
-      const int r = ii * 64 + lane;
-      src[j] = s_e + (size_t)MOE_WROW(r) * (K / 32);      // scale byte (r, block 0)
-      dst[j] = AP * A_BYTES + B_CODE_BYTES + ii * 256;
     }
   }
+  const uint8_t* csrc[PW_C];
+  int cdst[PW_C];
+#pragma unroll
+  for (int j = 0; j < PW_C; ++j) {
+    const int i = wave + j * NW;
+    csrc[j] = p.w;
+    cdst[j] = 0;
+    if (FMT == 1 && i < NC) {
+      const int r = i * 8 + lane / 8;
+      const int c = (lane % 8) ^ (r & 7);
+      csrc[j] = w_e + (size_t)MOE_WROW(r) * (K / 2) + c * 16;
+      cdst[j] = i * 1024;
+    }
+  }
+  // copies this wave issues per stage group and per code super-stage
+  const int g_cnt = NG / NW + (wave < NG % NW ? 1 : 0);
+  const int c_cnt = NC / NW + (wave < NC % NW ? 1 : 0);
 
-  // issue the copies of K step kt into stage slot
-#define MOE_ISSUE(kt, slot)                                                                      \
+#define MOE_ISSUE_GROUP(kt, slot)                                                                \
   do {                                                                                           \
-    _Pragma("unroll") for (int j = 0; j < PER_WAVE; ++j) {                                       \
+    _Pragma("unroll") for (int j = 0; j < PW_G; ++j) {                                           \
       const int i_ = wave + j * NW;                                                              \
-      if (i_ < NI) {                                                                             \
-        uint8_t* d_ = smem + (slot) * STAGE + dst[j];                                            \
-        if (FMT == 1 && i_ >= NA + NB) {                                                         \
-          const uintptr_t sp_ = (uintptr_t)(src[j] + (kt) * (BK / 32));                          \
+      if (i_ < NG) {                                                                             \
+        uint8_t* d_ = smem + (slot) * STAGE + gdst[j];                                           \
+        if (FMT == 1 && i_ >= NA) {                                                              \
+          const uintptr_t sp_ = (uintptr_t)(gsrc[j] + (kt) * (BK / 32));                         \
           dma4((const void*)(sp_ & ~(uintptr_t)3), d_);                                          \
-        } else if (FMT == 1 && i_ >= NA) {                                                       \
-          dma16(src[j] + (size_t)(kt) * CODEB, d_);                                              \
         } else {                                                                                 \
-          dma16(src[j] + (size_t)(kt) * ROWB, d_);                                               \
+          dma16(gsrc[j] + (size_t)(kt) * ROWB, d_);                                              \
         }                                                                                        \
       }                                                                                          \
     }                                                                                            \
+  } while (0)
+#define MOE_ISSUE_CODES(sk)                                                                      \
+  do {                                                                                           \
+    _Pragma("unroll") for (int j = 0; j < PW_C; ++j) {                                           \
+      const int i_ = wave + j * NW;                                                              \
+      if (FMT == 1 && i_ < NC) dma16(csrc[j] + (size_t)(sk) * 128, codes_lds + ((sk) % NSB) * CODE_SLOT + cdst[j]); \
+    }                                                                                            \
+  } while (0)
+  // everything a K step needs, codes first so the group's completion implies theirs
+#define MOE_ISSUE(kt)                                                                            \
+  do {                                                                                           \
+    if (FMT == 1 && (kt) % SUPER == 0) MOE_ISSUE_CODES((kt) / SUPER);                            \
+    MOE_ISSUE_GROUP(kt, (kt) % NS);                                                              \
   } while (0)
 
   f32x16 acc[FM][FN];
@@ -420,42 +467,49 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
     if (FMT == 1) sbyte[j] = (int)((s_e_off + (size_t)MOE_WROW(brow[j]) * (K / 32)) & 3);
   }
   const int arow0 = wm * C::WTM + (lane & 31);
-  const int kg = lane >> 5;                 // which 8-element half of a 16-wide K step
+  const int kg = lane >> 5;                 // which half of the stage's K range this lane feeds
 
   // prologue: NS - 1 stages in flight
 #pragma unroll
   for (int s0 = 0; s0 < NS - 1; ++s0)
-    if (s0 < nk) MOE_ISSUE(s0, s0);
+    if (s0 < nk) MOE_ISSUE(s0);
 
-  const bool hi_cnt = (NI % NW == 0) || wave < (NI % NW);
   for (int kt = 0; kt < nk; ++kt) {
     const int slot = kt % NS;
-    // this wave's copies for step kt have landed: at most (NS - 2) later steps outstanding
-    if (kt + NS - 2 < nk) {
-      if (hi_cnt) wait_vmcnt<CNT_HI * (NS - 2)>();
-      else wait_vmcnt<CNT_LO * (NS - 2)>();
-    } else {
-      wait_vmcnt<0>();
+    // copies issued after step kt's group: groups of steps kt+1 .. last issued, plus the
+    // code super-stages issued with them
+    {
+      const int later = min(nk - 1, kt + NS - 2) - kt;
+      int n = later * g_cnt;
+      if (FMT == 1) n += c_cnt * ((kt + later) / SUPER - kt / SUPER);
+      wait_vmcnt_dyn(n);
     }
     wait_lgkmcnt0();
     barrier_nofence();
-    if (kt + NS - 1 < nk) MOE_ISSUE(kt + NS - 1, (kt + NS - 1) % NS);
+    if (kt + NS - 1 < nk) MOE_ISSUE(kt + NS - 1);
 
     const uint8_t* sa = smem + slot * STAGE;
     const uint8_t* sb = sa + AP * A_BYTES;
+    u32x4 q4[FN];                           // MXFP4: this lane's 32 codes per fragment
+    float scl[FN];
+    if (FMT == 1) {
+      const uint8_t* cs = codes_lds + ((kt / SUPER) % NSB) * CODE_SLOT;
+      const int chunk = 2 * (kt % SUPER) + kg;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        q4[j] = *(const u32x4*)(cs + brow[j] * 128 + ((chunk ^ (brow[j] & 7)) << 4));
+        const uint32_t sc = sb[brow[j] * 4 + ((sbyte[j] + 2 * kt + kg) & 3)];
+        scl[j] = __uint_as_float(sc << 23);
+      }
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int cc = ks * 2 + kg;           // chunk (8 K elements) this lane feeds
+      const int cc = kg * KS + ks;          // chunk (8 K elements) this lane feeds
       bf16x8 fb[FN];
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        if (FMT == 0) {
-          fb[j] = *(const bf16x8*)(sb + swz<CPR>(brow[j], cc));
-        } else {
-          const uint32_t codes = *(const uint32_t*)(sb + brow[j] * CODEB + cc * 4);
-          const uint32_t sc = sb[B_CODE_BYTES + brow[j] * 4 + ((sbyte[j] + kt * (BK / 32) + (ks * 16) / 32) & 3)];
-          fb[j] = decode_fp4x8(codes, __uint_as_float(sc << 23));
-        }
+        if (FMT == 0) fb[j] = *(const bf16x8*)(sb + swz<CPR>(brow[j], cc));
+        else fb[j] = decode_fp4x8(q4[j][ks], scl[j]);
       }
       bf16x8 fa[AP][FM];
 #pragma unroll
@@ -471,11 +525,13 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[pa][i], fb[j], acc[i][j], 0, 0, 0);
       // every LDS read of the step ahead of its matrix instructions: the reads overlap and
       // the waits before the MFMAs can be partial
-      __builtin_amdgcn_sched_group_barrier(0x100, (FMT == 0 ? FN : 2 * FN) + AP * FM, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, (FMT == 0 ? FN : 0) + AP * FM, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, AP * FM * FN, 0);
     }
   }
 #undef MOE_ISSUE
+#undef MOE_ISSUE_GROUP
+#undef MOE_ISSUE_CODES
 #undef MOE_WROW
 
   // ---- epilogue: output register q of fragment (i, j) is row 8 (q >> 2) + 4 kg + (q & 3)

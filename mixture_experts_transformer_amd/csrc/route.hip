@@ -35,9 +35,10 @@ constexpr int RT_CHUNK = 32;          // K elements per MFMA group (8 steps of K
 int router_ksplit(int64_t T, int64_t D) {
   const int64_t chunks = D / RT_CHUNK;
   const int64_t tiles = (T + 15) / 16;
-  // aim at ~2048 waves in flight; keep >= 2 chunks per split
+  // aim at ~2048 waves in flight; keep >= 6 chunks per split so the top-k kernel's
+  // sum over splits stays short
   int64_t ks = (2048 + tiles - 1) / tiles;
-  int64_t maxks = chunks / 2 > 0 ? chunks / 2 : 1;
+  int64_t maxks = chunks / 6 > 0 ? chunks / 6 : 1;
   if (ks > maxks) ks = maxks;
   if (ks < 1) ks = 1;
   return (int)ks;
