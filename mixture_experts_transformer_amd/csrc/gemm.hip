@@ -41,9 +41,10 @@ namespace moe {
 constexpr float SWIGLU_ALPHA = 1.702f;
 constexpr float SWIGLU_LIMIT = 7.0f;
 
-template <int BM_, int BN_, int WM_, int WN_, int NS_, int BK_, bool STREAM_ = false>
+template <int BM_, int BN_, int WM_, int WN_, int NS_, int BK_, bool STREAM_ = false, int PF_ = 0>
 struct Tile {
   static constexpr bool STREAM = STREAM_;   // weight-streaming tile order
+  static constexpr int PF = PF_;            // L2 prefetch distance in stages beyond the copies (0: off)
   static constexpr int BM = BM_;      // routed rows per tile
   static constexpr int BN = BN_;      // weight rows per tile (mlp1: gate + linear halves)
   static constexpr int BK = BK_;      // K per pipeline stage (32 or 64)
@@ -89,20 +90,26 @@ struct Tile {
 #ifndef MOE_S_STREAM
 #define MOE_S_STREAM 1
 #endif
+#ifndef MOE_S_PF
+#define MOE_S_PF 0
+#endif
+#ifndef MOE_L_PF
+#define MOE_L_PF 0
+#endif
 #ifndef MOE_L_BM
-#define MOE_L_BM 192
+#define MOE_L_BM 256
 #endif
 #ifndef MOE_L_BN
-#define MOE_L_BN 192
+#define MOE_L_BN 256
 #endif
 #ifndef MOE_L_WM
 #define MOE_L_WM 2
 #endif
 #ifndef MOE_L_WN
-#define MOE_L_WN 2
+#define MOE_L_WN 4
 #endif
 #ifndef MOE_L_NS
-#define MOE_L_NS 3
+#define MOE_L_NS 2
 #endif
 #ifndef MOE_L_NS4
 #define MOE_L_NS4 3
@@ -118,10 +125,26 @@ struct Tile {
 #endif
 template <int MODE, int FMT> using SmallTile =
     Tile<MOE_S_BM, (MODE == 1 ? MOE_S_BN1 : MOE_S_BN2), MOE_S_WM, MOE_S_WN,
-         (FMT == 0 ? MOE_S_NS : (MODE == 1 ? MOE_S_NS4 : MOE_S_NSH)), 64, MOE_S_STREAM != 0>;
-template <int MODE, int FMT> using LargeTile =
-    Tile<MOE_L_BM, MOE_L_BN, MOE_L_WM, MOE_L_WN, (FMT == 0 ? MOE_L_NS : (MODE == 1 ? MOE_L_NS4 : MOE_L_NSH)),
-         MOE_L_BK>;
+         (FMT == 0 ? MOE_S_NS : (MODE == 1 ? MOE_S_NS4 : MOE_S_NSH)), 64, MOE_S_STREAM != 0, MOE_S_PF>;
+#ifndef MOE_L4_BM
+#define MOE_L4_BM 192
+#endif
+#ifndef MOE_L4_BN
+#define MOE_L4_BN 192
+#endif
+#ifndef MOE_L4_WM
+#define MOE_L4_WM 2
+#endif
+#ifndef MOE_L4_WN
+#define MOE_L4_WN 2
+#endif
+template <int MODE, int FMT> struct LargeTileSel {
+  using type = Tile<MOE_L_BM, MOE_L_BN, MOE_L_WM, MOE_L_WN, MOE_L_NS, MOE_L_BK, false, MOE_L_PF>;
+};
+template <int MODE> struct LargeTileSel<MODE, 1> {
+  using type = Tile<MOE_L4_BM, MOE_L4_BN, MOE_L4_WM, MOE_L4_WN, (MODE == 1 ? MOE_L_NS4 : MOE_L_NSH), 64, false, MOE_L_PF>;
+};
+template <int MODE, int FMT> using LargeTile = typename LargeTileSel<MODE, FMT>::type;
 
 struct GemmArgs {
   const uint16_t* a;        // mlp1: x [T][K]; mlp2: h (hi) [A][K]
@@ -202,6 +225,11 @@ typedef __attribute__((address_space(3))) void lds_void;
 // Direct global -> LDS copy of 16 bytes per lane: lane L fills LDS bytes [dst + 16 L, +16).
 static __device__ __forceinline__ void dma16(const void* src, uint8_t* dst_wave) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)dst_wave, 16, 0, 0);
+}
+// Direct global -> LDS copy of one byte per lane (lane L fills the dword at dst + 4 L): used
+// only to pull a line into L2 ahead of its real copy, into a scratch area nobody reads.
+static __device__ __forceinline__ void dma1(const void* src, uint8_t* dst_wave) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst_wave, 1, 0, 0);
 }
 // Direct global -> LDS copy of one dword per lane: lane L fills LDS bytes [dst + 4 L, +4).
 static __device__ __forceinline__ void dma4(const void* src, uint8_t* dst_wave) {
@@ -303,8 +331,11 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
   static_assert(BN % 32 == 0 && (BM * CPR) % 64 == 0 && (BN * CPR) % 64 == 0, "copy granularity");
   static_assert(FMT == 0 || BN % 64 == 0, "scale copies cover 64 rows");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE + CODE_BYTES];
+  constexpr int PF = C::PF;
+  constexpr int JUNK = PF > 0 ? 256 : 0;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE + CODE_BYTES + JUNK];
   uint8_t* const codes_lds = smem + NS * STAGE;
+  uint8_t* const junk_lds = smem + NS * STAGE + CODE_BYTES;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -416,9 +447,52 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
       cdst[j] = i * 1024;
     }
   }
-  // copies this wave issues per stage group and per code super-stage
-  const int g_cnt = NG / NW + (wave < NG % NW ? 1 : 0);
-  const int c_cnt = NC / NW + (wave < NC % NW ? 1 : 0);
+  // L2 prefetch slots: one lane per 128-byte line of a stage (A rows, bf16 B rows), 64 lines
+  // per instruction; MXFP4 code lines are prefetched per super-stage
+  constexpr int NPA = (PF > 0) ? AP * BM / 64 : 0;
+  constexpr int NPB = (PF > 0) ? BN / 64 : 0;               // B rows (bf16) or code rows (MXFP4)
+  constexpr int PW_P = (NPA + NPB + NW - 1) / NW + 1;
+  const uint8_t* psrc[PW_P];
+  int pstep[PW_P];
+#pragma unroll
+  for (int j = 0; j < PW_P; ++j) {
+    const int i = wave + j * NW;
+    psrc[j] = p.w;
+    pstep[j] = 0;
+    if (i < NPA) {
+      const int part = i / (BM / 64);
+      const int r = (i % (BM / 64)) * 64 + lane;
+      const int rc = min(r, rows - 1);
+      size_t elem;
+      if (MODE == 1) {
+        int asg = p.perm[gbase + rc];
+        asg = ((unsigned)asg < (unsigned)p.A) ? asg : 0;
+        elem = (size_t)(asg / p.k) * K;
+      } else {
+        elem = (size_t)(gbase + rc) * K;
+      }
+      psrc[j] = (const uint8_t*)((part == 0 ? p.a : p.a_lo) + elem);
+      pstep[j] = ROWB;
+    } else if (i < NPA + NPB) {
+      const int r = (i - NPA) * 64 + lane;
+      if (FMT == 0) {
+        psrc[j] = w_e + (size_t)MOE_WROW(r) * K * 2;
+        pstep[j] = ROWB;
+      } else {
+        psrc[j] = w_e + (size_t)MOE_WROW(r) * (K / 2);
+        pstep[j] = -128;                      // code lines: one per super-stage
+      }
+    }
+  }
+  const int nkc = (nk + SUPER - 1) / SUPER;  // code super-stages
+
+  // every copy and prefetch this wave issues is counted; mark[slot] = count right after the
+  // stage group that filled the slot, so the wait for a stage is exact: vmcnt completes in
+  // issue order
+  int issued = 0;
+  int mark[NS];
+#pragma unroll
+  for (int q = 0; q < NS; ++q) mark[q] = 0;
 
 #define MOE_ISSUE_GROUP(kt, slot)                                                                \
   do {                                                                                           \
@@ -432,6 +506,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
         } else {                                                                                 \
           dma16(gsrc[j] + (size_t)(kt) * ROWB, d_);                                              \
         }                                                                                        \
+        ++issued;                                                                                \
       }                                                                                          \
     }                                                                                            \
   } while (0)
@@ -439,14 +514,36 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
   do {                                                                                           \
     _Pragma("unroll") for (int j = 0; j < PW_C; ++j) {                                           \
       const int i_ = wave + j * NW;                                                              \
-      if (FMT == 1 && i_ < NC) dma16(csrc[j] + (size_t)(sk) * 128, codes_lds + ((sk) % NSB) * CODE_SLOT + cdst[j]); \
+      if (FMT == 1 && i_ < NC) {                                                                 \
+        dma16(csrc[j] + (size_t)(sk) * 128, codes_lds + ((sk) % NSB) * CODE_SLOT + cdst[j]);    \
+        ++issued;                                                                                \
+      }                                                                                          \
     }                                                                                            \
   } while (0)
-  // everything a K step needs, codes first so the group's completion implies theirs
+  // L2 prefetch of step kt's lines (or, MXFP4, of code super-stage kt / SUPER when kt starts one)
+#define MOE_PREFETCH(kt)                                                                         \
+  do {                                                                                           \
+    _Pragma("unroll") for (int j = 0; j < PW_P; ++j) {                                           \
+      const int i_ = wave + j * NW;                                                              \
+      if (i_ < NPA + NPB) {                                                                      \
+        if (pstep[j] >= 0) {                                                                     \
+          dma1(psrc[j] + (size_t)(kt) * pstep[j], junk_lds);                                     \
+          ++issued;                                                                              \
+        } else if ((kt) % SUPER == 0 && (kt) / SUPER < nkc) {                                    \
+          dma1(psrc[j] + (size_t)((kt) / SUPER) * 128, junk_lds);                                \
+          ++issued;                                                                              \
+        }                                                                                        \
+      }                                                                                          \
+    }                                                                                            \
+  } while (0)
+  // everything a K step needs, codes first so the group's completion implies theirs; then the
+  // prefetch of the step PF stages further on
 #define MOE_ISSUE(kt)                                                                            \
   do {                                                                                           \
     if (FMT == 1 && (kt) % SUPER == 0) MOE_ISSUE_CODES((kt) / SUPER);                            \
     MOE_ISSUE_GROUP(kt, (kt) % NS);                                                              \
+    mark[(kt) % NS] = issued;                                                                    \
+    if (PF > 0 && (kt) + PF < nk) MOE_PREFETCH((kt) + PF);                                       \
   } while (0)
 
   f32x16 acc[FM][FN];
@@ -469,7 +566,10 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
   const int arow0 = wm * C::WTM + (lane & 31);
   const int kg = lane >> 5;                 // which half of the stage's K range this lane feeds
 
-  // prologue: NS - 1 stages in flight
+  // prologue: prefetch what the ring will need first, then NS - 1 stages in flight
+  if (PF > 0) {
+    for (int s0 = NS - 1; s0 < NS - 1 + PF && s0 < nk; ++s0) MOE_PREFETCH(s0);
+  }
 #pragma unroll
   for (int s0 = 0; s0 < NS - 1; ++s0)
     if (s0 < nk) MOE_ISSUE(s0);
@@ -478,12 +578,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
     const int slot = kt % NS;
     // copies issued after step kt's group: groups of steps kt+1 .. last issued, plus the
     // code super-stages issued with them
-    {
-      const int later = min(nk - 1, kt + NS - 2) - kt;
-      int n = later * g_cnt;
-      if (FMT == 1) n += c_cnt * ((kt + later) / SUPER - kt / SUPER);
-      wait_vmcnt_dyn(n);
-    }
+    wait_vmcnt_dyn(issued - mark[slot]);
     wait_lgkmcnt0();
     barrier_nofence();
     if (kt + NS - 1 < nk) MOE_ISSUE(kt + NS - 1);
