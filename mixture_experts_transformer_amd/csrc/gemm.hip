@@ -41,10 +41,9 @@ namespace moe {
 constexpr float SWIGLU_ALPHA = 1.702f;
 constexpr float SWIGLU_LIMIT = 7.0f;
 
-template <int BM_, int BN_, int WM_, int WN_, int NS_, int BK_, bool STREAM_ = false, int PF_ = 0>
+template <int BM_, int BN_, int WM_, int WN_, int NS_, int BK_, bool STREAM_ = false>
 struct Tile {
   static constexpr bool STREAM = STREAM_;   // weight-streaming tile order
-  static constexpr int PF = PF_;            // L2 prefetch distance in stages beyond the copies (0: off)
   static constexpr int BM = BM_;      // routed rows per tile
   static constexpr int BN = BN_;      // weight rows per tile (mlp1: gate + linear halves)
   static constexpr int BK = BK_;      // K per pipeline stage (32 or 64)
@@ -90,12 +89,6 @@ struct Tile {
 #ifndef MOE_S_STREAM
 #define MOE_S_STREAM 1
 #endif
-#ifndef MOE_S_PF
-#define MOE_S_PF 0
-#endif
-#ifndef MOE_L_PF
-#define MOE_L_PF 0
-#endif
 #ifndef MOE_L_BM
 #define MOE_L_BM 256
 #endif
@@ -125,7 +118,7 @@ struct Tile {
 #endif
 template <int MODE, int FMT> using SmallTile =
     Tile<MOE_S_BM, (MODE == 1 ? MOE_S_BN1 : MOE_S_BN2), MOE_S_WM, MOE_S_WN,
-         (FMT == 0 ? MOE_S_NS : (MODE == 1 ? MOE_S_NS4 : MOE_S_NSH)), 64, MOE_S_STREAM != 0, MOE_S_PF>;
+         (FMT == 0 ? MOE_S_NS : (MODE == 1 ? MOE_S_NS4 : MOE_S_NSH)), 64, MOE_S_STREAM != 0>;
 #ifndef MOE_L4_BM
 #define MOE_L4_BM 192
 #endif
@@ -139,10 +132,10 @@ template <int MODE, int FMT> using SmallTile =
 #define MOE_L4_WN 2
 #endif
 template <int MODE, int FMT> struct LargeTileSel {
-  using type = Tile<MOE_L_BM, MOE_L_BN, MOE_L_WM, MOE_L_WN, MOE_L_NS, MOE_L_BK, false, MOE_L_PF>;
+  using type = Tile<MOE_L_BM, MOE_L_BN, MOE_L_WM, MOE_L_WN, MOE_L_NS, MOE_L_BK, false>;
 };
 template <int MODE> struct LargeTileSel<MODE, 1> {
-  using type = Tile<MOE_L4_BM, MOE_L4_BN, MOE_L4_WM, MOE_L4_WN, (MODE == 1 ? MOE_L_NS4 : MOE_L_NSH), 64, false, MOE_L_PF>;
+  using type = Tile<MOE_L4_BM, MOE_L4_BN, MOE_L4_WM, MOE_L4_WN, (MODE == 1 ? MOE_L_NS4 : MOE_L_NSH), 64, false>;
 };
 template <int MODE, int FMT> using LargeTile = typename LargeTileSel<MODE, FMT>::type;
 
@@ -169,21 +162,25 @@ static __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 }
 static __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// Locate row tile m in the flat list of all experts' tiles (experts ascending, BM rows
-// each, the last tile of an expert possibly partial).  Wave-wide: lane l looks at
-// experts 4l..4l+3.  Returns false past the last tile.
+// Row tiles of all experts in one flat list (experts ascending, BM rows each, the last
+// tile of an expert possibly partial).  Wave-wide: lane l looks at experts 4l..4l+3; the
+// scan gives every lane the number of tiles before its experts and the total.
+struct TileScan {
+  int tl[4];        // tiles of this lane's experts
+  int excl, incl;   // tiles before / up to and including this lane's experts
+  int total;        // tiles of all experts
+};
 template <int BM>
-static __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, int E, int m,
-                                                 int& e_out, int& row0_out, int& cnt_out) {
+static __device__ __forceinline__ TileScan tile_scan(const int32_t* __restrict__ offsets, int E) {
   const int lane = threadIdx.x & 63;
-  int tl[4];
+  TileScan ts;
   int s = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane * 4 + i;
     const int c = (e < E) ? offsets[e + 1] - offsets[e] : 0;
-    tl[i] = (c + BM - 1) / BM;
-    s += tl[i];
+    ts.tl[i] = c > 0 ? (c + BM - 1) / BM : 0;
+    s += ts.tl[i];
   }
   int incl = s;
 #pragma unroll
@@ -191,18 +188,27 @@ static __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ off
     const int v = __shfl_up(incl, off);
     if (lane >= off) incl += v;
   }
-  const int excl = incl - s;
-  const uint64_t hit = __ballot(m >= excl && m < incl);
+  ts.incl = incl;
+  ts.excl = incl - s;
+  ts.total = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+  return ts;
+}
+// Expert, first row and row count of tile m; false past the last tile.
+template <int BM>
+static __device__ __forceinline__ bool tile_lookup(const TileScan& ts, const int32_t* __restrict__ offsets,
+                                                   int m, int& e_out, int& row0_out, int& cnt_out) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t hit = __ballot(m >= ts.excl && m < ts.incl);
   if (hit == 0) return false;
   const int src = __ffsll((long long)hit) - 1;
-  int e = -1, r0 = 0, base = excl;
+  int e = -1, r0 = 0, base = ts.excl;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if (e < 0 && m < base + tl[i]) {
+    if (e < 0 && m < base + ts.tl[i]) {
       e = lane * 4 + i;
       r0 = (m - base) * BM;
     }
-    base += tl[i];
+    base += ts.tl[i];
   }
   e_out = __shfl(e, src);
   row0_out = __shfl(r0, src);
@@ -222,18 +228,23 @@ static __device__ __forceinline__ int swz(int r, int c) { return r * (CPR * 16) 
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Direct global -> LDS copy of 16 bytes per lane: lane L fills LDS bytes [dst + 16 L, +16).
+// Direct global -> LDS copies.  They are written as inline assembly: the copies have no
+// register results, their completion is waited for explicitly (vmcnt) before the barrier
+// that publishes a stage, and a copy the compiler can see makes it treat every later LDS
+// read as unordered and wait for all of them before the first use.  M0 carries the
+// wave's LDS destination; lane L lands at M0 + size * L.
+static __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)(const lds_void*)p;
+}
+// 16 bytes per lane: lane L fills LDS bytes [dst + 16 L, +16).
 static __device__ __forceinline__ void dma16(const void* src, uint8_t* dst_wave) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst_wave, 16, 0, 0);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds_addr(dst_wave)), "v"(src) : "memory", "m0");
 }
-// Direct global -> LDS copy of one byte per lane (lane L fills the dword at dst + 4 L): used
-// only to pull a line into L2 ahead of its real copy, into a scratch area nobody reads.
-static __device__ __forceinline__ void dma1(const void* src, uint8_t* dst_wave) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst_wave, 1, 0, 0);
-}
-// Direct global -> LDS copy of one dword per lane: lane L fills LDS bytes [dst + 4 L, +4).
+// One dword per lane: lane L fills LDS bytes [dst + 4 L, +4).
 static __device__ __forceinline__ void dma4(const void* src, uint8_t* dst_wave) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst_wave, 4, 0, 0);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :: "s"(lds_addr(dst_wave)), "v"(src) : "memory", "m0");
 }
 
 // s_waitcnt vmcnt(N) with the LDS/export counters left alone (gfx9 encoding).
@@ -291,7 +302,10 @@ static __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
 // global->LDS copies (no registers) issued NS-1 steps before use.  Before consuming a stage
 // every wave waits until its own copies for it have landed (vmcnt counts, in issue order,
 // exactly the copies issued after them) and the workgroup meets at a fence-free barrier,
-// which also frees the stage consumed in the previous step.
+// which also frees the stage consumed in the previous step.  Inside a stage the operand
+// fragments of MFMA step ks + 1 are read while step ks multiplies, and the last step of a
+// stage multiplies after the next stage's barrier, so LDS latency hides behind the
+// matrix cores.
 //
 // bf16 stage: rows x BK with 16-byte chunks; copy instruction i fills LDS bytes
 // [1024 i, +1024), lane L landing at row 1024 i / (16 CPR) + L / CPR, swizzle position
@@ -304,6 +318,10 @@ static __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
 // row & 7).  A super-stage's copies are issued just before the group of its first stage,
 // so that group's completion implies the codes'.  Each stage also copies, per row, the
 // aligned dword holding the stage's two scale bytes.
+//
+// Epilogue: each wave moves its outputs through its own slice of the (then idle) LDS,
+// 32 rows at a time, so that global stores are whole 8-byte (h) or 16-byte (y) chunks of
+// rows instead of one element per lane.
 template <int MODE, int FMT, class C>
 __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, CPR = C::CPR, NS = C::NS, NW = C::NW;
@@ -331,23 +349,31 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
   static_assert(BN % 32 == 0 && (BM * CPR) % 64 == 0 && (BN * CPR) % 64 == 0, "copy granularity");
   static_assert(FMT == 0 || BN % 64 == 0, "scale copies cover 64 rows");
 
-  constexpr int PF = C::PF;
-  constexpr int JUNK = PF > 0 ? 256 : 0;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE + CODE_BYTES + JUNK];
+  constexpr int SMEM = NS * STAGE + CODE_BYTES;
+  // epilogue slices (per wave, 32 output rows): mlp1 bf16 [32][pairs] (+ lo part), row
+  // stride 2 P + 8 bytes so the four 16-lane groups of one store hit disjoint banks; mlp2
+  // fp32 [32][WTN], row stride 4 WTN + 32 bytes so the two lane halves hit disjoint banks
+  constexpr int EP_P = C::WTN / 2;
+  constexpr int EP_S = (MODE == 1) ? 2 * EP_P + 8 : 4 * C::WTN + 32;
+  constexpr int EP_REG = 32 * EP_S * ((MODE == 1 && FMT == 1) ? 2 : 1);
+  static_assert(NW * EP_REG <= SMEM, "epilogue slices exceed the operand ring");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
   uint8_t* const codes_lds = smem + NS * STAGE;
-  uint8_t* const junk_lds = smem + NS * STAGE + CODE_BYTES;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WAVES_N;
   const int wn = wave % C::WAVES_N;
 
-  // ---- tile order.  Streaming tiles (few rows per expert): column tiles fastest, so
-  // workgroups launched together read neighbouring rows of one expert's weights.  Large
-  // tiles: XCD-contiguous ranges of the linear id, then groups of GM row tiles, so the
-  // workgroups sharing an XCD's L2 share operand tiles.
-  const int total = p.max_m_tiles * p.n_tiles;
+  // ---- tile order over the tiles that exist (the grid is an upper bound).  Streaming tiles
+  // (few rows per expert): column tiles fastest, so workgroups launched together read
+  // neighbouring rows of one expert's weights.  Large tiles: the workgroups of XCD x (block
+  // ids congruent to x mod 8) take the x-th eighth of the tiles, in groups of GM row tiles,
+  // so the workgroups sharing an XCD's L2 share operand tiles and every XCD gets an equal
+  // share however many row tiles the routing produced.
+  const TileScan ts = tile_scan<BM>(p.offsets, p.E);
+  const int total = ts.total * p.n_tiles;
   int m_tile, n_tile;
   if (C::STREAM) {
     const int lin = blockIdx.x;
@@ -355,20 +381,21 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
     m_tile = lin / p.n_tiles;
     n_tile = lin % p.n_tiles;
   } else {
-    const int nb = gridDim.x;               // multiple of 8
-    const int lin = (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3);
-    if (lin >= total) return;
+    const int share = (total + 7) >> 3;
+    const int xl = blockIdx.x >> 3;
+    const int lin = (blockIdx.x & 7) * share + xl;
+    if (xl >= share || lin >= total) return;
     constexpr int GM = 4;
     const int gsize = GM * p.n_tiles;
     const int g = lin / gsize;
     const int first_m = g * GM;
-    const int gm = min(p.max_m_tiles - first_m, GM);
+    const int gm = min(ts.total - first_m, GM);
     m_tile = first_m + (lin % gsize) % gm;
     n_tile = (lin % gsize) / gm;
   }
 
   int e, row0, cnt;
-  if (!find_tile<BM>(p.offsets, p.E, m_tile, e, row0, cnt)) return;
+  if (!tile_lookup<BM>(ts, p.offsets, m_tile, e, row0, cnt)) return;
   const int gbase = p.offsets[e] + row0;    // routed row of tile row 0
   const int rows = min(BM, cnt - row0);
   // a routing passed in by the caller is trusted only this far: rows stay inside [0, A)
@@ -447,48 +474,10 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
       cdst[j] = i * 1024;
     }
   }
-  // L2 prefetch slots: one lane per 128-byte line of a stage (A rows, bf16 B rows), 64 lines
-  // per instruction; MXFP4 code lines are prefetched per super-stage
-  constexpr int NPA = (PF > 0) ? AP * BM / 64 : 0;
-  constexpr int NPB = (PF > 0) ? BN / 64 : 0;               // B rows (bf16) or code rows (MXFP4)
-  constexpr int PW_P = (NPA + NPB + NW - 1) / NW + 1;
-  const uint8_t* psrc[PW_P];
-  int pstep[PW_P];
-#pragma unroll
-  for (int j = 0; j < PW_P; ++j) {
-    const int i = wave + j * NW;
-    psrc[j] = p.w;
-    pstep[j] = 0;
-    if (i < NPA) {
-      const int part = i / (BM / 64);
-      const int r = (i % (BM / 64)) * 64 + lane;
-      const int rc = min(r, rows - 1);
-      size_t elem;
-      if (MODE == 1) {
-        int asg = p.perm[gbase + rc];
-        asg = ((unsigned)asg < (unsigned)p.A) ? asg : 0;
-        elem = (size_t)(asg / p.k) * K;
-      } else {
-        elem = (size_t)(gbase + rc) * K;
-      }
-      psrc[j] = (const uint8_t*)((part == 0 ? p.a : p.a_lo) + elem);
-      pstep[j] = ROWB;
-    } else if (i < NPA + NPB) {
-      const int r = (i - NPA) * 64 + lane;
-      if (FMT == 0) {
-        psrc[j] = w_e + (size_t)MOE_WROW(r) * K * 2;
-        pstep[j] = ROWB;
-      } else {
-        psrc[j] = w_e + (size_t)MOE_WROW(r) * (K / 2);
-        pstep[j] = -128;                      // code lines: one per super-stage
-      }
-    }
-  }
-  const int nkc = (nk + SUPER - 1) / SUPER;  // code super-stages
 
-  // every copy and prefetch this wave issues is counted; mark[slot] = count right after the
-  // stage group that filled the slot, so the wait for a stage is exact: vmcnt completes in
-  // issue order
+  // every copy this wave issues is counted; mark[slot] = count right after the stage group
+  // that filled the slot, so the wait for a stage is exact: vmcnt completes in issue order.
+  // Both are wave-uniform (the wave index is read from the first lane).
   int issued = 0;
   int mark[NS];
 #pragma unroll
@@ -520,30 +509,12 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
       }                                                                                          \
     }                                                                                            \
   } while (0)
-  // L2 prefetch of step kt's lines (or, MXFP4, of code super-stage kt / SUPER when kt starts one)
-#define MOE_PREFETCH(kt)                                                                         \
-  do {                                                                                           \
-    _Pragma("unroll") for (int j = 0; j < PW_P; ++j) {                                           \
-      const int i_ = wave + j * NW;                                                              \
-      if (i_ < NPA + NPB) {                                                                      \
-        if (pstep[j] >= 0) {                                                                     \
-          dma1(psrc[j] + (size_t)(kt) * pstep[j], junk_lds);                                     \
-          ++issued;                                                                              \
-        } else if ((kt) % SUPER == 0 && (kt) / SUPER < nkc) {                                    \
-          dma1(psrc[j] + (size_t)((kt) / SUPER) * 128, junk_lds);                                \
-          ++issued;                                                                              \
-        }                                                                                        \
-      }                                                                                          \
-    }                                                                                            \
-  } while (0)
-  // everything a K step needs, codes first so the group's completion implies theirs; then the
-  // prefetch of the step PF stages further on
+  // everything a K step needs, codes first so the group's completion implies theirs
 #define MOE_ISSUE(kt)                                                                            \
   do {                                                                                           \
     if (FMT == 1 && (kt) % SUPER == 0) MOE_ISSUE_CODES((kt) / SUPER);                            \
     MOE_ISSUE_GROUP(kt, (kt) % NS);                                                              \
     mark[(kt) % NS] = issued;                                                                    \
-    if (PF > 0 && (kt) + PF < nk) MOE_PREFETCH((kt) + PF);                                       \
   } while (0)
 
   f32x16 acc[FM][FN];
@@ -566,27 +537,53 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
   const int arow0 = wm * C::WTM + (lane & 31);
   const int kg = lane >> 5;                 // which half of the stage's K range this lane feeds
 
-  // prologue: prefetch what the ring will need first, then NS - 1 stages in flight
-  if (PF > 0) {
-    for (int s0 = NS - 1; s0 < NS - 1 + PF && s0 < nk; ++s0) MOE_PREFETCH(s0);
-  }
+  // prologue: NS - 1 stages in flight
 #pragma unroll
   for (int s0 = 0; s0 < NS - 1; ++s0)
     if (s0 < nk) MOE_ISSUE(s0);
 
+  // double-buffered operand fragments: buffer ks & 1 feeds MFMA step ks
+  bf16x8 fa[2][AP][FM];
+  bf16x8 fb[2][FN];
+  u32x4 q4[FN];                             // MXFP4: this lane's 32 codes per fragment
+  float scl[FN];
+#define MOE_LOAD_FRAGS(buf, ks_, sa_, sb_)                                                       \
+  do {                                                                                           \
+    const int cc_ = kg * KS + (ks_);        /* chunk (8 K elements) this lane feeds */           \
+    _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                             \
+      if (FMT == 0) fb[buf][j] = *(const bf16x8*)((sb_) + swz<CPR>(brow[j], cc_));                \
+      else fb[buf][j] = decode_fp4x8(q4[j][ks_], scl[j]);                                        \
+    }                                                                                            \
+    _Pragma("unroll") for (int pa = 0; pa < AP; ++pa)                                            \
+    _Pragma("unroll") for (int i = 0; i < FM; ++i)                                               \
+      fa[buf][pa][i] = *(const bf16x8*)((sa_) + pa * A_BYTES + swz<CPR>(arow0 + i * 32, cc_));    \
+  } while (0)
+#define MOE_MMA(buf)                                                                             \
+  do {                                                                                           \
+    _Pragma("unroll") for (int i = 0; i < FM; ++i)                                               \
+    _Pragma("unroll") for (int pa = 0; pa < AP; ++pa)                                            \
+    _Pragma("unroll") for (int j = 0; j < FN; ++j)                                               \
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][pa][i], fb[buf][j], acc[i][j], 0, 0, 0); \
+  } while (0)
+  // one scheduling group per MFMA step: the next step's LDS reads ahead of this step's MFMAs
+#define MOE_SCHED()                                                                              \
+  do {                                                                                           \
+    __builtin_amdgcn_sched_group_barrier(0x100, (FMT == 0 ? FN : 0) + AP * FM, 0);               \
+    __builtin_amdgcn_sched_group_barrier(0x008, AP * FM * FN, 0);                                \
+  } while (0)
+
   for (int kt = 0; kt < nk; ++kt) {
     const int slot = kt % NS;
     // copies issued after step kt's group: groups of steps kt+1 .. last issued, plus the
-    // code super-stages issued with them
-    wait_vmcnt_dyn(issued - mark[slot]);
+    // code super-stages issued with them (none with two bf16 stages)
+    if (FMT == 0 && NS == 2) wait_vmcnt<0>();
+    else wait_vmcnt_dyn(__builtin_amdgcn_readfirstlane(issued - mark[slot]));
     wait_lgkmcnt0();
     barrier_nofence();
     if (kt + NS - 1 < nk) MOE_ISSUE(kt + NS - 1);
 
     const uint8_t* sa = smem + slot * STAGE;
     const uint8_t* sb = sa + AP * A_BYTES;
-    u32x4 q4[FN];                           // MXFP4: this lane's 32 codes per fragment
-    float scl[FN];
     if (FMT == 1) {
       const uint8_t* cs = codes_lds + ((kt / SUPER) % NSB) * CODE_SLOT;
       const int chunk = 2 * (kt % SUPER) + kg;
@@ -597,83 +594,112 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
         scl[j] = __uint_as_float(sc << 23);
       }
     }
+    MOE_LOAD_FRAGS(0, 0, sa, sb);
+    if (kt > 0) MOE_MMA((KS - 1) & 1);      // last MFMA step of the previous stage
+    MOE_SCHED();
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int cc = kg * KS + ks;          // chunk (8 K elements) this lane feeds
-      bf16x8 fb[FN];
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        if (FMT == 0) fb[j] = *(const bf16x8*)(sb + swz<CPR>(brow[j], cc));
-        else fb[j] = decode_fp4x8(q4[j][ks], scl[j]);
-      }
-      bf16x8 fa[AP][FM];
-#pragma unroll
-      for (int pa = 0; pa < AP; ++pa)
-#pragma unroll
-        for (int i = 0; i < FM; ++i) fa[pa][i] = *(const bf16x8*)(sa + pa * A_BYTES + swz<CPR>(arow0 + i * 32, cc));
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int pa = 0; pa < AP; ++pa)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[pa][i], fb[j], acc[i][j], 0, 0, 0);
-      // every LDS read of the step ahead of its matrix instructions: the reads overlap and
-      // the waits before the MFMAs can be partial
-      __builtin_amdgcn_sched_group_barrier(0x100, (FMT == 0 ? FN : 0) + AP * FM, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, AP * FM * FN, 0);
+    for (int ks = 0; ks < KS - 1; ++ks) {
+      MOE_LOAD_FRAGS((ks + 1) & 1, ks + 1, sa, sb);
+      MOE_MMA(ks & 1);
+      MOE_SCHED();
     }
   }
+  MOE_MMA((KS - 1) & 1);
+#undef MOE_LOAD_FRAGS
+#undef MOE_MMA
+#undef MOE_SCHED
 #undef MOE_ISSUE
 #undef MOE_ISSUE_GROUP
 #undef MOE_ISSUE_CODES
 #undef MOE_WROW
 
-  // ---- epilogue: output register q of fragment (i, j) is row 8 (q >> 2) + 4 kg + (q & 3)
+  // ---- epilogue.  Output register q of fragment (i, j) is row 8 (q >> 2) + 4 kg + (q & 3)
+  // of the fragment's 32 rows, column lane & 31.
+  barrier_nofence();                        // every wave is done with the operand ring
+  uint8_t* const ep = smem + wave * EP_REG;
   const uint16_t* bias = p.bias + (size_t)e * p.N;
   if (MODE == 1) {
-    // lane n < 16 of a fragment holds the gate column of pair 16 j' + n, lane n + 16 the
-    // linear column of the same pair: one lane exchange pairs them
+    // Lane n < 16 of a fragment holds the gate column of pair 16 j + n, lane n + 16 the
+    // linear column of the same pair.  One lane exchange per two registers gives the gate
+    // lane (gate, linear) for registers 0..7 and the linear lane the pair for 8..15, so each
+    // lane evaluates SwiGLU for eight of the fragment's sixteen rows.
     const bool gate_lane = (lane & 16) == 0;
+    const int pl = lane & 15;
+    const int f_wave = n_tile * PN + wn * EP_P;            // first pair of this wave
+    float bg[FN], bl[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int f = n_tile * PN + (wn * C::WTN + j * 32) / 2 + (lane & 15);
-      const float bg = (f < p.F) ? bf16_to_f32(bias[f]) : 0.f;
-      const float bl = (f < p.F) ? bf16_to_f32(bias[p.F + f]) : 0.f;
+      const int f = f_wave + j * 16 + pl;
+      bg[j] = (f < p.F) ? bf16_to_f32(bias[f]) : 0.f;
+      bl[j] = (f < p.F) ? bf16_to_f32(bias[p.F + f]) : 0.f;
+    }
+    constexpr int CH = EP_P / 4;                           // 8-byte chunks per slice row
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const float other = __shfl_xor(acc[i][j][q], 16);
-          const int rl = wm * C::WTM + i * 32 + 8 * (q >> 2) + 4 * kg + (q & 3);
-          if (!gate_lane || rl >= rows || f >= p.F) continue;
-          const float ug = acc[i][j][q] + bg;
-          const float ul = other + bl;
+      for (int j = 0; j < FN; ++j) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float send = gate_lane ? acc[i][j][q + 8] : acc[i][j][q];
+          const float recv = __shfl_xor(send, 16);
+          const float ug = (gate_lane ? acc[i][j][q] : recv) + bg[j];
+          const float ul = (gate_lane ? recv : acc[i][j][q + 8]) + bl[j];
           const float gc = fminf(ug, SWIGLU_LIMIT);
           const float lc = fminf(fmaxf(ul, -SWIGLU_LIMIT), SWIGLU_LIMIT);
           const float hv = gc / (1.0f + __expf(-SWIGLU_ALPHA * gc)) * (lc + 1.0f);
+          const int qq = gate_lane ? q : q + 8;
+          const int r = 8 * (qq >> 2) + 4 * kg + (qq & 3);
           const uint32_t hi = f32_to_bf16_rne(hv);
-          const size_t at = (size_t)(gbase + rl) * p.F + f;
-          p.h[at] = (uint16_t)hi;
-          if (FMT == 1) p.h_lo[at] = (uint16_t)f32_to_bf16_rne(hv - bf16_to_f32(hi));
+          uint16_t* d = (uint16_t*)(ep + r * EP_S) + j * 16 + pl;
+          d[0] = (uint16_t)hi;
+          if (FMT == 1) d[32 * EP_S / 2] = (uint16_t)f32_to_bf16_rne(hv - bf16_to_f32(hi));
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < (32 * CH + 63) / 64; ++t) {
+        const int idx = lane + 64 * t;
+        const int r = idx / CH, c = idx % CH;
+        const int rl = wm * C::WTM + i * 32 + r;
+        const int f0 = f_wave + c * 4;
+        if (idx < 32 * CH && rl < rows && f0 < p.F) {
+          const size_t at = (size_t)(gbase + rl) * p.F + f0;
+          *(uint2*)(p.h + at) = *(const uint2*)(ep + r * EP_S + c * 8);
+          if (FMT == 1) *(uint2*)(p.h_lo + at) = *(const uint2*)(ep + 32 * EP_S + r * EP_S + c * 8);
         }
       }
     }
   } else {
+    const int o_wave = n_tile * BN + wn * C::WTN;          // first output column of this wave
+    float bo[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int o = o_wave + j * 32 + (lane & 31);
+      bo[j] = (o < p.N) ? bf16_to_f32(bias[o]) : 0.f;
+    }
+    constexpr int CH = C::WTN / 4;                         // 16-byte chunks per slice row
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int rl = wm * C::WTM + i * 32 + 8 * (q >> 2) + 4 * kg + (q & 3);
-        if (rl >= rows) continue;
-        const int a = p.perm[gbase + rl];
-        if ((unsigned)a >= (unsigned)p.A) continue;
-        const float gw = p.gates[a];
-        float* yrow = p.y + (size_t)a * p.N;
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int o = n_tile * BN + wn * C::WTN + j * 32 + (lane & 31);
-          if (o < p.N) yrow[o] = gw * (acc[i][j][q] + bf16_to_f32(bias[o]));
+        for (int q = 0; q < 16; ++q) {
+          const int r = 8 * (q >> 2) + 4 * kg + (q & 3);
+          *(float*)(ep + r * EP_S + (j * 32 + (lane & 31)) * 4) = acc[i][j][q] + bo[j];
+        }
+#pragma unroll
+      for (int t = 0; t < (32 * CH + 63) / 64; ++t) {
+        const int idx = lane + 64 * t;
+        const int r = idx / CH, c = idx % CH;
+        const int rl = wm * C::WTM + i * 32 + r;
+        const int o0 = o_wave + c * 4;
+        if (idx < 32 * CH && rl < rows && o0 < p.N) {
+          const int a = p.perm[gbase + rl];
+          if ((unsigned)a < (unsigned)p.A) {
+            const float gw = p.gates[a];
+            f32x4 v = *(const f32x4*)(ep + r * EP_S + c * 16);
+            v *= gw;
+            *(f32x4*)(p.y + (size_t)a * p.N + o0) = v;
+          }
         }
       }
     }
