@@ -357,8 +357,11 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
   constexpr int EP_S = (MODE == 1) ? 2 * EP_P + 8 : 4 * C::WTN + 32;
   constexpr int EP_REG = 32 * EP_S * ((MODE == 1 && FMT == 1) ? 2 : 1);
   static_assert(NW * EP_REG <= SMEM, "epilogue slices exceed the operand ring");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
+  constexpr int ROWTAB = (MODE == 2) ? BM * 8 : 0;          // mlp2: assignment and gate per tile row
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM + ROWTAB];
   uint8_t* const codes_lds = smem + NS * STAGE;
+  int* const tab_a = (int*)(smem + SMEM);
+  float* const tab_g = (float*)(smem + SMEM + BM * 4);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -402,6 +405,14 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
   if (gbase < 0 || rows <= 0 || gbase + rows > p.A) return;
   const int K = p.K;
   const int nk = K / BK;
+  // mlp2: thread r < rows fetches tile row r's assignment now and its gate in the first K
+  // step, for the epilogue (which then needs no dependent global loads)
+  int rt_a = -1;
+  float rt_g = 0.f;
+  if (MODE == 2 && tid < rows) {
+    const int a = p.perm[gbase + tid];
+    rt_a = ((unsigned)a < (unsigned)p.A) ? a : -1;
+  }
 
   const uint8_t* w_e;
   const uint8_t* s_e = nullptr;
@@ -580,6 +591,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
     else wait_vmcnt_dyn(__builtin_amdgcn_readfirstlane(issued - mark[slot]));
     wait_lgkmcnt0();
     barrier_nofence();
+    if (MODE == 2 && kt == 0 && rt_a >= 0) rt_g = p.gates[rt_a];
     if (kt + NS - 1 < nk) MOE_ISSUE(kt + NS - 1);
 
     const uint8_t* sa = smem + slot * STAGE;
@@ -615,15 +627,22 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
 
   // ---- epilogue.  Output register q of fragment (i, j) is row 8 (q >> 2) + 4 kg + (q & 3)
   // of the fragment's 32 rows, column lane & 31.
+  if (MODE == 2 && tid < BM) {
+    tab_a[tid] = rt_a;
+    tab_g[tid] = rt_g;
+  }
+  wait_lgkmcnt0();
   barrier_nofence();                        // every wave is done with the operand ring
   uint8_t* const ep = smem + wave * EP_REG;
   const uint16_t* bias = p.bias + (size_t)e * p.N;
   if (MODE == 1) {
     // Lane n < 16 of a fragment holds the gate column of pair 16 j + n, lane n + 16 the
-    // linear column of the same pair.  One lane exchange per two registers gives the gate
-    // lane (gate, linear) for registers 0..7 and the linear lane the pair for 8..15, so each
-    // lane evaluates SwiGLU for eight of the fragment's sixteen rows.
+    // linear column of the same pair.  v_permlane16_swap of registers q and q + 8 exchanges
+    // odd 16-lane rows of the first with even rows of the second: afterwards a gate lane
+    // holds (gate, linear) of register q's row and a linear lane those of register q + 8's,
+    // so each lane evaluates SwiGLU for eight of the fragment's sixteen rows.
     const bool gate_lane = (lane & 16) == 0;
+    const int rlane = 4 * kg + (gate_lane ? 0 : 16);      // row offset of this lane's results
     const int pl = lane & 15;
     const int f_wave = n_tile * PN + wn * EP_P;            // first pair of this wave
     float bg[FN], bl[FN];
@@ -640,15 +659,14 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
       for (int j = 0; j < FN; ++j) {
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-          const float send = gate_lane ? acc[i][j][q + 8] : acc[i][j][q];
-          const float recv = __shfl_xor(send, 16);
-          const float ug = (gate_lane ? acc[i][j][q] : recv) + bg[j];
-          const float ul = (gate_lane ? recv : acc[i][j][q + 8]) + bl[j];
+          const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[i][j][q]),
+                                                           __float_as_uint(acc[i][j][q + 8]), false, false);
+          const float ug = __uint_as_float(sw[0]) + bg[j];
+          const float ul = __uint_as_float(sw[1]) + bl[j];
           const float gc = fminf(ug, SWIGLU_LIMIT);
           const float lc = fminf(fmaxf(ul, -SWIGLU_LIMIT), SWIGLU_LIMIT);
           const float hv = gc / (1.0f + __expf(-SWIGLU_ALPHA * gc)) * (lc + 1.0f);
-          const int qq = gate_lane ? q : q + 8;
-          const int r = 8 * (qq >> 2) + 4 * kg + (qq & 3);
+          const int r = 8 * (q >> 2) + rlane + (q & 3);
           const uint32_t hi = f32_to_bf16_rne(hv);
           uint16_t* d = (uint16_t*)(ep + r * EP_S) + j * 16 + pl;
           d[0] = (uint16_t)hi;
@@ -693,9 +711,9 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
         const int rl = wm * C::WTM + i * 32 + r;
         const int o0 = o_wave + c * 4;
         if (idx < 32 * CH && rl < rows && o0 < p.N) {
-          const int a = p.perm[gbase + rl];
-          if ((unsigned)a < (unsigned)p.A) {
-            const float gw = p.gates[a];
+          const int a = tab_a[rl];
+          if (a >= 0) {
+            const float gw = tab_g[rl];
             f32x4 v = *(const f32x4*)(ep + r * EP_S + c * 16);
             v *= gw;
             *(f32x4*)(p.y + (size_t)a * p.N + o0) = v;
