@@ -17,17 +17,12 @@
 //         contiguously.
 //   combine: out[t] = sum_j y[t*k + j] in slot order, fp32, no atomics.
 //
-// Matrix-core mapping: v_mfma_f32_16x16x32_bf16.  Operands are K-contiguous (rows of x,
-// h and the weights), so each lane feeds the instruction with one 16-byte LDS read per
-// operand: lane l supplies row l & 15 and K elements 8 (l >> 4) .. +7; output register r
-// of lane l is C[4 (l >> 4) + r][l & 15].  Tiles are staged in LDS with the 16-byte chunks
-// of each 128-byte row XOR-swizzled by (row & 7), so the eight rows a group of lanes
-// reads land in eight different bank groups.  LDS is double buffered: the next K step is
-// fetched into registers while the current one feeds the matrix cores, one barrier per
-// K step.
+// Matrix-core mapping: v_mfma_f32_32x32x16_bf16 on K-contiguous operands (rows of x, h
+// and the weights); operand tiles reach LDS by direct global->LDS copies through a ring of
+// stages, details at the kernel.
 //
 // MXFP4 weights (GPT-OSS-in-Transformers blog, MXFP4 paragraph: E2M1 values, one scale
-// per 32 elements) are decoded while a tile moves from registers to LDS with the gfx950
+// per 32 elements) are decoded from LDS into matrix-core operands with the gfx950
 // conversion v_cvt_scalef32_pk_bf16_fp4 (two codes per instruction, low nibble first,
 // multiplied by the block's power-of-two scale).  Every E2M1 value times 2^(s-127) with
 // s in [2, 252] is an exact bf16, so the matrix cores see the weights without rounding.
@@ -105,13 +100,13 @@ struct Tile {
 #define MOE_L_NS 2
 #endif
 #ifndef MOE_L_NS4
-#define MOE_L_NS4 3
+#define MOE_L_NS4 2
 #endif
 #ifndef MOE_L_NSH
 #define MOE_L_NSH 2                 // mlp2 with MXFP4 weights (two A parts per stage)
 #endif
 #ifndef MOE_S_NSH
-#define MOE_S_NSH 3
+#define MOE_S_NSH 2
 #endif
 #ifndef MOE_L_BK
 #define MOE_L_BK 64
@@ -134,8 +129,23 @@ template <int MODE, int FMT> using SmallTile =
 template <int MODE, int FMT> struct LargeTileSel {
   using type = Tile<MOE_L_BM, MOE_L_BN, MOE_L_WM, MOE_L_WN, MOE_L_NS, MOE_L_BK, false>;
 };
-template <int MODE> struct LargeTileSel<MODE, 1> {
-  using type = Tile<MOE_L4_BM, MOE_L4_BN, MOE_L4_WM, MOE_L4_WN, (MODE == 1 ? MOE_L_NS4 : MOE_L_NSH), 64, false>;
+#ifndef MOE_L41_BM
+#define MOE_L41_BM 256              // mlp1 with MXFP4 weights
+#endif
+#ifndef MOE_L41_BN
+#define MOE_L41_BN 256
+#endif
+#ifndef MOE_L41_WM
+#define MOE_L41_WM 2
+#endif
+#ifndef MOE_L41_WN
+#define MOE_L41_WN 4
+#endif
+template <> struct LargeTileSel<1, 1> {
+  using type = Tile<MOE_L41_BM, MOE_L41_BN, MOE_L41_WM, MOE_L41_WN, MOE_L_NS4, 64, false>;
+};
+template <> struct LargeTileSel<2, 1> {        // mlp2 with MXFP4 weights: h hi and lo parts
+  using type = Tile<MOE_L4_BM, MOE_L4_BN, MOE_L4_WM, MOE_L4_WN, MOE_L_NSH, 64, false>;
 };
 template <int MODE, int FMT> using LargeTile = typename LargeTileSel<MODE, FMT>::type;
 
@@ -388,7 +398,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
     const int xl = blockIdx.x >> 3;
     const int lin = (blockIdx.x & 7) * share + xl;
     if (xl >= share || lin >= total) return;
-    constexpr int GM = 4;
+    constexpr int GM = 4;                   // row tiles per group
     const int gsize = GM * p.n_tiles;
     const int g = lin / gsize;
     const int first_m = g * GM;

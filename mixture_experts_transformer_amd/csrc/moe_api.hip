@@ -367,8 +367,8 @@ int moe_profile_read(double* ms, int64_t* launches) {
 }
 
 const char* moe_version(void) {
-  return "moe-mi355x gfx950: router fp64-MFMA, top-k wave argmax, grouped GEMM v_mfma_f32_16x16x32_bf16 "
-         "(tiles 32x64 / 256x192 / 128x192 hi-lo), combine fp32";
+  return "moe-mi355x gfx950: router fp64-MFMA, top-k wave argmax, grouped GEMM v_mfma_f32_32x32x16_bf16 "
+         "(streaming tile 64x128, matrix-core tile 256x256, MXFP4 h as bf16 hi + lo), combine fp32";
 }
 
 }  // extern "C"
