@@ -508,7 +508,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
   do {                                                                                           \
     _Pragma("unroll") for (int j = 0; j < PW_G; ++j) {                                           \
       const int i_ = wave + j * NW;                                                              \
-      if (i_ < NG) {                                                                             \
+      if (i_ < NG && !(i_ < NA && (i_ % (BM / ROWS_PER_CP)) * ROWS_PER_CP >= rows)) {           \
         uint8_t* d_ = smem + (slot) * STAGE + gdst[j];                                           \
         if (FMT == 1 && i_ >= NA) {                                                              \
           const uintptr_t sp_ = (uintptr_t)(gsrc[j] + (kt) * (BK / 32));                         \
@@ -568,7 +568,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
   bf16x8 fb[2][FN];
   u32x4 q4[FN];                             // MXFP4: this lane's 32 codes per fragment
   float scl[FN];
-#define MOE_LOAD_FRAGS(buf, ks_, sa_, sb_)                                                       \
+#define MOE_LOAD_FRAGS(buf, ks_, sa_, sb_, FA)                                                   \
   do {                                                                                           \
     const int cc_ = kg * KS + (ks_);        /* chunk (8 K elements) this lane feeds */           \
     _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                             \
@@ -576,57 +576,67 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
       else fb[buf][j] = decode_fp4x8(q4[j][ks_], scl[j]);                                        \
     }                                                                                            \
     _Pragma("unroll") for (int pa = 0; pa < AP; ++pa)                                            \
-    _Pragma("unroll") for (int i = 0; i < FM; ++i)                                               \
+    _Pragma("unroll") for (int i = 0; i < (FA); ++i)                                             \
       fa[buf][pa][i] = *(const bf16x8*)((sa_) + pa * A_BYTES + swz<CPR>(arow0 + i * 32, cc_));    \
   } while (0)
-#define MOE_MMA(buf)                                                                             \
+#define MOE_MMA(buf, FA)                                                                         \
   do {                                                                                           \
-    _Pragma("unroll") for (int i = 0; i < FM; ++i)                                               \
+    _Pragma("unroll") for (int i = 0; i < (FA); ++i)                                             \
     _Pragma("unroll") for (int pa = 0; pa < AP; ++pa)                                            \
     _Pragma("unroll") for (int j = 0; j < FN; ++j)                                               \
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][pa][i], fb[buf][j], acc[i][j], 0, 0, 0); \
   } while (0)
   // one scheduling group per MFMA step: the next step's LDS reads ahead of this step's MFMAs
-#define MOE_SCHED()                                                                              \
+#define MOE_SCHED(FA)                                                                            \
   do {                                                                                           \
-    __builtin_amdgcn_sched_group_barrier(0x100, (FMT == 0 ? FN : 0) + AP * FM, 0);               \
-    __builtin_amdgcn_sched_group_barrier(0x008, AP * FM * FN, 0);                                \
+    __builtin_amdgcn_sched_group_barrier(0x100, (FMT == 0 ? FN : 0) + AP * (FA), 0);             \
+    __builtin_amdgcn_sched_group_barrier(0x008, AP * (FA) * FN, 0);                              \
   } while (0)
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int slot = kt % NS;
-    // copies issued after step kt's group: groups of steps kt+1 .. last issued, plus the
-    // code super-stages issued with them (none with two bf16 stages)
-    if (FMT == 0 && NS == 2) wait_vmcnt<0>();
-    else wait_vmcnt_dyn(__builtin_amdgcn_readfirstlane(issued - mark[slot]));
-    wait_lgkmcnt0();
-    barrier_nofence();
-    if (MODE == 2 && kt == 0 && rt_a >= 0) rt_g = p.gates[rt_a];
-    if (kt + NS - 1 < nk) MOE_ISSUE(kt + NS - 1);
-
-    const uint8_t* sa = smem + slot * STAGE;
-    const uint8_t* sb = sa + AP * A_BYTES;
-    if (FMT == 1) {
-      const uint8_t* cs = codes_lds + ((kt / SUPER) % NSB) * CODE_SLOT;
-      const int chunk = 2 * (kt % SUPER) + kg;
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        q4[j] = *(const u32x4*)(cs + brow[j] * 128 + ((chunk ^ (brow[j] & 7)) << 4));
-        const uint32_t sc = sb[brow[j] * 4 + ((sbyte[j] + 2 * kt + kg) & 3)];
-        scl[j] = __uint_as_float(sc << 23);
-      }
-    }
-    MOE_LOAD_FRAGS(0, 0, sa, sb);
-    if (kt > 0) MOE_MMA((KS - 1) & 1);      // last MFMA step of the previous stage
-    MOE_SCHED();
-#pragma unroll
-    for (int ks = 0; ks < KS - 1; ++ks) {
-      MOE_LOAD_FRAGS((ks + 1) & 1, ks + 1, sa, sb);
-      MOE_MMA(ks & 1);
-      MOE_SCHED();
-    }
+// the K loop for FA active 32-row fragment rows per wave (the rest are padding)
+#define MOE_MAIN_LOOP(FA)                                                                        \
+  do {                                                                                           \
+    for (int kt = 0; kt < nk; ++kt) {                                                            \
+      const int slot = kt % NS;                                                                  \
+      if (FMT == 0 && NS == 2) wait_vmcnt<0>();                                                  \
+      else wait_vmcnt_dyn(__builtin_amdgcn_readfirstlane(issued - mark[slot]));                  \
+      wait_lgkmcnt0();                                                                           \
+      barrier_nofence();                                                                         \
+      if (MODE == 2 && kt == 0 && rt_a >= 0) rt_g = p.gates[rt_a];                               \
+      if (kt + NS - 1 < nk) MOE_ISSUE(kt + NS - 1);                                              \
+                                                                                                 \
+      const uint8_t* sa = smem + slot * STAGE;                                                   \
+      const uint8_t* sb = sa + AP * A_BYTES;                                                     \
+      if (FMT == 1) {                                                                            \
+        const uint8_t* cs = codes_lds + ((kt / SUPER) % NSB) * CODE_SLOT;                        \
+        const int chunk = 2 * (kt % SUPER) + kg;                                                 \
+  _Pragma("unroll")                                                                              \
+        for (int j = 0; j < FN; ++j) {                                                           \
+          q4[j] = *(const u32x4*)(cs + brow[j] * 128 + ((chunk ^ (brow[j] & 7)) << 4));          \
+          const uint32_t sc = sb[brow[j] * 4 + ((sbyte[j] + 2 * kt + kg) & 3)];                  \
+          scl[j] = __uint_as_float(sc << 23);                                                    \
+        }                                                                                        \
+      }                                                                                          \
+      MOE_LOAD_FRAGS(0, 0, sa, sb, FA);                                                          \
+      if (kt > 0) MOE_MMA((KS - 1) & 1, FA);  /* last MFMA step of the previous stage */         \
+      MOE_SCHED(FA);                                                                             \
+  _Pragma("unroll")                                                                              \
+      for (int ks = 0; ks < KS - 1; ++ks) {                                                      \
+        MOE_LOAD_FRAGS((ks + 1) & 1, ks + 1, sa, sb, FA);                                        \
+        MOE_MMA(ks & 1, FA);                                                                     \
+        MOE_SCHED(FA);                                                                           \
+      }                                                                                          \
+    }                                                                                            \
+    MOE_MMA((KS - 1) & 1, FA);                                                                   \
+  } while (0)
+  // Row blocks of 32 past the tile's rows hold only padding: when every wave's rows fit in
+  // its first block, the other blocks' copies (above) and matrix instructions are skipped.
+  if (C::WAVES_M == 1 && FM == 2 && rows <= 32) {
+    MOE_MAIN_LOOP(1);
+  } else {
+    MOE_MAIN_LOOP(FM);
   }
-  MOE_MMA((KS - 1) & 1);
+#undef MOE_MAIN_LOOP
 #undef MOE_LOAD_FRAGS
 #undef MOE_MMA
 #undef MOE_SCHED
