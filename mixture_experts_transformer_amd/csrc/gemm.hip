@@ -35,6 +35,7 @@ namespace moe {
 
 constexpr float SWIGLU_ALPHA = 1.702f;
 constexpr float SWIGLU_LIMIT = 7.0f;
+constexpr float SWIGLU_NEG_ALPHA_LOG2E = -SWIGLU_ALPHA * 1.4426950408889634f;
 
 template <int BM_, int BN_, int WM_, int WN_, int NS_, int BK_, bool STREAM_ = false>
 struct Tile {
@@ -166,10 +167,6 @@ struct GemmArgs {
 };
 
 // ------------------------------------------------------------------------------ helpers
-static __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
 static __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 // Row tiles of all experts in one flat list (experts ascending, BM rows each, the last
@@ -685,12 +682,14 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
           const float ul = __uint_as_float(sw[1]) + bl[j];
           const float gc = fminf(ug, SWIGLU_LIMIT);
           const float lc = fminf(fmaxf(ul, -SWIGLU_LIMIT), SWIGLU_LIMIT);
-          const float hv = gc / (1.0f + __expf(-SWIGLU_ALPHA * gc)) * (lc + 1.0f);
+          // sigmoid(ALPHA gc) = 1 / (1 + 2^(-ALPHA log2(e) gc)), hardware exp2 and reciprocal
+          const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(gc * SWIGLU_NEG_ALPHA_LOG2E));
+          const float hv = gc * sg * (lc + 1.0f);
           const int r = 8 * (q >> 2) + rlane + (q & 3);
-          const uint32_t hi = f32_to_bf16_rne(hv);
-          uint16_t* d = (uint16_t*)(ep + r * EP_S) + j * 16 + pl;
-          d[0] = (uint16_t)hi;
-          if (FMT == 1) d[32 * EP_S / 2] = (uint16_t)f32_to_bf16_rne(hv - bf16_to_f32(hi));
+          const __bf16 hi = (__bf16)hv;                    // round to nearest even
+          __bf16* d = (__bf16*)(ep + r * EP_S) + j * 16 + pl;
+          d[0] = hi;
+          if (FMT == 1) d[32 * EP_S / 2] = (__bf16)(hv - (float)hi);
         }
       }
 #pragma unroll
