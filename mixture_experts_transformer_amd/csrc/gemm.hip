@@ -77,10 +77,10 @@ struct Tile {
 #define MOE_S_WN 4
 #endif
 #ifndef MOE_S_NS
-#define MOE_S_NS 3
+#define MOE_S_NS 2
 #endif
 #ifndef MOE_S_NS4
-#define MOE_S_NS4 4
+#define MOE_S_NS4 2
 #endif
 #ifndef MOE_S_STREAM
 #define MOE_S_STREAM 1
@@ -112,9 +112,16 @@ struct Tile {
 #ifndef MOE_L_BK
 #define MOE_L_BK 64
 #endif
+#ifndef MOE_S_WN2
+#define MOE_S_WN2 MOE_S_WN          // waves across the streaming mlp2 tile
+#endif
+#ifndef MOE_S_NS2
+#define MOE_S_NS2 2                 // stages of the streaming mlp2 tile, bf16 weights
+#endif
 template <int MODE, int FMT> using SmallTile =
-    Tile<MOE_S_BM, (MODE == 1 ? MOE_S_BN1 : MOE_S_BN2), MOE_S_WM, MOE_S_WN,
-         (FMT == 0 ? MOE_S_NS : (MODE == 1 ? MOE_S_NS4 : MOE_S_NSH)), 64, MOE_S_STREAM != 0>;
+    Tile<MOE_S_BM, (MODE == 1 ? MOE_S_BN1 : MOE_S_BN2), MOE_S_WM, (MODE == 1 ? MOE_S_WN : MOE_S_WN2),
+         (FMT == 0 ? (MODE == 1 ? MOE_S_NS : MOE_S_NS2) : (MODE == 1 ? MOE_S_NS4 : MOE_S_NSH)), 64,
+         MOE_S_STREAM != 0>;
 #ifndef MOE_L4_BM
 #define MOE_L4_BM 192
 #endif
