@@ -37,7 +37,7 @@ constexpr float SWIGLU_ALPHA = 1.702f;
 constexpr float SWIGLU_LIMIT = 7.0f;
 constexpr float SWIGLU_NEG_ALPHA_LOG2E = -SWIGLU_ALPHA * 1.4426950408889634f;
 
-template <int BM_, int BN_, int WM_, int WN_, int NS_, int BK_, bool STREAM_ = false>
+template <int BM_, int BN_, int WM_, int WN_, int NS_, int BK_, bool STREAM_ = false, int SUPER_ = 4>
 struct Tile {
   static constexpr bool STREAM = STREAM_;   // weight-streaming tile order
   static constexpr int BM = BM_;      // routed rows per tile
@@ -45,6 +45,7 @@ struct Tile {
   static constexpr int BK = BK_;      // K per pipeline stage (32 or 64)
   static constexpr int CPR = BK_ / 8; // 16-byte chunks per bf16 row segment
   static constexpr int NS = NS_;      // LDS stages; NS - 1 K steps are in flight
+  static constexpr int SUPER = SUPER_; // MXFP4: K steps per code super-stage (32 code bytes each)
   static constexpr int WAVES_M = WM_;
   static constexpr int WAVES_N = WN_;
   static constexpr int NW = WM_ * WN_;
@@ -55,6 +56,7 @@ struct Tile {
   static constexpr int FN = WTN / 32;
   static_assert(BM % (32 * WM_) == 0 && BN % (32 * WN_) == 0, "tile/wave mismatch");
   static_assert(BK == 32 || BK == 64, "K step");
+  static_assert(SUPER_ == 1 || SUPER_ == 2 || SUPER_ == 4, "code super-stage");
   static_assert((BM * CPR) % 64 == 0 && (BN * CPR) % 64 == 0, "copy granularity");
 };
 
@@ -118,10 +120,16 @@ struct Tile {
 #ifndef MOE_S_NS2
 #define MOE_S_NS2 2                 // stages of the streaming mlp2 tile, bf16 weights
 #endif
+#ifndef MOE_S_SUPER1
+#define MOE_S_SUPER1 4              // code super-stage of the streaming MXFP4 tiles: mlp1
+#endif
+#ifndef MOE_S_SUPER2
+#define MOE_S_SUPER2 2              // mlp2 (64-byte code segments, but three workgroups per CU)
+#endif
 template <int MODE, int FMT> using SmallTile =
     Tile<MOE_S_BM, (MODE == 1 ? MOE_S_BN1 : MOE_S_BN2), MOE_S_WM, (MODE == 1 ? MOE_S_WN : MOE_S_WN2),
          (FMT == 0 ? (MODE == 1 ? MOE_S_NS : MOE_S_NS2) : (MODE == 1 ? MOE_S_NS4 : MOE_S_NSH)), 64,
-         MOE_S_STREAM != 0>;
+         MOE_S_STREAM != 0, (FMT == 1 ? (MODE == 1 ? MOE_S_SUPER1 : MOE_S_SUPER2) : 4)>;
 #ifndef MOE_L4_BM
 #define MOE_L4_BM 192
 #endif
@@ -281,6 +289,15 @@ static __device__ __forceinline__ void barrier_nofence() {
   asm volatile("" ::: "memory");
 }
 
+// MXFP4 code super-stage in LDS: [rows][CCH 16-byte chunks], chunk c of row r stored at
+// position c ^ code_swz(r), so the rows that one fragment read touches spread over the banks.
+template <int CCH>
+static __device__ __forceinline__ int code_swz(int r) {
+  if (CCH == 8) return r & 7;
+  if (CCH == 4) return (r >> 2) & 3;
+  return (r >> 3) & 1;
+}
+
 // Decode 8 MXFP4 codes (one dword: element 2i in the low nibble of byte i) times the
 // power-of-two scale into one bf16x8 matrix-core operand.
 static __device__ __forceinline__ bf16x8 decode_fp4x8(uint32_t codes, float scale) {
@@ -348,18 +365,22 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
   constexpr int ROWB = CPR * 16;                            // bytes per bf16 row segment
   constexpr int A_BYTES = BM * ROWB;                        // per A part per stage
   static_assert(FMT == 0 || BK == 64, "MXFP4 staging assumes 64-wide K steps");
-  constexpr int SUPER = 4;                                  // stages per MXFP4 code super-stage
+  constexpr int SUPER = C::SUPER;                           // stages per MXFP4 code super-stage
   constexpr int NSB = 2;                                    // code super-stage slots
-  static_assert(FMT == 0 || 4 * NSB > NS + 2, "code ring too short for the stage ring");
+  // a slot is refilled NS - 1 steps ahead of its first use, after the barrier that ends
+  // the last use of its previous super-stage
+  static_assert(FMT == 0 || SUPER * (NSB - 1) > NS - 2, "code ring too short for the stage ring");
+  constexpr int CROW = 32 * SUPER;                          // code bytes per row per super-stage
+  constexpr int CCH = CROW / 16;                            // 16-byte code chunks per row
   constexpr int B_STAGE_BYTES = (FMT == 0) ? BN * ROWB : BN * 4;   // bf16 B tile, or scale dwords
   constexpr int STAGE = AP * A_BYTES + B_STAGE_BYTES;
-  constexpr int CODE_SLOT = BN * 128;
+  constexpr int CODE_SLOT = BN * CROW;
   constexpr int CODE_BYTES = (FMT == 1) ? NSB * CODE_SLOT : 0;
   constexpr int ROWS_PER_CP = 1024 / ROWB;                  // bf16 rows per copy instruction
   constexpr int NA = AP * (BM / ROWS_PER_CP);               // per stage: A copies
   constexpr int NBS = (FMT == 0) ? BN / ROWS_PER_CP : BN / 64;   // per stage: B copies / scale copies
   constexpr int NG = NA + NBS;                              // copies per stage group
-  constexpr int NC = (FMT == 1) ? BN * 128 / 1024 : 0;      // copies per code super-stage
+  constexpr int NC = (FMT == 1) ? BN * CROW / 1024 : 0;     // copies per code super-stage
   constexpr int PW_G = (NG + NW - 1) / NW;
   constexpr int PW_C = (NC + NW - 1) / NW + (NC == 0 ? 1 : 0);
   constexpr int PN = BN / 2;                                // mlp1: pairs per tile
@@ -496,8 +517,8 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
     csrc[j] = p.w;
     cdst[j] = 0;
     if (FMT == 1 && i < NC) {
-      const int r = i * 8 + lane / 8;
-      const int c = (lane % 8) ^ (r & 7);
+      const int r = i * (1024 / CROW) + lane / CCH;
+      const int c = (lane % CCH) ^ code_swz<CCH>(r);
       csrc[j] = w_e + (size_t)MOE_WROW(r) * (K / 2) + c * 16;
       cdst[j] = i * 1024;
     }
@@ -532,7 +553,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
     _Pragma("unroll") for (int j = 0; j < PW_C; ++j) {                                           \
       const int i_ = wave + j * NW;                                                              \
       if (FMT == 1 && i_ < NC) {                                                                 \
-        dma16(csrc[j] + (size_t)(sk) * 128, codes_lds + ((sk) % NSB) * CODE_SLOT + cdst[j]);    \
+        dma16(csrc[j] + (size_t)(sk) * CROW, codes_lds + ((sk) % NSB) * CODE_SLOT + cdst[j]);   \
         ++issued;                                                                                \
       }                                                                                          \
     }                                                                                            \
@@ -619,7 +640,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
         const int chunk = 2 * (kt % SUPER) + kg;                                                 \
   _Pragma("unroll")                                                                              \
         for (int j = 0; j < FN; ++j) {                                                           \
-          q4[j] = *(const u32x4*)(cs + brow[j] * 128 + ((chunk ^ (brow[j] & 7)) << 4));          \
+          q4[j] = *(const u32x4*)(cs + brow[j] * CROW + ((chunk ^ code_swz<CCH>(brow[j])) << 4)); \
           const uint32_t sc = sb[brow[j] * 4 + ((sbyte[j] + 2 * kt + kg) & 3)];                  \
           scl[j] = __uint_as_float(sc << 23);                                                    \
         }                                                                                        \
