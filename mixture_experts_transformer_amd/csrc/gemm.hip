@@ -131,16 +131,16 @@ template <int MODE, int FMT> using SmallTile =
          (FMT == 0 ? (MODE == 1 ? MOE_S_NS : MOE_S_NS2) : (MODE == 1 ? MOE_S_NS4 : MOE_S_NSH)), 64,
          MOE_S_STREAM != 0, (FMT == 1 ? (MODE == 1 ? MOE_S_SUPER1 : MOE_S_SUPER2) : 4)>;
 #ifndef MOE_L4_BM
-#define MOE_L4_BM 192
+#define MOE_L4_BM 256
 #endif
 #ifndef MOE_L4_BN
-#define MOE_L4_BN 192
+#define MOE_L4_BN 256
 #endif
 #ifndef MOE_L4_WM
 #define MOE_L4_WM 2
 #endif
 #ifndef MOE_L4_WN
-#define MOE_L4_WN 2
+#define MOE_L4_WN 4
 #endif
 template <int MODE, int FMT> struct LargeTileSel {
   using type = Tile<MOE_L_BM, MOE_L_BN, MOE_L_WM, MOE_L_WN, MOE_L_NS, MOE_L_BK, false>;
@@ -160,8 +160,11 @@ template <int MODE, int FMT> struct LargeTileSel {
 template <> struct LargeTileSel<1, 1> {
   using type = Tile<MOE_L41_BM, MOE_L41_BN, MOE_L41_WM, MOE_L41_WN, MOE_L_NS4, 64, false>;
 };
+#ifndef MOE_L4_SUPER
+#define MOE_L4_SUPER 1              // code super-stage of the large MXFP4 mlp2 tile (LDS)
+#endif
 template <> struct LargeTileSel<2, 1> {        // mlp2 with MXFP4 weights: h hi and lo parts
-  using type = Tile<MOE_L4_BM, MOE_L4_BN, MOE_L4_WM, MOE_L4_WN, MOE_L_NSH, 64, false>;
+  using type = Tile<MOE_L4_BM, MOE_L4_BN, MOE_L4_WM, MOE_L4_WN, MOE_L_NSH, 64, false, MOE_L4_SUPER>;
 };
 template <int MODE, int FMT> using LargeTile = typename LargeTileSel<MODE, FMT>::type;
 
