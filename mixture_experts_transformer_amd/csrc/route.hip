@@ -163,9 +163,17 @@ __global__ __launch_bounds__(64 * TK_WAVES) void topk_kernel(
     live[i] = e < E;
     v[i] = -INFINITY;
     if (live[i]) {
+      // all partials in flight at once (16 per batch), then added in split order
       double s = 0.0;
-#pragma unroll 8
-      for (int q = 0; q < ksplit; ++q) s += partial[((size_t)q * T + t) * E + e];
+      for (int q0 = 0; q0 < ksplit; q0 += 16) {
+        double pv[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          pv[q] = (q0 + q < ksplit) ? partial[((size_t)(q0 + q) * T + t) * E + e] : 0.0;
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          if (q0 + q < ksplit) s += pv[q];
+      }
       s += bf16_bits_to_f64(br[e]);
       v[i] = (float)s;   // round to nearest even
       if (logits) logits[(size_t)t * E + e] = v[i];
@@ -182,13 +190,27 @@ __global__ __launch_bounds__(64 * TK_WAVES) void topk_kernel(
       const int e = lane + 64 * i;
       if (live[i] && (be == NONE || beats(v[i], e, bv, be))) { bv = v[i]; be = e; }
     }
-    // wave argmax (butterfly: every lane ends with the same winner)
+    // wave argmax: the largest value by a butterfly on values alone, then the lowest expert
+    // holding it (a lane's own best already has the lowest index among its equal values)
+    float mv = (be == NONE) ? -INFINITY : bv;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oe = __shfl_xor(be, off);
-      if (oe != NONE && (be == NONE || beats(ov, oe, bv, be))) { bv = ov; be = oe; }
+    for (int off = 32; off >= 1; off >>= 1) mv = fmaxf(mv, __shfl_xor(mv, off));
+    // lanes whose best equals the maximum; among them the lowest expert index wins
+    const int cand = (be != NONE && bv == mv) ? be : NONE;
+    int ce = cand;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ce = min(ce, __shfl_xor(ce, off));
+    if (ce == NONE) {
+      // every remaining live value is NaN (outside the contract): keep the old rule, the
+      // lowest live expert wins, so the index is always valid
+      int le = be;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) le = min(le, __shfl_xor(le, off));
+      ce = le;
+      mv = __shfl(bv, 0);
     }
+    bv = mv;
+    be = ce;
 #pragma unroll
     for (int i = 0; i < PER; ++i)
       if (lane + 64 * i == be) live[i] = false;
