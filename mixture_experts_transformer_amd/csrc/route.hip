@@ -31,6 +31,7 @@ static __device__ __forceinline__ double bf16_bits_to_f64(uint32_t b) {
 // ------------------------------------------------------------------------------ router
 constexpr int RT_WAVES = 4;           // waves per workgroup, each owns 16 tokens
 constexpr int RT_CHUNK = 32;          // K elements per MFMA group (8 steps of K=4)
+constexpr int RT_PD = 4;              // chunks whose loads are in flight (up to 64 experts)
 
 int router_ksplit(int64_t T, int64_t D) {
   const int64_t chunks = D / RT_CHUNK;
@@ -75,33 +76,47 @@ __global__ __launch_bounds__(64 * RT_WAVES) void router_partial_kernel(
 #pragma unroll
   for (int b = 0; b < NEB; ++b) acc[b] = f64x4{0.0, 0.0, 0.0, 0.0};
 
-  uint4 xa = {0, 0, 0, 0};
-  uint4 wa[NEB];
-  if (c_begin < c_end) {
-    xa = *(const uint4*)(xrow + c_begin * RT_CHUNK);
+  // PD chunks in flight (fewer with many experts, for registers): slot q of the register
+  // ring holds chunk c0 + q
+  constexpr int PD = NEB >= 16 ? 1 : (NEB >= 8 ? 2 : RT_PD);
+  uint4 xa[PD];
+  uint4 wa[PD][NEB];
 #pragma unroll
-    for (int b = 0; b < NEB; ++b) wa[b] = *(const uint4*)(wrow[b] + c_begin * RT_CHUNK);
-  }
-  for (int c = c_begin; c < c_end; ++c) {
-    const uint4 xc = xa;
-    uint4 wc[NEB];
+  for (int q = 0; q < PD; ++q) {
+    xa[q] = uint4{0, 0, 0, 0};
 #pragma unroll
-    for (int b = 0; b < NEB; ++b) wc[b] = wa[b];
-    if (c + 1 < c_end) {   // prefetch the next chunk
-      xa = *(const uint4*)(xrow + (c + 1) * RT_CHUNK);
+    for (int b = 0; b < NEB; ++b) wa[q][b] = uint4{0, 0, 0, 0};
+    if (c_begin + q < c_end) {
+      xa[q] = *(const uint4*)(xrow + (c_begin + q) * RT_CHUNK);
 #pragma unroll
-      for (int b = 0; b < NEB; ++b) wa[b] = *(const uint4*)(wrow[b] + (c + 1) * RT_CHUNK);
+      for (int b = 0; b < NEB; ++b) wa[q][b] = *(const uint4*)(wrow[b] + (c_begin + q) * RT_CHUNK);
     }
-    const uint32_t xw[4] = {xc.x, xc.y, xc.z, xc.w};
+  }
+  for (int c0 = c_begin; c0 < c_end; c0 += PD) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t xb = (i & 1) ? (xw[i >> 1] >> 16) : (xw[i >> 1] & 0xFFFFu);
-      const double a = bf16_bits_to_f64(xb);
+    for (int q = 0; q < PD; ++q) {
+      const int c = c0 + q;
+      if (c >= c_end) break;
+      const uint4 xc = xa[q];
+      uint4 wc[NEB];
 #pragma unroll
-      for (int b = 0; b < NEB; ++b) {
-        const uint32_t ww[4] = {wc[b].x, wc[b].y, wc[b].z, wc[b].w};
-        const uint32_t wb = (i & 1) ? (ww[i >> 1] >> 16) : (ww[i >> 1] & 0xFFFFu);
-        acc[b] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bf16_bits_to_f64(wb), acc[b], 0, 0, 0);
+      for (int b = 0; b < NEB; ++b) wc[b] = wa[q][b];
+      if (c + PD < c_end) {   // refill the slot with the chunk PD ahead
+        xa[q] = *(const uint4*)(xrow + (c + PD) * RT_CHUNK);
+#pragma unroll
+        for (int b = 0; b < NEB; ++b) wa[q][b] = *(const uint4*)(wrow[b] + (c + PD) * RT_CHUNK);
+      }
+      const uint32_t xw[4] = {xc.x, xc.y, xc.z, xc.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t xb = (i & 1) ? (xw[i >> 1] >> 16) : (xw[i >> 1] & 0xFFFFu);
+        const double a = bf16_bits_to_f64(xb);
+#pragma unroll
+        for (int b = 0; b < NEB; ++b) {
+          const uint32_t ww[4] = {wc[b].x, wc[b].y, wc[b].z, wc[b].w};
+          const uint32_t wb = (i & 1) ? (ww[i >> 1] >> 16) : (ww[i >> 1] & 0xFFFFu);
+          acc[b] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bf16_bits_to_f64(wb), acc[b], 0, 0, 0);
+        }
       }
     }
   }
