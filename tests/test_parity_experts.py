@@ -35,16 +35,20 @@ def test_experts_workloads(name):
     experts_vs_oracle(make_inputs(name), name)
 
 
-# shapes chosen to cover both tile configurations, row tails inside a tile, column tails of
-# mlp1 (F not a multiple of the tile's pair count) and of mlp2 (D not a multiple of the tile
-# width), single-K-step and multi-step reductions
+# shapes chosen to cover both tile configurations (streaming 64x128 when T*k < 128*E, else
+# 256x256), row tails inside a tile, column tails of mlp1 (F not a multiple of the tile's
+# pair count: 64 or 128) and of mlp2 (D not a multiple of the tile width: 128 or 256),
+# single-K-step and multi-step reductions, and the degenerate layers
 @pytest.mark.parametrize("fmt", ["bf16", "mxfp4"])
 @pytest.mark.parametrize("T,D,E,k,F", [
-    (37, 128, 5, 2, 192),       # small tiles, ragged groups
-    (300, 64, 3, 3, 64),        # k = E
-    (1000, 192, 4, 2, 320),     # large tiles: mlp1 pair tail (320 = 3*96 + 32)
-    (700, 256, 2, 1, 128),      # large tiles: mlp2 column tail (256 = 192 + 64), k = 1
+    (37, 128, 5, 2, 192),       # streaming tiles, ragged groups, mlp1 pair tail (192 = 128 + 64)
+    (300, 64, 3, 3, 64),        # k = E, one K step
+    (1000, 192, 4, 2, 320),     # large tiles: mlp1 pair tail (320 = 2*128 + 64)
+    (700, 320, 2, 1, 128),      # large tiles: mlp2 column tail (320 = 256 + 64), k = 1
     (2500, 384, 8, 4, 448),     # large tiles, many row tiles per expert
+    (1, 64, 4, 2, 64),          # a single token
+    (513, 320, 1, 1, 192),      # E = k = 1 (a dense SwiGLU MLP): row tail 513 = 2*256 + 1
+    (200, 128, 256, 8, 128),    # 256 experts, most of them empty
 ])
 def test_experts_ragged_shapes(fmt, T, D, E, k, F):
     base = "C4" if fmt == "mxfp4" else "C2"
