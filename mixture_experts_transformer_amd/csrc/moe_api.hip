@@ -55,7 +55,7 @@ int ok() {
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t partial = 0, idx = 0, gates = 0, counts = 0, offsets = 0, perm = 0;
+  size_t partial = 0, hist = 0, idx = 0, gates = 0, counts = 0, offsets = 0, perm = 0;
   size_t h = 0, h_lo = 0, y = 0, total = 0;
 };
 
@@ -70,7 +70,10 @@ Layout layout(int64_t T, int64_t D, int64_t E, int64_t k, int64_t F, int fmt, in
     off += align256(bytes);
     return at;
   };
-  if (need & NEED_ROUTE) L.partial = take((size_t)moe::router_ksplit(T, D) * T * E * sizeof(double));
+  if (need & NEED_ROUTE) {
+    L.partial = take((size_t)moe::router_ksplit(T, D) * T * E * sizeof(double));
+    L.hist = take((size_t)moe::permute_groups(A) * E * 4);
+  }
   if (need & NEED_ROUTE_OUTPUTS) {
     L.idx = take(A * 4);
     L.gates = take(A * 4);
@@ -234,7 +237,7 @@ int moe_forward(const void* x, const void* router_w, const void* router_b, const
     return moe::launch_topk(partial, ks, (const uint16_t*)router_b, (int)T, (int)E, (int)k, nullptr, idx, gates, st);
   }));
   CHECK(launch(moe::ST_PERMUTE, "permute", [&](hipStream_t st) {
-    return moe::launch_permute(idx, (int)(T * k), (int)E, counts, offsets, perm, st);
+    return moe::launch_permute(idx, (int)(T * k), (int)E, (int32_t*)(ws + L.hist), counts, offsets, perm, st);
   }));
   CHECK(run_experts(ws, L, x, w1, b1, w2, b2, gates, offsets, perm, T, D, E, k, F, fmt, out));
   return ok();
@@ -268,7 +271,7 @@ int moe_route(const void* x, const void* router_w, const void* router_b, int64_t
                             st);
   }));
   CHECK(launch(moe::ST_PERMUTE, "permute", [&](hipStream_t st) {
-    return moe::launch_permute(topk_idx, (int)(T * k), (int)E, counts, offsets, perm, st);
+    return moe::launch_permute(topk_idx, (int)(T * k), (int)E, (int32_t*)(ws + L.hist), counts, offsets, perm, st);
   }));
   return ok();
 }

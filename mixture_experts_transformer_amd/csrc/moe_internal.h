@@ -25,9 +25,11 @@ hipError_t launch_router_partial(const uint16_t* x, const uint16_t* wr, int T, i
 // Sum of partials + bias -> fp32 logits, top-k (ties to lower index), softmax gates.
 hipError_t launch_topk(const double* partial, int ksplit, const uint16_t* br, int T, int E, int k,
                        float* logits, int32_t* idx, float* gates, hipStream_t st);
-// counts, exclusive offsets and the stable per-expert permutation of the T*k assignments.
-hipError_t launch_permute(const int32_t* idx, int A, int E, int32_t* counts, int32_t* offsets,
-                          int32_t* perm, hipStream_t st);
+// counts, exclusive offsets and the stable per-expert permutation of the A assignments.
+// hist: workspace of permute_groups(A) * E int32 (unused when permute_groups(A) == 1).
+int permute_groups(int64_t A);
+hipError_t launch_permute(const int32_t* idx, int A, int E, int32_t* hist, int32_t* counts,
+                          int32_t* offsets, int32_t* perm, hipStream_t st);
 
 // ---------------------------------------------------------------- experts
 struct ExpertArgs {

@@ -15,11 +15,12 @@
 // argmax.  Gates: softmax over the k selected logits, in fp64, stored as fp32.
 //
 // Grouping (torchtitan guide, grouped GEMM section: per-expert counts and their int32
-// cumulative sum as group offsets): one workgroup of 16 waves.  Each wave owns a
-// contiguous range of assignments, counts them per expert in LDS, and after a scan
-// places each assignment at offsets[e] + (earlier assignments of e), computing ranks
-// inside a 64-assignment step with ballots over the bits of the expert index.  The
-// result is the stable counting sort, independent of any atomic arrival order.
+// cumulative sum as group offsets): workgroups of 16 waves over chunks of the assignments
+// (one workgroup for few assignments; otherwise a per-chunk histogram pass first).  Each
+// wave owns a contiguous range, counts it per expert in LDS, and after a scan places each
+// assignment at offsets[e] + (earlier assignments of e), computing ranks inside a
+// 64-assignment step with ballots over the bits of the expert index.  The result is the
+// stable counting sort, independent of any atomic arrival order.
 #include "moe_internal.h"
 
 namespace moe {
@@ -254,33 +255,72 @@ hipError_t launch_topk(const double* partial, int ksplit, const uint16_t* br, in
 
 // ------------------------------------------------------------------------------ grouping
 constexpr int PM_WAVES = 16;
+constexpr int PM_CHUNK = 2048;        // assignments per workgroup when the grouping is split
 
+int permute_groups(int64_t A) {
+  const int64_t g = (A + PM_CHUNK - 1) / PM_CHUNK;
+  return g > 2 ? (int)g : 1;          // up to two chunks one workgroup is as fast
+}
+
+// Split grouping, pass 1: hist[g][e] = assignments of chunk g routed to expert e.
+__global__ __launch_bounds__(1024) void permute_hist_kernel(const int32_t* __restrict__ idx, int A, int E,
+                                                            int32_t* __restrict__ hist) {
+  __shared__ int h[256];
+  const int tid = threadIdx.x;
+  if (tid < 256) h[tid] = 0;
+  __syncthreads();
+  const int lo = blockIdx.x * PM_CHUNK;
+  const int hi = min(A, lo + PM_CHUNK);
+  for (int a = lo + tid; a < hi; a += blockDim.x) atomicAdd(&h[min(max(idx[a], 0), E - 1)], 1);
+  __syncthreads();
+  if (tid < E) hist[(size_t)blockIdx.x * E + tid] = h[tid];
+}
+
+// Grouping of the assignments [lo, hi) of this workgroup (all of them when hist is null;
+// chunk g = blockIdx.x of PM_CHUNK otherwise, placed after the chunks before it using the
+// histogram of pass 1).  Each wave owns a contiguous range, counts it per expert in LDS,
+// and after a scan places each assignment at its expert's base plus the earlier
+// assignments of that expert, ranked inside a 64-assignment step by ballots.
 __global__ __launch_bounds__(64 * PM_WAVES) void permute_kernel(
-    const int32_t* __restrict__ idx, int A, int E, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ perm) {
+    const int32_t* __restrict__ idx, int A, int E, const int32_t* __restrict__ hist, int G,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm) {
   __shared__ int cnt[PM_WAVES][256];
   __shared__ int base[PM_WAVES][256];
   __shared__ int tot[256];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int g = blockIdx.x;
+  const int c_lo = hist ? g * PM_CHUNK : 0;
+  const int c_hi = hist ? min(A, c_lo + PM_CHUNK) : A;
   for (int i = tid; i < PM_WAVES * 256; i += blockDim.x) (&cnt[0][0])[i] = 0;
   __syncthreads();
   // contiguous range per wave, a multiple of 64 long
-  const int per = ((A + PM_WAVES - 1) / PM_WAVES + 63) & ~63;
-  const int lo = min(A, wave * per);
-  const int hi = min(A, lo + per);
-  for (int a = lo + lane; a < hi; a += 64) atomicAdd(&cnt[wave][idx[a]], 1);
+  const int per = ((c_hi - c_lo + PM_WAVES - 1) / PM_WAVES + 63) & ~63;
+  const int lo = min(c_hi, c_lo + wave * per);
+  const int hi = min(c_hi, lo + per);
+  for (int a = lo + lane; a < hi; a += 64) atomicAdd(&cnt[wave][min(max(idx[a], 0), E - 1)], 1);
   __syncthreads();
-  // exclusive scan of the totals over experts (threads 0..255)
+  // totals over all assignments and, split, over the chunks before this one
+  int pre = 0;
   if (tid < 256) {
     int s = 0;
-    if (tid < E)
-      for (int w = 0; w < PM_WAVES; ++w) s += cnt[w][tid];
+    if (tid < E) {
+      if (hist) {
+        for (int q = 0; q < G; ++q) {
+          const int v = hist[(size_t)q * E + tid];
+          s += v;
+          if (q < g) pre += v;
+        }
+      } else {
+        for (int w = 0; w < PM_WAVES; ++w) s += cnt[w][tid];
+      }
+    }
     tot[tid] = s;
-    if (tid < E) counts[tid] = s;
+    if (tid < E && g == 0) counts[tid] = s;
   }
   __syncthreads();
+  // inclusive scan of the totals over experts (threads 0..255)
   for (int off = 1; off < 256; off <<= 1) {
     int v = 0;
     if (tid < 256 && tid >= off) v = tot[tid - off];
@@ -289,13 +329,16 @@ __global__ __launch_bounds__(64 * PM_WAVES) void permute_kernel(
     __syncthreads();
   }
   if (tid < E) {
-    int b = (tid == 0) ? 0 : tot[tid - 1];   // exclusive prefix
-    offsets[tid] = b;
+    const int first = (tid == 0) ? 0 : tot[tid - 1];   // exclusive prefix
+    if (g == 0) {
+      offsets[tid] = first;
+      if (tid == E - 1) offsets[E] = tot[tid];
+    }
+    int b = first + pre;
     for (int w = 0; w < PM_WAVES; ++w) {
       base[w][tid] = b;
       b += cnt[w][tid];
     }
-    if (tid == E - 1) offsets[E] = b;
   }
   __syncthreads();
   // place assignments: rank among equal experts inside each 64-wide step by ballots
@@ -304,7 +347,7 @@ __global__ __launch_bounds__(64 * PM_WAVES) void permute_kernel(
   for (int a0 = lo; a0 < hi; a0 += 64) {
     const int a = a0 + lane;
     const bool valid = a < hi;
-    const int e = valid ? idx[a] : 0;
+    const int e = valid ? min(max(idx[a], 0), E - 1) : 0;
     uint64_t match = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
       const uint64_t on = __ballot(valid && ((e >> b) & 1));
@@ -324,10 +367,16 @@ __global__ __launch_bounds__(64 * PM_WAVES) void permute_kernel(
   }
 }
 
-hipError_t launch_permute(const int32_t* idx, int A, int E, int32_t* counts, int32_t* offsets,
-                          int32_t* perm, hipStream_t st) {
-  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(64 * PM_WAVES), 0, st, idx, A, E, counts,
-                     offsets, perm);
+hipError_t launch_permute(const int32_t* idx, int A, int E, int32_t* hist, int32_t* counts,
+                          int32_t* offsets, int32_t* perm, hipStream_t st) {
+  const int G = permute_groups(A);
+  if (G > 1) {
+    hipLaunchKernelGGL(permute_hist_kernel, dim3(G), dim3(1024), 0, st, idx, A, E, hist);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(permute_kernel, dim3(G), dim3(64 * PM_WAVES), 0, st, idx, A, E,
+                     G > 1 ? (const int32_t*)hist : nullptr, G, counts, offsets, perm);
   return hipGetLastError();
 }
 
