@@ -38,8 +38,12 @@
  * are outside the contract (not checked on the device).
  *
  * Numerics: every product is accumulated in fp32 on the matrix cores except the
- * router (fp64).  The bf16 path rounds h to bf16 once; the MXFP4 path carries h
- * as a bf16 pair (hi + lo, 16 significant bits) into mlp2.  The output is fp32
+ * router (fp64).  The bf16 path rounds h to bf16 once.  With MXFP4 weights, small
+ * token counts carry h as a bf16 pair (hi + lo, 16 significant bits) into mlp2;
+ * large ones run both GEMMs on the scaled fp8 x fp4 matrix instructions, with x
+ * as two and h as three fp8 pieces that share one power-of-two scale per 32
+ * elements (x exactly but for values far below their block's largest; h to
+ * about 12 significant bits of the block's largest).  The output is fp32
  * and deterministic: no float atomics, fixed summation orders, bitwise equal
  * from run to run.
  *
@@ -47,8 +51,10 @@
  *   - Tensor pointers are DEVICE pointers owned by the caller; the library keeps
  *     none of them after the call returns.  Every pointer must be 16-byte
  *     aligned and non-null whenever T > 0 (logits may be null).
- *   - Shapes: 1 <= k <= E <= 256; D and F positive multiples of 64;
- *     0 <= T and T*k < 2^31.  T == 0 returns MOE_OK and launches nothing.
+ *   - Shapes: 1 <= k <= E <= 256; D and F positive multiples of 64 below 2^24;
+ *     0 <= T and T*k < 2^31; T*D, T*k*F and D*F below 2^30 (the expert kernels
+ *     address activation rows and one expert's weights with 32-bit offsets).
+ *     T == 0 returns MOE_OK and launches nothing.
  *   - Calls are asynchronous on the calling thread's stream (moe_set_stream)
  *     and return after enqueueing; device faults surface at the caller's next
  *     synchronisation.  Outputs are fully overwritten and must not alias inputs.
@@ -138,10 +144,11 @@ void moe_release(void);
 
 /* Kernel timing (tracing): while enabled, every launch is bracketed by HIP events on the
  * call's stream, and each kernel's summed device time and launch count accumulate per
- * stage.  Stages: 0 router, 1 top-k, 2 permute, 3 mlp1, 4 mlp2, 5 combine.
- * moe_profile_read synchronises on the recorded events; it fills ms[6] and launches[6]
- * (either may be NULL) and resets the counters. */
-#define MOE_NUM_STAGES 6
+ * stage.  Stages: 0 router, 1 top-k, 2 permute, 3 mlp1, 4 mlp2, 5 combine, 6 split (the
+ * fp8 pieces of the activations that the scaled matrix-core engine reads; MXFP4 weights
+ * at large token counts only).  moe_profile_read synchronises on the recorded events; it
+ * fills ms[7] and launches[7] (either may be NULL) and resets the counters. */
+#define MOE_NUM_STAGES 7
 int moe_profile_enable(int on);
 int moe_profile_read(double* ms, int64_t* launches);
 

@@ -166,11 +166,41 @@ template <> struct LargeTileSel<1, 1> {
 template <> struct LargeTileSel<2, 1> {        // mlp2 with MXFP4 weights: h hi and lo parts
   using type = Tile<MOE_L4_BM, MOE_L4_BN, MOE_L4_WM, MOE_L4_WN, MOE_L_NSH, 64, false, MOE_L4_SUPER>;
 };
+#ifndef MOE_LX_NS
+#define MOE_LX_NS 2                 // scaled-MFMA engine (fp8 activation pieces x MXFP4)
+#endif
+#ifndef MOE_LX_SUPER
+#define MOE_LX_SUPER 4
+#endif
+#ifndef MOE_LX2_SUPER
+#define MOE_LX2_SUPER 2             // mlp2 (three pieces of h per stage: LDS)
+#endif
+#ifndef MOE_LX_WM
+#define MOE_LX_WM 2
+#endif
+#ifndef MOE_LX_WN
+#define MOE_LX_WN 4
+#endif
+#ifndef MOE_LX2_WM
+#define MOE_LX2_WM MOE_LX_WM
+#endif
+#ifndef MOE_LX2_WN
+#define MOE_LX2_WN MOE_LX_WN
+#endif
+template <> struct LargeTileSel<1, 2> {
+  using type = Tile<256, 256, MOE_LX_WM, MOE_LX_WN, MOE_LX_NS, 64, false, MOE_LX_SUPER>;
+};
+template <> struct LargeTileSel<2, 2> {
+  using type = Tile<256, 256, MOE_LX2_WM, MOE_LX2_WN, MOE_LX_NS, 64, false, MOE_LX2_SUPER>;
+};
 template <int MODE, int FMT> using LargeTile = typename LargeTileSel<MODE, FMT>::type;
 
 struct GemmArgs {
   const uint16_t* a;        // mlp1: x [T][K]; mlp2: h (hi) [A][K]
   const uint16_t* a_lo;     // mlp2 + MXFP4: h lo [A][K]
+  const uint8_t* a8;        // scaled-MFMA engine: fp8 pieces of the A rows [rows][K / 64][pieces][64]
+  const uint32_t* a8s;      //   and their scales [rows][a8s_stride] (piece p in byte p)
+  int a8s_stride;           //   scale dwords per row (K / 32 rounded up to a multiple of 8)
   const int32_t* perm;
   const int32_t* offsets;
   const float* gates;
@@ -178,6 +208,9 @@ struct GemmArgs {
   const uint16_t* bias;     // [E][N]
   uint16_t* h;              // mlp1 output
   uint16_t* h_lo;
+  uint8_t* h8;              // mlp1 output for the scaled-MFMA engine: three fp8 pieces of h
+  uint32_t* h8s;            //   and their scales
+  int h8s_stride;
   float* y;                 // mlp2 output
   int E, k, K, N, F;
   int A;                    // routed rows (T * k)
@@ -235,17 +268,21 @@ static __device__ __forceinline__ bool tile_lookup(const TileScan& ts, const int
     }
     base += ts.tl[i];
   }
-  e_out = __shfl(e, src);
-  row0_out = __shfl(r0, src);
-  cnt_out = offsets[e_out + 1] - offsets[e_out];
+  e_out = __builtin_amdgcn_readfirstlane(__shfl(e, src));   // uniform: kept in scalar registers
+  row0_out = __builtin_amdgcn_readfirstlane(__shfl(r0, src));
+  cnt_out = __builtin_amdgcn_readfirstlane(offsets[e_out + 1] - offsets[e_out]);
   return true;
 }
 
 // LDS layout of a bf16 operand stage: [rows][BK] with the 16-byte chunks of a row
 // XOR-swizzled by row bits, which spreads the rows one chunk index touches over the banks.
+// Rows of twelve chunks (three fp8 pieces of 64 elements) XOR the two low chunk bits with
+// row bits 2..3, which keeps a chunk inside its aligned group of four: the 16-byte slots
+// of sixteen consecutive rows (row stride 192 bytes) then cover all 64 banks once.
 template <int CPR>
 static __device__ __forceinline__ int swz_pos(int r, int c) {
   if (CPR == 8) return c ^ (r & 7) ^ ((r >> 3) & 1);
+  if (CPR == 12) return c ^ ((r >> 2) & 3);
   return c ^ ((r >> 1) & 3) ^ ((r >> 3) & 1);
 }
 template <int CPR>
@@ -261,18 +298,28 @@ typedef __attribute__((address_space(3))) void lds_void;
 // reserved and does not preserve it around the asm; that is sound because nothing else in
 // these kernels uses M0 (tests/test_build.py checks the generated code for other uses).
 // Saving and restoring it in the asm measured up to 12 % slower.
+// Both are wave-uniform by construction; reading them from the first lane keeps them in
+// scalar registers where the compiler cannot prove uniformity itself.
 static __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
-  return (uint32_t)(uintptr_t)(const lds_void*)p;
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void*)p);
 }
-// 16 bytes per lane: lane L fills LDS bytes [dst + 16 L, +16).
-static __device__ __forceinline__ void dma16(const void* src, uint8_t* dst_wave) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(lds_addr(dst_wave)), "v"(src) : "memory", "m0");
+static __device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
-// One dword per lane: lane L fills LDS bytes [dst + 4 L, +4).
-static __device__ __forceinline__ void dma4(const void* src, uint8_t* dst_wave) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
-               :: "s"(lds_addr(dst_wave)), "v"(src) : "memory", "m0");
+// The source is a wave-uniform base (scalar registers) plus a per-lane 32-bit byte offset,
+// which keeps one vector register per copy slot instead of two.
+// 16 bytes per lane: lane L fills LDS bytes [dst + 16 L, +16) from base + off.
+static __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint8_t* dst_wave) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds_addr(dst_wave)), "v"(off), "s"(uniform_ptr(base)) : "memory", "m0");
+}
+// One dword per lane: lane L fills LDS bytes [dst + 4 L, +4) from base + off.
+static __device__ __forceinline__ void dma4(const void* base, uint32_t off, uint8_t* dst_wave) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               :: "s"(lds_addr(dst_wave)), "v"(off), "s"(uniform_ptr(base)) : "memory", "m0");
 }
 
 // s_waitcnt vmcnt(N) with the LDS/export counters left alone (gfx9 encoding).
@@ -309,6 +356,38 @@ static __device__ __forceinline__ bf16x8 decode_fp4x8(uint32_t codes, float scal
   const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
   const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
   return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// fp8 pieces (OCP E4M3: 3 mantissa bits, exponent bias 7, largest finite 448) of values
+// that share one E8M0 scale per 32-element block.  The piece scale for a block whose
+// largest remaining magnitude is m is the smallest power of two 2^(e - 127) with
+// m / 2^(e - 127) <= 448, so no value rounds past the fp8 range: with m = 1.f 2^x,
+// 2^(x - 8) maps m into [256, 512), and one more halving is needed when 1.f > 1.75.
+static __device__ __forceinline__ int mx_scale_exp(float m) {
+  if (!(m > 0.f)) return 0;                 // all-zero block (scale 2^-127)
+  const uint32_t mb = __float_as_uint(m);
+  const int x = (int)(mb >> 23) - 127;
+  const int q = x - 8 + ((mb & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return min(max(q + 127, 0), 254);
+}
+static __device__ __forceinline__ float mx_inv_scale(int e) { return __uint_as_float((uint32_t)(254 - e) << 23); }
+static __device__ __forceinline__ float mx_scale(int e) {
+  return e ? __uint_as_float((uint32_t)e << 23) : __uint_as_float(0x00400000u);   // 2^-127 is subnormal
+}
+// Four values times inv rounded to fp8 (nearest even), packed in order into one dword; when
+// `residual`, what the codes represent (times scl) is subtracted from the values.
+static __device__ __forceinline__ uint32_t mx_piece4(float* v, float inv, float scl, bool residual) {
+  int pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[0] * inv, v[1] * inv, 0, false);
+  pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[2] * inv, v[3] * inv, pk, true);
+  if (residual) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(pk, false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(pk, true);
+    v[0] -= lo[0] * scl;
+    v[1] -= lo[1] * scl;
+    v[2] -= hi[0] * scl;
+    v[3] -= hi[1] * scl;
+  }
+  return (uint32_t)pk;
 }
 
 // ------------------------------------------------------------------------------ kernel
@@ -363,10 +442,17 @@ template <int MODE, int FMT, class C>
 __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, CPR = C::CPR, NS = C::NS, NW = C::NW;
   constexpr int FM = C::FM, FN = C::FN;
-  constexpr int KS = BK / 16;                               // MFMA K steps per stage
-  constexpr int AP = (MODE == 2 && FMT == 1) ? 2 : 1;      // A parts (h hi, h lo)
+  constexpr bool MX = FMT == 2;                             // scaled MFMA on fp8 pieces
+  constexpr int KS = MX ? 1 : BK / 16;                      // MFMA K steps per stage
+  // A parts: bf16 (1), h hi + lo (2), or fp8 pieces (x: 2, h: 3)
+  constexpr int AP = MX ? (MODE == 1 ? 2 : 3) : ((MODE == 2 && FMT == 1) ? 2 : 1);
   constexpr int ROWB = CPR * 16;                            // bytes per bf16 row segment
-  constexpr int A_BYTES = BM * ROWB;                        // per A part per stage
+  constexpr int APL = MX ? 1 : AP;                          // A parts in LDS (pieces share rows)
+  constexpr int A_CPR = MX ? 4 * AP : CPR;                  // 16-byte chunks per A row per stage
+  constexpr int A_ROWB = A_CPR * 16;
+  constexpr int A_CPC = BM * A_CPR / 64;                    // A copies per part and stage
+  constexpr int A_BYTES = BM * A_ROWB;                      // per A part per stage
+  static_assert((BM * A_CPR) % 64 == 0, "A stage must tile the copy instructions");
   static_assert(FMT == 0 || BK == 64, "MXFP4 staging assumes 64-wide K steps");
   constexpr int SUPER = C::SUPER;                           // stages per MXFP4 code super-stage
   constexpr int NSB = 2;                                    // code super-stage slots
@@ -376,31 +462,42 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
   constexpr int CROW = 32 * SUPER;                          // code bytes per row per super-stage
   constexpr int CCH = CROW / 16;                            // 16-byte code chunks per row
   constexpr int B_STAGE_BYTES = (FMT == 0) ? BN * ROWB : BN * 4;   // bf16 B tile, or scale dwords
-  constexpr int STAGE = AP * A_BYTES + B_STAGE_BYTES;
+  constexpr int STAGE = APL * A_BYTES + B_STAGE_BYTES;
   constexpr int CODE_SLOT = BN * CROW;
-  constexpr int CODE_BYTES = (FMT == 1) ? NSB * CODE_SLOT : 0;
-  constexpr int ROWS_PER_CP = 1024 / ROWB;                  // bf16 rows per copy instruction
-  constexpr int NA = AP * (BM / ROWS_PER_CP);               // per stage: A copies
+  constexpr int CODE_BYTES = (FMT != 0) ? NSB * CODE_SLOT : 0;
+  constexpr int ROWS_PER_CP = 1024 / ROWB;                  // bf16 B rows per copy instruction
+  constexpr int NA = APL * A_CPC;                           // per stage: A copies
   constexpr int NBS = (FMT == 0) ? BN / ROWS_PER_CP : BN / 64;   // per stage: B copies / scale copies
   constexpr int NG = NA + NBS;                              // copies per stage group
-  constexpr int NC = (FMT == 1) ? BN * CROW / 1024 : 0;     // copies per code super-stage
+  constexpr int NC = (FMT != 0) ? BN * CROW / 1024 : 0;     // copies per code super-stage
+  // scaled-MFMA engine: A scale dwords (two per row and stage) in a ring of super-stages
+  // beside the codes, 8 SUPER bytes per row, chunks swizzled by row bit 3
+  constexpr int ASL_ROW = MX ? 8 * SUPER : 16;
+  constexpr int ASL_SLOT = BM * ASL_ROW;
+  constexpr int ASL_BYTES = MX ? NSB * ASL_SLOT : 0;
+  constexpr int NASC = MX ? BM * ASL_ROW / 1024 : 0;        // A scale copies per super-stage
+  constexpr int NCT = NC + NASC;
+  static_assert(!MX || (SUPER >= 2 && 1024 % ASL_ROW == 0), "A scale super-stage granularity");
   constexpr int PW_G = (NG + NW - 1) / NW;
-  constexpr int PW_C = (NC + NW - 1) / NW + (NC == 0 ? 1 : 0);
+  constexpr int PW_C = (NCT + NW - 1) / NW + (NCT == 0 ? 1 : 0);
   constexpr int PN = BN / 2;                                // mlp1: pairs per tile
   static_assert(BN % 32 == 0 && (BM * CPR) % 64 == 0 && (BN * CPR) % 64 == 0, "copy granularity");
   static_assert(FMT == 0 || BN % 64 == 0, "scale copies cover 64 rows");
 
-  constexpr int SMEM = NS * STAGE + CODE_BYTES;
+  constexpr int SMEM = NS * STAGE + CODE_BYTES + ASL_BYTES;
   // epilogue slices (per wave, 32 output rows): mlp1 bf16 [32][pairs] (+ lo part), row
   // stride 2 P + 8 bytes so the four 16-lane groups of one store hit disjoint banks; mlp2
   // fp32 [32][WTN], row stride 4 WTN + 32 bytes so the two lane halves hit disjoint banks
   constexpr int EP_P = C::WTN / 2;
-  constexpr int EP_S = (MODE == 1) ? 2 * EP_P + 8 : 4 * C::WTN + 32;
+  // (scaled-MFMA engine, mlp1: fp32 [32][32 pairs], one MXFP8 block of h per row)
+  constexpr int EP_S = (MODE == 1) ? (MX ? 4 * EP_P + 16 : 2 * EP_P + 8) : 4 * C::WTN + 32;
   constexpr int EP_REG = 32 * EP_S * ((MODE == 1 && FMT == 1) ? 2 : 1);
+  static_assert(!(MX && MODE == 1) || EP_P % 32 == 0, "whole 32-element blocks of h per wave and row");
   static_assert(NW * EP_REG <= SMEM, "epilogue slices exceed the operand ring");
   constexpr int ROWTAB = (MODE == 2) ? BM * 8 : 0;          // mlp2: assignment and gate per tile row
   __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM + ROWTAB];
   uint8_t* const codes_lds = smem + NS * STAGE;
+  uint8_t* const ascale_lds = codes_lds + CODE_BYTES;       // scaled-MFMA engine: A scales
   int* const tab_a = (int*)(smem + SMEM);
   float* const tab_g = (float*)(smem + SMEM + BM * 4);
 
@@ -455,16 +552,27 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
     rt_a = ((unsigned)a < (unsigned)p.A) ? a : -1;
   }
 
+  // A row behind tile row r (clamped into the group): mlp1 gathers token rows, mlp2 reads
+  // the routed rows in place
+  auto a_row = [&](int r) -> size_t {
+    const int rc = min(r, rows - 1);
+    if (MODE == 1) {
+      int asg = p.perm[gbase + rc];
+      asg = ((unsigned)asg < (unsigned)p.A) ? asg : 0;
+      return (size_t)(asg / p.k);
+    }
+    return (size_t)(gbase + rc);
+  };
+
   const uint8_t* w_e;
-  const uint8_t* s_e = nullptr;
   size_t s_e_off = 0;                       // byte offset of expert e's scales in p.w
   if (FMT == 0) {
     w_e = p.w + (size_t)e * p.N * K * 2;
   } else {
     w_e = p.w + (size_t)e * p.N * (K / 2);
     s_e_off = (size_t)p.E * p.N * (K / 2) + (size_t)e * p.N * (K / 32);
-    s_e = p.w + s_e_off;
   }
+  const uint8_t* const s_e4 = p.w + (s_e_off & ~(size_t)3);   // scale copies read aligned dwords
   // tile row -> weight row, clamped into the matrix.  mlp1 tiles interleave the halves in
   // 16-row groups: rows 32 j .. 32 j + 15 are gate rows of pairs 16 j .. 16 j + 15 and rows
   // 32 j + 16 .. 32 j + 31 the linear rows of the same pairs, so every 32-column output
@@ -474,56 +582,59 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
              : min(n_tile * BN + (rr), p.N - 1))
 
   // ---- this wave's copy slots: global byte source for K step 0 and LDS offset
-  const uint8_t* gsrc[PW_G];
+  // source offsets relative to the slot kind's base: A rows (x, h, h lo or pieces), the
+  // expert's bf16 weight rows, or the 4-aligned start of the expert's scale bytes
+  uint32_t goff[PW_G];
   int gdst[PW_G];
 #pragma unroll
   for (int j = 0; j < PW_G; ++j) {
     const int i = wave + j * NW;
-    gsrc[j] = p.w;
+    goff[j] = 0;
     gdst[j] = 0;
     if (i < NA) {
-      const int part = i / (BM / ROWS_PER_CP);
-      const int ii = i % (BM / ROWS_PER_CP);
-      const int r = ii * ROWS_PER_CP + lane / CPR;
-      const int c = swz_pos<CPR>(r, lane % CPR);           // logical chunk at this position
-      const int rc = min(r, rows - 1);
-      size_t elem;
-      if (MODE == 1) {
-        int asg = p.perm[gbase + rc];
-        asg = ((unsigned)asg < (unsigned)p.A) ? asg : 0;
-        elem = (size_t)(asg / p.k) * K;
+      const int part = i / A_CPC;
+      const int ii = i % A_CPC;
+      const int idx = ii * 64 + lane;                      // chunk of the part's stage tile
+      const int r = idx / A_CPR;
+      const int c = swz_pos<A_CPR>(r, idx % A_CPR);        // logical chunk at this position
+      if (MX) {
+        goff[j] = (uint32_t)(a_row(r) * (size_t)(AP * K) + c * 16);
       } else {
-        elem = (size_t)(gbase + rc) * K;
+        goff[j] = (uint32_t)((a_row(r) * K + c * 8) * 2);
       }
-      const uint16_t* base = part == 0 ? p.a : p.a_lo;
-      gsrc[j] = (const uint8_t*)(base + elem + c * 8);
       gdst[j] = part * A_BYTES + ii * 1024;
     } else if (i < NG) {
       const int ii = i - NA;
       if (FMT == 0) {
         const int r = ii * ROWS_PER_CP + lane / CPR;
         const int c = swz_pos<CPR>(r, lane % CPR);
-        gsrc[j] = w_e + ((size_t)MOE_WROW(r) * K + c * 8) * 2;
-        gdst[j] = AP * A_BYTES + ii * 1024;
+        goff[j] = (uint32_t)(((size_t)MOE_WROW(r) * K + c * 8) * 2);
+        gdst[j] = APL * A_BYTES + ii * 1024;
       } else {
         const int r = ii * 64 + lane;
-        gsrc[j] = s_e + (size_t)MOE_WROW(r) * (K / 32);   // scale byte (r, block 0)
-        gdst[j] = AP * A_BYTES + ii * 256;
+        goff[j] = (uint32_t)((s_e_off & 3) + (size_t)MOE_WROW(r) * (K / 32));   // scale byte (r, block 0)
+        gdst[j] = APL * A_BYTES + ii * 256;
       }
     }
   }
-  const uint8_t* csrc[PW_C];
+  uint32_t coff[PW_C];                      // relative to the expert's codes or the A scales
   int cdst[PW_C];
 #pragma unroll
   for (int j = 0; j < PW_C; ++j) {
     const int i = wave + j * NW;
-    csrc[j] = p.w;
+    coff[j] = 0;
     cdst[j] = 0;
-    if (FMT == 1 && i < NC) {
+    if (FMT != 0 && i < NC) {
       const int r = i * (1024 / CROW) + lane / CCH;
       const int c = (lane % CCH) ^ code_swz<CCH>(r);
-      csrc[j] = w_e + (size_t)MOE_WROW(r) * (K / 2) + c * 16;
+      coff[j] = (uint32_t)((size_t)MOE_WROW(r) * (K / 2) + c * 16);
       cdst[j] = i * 1024;
+    } else if (i < NCT) {
+      constexpr int CPS = ASL_ROW / 16;                    // chunks per row
+      const int r = (i - NC) * (1024 / ASL_ROW) + lane / CPS;
+      const int c = (lane % CPS) ^ (CPS > 1 ? (r >> 3) & (CPS - 1) : 0);
+      coff[j] = (uint32_t)((a_row(r) * (size_t)p.a8s_stride + c * 4) * 4);
+      cdst[j] = (i - NC) * 1024;
     }
   }
 
@@ -539,13 +650,16 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
   do {                                                                                           \
     _Pragma("unroll") for (int j = 0; j < PW_G; ++j) {                                           \
       const int i_ = wave + j * NW;                                                              \
-      if (i_ < NG && !(i_ < NA && (i_ % (BM / ROWS_PER_CP)) * ROWS_PER_CP >= rows)) {           \
+      if (i_ < NG && !(i_ < NA && (i_ % A_CPC) * 64 / A_CPR >= rows)) {                         \
         uint8_t* d_ = smem + (slot) * STAGE + gdst[j];                                           \
-        if (FMT == 1 && i_ >= NA) {                                                              \
-          const uintptr_t sp_ = (uintptr_t)(gsrc[j] + (kt) * (BK / 32));                         \
-          dma4((const void*)(sp_ & ~(uintptr_t)3), d_);                                          \
+        if (i_ < NA) {                                                                           \
+          const void* ab_ = MX ? (const void*)p.a8                                               \
+                                : (i_ < A_CPC ? (const void*)p.a : (const void*)p.a_lo);          \
+          dma16((const uint8_t*)ab_ + (size_t)(kt) * A_ROWB, goff[j], d_);                       \
+        } else if (FMT != 0) {                                                                   \
+          dma4(s_e4, (goff[j] + (kt) * (BK / 32)) & ~3u, d_);                                    \
         } else {                                                                                 \
-          dma16(gsrc[j] + (size_t)(kt) * ROWB, d_);                                              \
+          dma16(w_e + (size_t)(kt) * ROWB, goff[j], d_);                                         \
         }                                                                                        \
         ++issued;                                                                                \
       }                                                                                          \
@@ -555,8 +669,12 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
   do {                                                                                           \
     _Pragma("unroll") for (int j = 0; j < PW_C; ++j) {                                           \
       const int i_ = wave + j * NW;                                                              \
-      if (FMT == 1 && i_ < NC) {                                                                 \
-        dma16(csrc[j] + (size_t)(sk) * CROW, codes_lds + ((sk) % NSB) * CODE_SLOT + cdst[j]);   \
+      if (FMT != 0 && i_ < NC) {                                                                 \
+        dma16(w_e + (size_t)(sk) * CROW, coff[j], codes_lds + ((sk) % NSB) * CODE_SLOT + cdst[j]); \
+        ++issued;                                                                                \
+      } else if (i_ < NCT && ((i_ - NC) * (1024 / ASL_ROW)) < rows) {                            \
+        dma16((const uint8_t*)p.a8s + (size_t)(sk) * ASL_ROW, coff[j],                           \
+              ascale_lds + ((sk) % NSB) * ASL_SLOT + cdst[j]);                                   \
         ++issued;                                                                                \
       }                                                                                          \
     }                                                                                            \
@@ -564,7 +682,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
   // everything a K step needs, codes first so the group's completion implies theirs
 #define MOE_ISSUE(kt)                                                                            \
   do {                                                                                           \
-    if (FMT == 1 && (kt) % SUPER == 0) MOE_ISSUE_CODES((kt) / SUPER);                            \
+    if (FMT != 0 && (kt) % SUPER == 0) MOE_ISSUE_CODES((kt) / SUPER);                            \
     MOE_ISSUE_GROUP(kt, (kt) % NS);                                                              \
     mark[(kt) % NS] = issued;                                                                    \
   } while (0)
@@ -584,7 +702,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
   for (int j = 0; j < FN; ++j) {
     brow[j] = wn * C::WTN + j * 32 + (lane & 31);
     sbyte[j] = 0;
-    if (FMT == 1) sbyte[j] = (int)((s_e_off + (size_t)MOE_WROW(brow[j]) * (K / 32)) & 3);
+    if (FMT != 0) sbyte[j] = (int)((s_e_off + (size_t)MOE_WROW(brow[j]) * (K / 32)) & 3);
   }
   const int arow0 = wm * C::WTM + (lane & 31);
   const int kg = lane >> 5;                 // which half of the stage's K range this lane feeds
@@ -660,12 +778,100 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
     }                                                                                            \
     MOE_MMA((KS - 1) & 1, FA);                                                                   \
   } while (0)
-  // Row blocks of 32 past the tile's rows hold only padding: when every wave's rows fit in
-  // its first block, the other blocks' copies (above) and matrix instructions are skipped.
-  if (C::WAVES_M == 1 && FM == 2 && rows <= 32) {
-    MOE_MAIN_LOOP(1);
+  if constexpr (!MX) {
+    // Row blocks of 32 past the tile's rows hold only padding: when every wave's rows fit in
+    // its first block, the other blocks' copies (above) and matrix instructions are skipped.
+    if (C::WAVES_M == 1 && FM == 2 && rows <= 32) {
+      MOE_MAIN_LOOP(1);
+    } else {
+      MOE_MAIN_LOOP(FM);
+    }
   } else {
-    MOE_MAIN_LOOP(FM);
+    // Scaled matrix-core engine, one 64-wide K step per stage.  Per stage a lane loads its B
+    // codes and scale bytes and the A scale records of its row blocks, then the A pieces one
+    // row block ahead of the block it multiplies.  The last row block of a stage multiplies
+    // after the next stage's barrier, behind that stage's first loads.
+    i32x8 fap[AP], fbp[FN];                 // deferred operands of the previous stage
+    uint32_t sap, sbp[FN];
+#define MX_LOAD_A(dst, i_)                                                                       \
+  do {                                                                                           \
+    _Pragma("unroll") for (int pa = 0; pa < AP; ++pa) {                                          \
+      const int r_ = arow0 + 32 * (i_);                                                          \
+      const i32x4 lo_ = *(const i32x4*)(sa + swz<A_CPR>(r_, 2 * AP * kg + 2 * pa));              \
+      const i32x4 hi_ = *(const i32x4*)(sa + swz<A_CPR>(r_, 2 * AP * kg + 2 * pa + 1));          \
+      (dst)[pa] = __builtin_shufflevector(lo_, hi_, 0, 1, 2, 3, 4, 5, 6, 7);                     \
+    }                                                                                            \
+  } while (0)
+    // the scale dword of this lane's row and K block holds piece pa's scale in byte pa,
+    // which op_sel selects
+#define MX_MMA(i_, FA, FB, SA, SB)                                                               \
+  do {                                                                                           \
+    _Pragma("unroll") for (int pa = 0; pa < AP; ++pa)                                            \
+    _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                             \
+      if (pa == 0)                                                                               \
+        acc[i_][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                             \
+            (FA)[pa], (FB)[j], acc[i_][j], 0, 4, 0, (int)(SA), 0, (int)(SB)[j]);                  \
+      else if (pa == 1)                                                                          \
+        acc[i_][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                             \
+            (FA)[pa], (FB)[j], acc[i_][j], 0, 4, 1, (int)(SA), 0, (int)(SB)[j]);                  \
+      else                                                                                       \
+        acc[i_][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                             \
+            (FA)[pa], (FB)[j], acc[i_][j], 0, 4, 2, (int)(SA), 0, (int)(SB)[j]);                  \
+    }                                                                                            \
+  } while (0)
+    for (int kt = 0; kt < nk; ++kt) {
+      const int slot = kt % NS;
+      wait_vmcnt_dyn(__builtin_amdgcn_readfirstlane(issued - mark[slot]));
+      wait_lgkmcnt0();
+      barrier_nofence();
+      if (MODE == 2 && kt == 0 && rt_a >= 0) rt_g = p.gates[rt_a];
+      if (kt + NS - 1 < nk) MOE_ISSUE(kt + NS - 1);
+
+      const uint8_t* sa = smem + slot * STAGE;
+      const uint8_t* sas = ascale_lds + ((kt / SUPER) % NSB) * ASL_SLOT;
+      const uint8_t* sb = sa + A_BYTES;
+      const uint8_t* cs = codes_lds + ((kt / SUPER) % NSB) * CODE_SLOT;
+      const int chunk = 2 * (kt % SUPER) + kg;
+      i32x8 fb[FN];
+      uint32_t sbv[FN];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const i32x4 q = *(const i32x4*)(cs + brow[j] * CROW + ((chunk ^ code_swz<CCH>(brow[j])) << 4));
+        fb[j] = __builtin_shufflevector(q, q, 0, 1, 2, 3, -1, -1, -1, -1);
+        sbv[j] = sb[brow[j] * 4 + ((sbyte[j] + 2 * kt + kg) & 3)];
+      }
+      uint32_t sav[FM];
+      const int dw = (kt % SUPER) * 2 + kg;                // scale dword of this stage and K block
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = arow0 + 32 * i;
+        const int pos = (dw >> 2) ^ (ASL_ROW > 16 ? (r >> 3) & (ASL_ROW / 16 - 1) : 0);
+        sav[i] = *(const uint32_t*)(sas + r * ASL_ROW + pos * 16 + (dw & 3) * 4);
+      }
+      i32x8 fa[2][AP];
+      MX_LOAD_A(fa[0], 0);
+      if (kt > 0) MX_MMA(FM - 1, fap, fbp, sap, sbp);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * FN + FM + 2 * AP, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, AP * FN, 0);
+#pragma unroll
+      for (int i = 0; i + 1 < FM; ++i) {
+        MX_LOAD_A(fa[(i + 1) & 1], i + 1);
+        MX_MMA(i, fa[i & 1], fb, sav[i], sbv);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * AP, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, AP * FN, 0);
+      }
+#pragma unroll
+      for (int pa = 0; pa < AP; ++pa) fap[pa] = fa[(FM - 1) & 1][pa];
+      sap = sav[FM - 1];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        fbp[j] = fb[j];
+        sbp[j] = sbv[j];
+      }
+    }
+    MX_MMA(FM - 1, fap, fbp, sap, sbp);
+#undef MX_LOAD_A
+#undef MX_MMA
   }
 #undef MOE_MAIN_LOOP
 #undef MOE_LOAD_FRAGS
@@ -720,11 +926,54 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
           const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(gc * SWIGLU_NEG_ALPHA_LOG2E));
           const float hv = gc * sg * (lc + 1.0f);
           const int r = 8 * (q >> 2) + rlane + (q & 3);
-          const __bf16 hi = (__bf16)hv;                    // round to nearest even
-          __bf16* d = (__bf16*)(ep + r * EP_S) + j * 16 + pl;
-          d[0] = hi;
-          if (FMT == 1) d[32 * EP_S / 2] = (__bf16)(hv - (float)hi);
+          if (MX) {
+            *(float*)(ep + r * EP_S + (j * 16 + pl) * 4) = hv;
+          } else {
+            const __bf16 hi = (__bf16)hv;                  // round to nearest even
+            __bf16* d = (__bf16*)(ep + r * EP_S) + j * 16 + pl;
+            d[0] = hi;
+            if (FMT == 1) d[32 * EP_S / 2] = (__bf16)(hv - (float)hi);
+          }
         }
+      }
+      if constexpr (MX) {
+        // three fp8 pieces of each 32-element block of the rows, in the layout the
+        // matrix-core loop of mlp2 reads (the split kernel's): lane l takes half l & 1 of
+        // row l >> 1
+        const int r = lane >> 1, hh = lane & 1;
+        const int rl = wm * C::WTM + i * 32 + r;
+        const size_t row = (size_t)(gbase + rl);
+#pragma unroll
+        for (int bb = 0; bb < EP_P / 32; ++bb) {
+        const int f0 = f_wave + 32 * bb;
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const f32x4 w4 = *(const f32x4*)(ep + r * EP_S + bb * 128 + hh * 64 + u * 16);
+          v[4 * u] = w4[0]; v[4 * u + 1] = w4[1]; v[4 * u + 2] = w4[2]; v[4 * u + 3] = w4[3];
+        }
+        const bool st = rl < rows && f0 < p.F;
+        uint8_t* const dst = p.h8 + row * (size_t)(3 * p.F) + (f0 >> 6) * 192 + ((f0 >> 5) & 1) * 16 + hh * 96;
+        uint32_t sc = 0;
+#pragma unroll
+        for (int pc = 0; pc < 3; ++pc) {
+          float m = 0.f;
+#pragma unroll
+          for (int u = 0; u < 16; ++u) m = fmaxf(m, fabsf(v[u]));
+          m = fmaxf(m, __shfl_xor(m, 1));
+          const int se = mx_scale_exp(m);
+          sc |= (uint32_t)se << (8 * pc);
+          const float inv = mx_inv_scale(se), scl = mx_scale(se);
+          uint4 o;
+          o.x = mx_piece4(v, inv, scl, pc < 2);
+          o.y = mx_piece4(v + 4, inv, scl, pc < 2);
+          o.z = mx_piece4(v + 8, inv, scl, pc < 2);
+          o.w = mx_piece4(v + 12, inv, scl, pc < 2);
+          if (st) *(uint4*)(dst + pc * 32) = o;
+        }
+        if (st && hh == 0) p.h8s[row * p.h8s_stride + (f0 >> 5)] = sc;
+        }
+        continue;
       }
 #pragma unroll
       for (int t = 0; t < (32 * CH + 63) / 64; ++t) {
@@ -802,30 +1051,112 @@ static hipError_t launch_gemm(GemmArgs g, int64_t A, hipStream_t st) {
 
 template <int MODE>
 static hipError_t launch_any(const GemmArgs& g, int fmt, int cfg, int64_t A, hipStream_t st) {
+  if (fmt == 2) return launch_gemm<MODE, 2, LargeTile<MODE, 2>>(g, A, st);
   if (fmt == 0)
     return cfg == 0 ? launch_gemm<MODE, 0, SmallTile<MODE, 0>>(g, A, st) : launch_gemm<MODE, 0, LargeTile<MODE, 0>>(g, A, st);
   return cfg == 0 ? launch_gemm<MODE, 1, SmallTile<MODE, 1>>(g, A, st)
                   : launch_gemm<MODE, 1, LargeTile<MODE, 1>>(g, A, st);
 }
 
+bool mx_engine(int fmt, int cfg) { return fmt == 1 && cfg == 1; }
+
 hipError_t launch_mlp1(const ExpertArgs& a, int cfg, hipStream_t st) {
   GemmArgs g{};
   g.a = a.x; g.a_lo = nullptr; g.perm = a.perm; g.offsets = a.offsets; g.gates = a.gates;
+  g.a8 = a.xq; g.a8s = a.xs; g.a8s_stride = mx_scale_stride(a.D);
+  g.h8 = a.hq; g.h8s = a.hs; g.h8s_stride = mx_scale_stride(a.F);
   g.w = (const uint8_t*)a.w1; g.bias = a.b1; g.h = a.h; g.h_lo = a.h_lo; g.y = nullptr;
   g.E = a.E; g.k = a.k; g.K = a.D; g.N = 2 * a.F; g.F = a.F;
   const int64_t A = (int64_t)a.T * a.k;
   g.A = (int)A;
-  return launch_any<1>(g, a.fmt, cfg, A, st);
+  return launch_any<1>(g, mx_engine(a.fmt, cfg) ? 2 : a.fmt, cfg, A, st);
 }
 
 hipError_t launch_mlp2(const ExpertArgs& a, int cfg, hipStream_t st) {
   GemmArgs g{};
   g.a = a.h; g.a_lo = a.h_lo; g.perm = a.perm; g.offsets = a.offsets; g.gates = a.gates;
+  g.a8 = a.hq; g.a8s = a.hs; g.a8s_stride = mx_scale_stride(a.F);
   g.w = (const uint8_t*)a.w2; g.bias = a.b2; g.h = nullptr; g.h_lo = nullptr; g.y = a.y;
   g.E = a.E; g.k = a.k; g.K = a.F; g.N = a.D; g.F = a.F;
   const int64_t A = (int64_t)a.T * a.k;
   g.A = (int)A;
-  return launch_any<2>(g, a.fmt, cfg, A, st);
+  return launch_any<2>(g, mx_engine(a.fmt, cfg) ? 2 : a.fmt, cfg, A, st);
+}
+
+// ------------------------------------------------------------------------------ fp8 pieces
+// Activations for the scaled matrix-core engine, whose A operand is fp8 E4M3 with one
+// E8M0 scale per 32 K elements (OCP microscaling formats: E4M3 has 3 mantissa bits,
+// exponent bias 7, largest finite 448).  Every 32-element block of a row is written as NP
+// pieces, v ~ sum_p q_p 2^(s_p - 127): piece p rounds (to nearest even) what the earlier
+// pieces left, divided by a power of two chosen from the block's largest remainder m,
+// 2^(s - 127) = the smallest power of two with m / 2^(s - 127) <= 448, so no value rounds
+// past the fp8 range.  Each piece keeps four significant bits of every value within the
+// block's normal range; two pieces hold a bf16 value (eight bits) exactly unless it is
+// far below its block's largest.
+//
+// Layout: one 64-element group of a row (64 NP bytes) per stage of the matrix-core loop,
+// as 16-byte chunks indexed c = 2 NP h + 2 p + t: piece p, elements 32 t + 16 h .. +15 of
+// the group.  Lane half h of the matrix instruction takes elements 16h..16h+15 and
+// 32+16h..32+16h+15 of a K step, so each lane reads two consecutive chunks per piece, and
+// the two lane halves read chunks 2 NP apart (different LDS banks under the row swizzle).
+// Row r, group g starts at byte (r K / 64 + g) 64 NP.  Scales: one dword per row and
+// 32-element block at rec[r * RS + b], piece p's E8M0 scale in byte p; RS = K / 32 rounded
+// up to a multiple of 8, the padding zero, so that the matrix-core loop can copy whole
+// 16-byte chunks of four stages.
+//
+// One thread per 32-element block.
+int mx_scale_stride(int K) { return (K / 32 + 7) & ~7; }
+
+template <int NP>
+__global__ __launch_bounds__(256) void mx_split_kernel(const uint16_t* __restrict__ src, int64_t nblk, int K,
+                                                       int RS, uint8_t* __restrict__ q, uint32_t* __restrict__ rec) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= nblk) return;
+  const int nb = K >> 5;
+  const int64_t row = gid / nb;
+  const int b = (int)(gid - row * nb);
+  const uint4* s4 = (const uint4*)(src + row * K + b * 32);
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 w = s4[i];
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[8 * i + 2 * j] = __uint_as_float(ww[j] << 16);
+      v[8 * i + 2 * j + 1] = __uint_as_float(ww[j] & 0xFFFF0000u);
+    }
+  }
+  uint32_t sc[NP];
+  uint8_t* const dst = q + row * NP * K + (b >> 1) * (NP * 64) + (b & 1) * 16;
+#pragma unroll
+  for (int pc = 0; pc < NP; ++pc) {
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(v[i]));
+    const int e = mx_scale_exp(m);
+    sc[pc] = (uint32_t)e;
+    const float inv = mx_inv_scale(e), scl = mx_scale(e);
+    uint32_t o[8];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) o[w] = mx_piece4(v + 4 * w, inv, scl, pc + 1 < NP);
+    *(uint4*)(dst + pc * 32) = make_uint4(o[0], o[1], o[2], o[3]);
+    *(uint4*)(dst + NP * 32 + pc * 32) = make_uint4(o[4], o[5], o[6], o[7]);
+  }
+  uint32_t r = 0;
+#pragma unroll
+  for (int pc = 0; pc < NP; ++pc) r |= sc[pc] << (8 * pc);
+  uint32_t* const rrow = rec + row * RS;
+  rrow[b] = r;
+  if (b == nb - 1)
+    for (int pad = nb; pad < RS; ++pad) rrow[pad] = 0;
+}
+
+hipError_t launch_mx_split(const uint16_t* src, int64_t rows, int K, uint8_t* q, uint32_t* rec, hipStream_t st) {
+  const int64_t nblk = rows * (K / 32);
+  const unsigned blocks = (unsigned)((nblk + 255) / 256);
+  hipLaunchKernelGGL(mx_split_kernel<2>, dim3(blocks), dim3(256), 0, st, src, nblk, K, mx_scale_stride(K), q, rec);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------------------ combine

@@ -56,7 +56,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
   size_t partial = 0, hist = 0, idx = 0, gates = 0, counts = 0, offsets = 0, perm = 0;
-  size_t h = 0, h_lo = 0, y = 0, total = 0;
+  size_t h = 0, h_lo = 0, xq = 0, xs = 0, hq = 0, hs = 0, y = 0, total = 0;
 };
 
 enum Need { NEED_ROUTE = 1, NEED_EXPERTS = 2, NEED_ROUTE_OUTPUTS = 4 };
@@ -82,8 +82,15 @@ Layout layout(int64_t T, int64_t D, int64_t E, int64_t k, int64_t F, int fmt, in
     L.perm = take(A * 4);
   }
   if (need & NEED_EXPERTS) {
-    L.h = take(A * (size_t)F * 2);
-    if (fmt == MOE_FMT_MXFP4) L.h_lo = take(A * (size_t)F * 2);
+    if (moe::mx_engine(fmt, moe::expert_tile_config((int64_t)A, E))) {
+      L.xq = take(2 * (size_t)T * D);
+      L.xs = take((size_t)T * moe::mx_scale_stride((int)D) * 4);
+      L.hq = take(3 * A * (size_t)F);
+      L.hs = take(A * (size_t)moe::mx_scale_stride((int)F) * 4);
+    } else {
+      L.h = take(A * (size_t)F * 2);
+      if (fmt == MOE_FMT_MXFP4) L.h_lo = take(A * (size_t)F * 2);
+    }
     L.y = take(A * (size_t)D * 4);
   }
   L.total = off;
@@ -100,6 +107,9 @@ int check_shapes(int64_t T, int64_t D, int64_t E, int64_t k, int64_t F, bool wit
   if (T * k >= ((int64_t)1 << 31)) return fail(MOE_EINVAL, "T*k = %lld must be < 2^31", (long long)(T * k));
   if (D >= ((int64_t)1 << 24) || (with_f && F >= ((int64_t)1 << 24)))
     return fail(MOE_EINVAL, "D and F must be < 2^24");
+  // the expert kernels address rows of x, h and one expert's weights with 32-bit offsets
+  if (T * D >= ((int64_t)1 << 30) || (with_f && (T * k * F >= ((int64_t)1 << 30) || D * F >= ((int64_t)1 << 30))))
+    return fail(MOE_EINVAL, "T*D, T*k*F and D*F must each be < 2^30");
   return MOE_OK;
 }
 
@@ -191,9 +201,17 @@ int run_experts(const uint8_t* ws, const Layout& L, const void* x, const void* w
   ea.h = (uint16_t*)(ws + L.h);
   ea.h_lo = fmt == MOE_FMT_MXFP4 ? (uint16_t*)(ws + L.h_lo) : nullptr;
   ea.y = (float*)(ws + L.y);
+  ea.xq = (uint8_t*)(ws + L.xq);
+  ea.xs = (uint32_t*)(ws + L.xs);
+  ea.hq = (uint8_t*)(ws + L.hq);
+  ea.hs = (uint32_t*)(ws + L.hs);
   ea.out = out;
   ea.T = (int)T; ea.D = (int)D; ea.E = (int)E; ea.k = (int)k; ea.F = (int)F; ea.fmt = fmt;
   const int cfg = moe::expert_tile_config(T * k, E);
+  if (moe::mx_engine(fmt, cfg))
+    CHECK(launch(moe::ST_SPLIT, "split", [&](hipStream_t st) {
+      return moe::launch_mx_split(ea.x, T, (int)D, ea.xq, ea.xs, st);
+    }));
   CHECK(launch(moe::ST_MLP1, "mlp1", [&](hipStream_t st) { return moe::launch_mlp1(ea, cfg, st); }));
   CHECK(launch(moe::ST_MLP2, "mlp2", [&](hipStream_t st) { return moe::launch_mlp2(ea, cfg, st); }));
   CHECK(launch(moe::ST_COMBINE, "combine",

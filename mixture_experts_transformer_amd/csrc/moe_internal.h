@@ -12,8 +12,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-enum Stage { ST_ROUTER = 0, ST_TOPK = 1, ST_PERMUTE = 2, ST_MLP1 = 3, ST_MLP2 = 4, ST_COMBINE = 5 };
+enum Stage { ST_ROUTER = 0, ST_TOPK = 1, ST_PERMUTE = 2, ST_MLP1 = 3, ST_MLP2 = 4, ST_COMBINE = 5, ST_SPLIT = 6 };
 
 // ---------------------------------------------------------------- routing
 // Number of K splits the router uses for T tokens of width D (>= 1).
@@ -43,6 +45,13 @@ struct ExpertArgs {
   const int32_t* perm;      // [A]
   uint16_t* h;              // [A][F] bf16 (hi part for MXFP4)
   uint16_t* h_lo;           // [A][F] bf16 low part (MXFP4 only)
+  // scaled-MFMA engine (h and h_lo unused): fp8 pieces of x (two) and of h (three), each
+  // row stored as 64-element groups of 64 bytes per piece, and their scales, one dword per
+  // row and 32-element block (piece p in byte p), mx_scale_stride(K) dwords per row
+  uint8_t* xq;              // [T][2 D]
+  uint32_t* xs;             // [T][mx_scale_stride(D)]
+  uint8_t* hq;              // [A][3 F]
+  uint32_t* hs;             // [A][mx_scale_stride(F)]
   float* y;                 // [A][D] fp32, row a = assignment id
   float* out;               // [T][D] fp32
   int T, D, E, k, F, fmt;
@@ -50,6 +59,14 @@ struct ExpertArgs {
 
 // Tile configuration chosen for a routed-row count (the same choice for every stage).
 int expert_tile_config(int64_t A, int64_t E);
+// Whether the expert GEMMs run on the scaled matrix-core engine (MXFP4 weights,
+// matrix-core tiles): mlp1 then reads x as fp8 pieces written by launch_mx_split and
+// writes h as fp8 pieces, which mlp2 reads.
+bool mx_engine(int fmt, int cfg);
+// Scale dwords per row of the pieces of a K-wide row (K / 32 rounded up to a multiple of 8).
+int mx_scale_stride(int K);
+// Two fp8 pieces of each bf16 row of src [rows][K] and their scales, for mlp1's A rows.
+hipError_t launch_mx_split(const uint16_t* src, int64_t rows, int K, uint8_t* q, uint32_t* rec, hipStream_t st);
 hipError_t launch_mlp1(const ExpertArgs& a, int cfg, hipStream_t st);
 hipError_t launch_mlp2(const ExpertArgs& a, int cfg, hipStream_t st);
 hipError_t launch_combine(const float* y, int T, int D, int k, float* out, hipStream_t st);

@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 FMT = {"bf16": 0, "mxfp4": 1}
-STAGES = ("router", "topk", "permute", "mlp1", "mlp2", "combine")
+STAGES = ("router", "topk", "permute", "mlp1", "mlp2", "combine", "split")
 
 _c_void_p = ctypes.c_void_p
 _i64 = ctypes.c_int64
