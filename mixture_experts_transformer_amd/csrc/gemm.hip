@@ -37,8 +37,9 @@ constexpr float SWIGLU_ALPHA = 1.702f;
 constexpr float SWIGLU_LIMIT = 7.0f;
 constexpr float SWIGLU_NEG_ALPHA_LOG2E = -SWIGLU_ALPHA * 1.4426950408889634f;
 
-template <int BM_, int BN_, int WM_, int WN_, int NS_, int BK_, bool STREAM_ = false, int SUPER_ = 4>
+template <int BM_, int BN_, int WM_, int WN_, int NS_, int BK_, bool STREAM_ = false, int SUPER_ = 4, int WPE_ = 1>
 struct Tile {
+  static constexpr int WPE = WPE_;    // waves per SIMD the register allocation must allow
   static constexpr bool STREAM = STREAM_;   // weight-streaming tile order
   static constexpr int BM = BM_;      // routed rows per tile
   static constexpr int BN = BN_;      // weight rows per tile (mlp1: gate + linear halves)
@@ -439,7 +440,7 @@ static __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
 // 32 rows at a time, so that global stores are whole 8-byte (h) or 16-byte (y) chunks of
 // rows instead of one element per lane.
 template <int MODE, int FMT, class C>
-__global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
+__global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmArgs p) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, CPR = C::CPR, NS = C::NS, NW = C::NW;
   constexpr int FM = C::FM, FN = C::FN;
   constexpr bool MX = FMT == 2;                             // scaled MFMA on fp8 pieces
@@ -728,12 +729,12 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
     _Pragma("unroll") for (int i = 0; i < (FA); ++i)                                             \
       fa[buf][pa][i] = *(const bf16x8*)((sa_) + pa * A_BYTES + swz<CPR>(arow0 + i * 32, cc_));    \
   } while (0)
-#define MOE_MMA(buf, FA)                                                                         \
+#define MOE_MMA(buf, FA, ACC)                                                                    \
   do {                                                                                           \
     _Pragma("unroll") for (int i = 0; i < (FA); ++i)                                             \
     _Pragma("unroll") for (int pa = 0; pa < AP; ++pa)                                            \
     _Pragma("unroll") for (int j = 0; j < FN; ++j)                                               \
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][pa][i], fb[buf][j], acc[i][j], 0, 0, 0); \
+      ACC[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][pa][i], fb[buf][j], ACC[i][j], 0, 0, 0); \
   } while (0)
   // one scheduling group per MFMA step: the next step's LDS reads ahead of this step's MFMAs
 #define MOE_SCHED(FA)                                                                            \
@@ -742,8 +743,8 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
     __builtin_amdgcn_sched_group_barrier(0x008, AP * (FA) * FN, 0);                              \
   } while (0)
 
-// the K loop for FA active 32-row fragment rows per wave (the rest are padding)
-#define MOE_MAIN_LOOP(FA)                                                                        \
+// the K loop for FA active 32-row fragment rows per wave (the rest are padding), into ACC
+#define MOE_MAIN_LOOP(FA, ACC)                                                                   \
   do {                                                                                           \
     for (int kt = 0; kt < nk; ++kt) {                                                            \
       const int slot = kt % NS;                                                                  \
@@ -767,32 +768,19 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
         }                                                                                        \
       }                                                                                          \
       MOE_LOAD_FRAGS(0, 0, sa, sb, FA);                                                          \
-      if (kt > 0) MOE_MMA((KS - 1) & 1, FA);  /* last MFMA step of the previous stage */         \
+      if (kt > 0) MOE_MMA((KS - 1) & 1, FA, ACC);  /* last MFMA step of the previous stage */    \
       MOE_SCHED(FA);                                                                             \
   _Pragma("unroll")                                                                              \
       for (int ks = 0; ks < KS - 1; ++ks) {                                                      \
         MOE_LOAD_FRAGS((ks + 1) & 1, ks + 1, sa, sb, FA);                                        \
-        MOE_MMA(ks & 1, FA);                                                                     \
+        MOE_MMA(ks & 1, FA, ACC);                                                                \
         MOE_SCHED(FA);                                                                           \
       }                                                                                          \
     }                                                                                            \
-    MOE_MMA((KS - 1) & 1, FA);                                                                   \
+    MOE_MMA((KS - 1) & 1, FA, ACC);                                                              \
   } while (0)
-  if constexpr (!MX) {
-    // Row blocks of 32 past the tile's rows hold only padding: when every wave's rows fit in
-    // its first block, the other blocks' copies (above) and matrix instructions are skipped.
-    if (C::WAVES_M == 1 && FM == 2 && rows <= 32) {
-      MOE_MAIN_LOOP(1);
-    } else {
-      MOE_MAIN_LOOP(FM);
-    }
-  } else {
-    // Scaled matrix-core engine, one 64-wide K step per stage.  Per stage a lane loads its B
-    // codes and scale bytes and the A scale records of its row blocks, then the A pieces one
-    // row block ahead of the block it multiplies.  The last row block of a stage multiplies
-    // after the next stage's barrier, behind that stage's first loads.
-    i32x8 fap[AP], fbp[FN];                 // deferred operands of the previous stage
-    uint32_t sap, sbp[FN];
+  // scaled-MFMA engine: the A pieces of row block i_ (this lane's row, its two chunks per
+  // piece) from the stage at sa
 #define MX_LOAD_A(dst, i_)                                                                       \
   do {                                                                                           \
     _Pragma("unroll") for (int pa = 0; pa < AP; ++pa) {                                          \
@@ -802,77 +790,112 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmArgs p) {
       (dst)[pa] = __builtin_shufflevector(lo_, hi_, 0, 1, 2, 3, 4, 5, 6, 7);                     \
     }                                                                                            \
   } while (0)
-    // the scale dword of this lane's row and K block holds piece pa's scale in byte pa,
-    // which op_sel selects
-#define MX_MMA(i_, FA, FB, SA, SB)                                                               \
+  // the scale dword of this lane's row and K block holds piece pa's scale in byte pa,
+  // which op_sel selects
+#define MX_MMA(ACC, i_, FA, FB, SA, SB)                                                               \
   do {                                                                                           \
     _Pragma("unroll") for (int pa = 0; pa < AP; ++pa)                                            \
     _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                             \
       if (pa == 0)                                                                               \
-        acc[i_][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                             \
-            (FA)[pa], (FB)[j], acc[i_][j], 0, 4, 0, (int)(SA), 0, (int)(SB)[j]);                  \
+        ACC[i_][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                             \
+            (FA)[pa], (FB)[j], ACC[i_][j], 0, 4, 0, (int)(SA), 0, (int)(SB)[j]);                  \
       else if (pa == 1)                                                                          \
-        acc[i_][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                             \
-            (FA)[pa], (FB)[j], acc[i_][j], 0, 4, 1, (int)(SA), 0, (int)(SB)[j]);                  \
+        ACC[i_][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                             \
+            (FA)[pa], (FB)[j], ACC[i_][j], 0, 4, 1, (int)(SA), 0, (int)(SB)[j]);                  \
       else                                                                                       \
-        acc[i_][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                             \
-            (FA)[pa], (FB)[j], acc[i_][j], 0, 4, 2, (int)(SA), 0, (int)(SB)[j]);                  \
+        ACC[i_][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                             \
+            (FA)[pa], (FB)[j], ACC[i_][j], 0, 4, 2, (int)(SA), 0, (int)(SB)[j]);                  \
     }                                                                                            \
   } while (0)
-    for (int kt = 0; kt < nk; ++kt) {
-      const int slot = kt % NS;
-      wait_vmcnt_dyn(__builtin_amdgcn_readfirstlane(issued - mark[slot]));
-      wait_lgkmcnt0();
-      barrier_nofence();
-      if (MODE == 2 && kt == 0 && rt_a >= 0) rt_g = p.gates[rt_a];
-      if (kt + NS - 1 < nk) MOE_ISSUE(kt + NS - 1);
-
-      const uint8_t* sa = smem + slot * STAGE;
-      const uint8_t* sas = ascale_lds + ((kt / SUPER) % NSB) * ASL_SLOT;
-      const uint8_t* sb = sa + A_BYTES;
-      const uint8_t* cs = codes_lds + ((kt / SUPER) % NSB) * CODE_SLOT;
-      const int chunk = 2 * (kt % SUPER) + kg;
-      i32x8 fb[FN];
-      uint32_t sbv[FN];
+  if constexpr (!MX) {
+    // Row blocks of 32 past the tile's rows hold only padding: when every wave's rows fit in
+    // its first block, the other blocks' copies (above) and matrix instructions are skipped.
+    // That loop accumulates into an array of its own, so the unused blocks are not carried
+    // through it.
+    if (C::WAVES_M == 1 && FM == 2 && rows <= 32) {
+      f32x16 acc1[1][FN];
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const i32x4 q = *(const i32x4*)(cs + brow[j] * CROW + ((chunk ^ code_swz<CCH>(brow[j])) << 4));
-        fb[j] = __builtin_shufflevector(q, q, 0, 1, 2, 3, -1, -1, -1, -1);
-        sbv[j] = sb[brow[j] * 4 + ((sbyte[j] + 2 * kt + kg) & 3)];
-      }
-      uint32_t sav[FM];
-      const int dw = (kt % SUPER) * 2 + kg;                // scale dword of this stage and K block
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int r = arow0 + 32 * i;
-        const int pos = (dw >> 2) ^ (ASL_ROW > 16 ? (r >> 3) & (ASL_ROW / 16 - 1) : 0);
-        sav[i] = *(const uint32_t*)(sas + r * ASL_ROW + pos * 16 + (dw & 3) * 4);
-      }
-      i32x8 fa[2][AP];
-      MX_LOAD_A(fa[0], 0);
-      if (kt > 0) MX_MMA(FM - 1, fap, fbp, sap, sbp);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * FN + FM + 2 * AP, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, AP * FN, 0);
+        for (int q = 0; q < 16; ++q) acc1[0][j][q] = 0.f;
+      MOE_MAIN_LOOP(1, acc1);
 #pragma unroll
-      for (int i = 0; i + 1 < FM; ++i) {
-        MX_LOAD_A(fa[(i + 1) & 1], i + 1);
-        MX_MMA(i, fa[i & 1], fb, sav[i], sbv);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * AP, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, AP * FN, 0);
-      }
-#pragma unroll
-      for (int pa = 0; pa < AP; ++pa) fap[pa] = fa[(FM - 1) & 1][pa];
-      sap = sav[FM - 1];
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        fbp[j] = fb[j];
-        sbp[j] = sbv[j];
-      }
+      for (int j = 0; j < FN; ++j) acc[0][j] = acc1[0][j];
+    } else {
+      MOE_MAIN_LOOP(FM, acc);
     }
-    MX_MMA(FM - 1, fap, fbp, sap, sbp);
+  } else {
+    // Scaled matrix-core engine, one 64-wide K step per stage.  Per stage a lane loads its B
+    // codes and scale bytes and the A scale dwords of its row blocks, then the A pieces one
+    // row block ahead of the block it multiplies.  The last row block of a stage multiplies
+    // after the next stage's barrier, behind that stage's first loads.
+#define MX_LOOP(FA, ACC)                                                                         \
+  do {                                                                                           \
+    i32x8 fap[AP], fbp[FN];                 /* deferred operands of the previous stage */        \
+    uint32_t sap, sbp[FN];                                                                       \
+    for (int kt = 0; kt < nk; ++kt) {                                                            \
+      const int slot = kt % NS;                                                                  \
+      wait_vmcnt_dyn(__builtin_amdgcn_readfirstlane(issued - mark[slot]));                       \
+      wait_lgkmcnt0();                                                                           \
+      barrier_nofence();                                                                         \
+      if (MODE == 2 && kt == 0 && rt_a >= 0) rt_g = p.gates[rt_a];                               \
+      if (kt + NS - 1 < nk) MOE_ISSUE(kt + NS - 1);                                              \
+      const uint8_t* sa = smem + slot * STAGE;                                                   \
+      const uint8_t* sas = ascale_lds + ((kt / SUPER) % NSB) * ASL_SLOT;                         \
+      const uint8_t* sb = sa + A_BYTES;                                                          \
+      const uint8_t* cs = codes_lds + ((kt / SUPER) % NSB) * CODE_SLOT;                          \
+      const int chunk = 2 * (kt % SUPER) + kg;                                                   \
+      i32x8 fb[FN];                                                                              \
+      uint32_t sbv[FN];                                                                          \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                           \
+        const i32x4 q = *(const i32x4*)(cs + brow[j] * CROW + ((chunk ^ code_swz<CCH>(brow[j])) << 4)); \
+        fb[j] = __builtin_shufflevector(q, q, 0, 1, 2, 3, -1, -1, -1, -1);                       \
+        sbv[j] = sb[brow[j] * 4 + ((sbyte[j] + 2 * kt + kg) & 3)];                               \
+      }                                                                                          \
+      uint32_t sav[FA];                                                                          \
+      const int dw = (kt % SUPER) * 2 + kg;  /* scale dword of this stage and K block */         \
+      _Pragma("unroll") for (int i = 0; i < (FA); ++i) {                                         \
+        const int r = arow0 + 32 * i;                                                            \
+        const int pos = (dw >> 2) ^ (ASL_ROW > 16 ? (r >> 3) & (ASL_ROW / 16 - 1) : 0);          \
+        sav[i] = *(const uint32_t*)(sas + r * ASL_ROW + pos * 16 + (dw & 3) * 4);                \
+      }                                                                                          \
+      i32x8 fa[2][AP];                                                                           \
+      MX_LOAD_A(fa[0], 0);                                                                       \
+      if (kt > 0) MX_MMA(ACC, (FA) - 1, fap, fbp, sap, sbp);                                     \
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * FN + (FA) + 2 * AP, 0);                    \
+      __builtin_amdgcn_sched_group_barrier(0x008, AP * FN, 0);                                   \
+      _Pragma("unroll") for (int i = 0; i + 1 < (FA); ++i) {                                     \
+        MX_LOAD_A(fa[(i + 1) & 1], i + 1);                                                       \
+        MX_MMA(ACC, i, fa[i & 1], fb, sav[i], sbv);                                              \
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * AP, 0);                                  \
+        __builtin_amdgcn_sched_group_barrier(0x008, AP * FN, 0);                                 \
+      }                                                                                          \
+      _Pragma("unroll") for (int pa = 0; pa < AP; ++pa) fap[pa] = fa[((FA) - 1) & 1][pa];        \
+      sap = sav[(FA) - 1];                                                                       \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                           \
+        fbp[j] = fb[j];                                                                          \
+        sbp[j] = sbv[j];                                                                         \
+      }                                                                                          \
+    }                                                                                            \
+    MX_MMA(ACC, (FA) - 1, fap, fbp, sap, sbp);                                                   \
+  } while (0)
+    // as above: padding row blocks of a single-block group are skipped
+    if (C::WAVES_M == 1 && FM == 2 && rows <= 32) {
+      f32x16 acc1[1][FN];
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc1[0][j][q] = 0.f;
+      MX_LOOP(1, acc1);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[0][j] = acc1[0][j];
+    } else {
+      MX_LOOP(FM, acc);
+    }
+#undef MX_LOOP
+  }
 #undef MX_LOAD_A
 #undef MX_MMA
-  }
 #undef MOE_MAIN_LOOP
 #undef MOE_LOAD_FRAGS
 #undef MOE_MMA
@@ -1058,6 +1081,9 @@ static hipError_t launch_any(const GemmArgs& g, int fmt, int cfg, int64_t A, hip
                   : launch_gemm<MODE, 1, LargeTile<MODE, 1>>(g, A, st);
 }
 
+// Streaming tiles keep the decoded-bf16 path: with few rows per expert the stage loop is
+// bound by memory latency, and the scaled engine's wider tiles (a whole 32-element block of
+// h per wave) measured slower there.
 bool mx_engine(int fmt, int cfg) { return fmt == 1 && cfg == 1; }
 
 hipError_t launch_mlp1(const ExpertArgs& a, int cfg, hipStream_t st) {
