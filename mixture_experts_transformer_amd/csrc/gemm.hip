@@ -478,6 +478,13 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   constexpr int ASL_BYTES = MX ? NSB * ASL_SLOT : 0;
   constexpr int NASC = MX ? BM * ASL_ROW / 1024 : 0;        // A scale copies per super-stage
   constexpr int NCT = NC + NASC;
+  // Code windows aligned to 128-byte lines: with 128 code bytes per row and window, each
+  // row's windows start at the line boundary at or below its codes (a row starts 32 s
+  // bytes past one when its length is not a multiple of 128), so every line is fetched by
+  // one window instead of two.  Row r's stage kt then sits at position kt + s(r) of the
+  // row's window sequence.  The windows need their own issue schedule (below), which fits
+  // a two-stage ring.
+  constexpr bool WALIGN = FMT != 0 && CROW == 128 && NS == 2;
   static_assert(!MX || (SUPER >= 2 && 1024 % ASL_ROW == 0), "A scale super-stage granularity");
   constexpr int PW_G = (NG + NW - 1) / NW;
   constexpr int PW_C = (NCT + NW - 1) / NW + (NCT == 0 ? 1 : 0);
@@ -574,6 +581,12 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
     s_e_off = (size_t)p.E * p.N * (K / 2) + (size_t)e * p.N * (K / 32);
   }
   const uint8_t* const s_e4 = p.w + (s_e_off & ~(size_t)3);   // scale copies read aligned dwords
+  // code-window shift of a weight row (in 32-byte stages), 0 unless the buffer is
+  // 128-byte aligned; windows start below the row, so copies are relative to w_e - 128
+  const bool walign = WALIGN && (((uintptr_t)p.w) & 127) == 0;
+  const size_t w_e_off = (size_t)(w_e - p.w);
+  const uint8_t* const wbase = WALIGN ? w_e - 128 : w_e;
+#define MOE_CSHIFT(wr) (walign ? (int)(((w_e_off + (size_t)(wr) * (K / 2)) >> 5) & 3) : 0)
   // tile row -> weight row, clamped into the matrix.  mlp1 tiles interleave the halves in
   // 16-row groups: rows 32 j .. 32 j + 15 are gate rows of pairs 16 j .. 16 j + 15 and rows
   // 32 j + 16 .. 32 j + 31 the linear rows of the same pairs, so every 32-column output
@@ -628,7 +641,8 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
     if (FMT != 0 && i < NC) {
       const int r = i * (1024 / CROW) + lane / CCH;
       const int c = (lane % CCH) ^ code_swz<CCH>(r);
-      coff[j] = (uint32_t)((size_t)MOE_WROW(r) * (K / 2) + c * 16);
+      const int wr = MOE_WROW(r);
+      coff[j] = (uint32_t)((size_t)wr * (K / 2) + (WALIGN ? 128 - 32 * MOE_CSHIFT(wr) : 0) + c * 16);
       cdst[j] = i * 1024;
     } else if (i < NCT) {
       constexpr int CPS = ASL_ROW / 16;                    // chunks per row
@@ -666,26 +680,46 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
       }                                                                                          \
     }                                                                                            \
   } while (0)
-#define MOE_ISSUE_CODES(sk)                                                                      \
+// code window w of the tile's rows into slot w % NSB
+#define MOE_ISSUE_WIN(w)                                                                         \
   do {                                                                                           \
     _Pragma("unroll") for (int j = 0; j < PW_C; ++j) {                                           \
       const int i_ = wave + j * NW;                                                              \
       if (FMT != 0 && i_ < NC) {                                                                 \
-        dma16(w_e + (size_t)(sk) * CROW, coff[j], codes_lds + ((sk) % NSB) * CODE_SLOT + cdst[j]); \
+        dma16(wbase + (size_t)(w) * CROW, coff[j], codes_lds + ((w) % NSB) * CODE_SLOT + cdst[j]); \
         ++issued;                                                                                \
-      } else if (i_ < NCT && ((i_ - NC) * (1024 / ASL_ROW)) < rows) {                            \
+      }                                                                                          \
+    }                                                                                            \
+  } while (0)
+// A scale super-stage sk (scaled-MFMA engine)
+#define MOE_ISSUE_ASC(sk)                                                                        \
+  do {                                                                                           \
+    _Pragma("unroll") for (int j = 0; j < PW_C; ++j) {                                           \
+      const int i_ = wave + j * NW;                                                              \
+      if (i_ >= NC && i_ < NCT && ((i_ - NC) * (1024 / ASL_ROW)) < rows) {                       \
         dma16((const uint8_t*)p.a8s + (size_t)(sk) * ASL_ROW, coff[j],                           \
               ascale_lds + ((sk) % NSB) * ASL_SLOT + cdst[j]);                                   \
         ++issued;                                                                                \
       }                                                                                          \
     }                                                                                            \
   } while (0)
-  // everything a K step needs, codes first so the group's completion implies theirs
+  // everything a K step needs, codes first so the group's completion implies theirs.
+  // Aligned code windows go out one window ahead instead: window w (stages 4 w - s .. of a
+  // row with shift s) right after the barrier of stage 4 (w - 1), when window w - 2's slot
+  // is free, ahead of the group of stage 4 w - 3, its first use.
 #define MOE_ISSUE(kt)                                                                            \
   do {                                                                                           \
-    if (FMT != 0 && (kt) % SUPER == 0) MOE_ISSUE_CODES((kt) / SUPER);                            \
+    if (FMT != 0 && (kt) % SUPER == 0) {                                                         \
+      if (!WALIGN) MOE_ISSUE_WIN((kt) / SUPER);                                                  \
+      MOE_ISSUE_ASC((kt) / SUPER);                                                               \
+    }                                                                                            \
     MOE_ISSUE_GROUP(kt, (kt) % NS);                                                              \
     mark[(kt) % NS] = issued;                                                                    \
+  } while (0)
+  const int nwin = (nk + 2) / 4 + 1;        // aligned windows any row needs
+#define MOE_ISSUE_NEXT_WIN(kt)                                                                   \
+  do {                                                                                           \
+    if (WALIGN && (kt) % 4 == 0 && (kt) / 4 + 1 < nwin) MOE_ISSUE_WIN((kt) / 4 + 1);             \
   } while (0)
 
   f32x16 acc[FM][FN];
@@ -699,16 +733,28 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   // B-tile row of this lane for fragment j; byte of its scale dword for K step 0
   int brow[FN];
   int sbyte[FN];
+  int csh[FN];                              // code-window shift of the fragment row
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     brow[j] = wn * C::WTN + j * 32 + (lane & 31);
     sbyte[j] = 0;
+    csh[j] = 0;
     if (FMT != 0) sbyte[j] = (int)((s_e_off + (size_t)MOE_WROW(brow[j]) * (K / 32)) & 3);
+    if (WALIGN) csh[j] = MOE_CSHIFT(MOE_WROW(brow[j]));
   }
+  // this lane's 32 codes of fragment j for stage kt in the code ring
+#define MOE_CODES_AT(kt_, j_)                                                                    \
+  ([&]() {                                                                                       \
+    const int t_ = (kt_) + csh[j_];                                                              \
+    const int c_ = 2 * (t_ % SUPER) + kg;                                                        \
+    return codes_lds + ((t_ / SUPER) % NSB) * CODE_SLOT + brow[j_] * CROW +                      \
+           ((c_ ^ code_swz<CCH>(brow[j_])) << 4);                                               \
+  }())
   const int arow0 = wm * C::WTM + (lane & 31);
   const int kg = lane >> 5;                 // which half of the stage's K range this lane feeds
 
   // prologue: NS - 1 stages in flight
+  if (WALIGN) MOE_ISSUE_WIN(0);
 #pragma unroll
   for (int s0 = 0; s0 < NS - 1; ++s0)
     if (s0 < nk) MOE_ISSUE(s0);
@@ -753,16 +799,15 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
       wait_lgkmcnt0();                                                                           \
       barrier_nofence();                                                                         \
       if (MODE == 2 && kt == 0 && rt_a >= 0) rt_g = p.gates[rt_a];                               \
+      MOE_ISSUE_NEXT_WIN(kt);                                                                    \
       if (kt + NS - 1 < nk) MOE_ISSUE(kt + NS - 1);                                              \
                                                                                                  \
       const uint8_t* sa = smem + slot * STAGE;                                                   \
       const uint8_t* sb = sa + AP * A_BYTES;                                                     \
       if (FMT == 1) {                                                                            \
-        const uint8_t* cs = codes_lds + ((kt / SUPER) % NSB) * CODE_SLOT;                        \
-        const int chunk = 2 * (kt % SUPER) + kg;                                                 \
   _Pragma("unroll")                                                                              \
         for (int j = 0; j < FN; ++j) {                                                           \
-          q4[j] = *(const u32x4*)(cs + brow[j] * CROW + ((chunk ^ code_swz<CCH>(brow[j])) << 4)); \
+          q4[j] = *(const u32x4*)MOE_CODES_AT(kt, j);                                            \
           const uint32_t sc = sb[brow[j] * 4 + ((sbyte[j] + 2 * kt + kg) & 3)];                  \
           scl[j] = __uint_as_float(sc << 23);                                                    \
         }                                                                                        \
@@ -839,16 +884,15 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
       wait_lgkmcnt0();                                                                           \
       barrier_nofence();                                                                         \
       if (MODE == 2 && kt == 0 && rt_a >= 0) rt_g = p.gates[rt_a];                               \
+      MOE_ISSUE_NEXT_WIN(kt);                                                                    \
       if (kt + NS - 1 < nk) MOE_ISSUE(kt + NS - 1);                                              \
       const uint8_t* sa = smem + slot * STAGE;                                                   \
       const uint8_t* sas = ascale_lds + ((kt / SUPER) % NSB) * ASL_SLOT;                         \
       const uint8_t* sb = sa + A_BYTES;                                                          \
-      const uint8_t* cs = codes_lds + ((kt / SUPER) % NSB) * CODE_SLOT;                          \
-      const int chunk = 2 * (kt % SUPER) + kg;                                                   \
       i32x8 fb[FN];                                                                              \
       uint32_t sbv[FN];                                                                          \
       _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                           \
-        const i32x4 q = *(const i32x4*)(cs + brow[j] * CROW + ((chunk ^ code_swz<CCH>(brow[j])) << 4)); \
+        const i32x4 q = *(const i32x4*)MOE_CODES_AT(kt, j);                                      \
         fb[j] = __builtin_shufflevector(q, q, 0, 1, 2, 3, -1, -1, -1, -1);                       \
         sbv[j] = sb[brow[j] * 4 + ((sbyte[j] + 2 * kt + kg) & 3)];                               \
       }                                                                                          \
@@ -902,7 +946,11 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
 #undef MOE_SCHED
 #undef MOE_ISSUE
 #undef MOE_ISSUE_GROUP
-#undef MOE_ISSUE_CODES
+#undef MOE_ISSUE_WIN
+#undef MOE_ISSUE_ASC
+#undef MOE_ISSUE_NEXT_WIN
+#undef MOE_CODES_AT
+#undef MOE_CSHIFT
 #undef MOE_WROW
 
   // ---- epilogue.  Output register q of fragment (i, j) is row 8 (q >> 2) + 4 kg + (q & 3)
@@ -911,6 +959,9 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
     tab_a[tid] = rt_a;
     tab_g[tid] = rt_g;
   }
+  // copies still in flight (a code window issued for shifted rows that this tile has
+  // none of) must land before the ring's memory becomes the epilogue slices
+  wait_vmcnt<0>();
   wait_lgkmcnt0();
   barrier_nofence();                        // every wave is done with the operand ring
   uint8_t* const ep = smem + wave * EP_REG;
