@@ -478,13 +478,13 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   constexpr int ASL_BYTES = MX ? NSB * ASL_SLOT : 0;
   constexpr int NASC = MX ? BM * ASL_ROW / 1024 : 0;        // A scale copies per super-stage
   constexpr int NCT = NC + NASC;
-  // Code windows aligned to 128-byte lines: with 128 code bytes per row and window, each
-  // row's windows start at the line boundary at or below its codes (a row starts 32 s
-  // bytes past one when its length is not a multiple of 128), so every line is fetched by
-  // one window instead of two.  Row r's stage kt then sits at position kt + s(r) of the
-  // row's window sequence.  The windows need their own issue schedule (below), which fits
-  // a two-stage ring.
-  constexpr bool WALIGN = FMT != 0 && CROW == 128 && NS == 2;
+  // Code windows aligned to their own size (64 or 128 bytes per row): each row's windows
+  // start at the boundary at or below its codes (a row starts 32 s bytes past one when its
+  // length is not a multiple of the window), so every 64-byte sector or 128-byte line is
+  // fetched by one window instead of two.  Row r's stage kt then sits at position
+  // kt + s(r) of the row's window sequence.  The windows need their own issue schedule
+  // (below), which fits a two-stage ring.
+  constexpr bool WALIGN = FMT != 0 && (CROW == 64 || CROW == 128) && NS == 2;
   static_assert(!MX || (SUPER >= 2 && 1024 % ASL_ROW == 0), "A scale super-stage granularity");
   constexpr int PW_G = (NG + NW - 1) / NW;
   constexpr int PW_C = (NCT + NW - 1) / NW + (NCT == 0 ? 1 : 0);
@@ -581,12 +581,12 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
     s_e_off = (size_t)p.E * p.N * (K / 2) + (size_t)e * p.N * (K / 32);
   }
   const uint8_t* const s_e4 = p.w + (s_e_off & ~(size_t)3);   // scale copies read aligned dwords
-  // code-window shift of a weight row (in 32-byte stages), 0 unless the buffer is
-  // 128-byte aligned; windows start below the row, so copies are relative to w_e - 128
-  const bool walign = WALIGN && (((uintptr_t)p.w) & 127) == 0;
+  // code-window shift of a weight row (in 32-byte stages), 0 unless the buffer is aligned
+  // to the window; windows start below the row, so copies are relative to w_e - CROW
+  const bool walign = WALIGN && (((uintptr_t)p.w) & (CROW - 1)) == 0;
   const size_t w_e_off = (size_t)(w_e - p.w);
-  const uint8_t* const wbase = WALIGN ? w_e - 128 : w_e;
-#define MOE_CSHIFT(wr) (walign ? (int)(((w_e_off + (size_t)(wr) * (K / 2)) >> 5) & 3) : 0)
+  const uint8_t* const wbase = WALIGN ? w_e - CROW : w_e;
+#define MOE_CSHIFT(wr) (walign ? (int)(((w_e_off + (size_t)(wr) * (K / 2)) >> 5) & (SUPER - 1)) : 0)
   // tile row -> weight row, clamped into the matrix.  mlp1 tiles interleave the halves in
   // 16-row groups: rows 32 j .. 32 j + 15 are gate rows of pairs 16 j .. 16 j + 15 and rows
   // 32 j + 16 .. 32 j + 31 the linear rows of the same pairs, so every 32-column output
@@ -642,7 +642,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
       const int r = i * (1024 / CROW) + lane / CCH;
       const int c = (lane % CCH) ^ code_swz<CCH>(r);
       const int wr = MOE_WROW(r);
-      coff[j] = (uint32_t)((size_t)wr * (K / 2) + (WALIGN ? 128 - 32 * MOE_CSHIFT(wr) : 0) + c * 16);
+      coff[j] = (uint32_t)((size_t)wr * (K / 2) + (WALIGN ? CROW - 32 * MOE_CSHIFT(wr) : 0) + c * 16);
       cdst[j] = i * 1024;
     } else if (i < NCT) {
       constexpr int CPS = ASL_ROW / 16;                    // chunks per row
@@ -704,9 +704,9 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
     }                                                                                            \
   } while (0)
   // everything a K step needs, codes first so the group's completion implies theirs.
-  // Aligned code windows go out one window ahead instead: window w (stages 4 w - s .. of a
-  // row with shift s) right after the barrier of stage 4 (w - 1), when window w - 2's slot
-  // is free, ahead of the group of stage 4 w - 3, its first use.
+  // Aligned code windows go out one window ahead instead: window w (stages S w - s .. of a
+  // row with shift s, S = SUPER) right after the barrier of stage S (w - 1), when window
+  // w - 2's slot is free, ahead of the group of stage S (w - 1) + 1, its first use.
 #define MOE_ISSUE(kt)                                                                            \
   do {                                                                                           \
     if (FMT != 0 && (kt) % SUPER == 0) {                                                         \
@@ -716,10 +716,10 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
     MOE_ISSUE_GROUP(kt, (kt) % NS);                                                              \
     mark[(kt) % NS] = issued;                                                                    \
   } while (0)
-  const int nwin = (nk + 2) / 4 + 1;        // aligned windows any row needs
+  const int nwin = (nk + SUPER - 2) / SUPER + 1;   // aligned windows any row needs
 #define MOE_ISSUE_NEXT_WIN(kt)                                                                   \
   do {                                                                                           \
-    if (WALIGN && (kt) % 4 == 0 && (kt) / 4 + 1 < nwin) MOE_ISSUE_WIN((kt) / 4 + 1);             \
+    if (WALIGN && (kt) % SUPER == 0 && (kt) / SUPER + 1 < nwin) MOE_ISSUE_WIN((kt) / SUPER + 1); \
   } while (0)
 
   f32x16 acc[FM][FN];
