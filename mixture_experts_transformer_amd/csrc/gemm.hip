@@ -313,14 +313,18 @@ static __device__ __forceinline__ const void* uniform_ptr(const void* p) {
 // The source is a wave-uniform base (scalar registers) plus a per-lane 32-bit byte offset,
 // which keeps one vector register per copy slot instead of two.
 // 16 bytes per lane: lane L fills LDS bytes [dst + 16 L, +16) from base + off.
-static __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint8_t* dst_wave) {
+// The LDS destination is a wave-uniform LDS byte address (kept as an integer: converting a
+// generic pointer costs a null check per copy).
+static __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t dst_wave) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :: "s"(lds_addr(dst_wave)), "v"(off), "s"(uniform_ptr(base)) : "memory", "m0");
+               :: "s"(__builtin_amdgcn_readfirstlane(dst_wave)), "v"(off), "s"(uniform_ptr(base))
+               : "memory", "m0");
 }
 // One dword per lane: lane L fills LDS bytes [dst + 4 L, +4) from base + off.
-static __device__ __forceinline__ void dma4(const void* base, uint32_t off, uint8_t* dst_wave) {
+static __device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t dst_wave) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
-               :: "s"(lds_addr(dst_wave)), "v"(off), "s"(uniform_ptr(base)) : "memory", "m0");
+               :: "s"(__builtin_amdgcn_readfirstlane(dst_wave)), "v"(off), "s"(uniform_ptr(base))
+               : "memory", "m0");
 }
 
 // s_waitcnt vmcnt(N) with the LDS/export counters left alone (gfx9 encoding).
@@ -506,6 +510,10 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM + ROWTAB];
   uint8_t* const codes_lds = smem + NS * STAGE;
   uint8_t* const ascale_lds = codes_lds + CODE_BYTES;       // scaled-MFMA engine: A scales
+  // the same regions as LDS byte addresses, for the copies
+  const uint32_t smem_l = lds_addr(smem);
+  const uint32_t codes_l = smem_l + NS * STAGE;
+  const uint32_t ascale_l = codes_l + CODE_BYTES;
   int* const tab_a = (int*)(smem + SMEM);
   float* const tab_g = (float*)(smem + SMEM + BM * 4);
 
@@ -666,7 +674,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
     _Pragma("unroll") for (int j = 0; j < PW_G; ++j) {                                           \
       const int i_ = wave + j * NW;                                                              \
       if (i_ < NG && !(i_ < NA && (i_ % A_CPC) * 64 / A_CPR >= rows)) {                         \
-        uint8_t* d_ = smem + (slot) * STAGE + gdst[j];                                           \
+        const uint32_t d_ = smem_l + (slot) * STAGE + gdst[j];                                   \
         if (i_ < NA) {                                                                           \
           const void* ab_ = MX ? (const void*)p.a8                                               \
                                 : (i_ < A_CPC ? (const void*)p.a : (const void*)p.a_lo);          \
@@ -686,7 +694,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
     _Pragma("unroll") for (int j = 0; j < PW_C; ++j) {                                           \
       const int i_ = wave + j * NW;                                                              \
       if (FMT != 0 && i_ < NC) {                                                                 \
-        dma16(wbase + (size_t)(w) * CROW, coff[j], codes_lds + ((w) % NSB) * CODE_SLOT + cdst[j]); \
+        dma16(wbase + (size_t)(w) * CROW, coff[j], codes_l + ((w) % NSB) * CODE_SLOT + cdst[j]);   \
         ++issued;                                                                                \
       }                                                                                          \
     }                                                                                            \
@@ -698,7 +706,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
       const int i_ = wave + j * NW;                                                              \
       if (i_ >= NC && i_ < NCT && ((i_ - NC) * (1024 / ASL_ROW)) < rows) {                       \
         dma16((const uint8_t*)p.a8s + (size_t)(sk) * ASL_ROW, coff[j],                           \
-              ascale_lds + ((sk) % NSB) * ASL_SLOT + cdst[j]);                                   \
+              ascale_l + ((sk) % NSB) * ASL_SLOT + cdst[j]);                                     \
         ++issued;                                                                                \
       }                                                                                          \
     }                                                                                            \
@@ -717,6 +725,14 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
     mark[(kt) % NS] = issued;                                                                    \
   } while (0)
   const int nwin = (nk + SUPER - 2) / SUPER + 1;   // aligned windows any row needs
+  // Wait for a stage's copies.  With two stages nothing is issued between the group of
+  // the stage about to be consumed and this wait, so it is a plain vmcnt(0) (no count
+  // dispatch on the scalar unit).
+#define MOE_WAIT_STAGE(slot_)                                                                    \
+  do {                                                                                           \
+    if (NS == 2) wait_vmcnt<0>();                                                                \
+    else wait_vmcnt_dyn(__builtin_amdgcn_readfirstlane(issued - mark[slot_]));                   \
+  } while (0)
 #define MOE_ISSUE_NEXT_WIN(kt)                                                                   \
   do {                                                                                           \
     if (WALIGN && (kt) % SUPER == 0 && (kt) / SUPER + 1 < nwin) MOE_ISSUE_WIN((kt) / SUPER + 1); \
@@ -794,8 +810,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   do {                                                                                           \
     for (int kt = 0; kt < nk; ++kt) {                                                            \
       const int slot = kt % NS;                                                                  \
-      if (FMT == 0 && NS == 2) wait_vmcnt<0>();                                                  \
-      else wait_vmcnt_dyn(__builtin_amdgcn_readfirstlane(issued - mark[slot]));                  \
+      MOE_WAIT_STAGE(slot);                                                                      \
       wait_lgkmcnt0();                                                                           \
       barrier_nofence();                                                                         \
       if (MODE == 2 && kt == 0 && rt_a >= 0) rt_g = p.gates[rt_a];                               \
@@ -880,7 +895,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
     uint32_t sap, sbp[FN];                                                                       \
     for (int kt = 0; kt < nk; ++kt) {                                                            \
       const int slot = kt % NS;                                                                  \
-      wait_vmcnt_dyn(__builtin_amdgcn_readfirstlane(issued - mark[slot]));                       \
+      MOE_WAIT_STAGE(slot);                                                                      \
       wait_lgkmcnt0();                                                                           \
       barrier_nofence();                                                                         \
       if (MODE == 2 && kt == 0 && rt_a >= 0) rt_g = p.gates[rt_a];                               \
@@ -949,6 +964,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
 #undef MOE_ISSUE_WIN
 #undef MOE_ISSUE_ASC
 #undef MOE_ISSUE_NEXT_WIN
+#undef MOE_WAIT_STAGE
 #undef MOE_CODES_AT
 #undef MOE_CSHIFT
 #undef MOE_WROW
