@@ -482,6 +482,10 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   constexpr int ASL_BYTES = MX ? NSB * ASL_SLOT : 0;
   constexpr int NASC = MX ? BM * ASL_ROW / 1024 : 0;        // A scale copies per super-stage
   constexpr int NCT = NC + NASC;
+  // with four-stage code super-stages the K loop is unrolled over one, which makes the
+  // stage slot and the super-stage boundaries compile-time constants (measured: a few
+  // percent there; elsewhere it costs registers, spills in the three-piece mlp2 tile)
+  constexpr int UNR = (FMT != 0 && SUPER >= 4 && SUPER % NS == 0) ? SUPER : 1;
   // Code windows aligned to their own size (64 or 128 bytes per row): each row's windows
   // start at the boundary at or below its codes (a row starts 32 s bytes past one when its
   // length is not a multiple of the window), so every 64-byte sector or 128-byte line is
@@ -808,8 +812,11 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
 // the K loop for FA active 32-row fragment rows per wave (the rest are padding), into ACC
 #define MOE_MAIN_LOOP(FA, ACC)                                                                   \
   do {                                                                                           \
-    for (int kt = 0; kt < nk; ++kt) {                                                            \
-      const int slot = kt % NS;                                                                  \
+    for (int kt0 = 0; kt0 < nk; kt0 += UNR) {                                                    \
+    _Pragma("unroll") for (int u_ = 0; u_ < UNR; ++u_) {                                         \
+      const int kt = kt0 + u_;                                                                   \
+      if (kt >= nk) break;                                                                       \
+      const int slot = UNR > 1 ? u_ % NS : kt % NS;                                              \
       MOE_WAIT_STAGE(slot);                                                                      \
       wait_lgkmcnt0();                                                                           \
       barrier_nofence();                                                                         \
@@ -836,6 +843,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
         MOE_MMA(ks & 1, FA, ACC);                                                                \
         MOE_SCHED(FA);                                                                           \
       }                                                                                          \
+    }                                                                                            \
     }                                                                                            \
     MOE_MMA((KS - 1) & 1, FA, ACC);                                                              \
   } while (0)
@@ -893,8 +901,11 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   do {                                                                                           \
     i32x8 fap[AP], fbp[FN];                 /* deferred operands of the previous stage */        \
     uint32_t sap, sbp[FN];                                                                       \
-    for (int kt = 0; kt < nk; ++kt) {                                                            \
-      const int slot = kt % NS;                                                                  \
+    for (int kt0 = 0; kt0 < nk; kt0 += UNR) {                                                    \
+    _Pragma("unroll") for (int u_ = 0; u_ < UNR; ++u_) {                                         \
+      const int kt = kt0 + u_;                                                                   \
+      if (kt >= nk) break;                                                                       \
+      const int slot = UNR > 1 ? u_ % NS : kt % NS;                                              \
       MOE_WAIT_STAGE(slot);                                                                      \
       wait_lgkmcnt0();                                                                           \
       barrier_nofence();                                                                         \
@@ -935,6 +946,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
         fbp[j] = fb[j];                                                                          \
         sbp[j] = sbv[j];                                                                         \
       }                                                                                          \
+    }                                                                                            \
     }                                                                                            \
     MX_MMA(ACC, (FA) - 1, fap, fbp, sap, sbp);                                                   \
   } while (0)
