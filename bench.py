@@ -30,7 +30,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/sec + TFLOP/s (frac. of peak) at GPT-OSS-20B shape, bf16 & MXFP4"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
-BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak (the engine every GEMM here issues)
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 matrix peak: the rate of the scaled fp8 x fp4 instruction
 FP4_PEAK_TFLOPS = 10100.0      # MI355X dense FP4 matrix peak (reported for MXFP4 weights only)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 GEMM_SRC = os.path.join(ROOT, "mixture_experts_transformer_amd", "csrc", "gemm.hip")
@@ -40,12 +41,20 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def mx_engine(cfg):
+    """True where the library runs the expert GEMMs on the scaled fp8 x fp4 instruction: MXFP4
+    weights with at least 128 routed rows per expert on average (its matrix-core tiles)."""
+    return cfg.fmt == "mxfp4" and cfg.T * cfg.k >= 128 * cfg.E
+
+
 def algorithmic(cfg, counts):
     """Algorithmic flops and bytes of one forward, and per-kernel bytes for mlp1/mlp2.
 
     Bytes count each input once and the output once: touched experts' weights and biases,
-    the router, x (bf16) and out (fp32).  Per kernel, mlp1 also writes h and mlp2 reads h
-    and writes y (fp32).
+    the router, x (bf16) and out (fp32).  Per kernel, mlp1 reads x (bf16; on the scaled
+    engine its two fp8 pieces, the same two bytes per element) and writes h, mlp2 reads h
+    and writes y (fp32); h is bf16 (bf16 weights), a bf16 pair (MXFP4, few rows) or three
+    fp8 pieces and one scale dword per 32 elements (scaled engine).
     """
     T, D, E, k, F = cfg.T, cfg.D, cfg.E, cfg.k, cfg.F
     A = T * k
@@ -55,7 +64,10 @@ def algorithmic(cfg, counts):
     else:
         w1_e, w2_e = 2 * F * (D // 2 + D // 32), D * (F // 2 + F // 32)
     b1_e, b2_e = 2 * F * 2, D * 2
-    hbytes = A * F * 2 * (2 if cfg.fmt == "mxfp4" else 1)
+    if mx_engine(cfg):
+        hbytes = A * (3 * F + ((F // 32 + 7) // 8 * 8) * 4)
+    else:
+        hbytes = A * F * 2 * (2 if cfg.fmt == "mxfp4" else 1)
     flops = T * (2 * D * E + 6 * k * D * F)
     step_bytes = touched * (w1_e + b1_e + w2_e + b2_e) + E * D * 2 + E * 2 + T * D * 2 + T * D * 4
     mlp1_bytes = touched * (w1_e + b1_e) + T * D * 2 + hbytes
@@ -159,16 +171,26 @@ def bench_workload(name, steps, warmup, with_cpu):
     dom = max(("mlp1", "mlp2"), key=lambda s: stages[s][0])
     tms, n = stages[dom]
     avg_s = tms / n / 1e3
-    hbm_bound = alg[dom]["flops"] / alg[dom]["bytes"] < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    # the matrix instruction the kernel issues: bf16 (bf16 weights, or MXFP4 decoded to bf16
+    # at few rows per expert), or the scaled fp8 x fp4 one, which runs at the fp8 rate and
+    # issues each flop once per activation piece (x: 2, h: 3)
+    mx = mx_engine(cfg)
+    peak_t = FP8_PEAK_TFLOPS if mx else BF16_PEAK_TFLOPS
+    pieces = (2 if dom == "mlp1" else 3) if mx else (2 if (cfg.fmt == "mxfp4" and dom == "mlp2") else 1)
+    hbm_bound = alg[dom]["flops"] * pieces / alg[dom]["bytes"] < peak_t * 1e12 / (HBM_PEAK_GBS * 1e9)
     if hbm_bound:
         achieved = alg[dom]["bytes"] / avg_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
     else:
         achieved = alg[dom]["flops"] / avg_s / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_t, "unit": "TFLOP/s",
+                "frac": round(achieved / peak_t, 4)}
     roof["kernel"] = dom
+    roof["instruction"] = ("v_mfma_scale_f32_32x32x64_f8f6f4 (fp8 E4M3 activation pieces x MXFP4)" if mx
+                           else "v_mfma_f32_32x32x16_bf16")
+    roof["issued_flop_per_algorithmic_flop"] = pieces
+    roof["issued_frac"] = round(alg[dom]["flops"] * pieces / avg_s / 1e12 / peak_t, 4)
     roof["avg_launch_us"] = round(avg_s * 1e6, 2)
     roof["traffic"] = stored_traffic(name, dom)
 
@@ -184,7 +206,7 @@ def bench_workload(name, steps, warmup, with_cpu):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8xfp4" if mx else "bf16",
         "data": "synthetic",
         "config": {"workload": f"{name}: T={cfg.T} D={cfg.D} E={cfg.E} k={cfg.k} F={cfg.F} "
                                f"{cfg.fmt} expert weights ({cfg.note})",
@@ -192,8 +214,10 @@ def bench_workload(name, steps, warmup, with_cpu):
                    "weights": cfg.fmt, "weight_copies_rotated": copies, "touched_experts": alg["touched"]},
         "step_tflops": round(alg["flops"] / step_s / 1e12, 2),
         "step_mfma_frac": round(alg["flops"] / step_s / 1e12 / BF16_PEAK_TFLOPS, 4),
-        # MXFP4 weights are decoded to bf16 for the bf16 matrix cores; the fraction of the
-        # FP4 peak is reported beside it so nothing is hidden
+        # for MXFP4 weights the fractions of the fp8 and FP4 peaks are reported beside the
+        # bf16 one so nothing is hidden
+        "step_fp8_peak_frac": (round(alg["flops"] / step_s / 1e12 / FP8_PEAK_TFLOPS, 4)
+                               if cfg.fmt == "mxfp4" else None),
         "step_fp4_peak_frac": (round(alg["flops"] / step_s / 1e12 / FP4_PEAK_TFLOPS, 4)
                                if cfg.fmt == "mxfp4" else None),
         "step_hbm_gbs": round(alg["bytes"] / step_s / 1e9, 1),

@@ -127,10 +127,17 @@ struct Tile {
 #ifndef MOE_S_SUPER2
 #define MOE_S_SUPER2 2              // mlp2 (64-byte code segments, but three workgroups per CU)
 #endif
+#ifndef MOE_S_WPE
+#define MOE_S_WPE 1                 // streaming tiles: waves per SIMD the registers must allow
+#endif
+#ifndef MOE_S_WPE4
+#define MOE_S_WPE4 4                //   with MXFP4 weights (register cap: measured a few percent faster)
+#endif
 template <int MODE, int FMT> using SmallTile =
     Tile<MOE_S_BM, (MODE == 1 ? MOE_S_BN1 : MOE_S_BN2), MOE_S_WM, (MODE == 1 ? MOE_S_WN : MOE_S_WN2),
          (FMT == 0 ? (MODE == 1 ? MOE_S_NS : MOE_S_NS2) : (MODE == 1 ? MOE_S_NS4 : MOE_S_NSH)), 64,
-         MOE_S_STREAM != 0, (FMT == 1 ? (MODE == 1 ? MOE_S_SUPER1 : MOE_S_SUPER2) : 4)>;
+         MOE_S_STREAM != 0, (FMT == 1 ? (MODE == 1 ? MOE_S_SUPER1 : MOE_S_SUPER2) : 4),
+         (FMT == 0 ? MOE_S_WPE : MOE_S_WPE4)>;
 #ifndef MOE_L4_BM
 #define MOE_L4_BM 256
 #endif
