@@ -22,13 +22,18 @@
 // stages, details at the kernel.
 //
 // MXFP4 weights (GPT-OSS-in-Transformers blog, MXFP4 paragraph: E2M1 values, one scale
-// per 32 elements) are decoded from LDS into matrix-core operands with the gfx950
-// conversion v_cvt_scalef32_pk_bf16_fp4 (two codes per instruction, low nibble first,
-// multiplied by the block's power-of-two scale).  Every E2M1 value times 2^(s-127) with
-// s in [2, 252] is an exact bf16, so the matrix cores see the weights without rounding.
-// mlp1's inputs are bf16 and exact; h is written as a bf16 pair (hi + lo) and mlp2 runs
-// both parts through the matrix cores against the same decoded weight tile, which keeps
-// h at 16 significant bits where a single bf16 would cost the output its accuracy.
+// per 32 elements) take one of two routes.
+//   Few rows per expert (weight streaming): the codes are decoded from LDS into bf16
+//   matrix-core operands with v_cvt_scalef32_pk_bf16_fp4 (two codes per instruction, low
+//   nibble first, times the block's power-of-two scale; every E2M1 value times 2^(s-127)
+//   with s in [2, 252] is an exact bf16).  h is written as a bf16 pair (hi + lo) and mlp2
+//   runs both parts against the same decoded tile, keeping h at 16 significant bits where
+//   a single bf16 would cost the output its accuracy.
+//   Many rows per expert (matrix-core tiles): the scaled instruction
+//   v_mfma_scale_f32_32x32x64_f8f6f4 takes the codes as its fp4 B operand and the scale
+//   bytes as its B scales unchanged; the activations enter as fp8 E4M3 pieces with their
+//   own block scales (x: two pieces from the split kernel, h: three pieces written by
+//   mlp1's epilogue), so no weight is ever decoded.
 #include "moe_internal.h"
 
 namespace moe {

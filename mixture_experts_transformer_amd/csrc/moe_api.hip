@@ -389,7 +389,8 @@ int moe_profile_read(double* ms, int64_t* launches) {
 
 const char* moe_version(void) {
   return "moe-mi355x gfx950: router fp64-MFMA, top-k wave argmax, grouped GEMM v_mfma_f32_32x32x16_bf16 "
-         "(streaming tile 64x128, matrix-core tile 256x256, MXFP4 h as bf16 hi + lo), combine fp32";
+         "(streaming tile 64x128; matrix-core tile 256x256) and, for MXFP4 on matrix-core tiles, "
+         "v_mfma_scale_f32_32x32x64_f8f6f4 on fp8 activation pieces; combine fp32";
 }
 
 }  // extern "C"
