@@ -108,12 +108,6 @@ struct Tile {
 #ifndef MOE_L_NS
 #define MOE_L_NS 2
 #endif
-#ifndef MOE_L_NS4
-#define MOE_L_NS4 2
-#endif
-#ifndef MOE_L_NSH
-#define MOE_L_NSH 2                 // mlp2 with MXFP4 weights (two A parts per stage)
-#endif
 #ifndef MOE_S_NSH
 #define MOE_S_NSH 2
 #endif
@@ -138,46 +132,20 @@ struct Tile {
 #ifndef MOE_S_WPE4
 #define MOE_S_WPE4 4                //   with MXFP4 weights (register cap: measured a few percent faster)
 #endif
+#ifndef MOE_S_BN14
+#define MOE_S_BN14 MOE_S_BN1        // streaming tile width with MXFP4 weights: mlp1
+#endif
+#ifndef MOE_S_BN24
+#define MOE_S_BN24 MOE_S_BN2        //   mlp2
+#endif
 template <int MODE, int FMT> using SmallTile =
-    Tile<MOE_S_BM, (MODE == 1 ? MOE_S_BN1 : MOE_S_BN2), MOE_S_WM, (MODE == 1 ? MOE_S_WN : MOE_S_WN2),
+    Tile<MOE_S_BM, (MODE == 1 ? (FMT == 0 ? MOE_S_BN1 : MOE_S_BN14) : (FMT == 0 ? MOE_S_BN2 : MOE_S_BN24)),
+         MOE_S_WM, (MODE == 1 ? MOE_S_WN : MOE_S_WN2),
          (FMT == 0 ? (MODE == 1 ? MOE_S_NS : MOE_S_NS2) : (MODE == 1 ? MOE_S_NS4 : MOE_S_NSH)), 64,
          MOE_S_STREAM != 0, (FMT == 1 ? (MODE == 1 ? MOE_S_SUPER1 : MOE_S_SUPER2) : 4),
          (FMT == 0 ? MOE_S_WPE : MOE_S_WPE4)>;
-#ifndef MOE_L4_BM
-#define MOE_L4_BM 256
-#endif
-#ifndef MOE_L4_BN
-#define MOE_L4_BN 256
-#endif
-#ifndef MOE_L4_WM
-#define MOE_L4_WM 2
-#endif
-#ifndef MOE_L4_WN
-#define MOE_L4_WN 4
-#endif
-template <int MODE, int FMT> struct LargeTileSel {
+template <int MODE, int FMT> struct LargeTileSel {   // bf16 weights
   using type = Tile<MOE_L_BM, MOE_L_BN, MOE_L_WM, MOE_L_WN, MOE_L_NS, MOE_L_BK, false>;
-};
-#ifndef MOE_L41_BM
-#define MOE_L41_BM 256              // mlp1 with MXFP4 weights
-#endif
-#ifndef MOE_L41_BN
-#define MOE_L41_BN 256
-#endif
-#ifndef MOE_L41_WM
-#define MOE_L41_WM 2
-#endif
-#ifndef MOE_L41_WN
-#define MOE_L41_WN 4
-#endif
-template <> struct LargeTileSel<1, 1> {
-  using type = Tile<MOE_L41_BM, MOE_L41_BN, MOE_L41_WM, MOE_L41_WN, MOE_L_NS4, 64, false>;
-};
-#ifndef MOE_L4_SUPER
-#define MOE_L4_SUPER 1              // code super-stage of the large MXFP4 mlp2 tile (LDS)
-#endif
-template <> struct LargeTileSel<2, 1> {        // mlp2 with MXFP4 weights: h hi and lo parts
-  using type = Tile<MOE_L4_BM, MOE_L4_BN, MOE_L4_WM, MOE_L4_WN, MOE_L_NSH, 64, false, MOE_L4_SUPER>;
 };
 #ifndef MOE_LX_NS
 #define MOE_LX_NS 2                 // scaled-MFMA engine (fp8 activation pieces x MXFP4)
@@ -478,13 +446,13 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   static_assert(FMT == 0 || SUPER * (NSB - 1) > NS - 2, "code ring too short for the stage ring");
   constexpr int CROW = 32 * SUPER;                          // code bytes per row per super-stage
   constexpr int CCH = CROW / 16;                            // 16-byte code chunks per row
-  constexpr int B_STAGE_BYTES = (FMT == 0) ? BN * ROWB : BN * 4;   // bf16 B tile, or scale dwords
+  constexpr int B_STAGE_BYTES = (FMT == 0) ? BN * ROWB : 0;  // bf16 B tile (MXFP4: none)
   constexpr int STAGE = APL * A_BYTES + B_STAGE_BYTES;
   constexpr int CODE_SLOT = BN * CROW;
   constexpr int CODE_BYTES = (FMT != 0) ? NSB * CODE_SLOT : 0;
   constexpr int ROWS_PER_CP = 1024 / ROWB;                  // bf16 B rows per copy instruction
   constexpr int NA = APL * A_CPC;                           // per stage: A copies
-  constexpr int NBS = (FMT == 0) ? BN / ROWS_PER_CP : BN / 64;   // per stage: B copies / scale copies
+  constexpr int NBS = (FMT == 0) ? BN / ROWS_PER_CP : 0;    // per stage: B copies
   constexpr int NG = NA + NBS;                              // copies per stage group
   constexpr int NC = (FMT != 0) ? BN * CROW / 1024 : 0;     // copies per code super-stage
   // scaled-MFMA engine: A scale dwords (two per row and stage) in a ring of super-stages
@@ -493,7 +461,16 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   constexpr int ASL_SLOT = BM * ASL_ROW;
   constexpr int ASL_BYTES = MX ? NSB * ASL_SLOT : 0;
   constexpr int NASC = MX ? BM * ASL_ROW / 1024 : 0;        // A scale copies per super-stage
-  constexpr int NCT = NC + NASC;
+  // MXFP4 weight scales travel per super-stage, beside the A scales: per row and super-stage
+  // the 16 bytes that end at the 4-aligned address at or past the earlier of the super-stage's
+  // last scale byte and the row's last one (a super-stage needs 2 SUPER <= 8 of them, so the
+  // record covers them; stopping at the row keeps the last row's records inside the weight
+  // buffer, whose size is a multiple of 4); one copy covers 64 rows
+  constexpr int SCW_SLOT = (FMT != 0) ? BN * 16 : 0;
+  constexpr int SCW_BYTES = NSB * SCW_SLOT;
+  constexpr int NSW = (FMT != 0) ? BN / 64 : 0;             // scale copies per window
+  constexpr int NCT = NC + NASC + NSW;
+  static_assert(FMT == 0 || (SUPER % 2 == 0 && SUPER <= 4), "scale records: even windows of <= 8 scale bytes");
   // with four-stage code super-stages the K loop is unrolled over one, which makes the
   // stage slot and the super-stage boundaries compile-time constants (measured: a few
   // percent there; elsewhere it costs registers, spills in the three-piece mlp2 tile)
@@ -512,7 +489,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   static_assert(BN % 32 == 0 && (BM * CPR) % 64 == 0 && (BN * CPR) % 64 == 0, "copy granularity");
   static_assert(FMT == 0 || BN % 64 == 0, "scale copies cover 64 rows");
 
-  constexpr int SMEM = NS * STAGE + CODE_BYTES + ASL_BYTES;
+  constexpr int SMEM = NS * STAGE + CODE_BYTES + ASL_BYTES + SCW_BYTES;
   // epilogue slices (per wave, 32 output rows): mlp1 bf16 [32][pairs] (+ lo part), row
   // stride 2 P + 8 bytes so the four 16-lane groups of one store hit disjoint banks; mlp2
   // fp32 [32][WTN], row stride 4 WTN + 32 bytes so the two lane halves hit disjoint banks
@@ -526,10 +503,12 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM + ROWTAB];
   uint8_t* const codes_lds = smem + NS * STAGE;
   uint8_t* const ascale_lds = codes_lds + CODE_BYTES;       // scaled-MFMA engine: A scales
+  uint8_t* const wsc_lds = ascale_lds + ASL_BYTES;          // MXFP4 weight scale windows
   // the same regions as LDS byte addresses, for the copies
   const uint32_t smem_l = lds_addr(smem);
   const uint32_t codes_l = smem_l + NS * STAGE;
   const uint32_t ascale_l = codes_l + CODE_BYTES;
+  const uint32_t wsc_l = ascale_l + ASL_BYTES;
   int* const tab_a = (int*)(smem + SMEM);
   float* const tab_g = (float*)(smem + SMEM + BM * 4);
 
@@ -604,13 +583,24 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
     w_e = p.w + (size_t)e * p.N * (K / 2);
     s_e_off = (size_t)p.E * p.N * (K / 2) + (size_t)e * p.N * (K / 32);
   }
-  const uint8_t* const s_e4 = p.w + (s_e_off & ~(size_t)3);   // scale copies read aligned dwords
+  // scale records: offsets relative to 32 bytes before the expert's scales (a record can
+  // start up to 24 bytes before a row's first scale byte)
+  const uint8_t* const scbase = p.w + s_e_off - 32;
+  const int s_al = (int)(s_e_off & 3);
   // code-window shift of a weight row (in 32-byte stages), 0 unless the buffer is aligned
   // to the window; windows start below the row, so copies are relative to w_e - CROW
   const bool walign = WALIGN && (((uintptr_t)p.w) & (CROW - 1)) == 0;
   const size_t w_e_off = (size_t)(w_e - p.w);
   const uint8_t* const wbase = WALIGN ? w_e - CROW : w_e;
 #define MOE_CSHIFT(wr) (walign ? (int)(((w_e_off + (size_t)(wr) * (K / 2)) >> 5) & (SUPER - 1)) : 0)
+  // start of super-stage w's 16-byte scale record of a row whose scales are [rs, re)
+  // (offsets relative to the expert's scales): the super-stage's bytes end at
+  // rs + 2 SUPER (w + 1), the record at the 4-aligned address at or past the earlier end
+#define MOE_SCW_START(rs, re, w)                                                                 \
+  ([&]() {                                                                                       \
+    const int e_ = min((int)(rs) + 2 * SUPER * ((w) + 1), (int)(re));                            \
+    return e_ + ((4 - ((s_al + e_) & 3)) & 3) - 16;                                              \
+  }())
   // tile row -> weight row, clamped into the matrix.  mlp1 tiles interleave the halves in
   // 16-row groups: rows 32 j .. 32 j + 15 are gate rows of pairs 16 j .. 16 j + 15 and rows
   // 32 j + 16 .. 32 j + 31 the linear rows of the same pairs, so every 32-column output
@@ -648,32 +638,36 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
         const int c = swz_pos<CPR>(r, lane % CPR);
         goff[j] = (uint32_t)(((size_t)MOE_WROW(r) * K + c * 8) * 2);
         gdst[j] = APL * A_BYTES + ii * 1024;
-      } else {
-        const int r = ii * 64 + lane;
-        goff[j] = (uint32_t)((s_e_off & 3) + (size_t)MOE_WROW(r) * (K / 32));   // scale byte (r, block 0)
-        gdst[j] = APL * A_BYTES + ii * 256;
       }
     }
   }
-  uint32_t coff[PW_C];                      // relative to the expert's codes or the A scales
+  uint32_t coff[PW_C];                      // codes, A scales (window 0); weight scale rows: rs
   int cdst[PW_C];
+  int cre[PW_C];                            // weight scale rows: re
 #pragma unroll
   for (int j = 0; j < PW_C; ++j) {
     const int i = wave + j * NW;
     coff[j] = 0;
     cdst[j] = 0;
+    cre[j] = 0;
     if (FMT != 0 && i < NC) {
       const int r = i * (1024 / CROW) + lane / CCH;
       const int c = (lane % CCH) ^ code_swz<CCH>(r);
       const int wr = MOE_WROW(r);
       coff[j] = (uint32_t)((size_t)wr * (K / 2) + (WALIGN ? CROW - 32 * MOE_CSHIFT(wr) : 0) + c * 16);
       cdst[j] = i * 1024;
-    } else if (i < NCT) {
+    } else if (i < NC + NASC) {
       constexpr int CPS = ASL_ROW / 16;                    // chunks per row
       const int r = (i - NC) * (1024 / ASL_ROW) + lane / CPS;
       const int c = (lane % CPS) ^ (CPS > 1 ? (r >> 3) & (CPS - 1) : 0);
       coff[j] = (uint32_t)((a_row(r) * (size_t)p.a8s_stride + c * 4) * 4);
       cdst[j] = (i - NC) * 1024;
+    } else if (i < NCT) {
+      const int r = (i - NC - NASC) * 64 + lane;           // lane = weight row of the tile
+      const int wr = MOE_WROW(r);
+      coff[j] = (uint32_t)(wr * (K / 32));
+      cre[j] = (wr + 1) * (K / 32);
+      cdst[j] = (i - NC - NASC) * 1024;
     }
   }
 
@@ -695,8 +689,6 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
           const void* ab_ = MX ? (const void*)p.a8                                               \
                                 : (i_ < A_CPC ? (const void*)p.a : (const void*)p.a_lo);          \
           dma16((const uint8_t*)ab_ + (size_t)(kt) * A_ROWB, goff[j], d_);                       \
-        } else if (FMT != 0) {                                                                   \
-          dma4(s_e4, (goff[j] + (kt) * (BK / 32)) & ~3u, d_);                                    \
         } else {                                                                                 \
           dma16(w_e + (size_t)(kt) * ROWB, goff[j], d_);                                         \
         }                                                                                        \
@@ -715,14 +707,18 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
       }                                                                                          \
     }                                                                                            \
   } while (0)
-// A scale super-stage sk (scaled-MFMA engine)
+// the scales of super-stage sk: weight scale records, and A scales (scaled-MFMA engine)
 #define MOE_ISSUE_ASC(sk)                                                                        \
   do {                                                                                           \
     _Pragma("unroll") for (int j = 0; j < PW_C; ++j) {                                           \
       const int i_ = wave + j * NW;                                                              \
-      if (i_ >= NC && i_ < NCT && ((i_ - NC) * (1024 / ASL_ROW)) < rows) {                       \
+      if (i_ >= NC && i_ < NC + NASC && ((i_ - NC) * (1024 / ASL_ROW)) < rows) {                 \
         dma16((const uint8_t*)p.a8s + (size_t)(sk) * ASL_ROW, coff[j],                           \
               ascale_l + ((sk) % NSB) * ASL_SLOT + cdst[j]);                                     \
+        ++issued;                                                                                \
+      } else if (i_ >= NC + NASC && i_ < NCT) {                                                  \
+        dma16(scbase, (uint32_t)(MOE_SCW_START((int)coff[j], cre[j], sk) + 32),                  \
+              wsc_l + ((sk) % NSB) * SCW_SLOT + cdst[j]);                                        \
         ++issued;                                                                                \
       }                                                                                          \
     }                                                                                            \
@@ -762,18 +758,38 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-  // B-tile row of this lane for fragment j; byte of its scale dword for K step 0
+  const int kg = lane >> 5;                 // which half of the stage's K range this lane feeds
+  // B-tile row of this lane for fragment j
   int brow[FN];
-  int sbyte[FN];
   int csh[FN];                              // code-window shift of the fragment row
+  int sidx[FN];                             // scale ring byte of the fragment row's first stage
+                                            //   of a super-stage (K block kg), in slot 0
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     brow[j] = wn * C::WTN + j * 32 + (lane & 31);
-    sbyte[j] = 0;
     csh[j] = 0;
-    if (FMT != 0) sbyte[j] = (int)((s_e_off + (size_t)MOE_WROW(brow[j]) * (K / 32)) & 3);
+    sidx[j] = 0;
     if (WALIGN) csh[j] = MOE_CSHIFT(MOE_WROW(brow[j]));
+    if (FMT != 0) {
+      const int rs = MOE_WROW(brow[j]) * (K / 32);
+      sidx[j] = brow[j] * 16 + rs - MOE_SCW_START(rs, 1 << 30, 0) + kg;
+    }
   }
+  // the last super-stage's records stop at the row's end, so its bytes sit further into
+  // the record: move the fragments' scale bytes there when it starts
+  const int sk_last = (nk - 1) / SUPER;
+#define MOE_SCALE_LAST(kt_)                                                                      \
+  do {                                                                                           \
+    if (FMT != 0 && (kt_) == SUPER * sk_last) {                                                  \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                           \
+        const int rs_ = MOE_WROW(brow[j]) * (K / 32);                                            \
+        sidx[j] += MOE_SCW_START(rs_, 1 << 30, sk_last) - MOE_SCW_START(rs_, rs_ + K / 32, sk_last); \
+      }                                                                                          \
+    }                                                                                            \
+  } while (0)
+  // this lane's scale byte of fragment j for stage kt (K block kg) in the scale ring
+#define MOE_SCALE_AT(kt_, j_)                                                                    \
+  ((uint32_t)wsc_lds[(((kt_) / SUPER) % NSB) * SCW_SLOT + sidx[j_] + 2 * ((kt_) % SUPER)])
   // this lane's 32 codes of fragment j for stage kt in the code ring
 #define MOE_CODES_AT(kt_, j_)                                                                    \
   ([&]() {                                                                                       \
@@ -783,7 +799,6 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
            ((c_ ^ code_swz<CCH>(brow[j_])) << 4);                                               \
   }())
   const int arow0 = wm * C::WTM + (lane & 31);
-  const int kg = lane >> 5;                 // which half of the stage's K range this lane feeds
 
   // prologue: NS - 1 stages in flight
   if (WALIGN) MOE_ISSUE_WIN(0);
@@ -839,10 +854,11 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
       const uint8_t* sa = smem + slot * STAGE;                                                   \
       const uint8_t* sb = sa + AP * A_BYTES;                                                     \
       if (FMT == 1) {                                                                            \
+        if (UNR == 1 || u_ == 0) MOE_SCALE_LAST(kt);                                             \
   _Pragma("unroll")                                                                              \
         for (int j = 0; j < FN; ++j) {                                                           \
           q4[j] = *(const u32x4*)MOE_CODES_AT(kt, j);                                            \
-          const uint32_t sc = sb[brow[j] * 4 + ((sbyte[j] + 2 * kt + kg) & 3)];                  \
+          const uint32_t sc = MOE_SCALE_AT(kt, j);                                               \
           scl[j] = __uint_as_float(sc << 23);                                                    \
         }                                                                                        \
       }                                                                                          \
@@ -929,10 +945,11 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
       const uint8_t* sb = sa + A_BYTES;                                                          \
       i32x8 fb[FN];                                                                              \
       uint32_t sbv[FN];                                                                          \
+      if (UNR == 1 || u_ == 0) MOE_SCALE_LAST(kt);                                               \
       _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                           \
         const i32x4 q = *(const i32x4*)MOE_CODES_AT(kt, j);                                      \
         fb[j] = __builtin_shufflevector(q, q, 0, 1, 2, 3, -1, -1, -1, -1);                       \
-        sbv[j] = sb[brow[j] * 4 + ((sbyte[j] + 2 * kt + kg) & 3)];                               \
+        sbv[j] = MOE_SCALE_AT(kt, j);                                                            \
       }                                                                                          \
       uint32_t sav[FA];                                                                          \
       const int dw = (kt % SUPER) * 2 + kg;  /* scale dword of this stage and K block */         \
@@ -991,6 +1008,9 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
 #undef MOE_WAIT_STAGE
 #undef MOE_CODES_AT
 #undef MOE_CSHIFT
+#undef MOE_SCW_START
+#undef MOE_SCALE_AT
+#undef MOE_SCALE_LAST
 #undef MOE_WROW
 
   // ---- epilogue.  Output register q of fragment (i, j) is row 8 (q >> 2) + 4 kg + (q & 3)
@@ -1168,8 +1188,9 @@ static hipError_t launch_any(const GemmArgs& g, int fmt, int cfg, int64_t A, hip
   if (fmt == 2) return launch_gemm<MODE, 2, LargeTile<MODE, 2>>(g, A, st);
   if (fmt == 0)
     return cfg == 0 ? launch_gemm<MODE, 0, SmallTile<MODE, 0>>(g, A, st) : launch_gemm<MODE, 0, LargeTile<MODE, 0>>(g, A, st);
-  return cfg == 0 ? launch_gemm<MODE, 1, SmallTile<MODE, 1>>(g, A, st)
-                  : launch_gemm<MODE, 1, LargeTile<MODE, 1>>(g, A, st);
+  // MXFP4 on matrix-core tiles runs on the scaled engine (fmt 2)
+  if (cfg != 0) return hipErrorInvalidValue;
+  return launch_gemm<MODE, 1, SmallTile<MODE, 1>>(g, A, st);
 }
 
 // Streaming tiles keep the decoded-bf16 path: with few rows per expert the stage loop is
