@@ -138,9 +138,15 @@ struct Tile {
 #ifndef MOE_S_BN24
 #define MOE_S_BN24 MOE_S_BN2        //   mlp2
 #endif
+#ifndef MOE_S_WN4
+#define MOE_S_WN4 MOE_S_WN          // waves across the streaming MXFP4 tiles: mlp1
+#endif
+#ifndef MOE_S_WN24
+#define MOE_S_WN24 MOE_S_WN2        //   mlp2
+#endif
 template <int MODE, int FMT> using SmallTile =
     Tile<MOE_S_BM, (MODE == 1 ? (FMT == 0 ? MOE_S_BN1 : MOE_S_BN14) : (FMT == 0 ? MOE_S_BN2 : MOE_S_BN24)),
-         MOE_S_WM, (MODE == 1 ? MOE_S_WN : MOE_S_WN2),
+         MOE_S_WM, (MODE == 1 ? (FMT == 0 ? MOE_S_WN : MOE_S_WN4) : (FMT == 0 ? MOE_S_WN2 : MOE_S_WN24)),
          (FMT == 0 ? (MODE == 1 ? MOE_S_NS : MOE_S_NS2) : (MODE == 1 ? MOE_S_NS4 : MOE_S_NSH)), 64,
          MOE_S_STREAM != 0, (FMT == 1 ? (MODE == 1 ? MOE_S_SUPER1 : MOE_S_SUPER2) : 4),
          (FMT == 0 ? MOE_S_WPE : MOE_S_WPE4)>;

@@ -185,6 +185,24 @@ int launch(int stage, const char* name, F&& fn) {
   return MOE_OK;
 }
 
+// router -> top-k -> grouping
+int run_route(uint8_t* ws, const Layout& L, const void* x, const void* router_w, const void* router_b, int64_t T,
+              int64_t D, int64_t E, int64_t k, float* logits, int32_t* idx, float* gates, int32_t* counts,
+              int32_t* offsets, int32_t* perm) {
+  double* partial = (double*)(ws + L.partial);
+  const int ks = moe::router_ksplit(T, D);
+  CHECK(launch(moe::ST_ROUTER, "router", [&](hipStream_t st) {
+    return moe::launch_router_partial((const uint16_t*)x, (const uint16_t*)router_w, (int)T, (int)D, (int)E, ks,
+                                      partial, st);
+  }));
+  CHECK(launch(moe::ST_TOPK, "topk", [&](hipStream_t st) {
+    return moe::launch_topk(partial, ks, (const uint16_t*)router_b, (int)T, (int)E, (int)k, logits, idx, gates, st);
+  }));
+  return launch(moe::ST_PERMUTE, "permute", [&](hipStream_t st) {
+    return moe::launch_permute(idx, (int)(T * k), (int)E, (int32_t*)(ws + L.hist), counts, offsets, perm, st);
+  });
+}
+
 int run_experts(const uint8_t* ws, const Layout& L, const void* x, const void* w1, const void* b1,
                 const void* w2, const void* b2, const float* gates, const int32_t* offsets,
                 const int32_t* perm, int64_t T, int64_t D, int64_t E, int64_t k, int64_t F, int fmt,
@@ -240,23 +258,12 @@ int moe_forward(const void* x, const void* router_w, const void* router_b, const
   const Layout L = layout(T, D, E, k, F, fmt, NEED_ROUTE | NEED_ROUTE_OUTPUTS | NEED_EXPERTS);
   uint8_t* ws = nullptr;
   CHECK(ensure_workspace(L.total, &ws));
-  const int ks = moe::router_ksplit(T, D);
-  double* partial = (double*)(ws + L.partial);
   int32_t* idx = (int32_t*)(ws + L.idx);
   float* gates = (float*)(ws + L.gates);
   int32_t* counts = (int32_t*)(ws + L.counts);
   int32_t* offsets = (int32_t*)(ws + L.offsets);
   int32_t* perm = (int32_t*)(ws + L.perm);
-  CHECK(launch(moe::ST_ROUTER, "router", [&](hipStream_t st) {
-    return moe::launch_router_partial((const uint16_t*)x, (const uint16_t*)router_w, (int)T, (int)D, (int)E, ks,
-                                      partial, st);
-  }));
-  CHECK(launch(moe::ST_TOPK, "topk", [&](hipStream_t st) {
-    return moe::launch_topk(partial, ks, (const uint16_t*)router_b, (int)T, (int)E, (int)k, nullptr, idx, gates, st);
-  }));
-  CHECK(launch(moe::ST_PERMUTE, "permute", [&](hipStream_t st) {
-    return moe::launch_permute(idx, (int)(T * k), (int)E, (int32_t*)(ws + L.hist), counts, offsets, perm, st);
-  }));
+  CHECK(run_route(ws, L, x, router_w, router_b, T, D, E, k, nullptr, idx, gates, counts, offsets, perm));
   CHECK(run_experts(ws, L, x, w1, b1, w2, b2, gates, offsets, perm, T, D, E, k, F, fmt, out));
   return ok();
 }
@@ -278,19 +285,7 @@ int moe_route(const void* x, const void* router_w, const void* router_b, int64_t
   const Layout L = layout(T, D, E, k, 64, MOE_FMT_BF16, NEED_ROUTE);
   uint8_t* ws = nullptr;
   CHECK(ensure_workspace(L.total, &ws));
-  const int ks = moe::router_ksplit(T, D);
-  double* partial = (double*)(ws + L.partial);
-  CHECK(launch(moe::ST_ROUTER, "router", [&](hipStream_t st) {
-    return moe::launch_router_partial((const uint16_t*)x, (const uint16_t*)router_w, (int)T, (int)D, (int)E, ks,
-                                      partial, st);
-  }));
-  CHECK(launch(moe::ST_TOPK, "topk", [&](hipStream_t st) {
-    return moe::launch_topk(partial, ks, (const uint16_t*)router_b, (int)T, (int)E, (int)k, logits, topk_idx, gates,
-                            st);
-  }));
-  CHECK(launch(moe::ST_PERMUTE, "permute", [&](hipStream_t st) {
-    return moe::launch_permute(topk_idx, (int)(T * k), (int)E, (int32_t*)(ws + L.hist), counts, offsets, perm, st);
-  }));
+  CHECK(run_route(ws, L, x, router_w, router_b, T, D, E, k, logits, topk_idx, gates, counts, offsets, perm));
   return ok();
 }
 

@@ -11,8 +11,10 @@
 // sums are added in a fixed order by the top-k kernel (deterministic).
 //
 // Top-k ("gptoss" re-implementation page, basic parameters: top-4 of 32 experts): one
-// wave per token, lanes own experts, k rounds of a wave-wide (value desc, index asc)
-// argmax.  Gates: softmax over the k selected logits, in fp64, stored as fp32.
+// wave per token, lanes own experts.  Up to 64 experts each lane counts the experts that
+// beat its own (value desc, index asc) and the ranks below k are the selection; beyond,
+// k rounds of a wave-wide argmax.  Gates: softmax over the k selected logits, in fp64,
+// stored as fp32.
 //
 // Grouping (torchtitan guide, grouped GEMM section: per-expert counts and their int32
 // cumulative sum as group offsets): workgroups of 16 waves over chunks of the assignments
@@ -34,13 +36,19 @@ constexpr int RT_WAVES = 4;           // waves per workgroup, each owns 16 token
 constexpr int RT_CHUNK = 32;          // K elements per MFMA group (8 steps of K=4)
 constexpr int RT_PD = 4;              // chunks whose loads are in flight (up to 64 experts)
 
+#ifndef RT_TARGET_WAVES
+#define RT_TARGET_WAVES 2048
+#endif
+#ifndef RT_MIN_CHUNKS
+#define RT_MIN_CHUNKS 6
+#endif
 int router_ksplit(int64_t T, int64_t D) {
   const int64_t chunks = D / RT_CHUNK;
   const int64_t tiles = (T + 15) / 16;
   // aim at ~2048 waves in flight; keep >= 6 chunks per split so the top-k kernel's
   // sum over splits stays short
-  int64_t ks = (2048 + tiles - 1) / tiles;
-  int64_t maxks = chunks / 6 > 0 ? chunks / 6 : 1;
+  int64_t ks = (RT_TARGET_WAVES + tiles - 1) / tiles;
+  int64_t maxks = chunks / RT_MIN_CHUNKS > 0 ? chunks / RT_MIN_CHUNKS : 1;
   if (ks > maxks) ks = maxks;
   if (ks < 1) ks = 1;
   return (int)ks;
@@ -49,19 +57,15 @@ int router_ksplit(int64_t T, int64_t D) {
 // v_mfma_f64_16x16x4f64 lane layout (measured on gfx950): A lane l supplies A[l & 15][l >> 4],
 // B lane l supplies B[l >> 4][l & 15], and output register r of lane l holds C[m][n] with
 // m = (l >> 4) + 4 r, n = l & 15.
+//
+// One wave's share: the dot products of tokens t0 .. t0 + 15 with experts 0 .. 16 NEB - 1 over
+// the 32-element chunks [c_begin, c_end) of D, summed in chunk order.  acc[b][r] of lane l
+// is token t0 + (l >> 4) + 4 r, expert 16 b + (l & 15).
 template <int NEB>
-__global__ __launch_bounds__(64 * RT_WAVES) void router_partial_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int D, int E,
-    int ksplit, double* __restrict__ partial) {
+static __device__ __forceinline__ void router_wave(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+                                                   int T, int D, int E, int t0, int c_begin, int c_end,
+                                                   f64x4 (&acc)[NEB]) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int t0 = (blockIdx.x * RT_WAVES + wave) * 16;
-  if (t0 >= T) return;
-  const int s = blockIdx.y;
-  const int nchunks = D / RT_CHUNK;
-  const int c_begin = (int)((int64_t)nchunks * s / ksplit);
-  const int c_end = (int)((int64_t)nchunks * (s + 1) / ksplit);
-
   const int row = lane & 15;   // token (A) / expert-in-block (B)
   const int kg = lane >> 4;    // which 8-element run of the 32-element chunk
   const int t = min(t0 + row, T - 1);
@@ -73,7 +77,6 @@ __global__ __launch_bounds__(64 * RT_WAVES) void router_partial_kernel(
     wrow[b] = wr + (size_t)e * D + kg * 8;
   }
 
-  f64x4 acc[NEB];
 #pragma unroll
   for (int b = 0; b < NEB; ++b) acc[b] = f64x4{0.0, 0.0, 0.0, 0.0};
 
@@ -121,6 +124,24 @@ __global__ __launch_bounds__(64 * RT_WAVES) void router_partial_kernel(
       }
     }
   }
+}
+
+template <int NEB>
+__global__ __launch_bounds__(64 * RT_WAVES) void router_partial_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int D, int E,
+    int ksplit, double* __restrict__ partial) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int t0 = (blockIdx.x * RT_WAVES + wave) * 16;
+  if (t0 >= T) return;
+  const int s = blockIdx.y;
+  const int nchunks = D / RT_CHUNK;
+  const int c_begin = (int)((int64_t)nchunks * s / ksplit);
+  const int c_end = (int)((int64_t)nchunks * (s + 1) / ksplit);
+  f64x4 acc[NEB];
+  router_wave<NEB>(x, wr, T, D, E, t0, c_begin, c_end, acc);
+  const int row = lane & 15;
+  const int kg = lane >> 4;
   // partial[s][t][e]: token t0 + kg + 4r, expert b*16 + row
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -162,39 +183,32 @@ static __device__ __forceinline__ bool beats(float v, int e, float v2, int e2) {
   return v > v2 || (v == v2 && e < e2);
 }
 
-__global__ __launch_bounds__(64 * TK_WAVES) void topk_kernel(
-    const double* __restrict__ partial, int ksplit, const uint16_t* __restrict__ br, int T, int E,
-    int k, float* __restrict__ logits, int32_t* __restrict__ idx, float* __restrict__ gates) {
-  __shared__ float sel_v[TK_WAVES][256];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int t = blockIdx.x * TK_WAVES + wave;
-  if (t >= T) return;
-  constexpr int PER = 4;   // E <= 256 = 4 * 64
-  float v[PER];
-  bool live[PER];
+// Logit of token t and expert e from the split partial sums: added in split order (16
+// loads in flight per batch), plus the bias, then rounded once to fp32 (nearest even).
+static __device__ __forceinline__ float logit_from_partials(const double* __restrict__ partial, int ksplit,
+                                                            const uint16_t* __restrict__ br, int T, int E,
+                                                            int t, int e) {
+  double s = 0.0;
+  for (int q0 = 0; q0 < ksplit; q0 += 16) {
+    double pv[16];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = lane + 64 * i;
-    live[i] = e < E;
-    v[i] = -INFINITY;
-    if (live[i]) {
-      // all partials in flight at once (16 per batch), then added in split order
-      double s = 0.0;
-      for (int q0 = 0; q0 < ksplit; q0 += 16) {
-        double pv[16];
+    for (int q = 0; q < 16; ++q)
+      pv[q] = (q0 + q < ksplit) ? partial[((size_t)(q0 + q) * T + t) * E + e] : 0.0;
 #pragma unroll
-        for (int q = 0; q < 16; ++q)
-          pv[q] = (q0 + q < ksplit) ? partial[((size_t)(q0 + q) * T + t) * E + e] : 0.0;
-#pragma unroll
-        for (int q = 0; q < 16; ++q)
-          if (q0 + q < ksplit) s += pv[q];
-      }
-      s += bf16_bits_to_f64(br[e]);
-      v[i] = (float)s;   // round to nearest even
-      if (logits) logits[(size_t)t * E + e] = v[i];
-    }
+    for (int q = 0; q < 16; ++q)
+      if (q0 + q < ksplit) s += pv[q];
   }
+  s += bf16_bits_to_f64(br[e]);
+  return (float)s;
+}
+
+// Top-k of token t by one wave: lane l holds the logits v[i] of experts l + 64 i where
+// live[i].  Writes idx and gates of the token; sel is k floats of this wave's LDS.
+static __device__ __forceinline__ void topk_wave(float (&v)[4], bool (&live)[4], int k, int t,
+                                                 int32_t* __restrict__ idx, float* __restrict__ gates,
+                                                 float* sel) {
+  constexpr int PER = 4;
+  const int lane = threadIdx.x & 63;
   for (int j = 0; j < k; ++j) {
     // lane-local best among live entries; any live entry beats "none" (NONE), so the
     // winner is always a valid expert index even for NaN logits (outside the contract)
@@ -232,17 +246,125 @@ __global__ __launch_bounds__(64 * TK_WAVES) void topk_kernel(
       if (lane + 64 * i == be) live[i] = false;
     if (lane == 0) {
       idx[(size_t)t * k + j] = be;
-      sel_v[wave][j] = bv;
+      sel[j] = bv;
     }
   }
+  __builtin_amdgcn_wave_barrier();
   // gates: softmax over the k selected logits, in fp64
-  const double top = (double)sel_v[wave][0];
+  const double top = (double)sel[0];
   double part = 0.0;
-  for (int j = lane; j < k; j += 64) part += exp((double)sel_v[wave][j] - top);
+  for (int j = lane; j < k; j += 64) part += exp((double)sel[j] - top);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
   for (int j = lane; j < k; j += 64)
-    gates[(size_t)t * k + j] = (float)(exp((double)sel_v[wave][j] - top) / part);
+    gates[(size_t)t * k + j] = (float)(exp((double)sel[j] - top) / part);
+}
+
+// Top-k and gates of NT tokens at once by one wave, lane e holding expert e's logit v[i]
+// (at most 64 experts; live[i] false for lanes past E and skipped tokens, t[i] < 0).  The
+// same selection as the top-k kernel's, by rank instead of k rounds of wave-wide argmax:
+// each lane counts the experts that beat it (larger logit, or equal and lower index;
+// -0 equals +0, NaN loses to every number), the experts of rank j < k are the token's j-th,
+// and lane j then holds the j-th for the gates.  key/sel_v/sel_e: NT x 64 entries of this
+// wave's LDS each.
+static __device__ __forceinline__ uint32_t order_key(float v) {
+  const uint32_t b = __float_as_uint(v + 0.0f);          // -0 -> +0
+  if (v != v) return 0u;                                 // NaN: below everything
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);     // monotone in v, >= 0x007FFFFF
+}
+template <int NT>
+static __device__ __forceinline__ void topk_rank_lanes(const float (&v)[NT], const bool (&live)[NT], const int (&t)[NT],
+                                                       int E, int k, int32_t* __restrict__ idx,
+                                                       float* __restrict__ gates, uint32_t (*key)[64],
+                                                       float (*sel_v)[64], int (*sel_e)[64]) {
+  const int lane = threadIdx.x & 63;
+  uint32_t my[NT];
+  int rank[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    my[i] = live[i] ? order_key(v[i]) : 0u;
+    key[i][lane] = my[i];                                // lanes past E: 0, never beat
+    rank[i] = 0;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  for (int e0 = 0; e0 < E; e0 += 4) {
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const uint4 q = *(const uint4*)&key[i][e0];        // the same address in every lane
+      const uint32_t kk[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) rank[i] += (kk[u] > my[i] || (kk[u] == my[i] && e0 + u < lane)) ? 1 : 0;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NT; ++i)
+    if (live[i] && rank[i] < k) {
+      sel_v[i][rank[i]] = v[i];
+      sel_e[i][rank[i]] = lane;
+    }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // gates: softmax over the k selected logits, in fp64 (lane j < k holds the j-th)
+  double ex[NT], sum[NT];
+  int my_e[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const float top = sel_v[i][0];
+    my_e[i] = lane < k ? sel_e[i][lane] : 0;
+    ex[i] = lane < k ? exp((double)sel_v[i][lane] - (double)top) : 0.0;
+    sum[i] = ex[i];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+    for (int i = 0; i < NT; ++i) sum[i] += __shfl_xor(sum[i], off);
+#pragma unroll
+  for (int i = 0; i < NT; ++i)
+    if (t[i] >= 0 && lane < k) {
+      idx[(size_t)t[i] * k + lane] = my_e[i];
+      gates[(size_t)t[i] * k + lane] = (float)(ex[i] / sum[i]);
+    }
+}
+
+__global__ __launch_bounds__(64 * TK_WAVES) void topk_kernel(
+    const double* __restrict__ partial, int ksplit, const uint16_t* __restrict__ br, int T, int E,
+    int k, float* __restrict__ logits, int32_t* __restrict__ idx, float* __restrict__ gates) {
+  __shared__ float sel_v[TK_WAVES][256];
+  __shared__ uint32_t rk_key[TK_WAVES][1][64];
+  __shared__ float rk_v[TK_WAVES][1][64];
+  __shared__ int rk_e[TK_WAVES][1][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * TK_WAVES + wave;
+  if (t >= T) return;
+  if (E <= 64) {
+    // one expert per lane: selection by rank
+    const bool live[1] = {lane < E};
+    const int tt[1] = {t};
+    float v[1] = {-INFINITY};
+    if (live[0]) {
+      v[0] = logit_from_partials(partial, ksplit, br, T, E, t, lane);
+      if (logits) logits[(size_t)t * E + lane] = v[0];
+    }
+    topk_rank_lanes<1>(v, live, tt, E, k, idx, gates, rk_key[wave], rk_v[wave], rk_e[wave]);
+    return;
+  }
+  float v[4];
+  bool live[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {    // E <= 256 = 4 * 64
+    const int e = lane + 64 * i;
+    live[i] = e < E;
+    v[i] = -INFINITY;
+    if (live[i]) {
+      v[i] = logit_from_partials(partial, ksplit, br, T, E, t, e);
+      if (logits) logits[(size_t)t * E + e] = v[i];
+    }
+  }
+  topk_wave(v, live, k, t, idx, gates, sel_v[wave]);
 }
 
 hipError_t launch_topk(const double* partial, int ksplit, const uint16_t* br, int T, int E, int k,
@@ -281,66 +403,104 @@ __global__ __launch_bounds__(1024) void permute_hist_kernel(const int32_t* __res
 // histogram of pass 1).  Each wave owns a contiguous range, counts it per expert in LDS,
 // and after a scan places each assignment at its expert's base plus the earlier
 // assignments of that expert, ranked inside a 64-assignment step by ballots.
-__global__ __launch_bounds__(64 * PM_WAVES) void permute_kernel(
-    const int32_t* __restrict__ idx, int A, int E, const int32_t* __restrict__ hist, int G,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm) {
-  __shared__ int cnt[PM_WAVES][256];
-  __shared__ int base[PM_WAVES][256];
-  __shared__ int tot[256];
+// The body, for a workgroup of NW waves (threads 0 .. 64 NW - 1) and its LDS.
+template <int NW>
+static __device__ __forceinline__ void group_assignments(
+    const int32_t* idx, int A, int E, const int32_t* __restrict__ hist, int G, int g,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+    int (*cnt)[256], int (*base)[256], int* tot) {
+  static_assert(NW * 64 >= 256, "the scan over experts takes 256 threads");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int g = blockIdx.x;
   const int c_lo = hist ? g * PM_CHUNK : 0;
   const int c_hi = hist ? min(A, c_lo + PM_CHUNK) : A;
-  for (int i = tid; i < PM_WAVES * 256; i += blockDim.x) (&cnt[0][0])[i] = 0;
+  for (int i = tid; i < NW * 256; i += NW * 64) (&cnt[0][0])[i] = 0;
   __syncthreads();
   // contiguous range per wave, a multiple of 64 long
-  const int per = ((c_hi - c_lo + PM_WAVES - 1) / PM_WAVES + 63) & ~63;
+  const int per = ((c_hi - c_lo + NW - 1) / NW + 63) & ~63;
   const int lo = min(c_hi, c_lo + wave * per);
   const int hi = min(c_hi, lo + per);
   for (int a = lo + lane; a < hi; a += 64) atomicAdd(&cnt[wave][min(max(idx[a], 0), E - 1)], 1);
   __syncthreads();
-  // totals over all assignments and, split, over the chunks before this one
-  int pre = 0;
-  if (tid < 256) {
-    int s = 0;
-    if (tid < E) {
-      if (hist) {
-        for (int q = 0; q < G; ++q) {
-          const int v = hist[(size_t)q * E + tid];
-          s += v;
-          if (q < g) pre += v;
+  // totals over all assignments and, split, over the chunks before this one; their
+  // exclusive scan over experts gives the offsets, and each wave's base per expert follows
+  if (E <= 64) {
+    // one expert per lane of wave 0: the scan is a wave-wide prefix sum
+    if (wave == 0) {
+      int s = 0, pre = 0;
+      if (lane < E) {
+        if (hist) {
+          for (int q = 0; q < G; ++q) {
+            const int v = hist[(size_t)q * E + lane];
+            s += v;
+            if (q < g) pre += v;
+          }
+        } else {
+          for (int w = 0; w < NW; ++w) s += cnt[w][lane];
         }
-      } else {
-        for (int w = 0; w < PM_WAVES; ++w) s += cnt[w][tid];
+      }
+      int inc = s;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(inc, off);
+        if (lane >= off) inc += y;
+      }
+      if (lane < E) {
+        if (g == 0) {
+          counts[lane] = s;
+          offsets[lane] = inc - s;
+          if (lane == E - 1) offsets[E] = inc;
+        }
+        int b = inc - s + pre;
+        for (int w = 0; w < NW; ++w) {
+          base[w][lane] = b;
+          b += cnt[w][lane];
+        }
       }
     }
-    tot[tid] = s;
-    if (tid < E && g == 0) counts[tid] = s;
-  }
-  __syncthreads();
-  // inclusive scan of the totals over experts (threads 0..255)
-  for (int off = 1; off < 256; off <<= 1) {
-    int v = 0;
-    if (tid < 256 && tid >= off) v = tot[tid - off];
     __syncthreads();
-    if (tid < 256) tot[tid] += v;
+  } else {
+    int pre = 0;
+    if (tid < 256) {
+      int s = 0;
+      if (tid < E) {
+        if (hist) {
+          for (int q = 0; q < G; ++q) {
+            const int v = hist[(size_t)q * E + tid];
+            s += v;
+            if (q < g) pre += v;
+          }
+        } else {
+          for (int w = 0; w < NW; ++w) s += cnt[w][tid];
+        }
+      }
+      tot[tid] = s;
+      if (tid < E && g == 0) counts[tid] = s;
+    }
+    __syncthreads();
+    // inclusive scan of the totals over experts (threads 0..255)
+    for (int off = 1; off < 256; off <<= 1) {
+      int v = 0;
+      if (tid < 256 && tid >= off) v = tot[tid - off];
+      __syncthreads();
+      if (tid < 256) tot[tid] += v;
+      __syncthreads();
+    }
+    if (tid < E) {
+      const int first = (tid == 0) ? 0 : tot[tid - 1];   // exclusive prefix
+      if (g == 0) {
+        offsets[tid] = first;
+        if (tid == E - 1) offsets[E] = tot[tid];
+      }
+      int b = first + pre;
+      for (int w = 0; w < NW; ++w) {
+        base[w][tid] = b;
+        b += cnt[w][tid];
+      }
+    }
     __syncthreads();
   }
-  if (tid < E) {
-    const int first = (tid == 0) ? 0 : tot[tid - 1];   // exclusive prefix
-    if (g == 0) {
-      offsets[tid] = first;
-      if (tid == E - 1) offsets[E] = tot[tid];
-    }
-    int b = first + pre;
-    for (int w = 0; w < PM_WAVES; ++w) {
-      base[w][tid] = b;
-      b += cnt[w][tid];
-    }
-  }
-  __syncthreads();
   // place assignments: rank among equal experts inside each 64-wide step by ballots
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
@@ -365,6 +525,15 @@ __global__ __launch_bounds__(64 * PM_WAVES) void permute_kernel(
     }
     __builtin_amdgcn_wave_barrier();
   }
+}
+
+__global__ __launch_bounds__(64 * PM_WAVES) void permute_kernel(
+    const int32_t* __restrict__ idx, int A, int E, const int32_t* __restrict__ hist, int G,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm) {
+  __shared__ int cnt[PM_WAVES][256];
+  __shared__ int base[PM_WAVES][256];
+  __shared__ int tot[256];
+  group_assignments<PM_WAVES>(idx, A, E, hist, G, blockIdx.x, counts, offsets, perm, cnt, base, tot);
 }
 
 hipError_t launch_permute(const int32_t* idx, int A, int E, int32_t* hist, int32_t* counts,

@@ -58,6 +58,8 @@ def rand_layer(seed, T, D, E, bias_std=0.5):
 @pytest.mark.parametrize("T,D,E,k", [
     (1, 64, 4, 2), (15, 64, 5, 1), (17, 128, 16, 16), (63, 64, 33, 4), (65, 192, 100, 8),
     (1000, 64, 256, 4), (300, 2880, 1, 1), (129, 256, 7, 7), (2049, 64, 64, 2),
+    # one expert per lane in the top-k (E <= 64): at 64 experts, k = E, 4096 assignments
+    (2048, 64, 64, 2), (1024, 128, 64, 4), (16, 64, 64, 64), (33, 2880, 64, 3),
 ])
 def test_route_ragged_shapes(T, D, E, k):
     run_and_compare(*rand_layer(T * 7 + E, T, D, E), k, f"ragged T={T} D={D} E={E} k={k}")
@@ -99,3 +101,21 @@ def test_route_is_deterministic():
     b = moe.route(u16(x), u16(wr), u16(br), 4)
     for key in ("logits", "idx", "gates", "counts", "offsets", "perm"):
         assert torch.equal(a[key], b[key]), key
+
+
+def test_route_reused_and_garbage_workspace():
+    """A caller's workspace full of random bytes, or left by earlier calls of other shapes,
+    must not change any result."""
+    shapes = [(256, 2880, 32, 4), (100, 64, 8, 2), (256, 2880, 32, 4), (1024, 128, 64, 4), (17, 64, 5, 5)]
+    nbytes = max(moe.workspace_bytes(T, D, E, k, 64) for T, D, E, k in shapes)
+    g = torch.Generator().manual_seed(7)
+    ws = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, generator=g).cuda()
+    moe.set_workspace(ws)
+    try:
+        for i, (T, D, E, k) in enumerate(shapes):
+            run_and_compare(*rand_layer(100 + i, T, D, E), k, f"garbage/reused workspace #{i} T={T} E={E}")
+        # every arrival word set to what a launch leaves behind, except for the tag
+        ws.fill_(0xFF)
+        run_and_compare(*rand_layer(200, 256, 2880, 32), 4, "workspace of 0xFF bytes")
+    finally:
+        moe.set_workspace(None)
