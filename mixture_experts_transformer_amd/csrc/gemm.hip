@@ -910,10 +910,10 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
     }                                                                                            \
   } while (0)
   if constexpr (!MX) {
-    // Row blocks of 32 past the tile's rows hold only padding: when every wave's rows fit in
-    // its first block, the other blocks' copies (above) and matrix instructions are skipped.
-    // That loop accumulates into an array of its own, so the unused blocks are not carried
-    // through it.
+    // Row blocks of 32 past the tile's rows hold only padding: their copies (above) and
+    // matrix instructions are skipped.  When every wave's rows of a streaming tile fit in its
+    // first block, that loop accumulates into an array of its own, so the unused block is not
+    // carried through it.
     if (C::WAVES_M == 1 && FM == 2 && rows <= 32) {
       f32x16 acc1[1][FN];
 #pragma unroll
@@ -923,6 +923,13 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
       MOE_MAIN_LOOP(1, acc1);
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[0][j] = acc1[0][j];
+    } else if (FM == 4 && rows - wm * C::WTM <= 3 * 32) {
+      // the tile's last rows: this wave multiplies only the 32-row blocks that hold some
+      // (at least one), as the full tile's loop does in every other respect
+      const int wrows = rows - wm * C::WTM;
+      if (wrows > 64) MOE_MAIN_LOOP(FM >= 3 ? 3 : FM, acc);
+      else if (wrows > 32) MOE_MAIN_LOOP(FM >= 2 ? 2 : FM, acc);
+      else MOE_MAIN_LOOP(1, acc);
     } else {
       MOE_MAIN_LOOP(FM, acc);
     }
