@@ -306,6 +306,16 @@ static __device__ __forceinline__ void dma16(const void* base, uint32_t off, uin
                :: "s"(__builtin_amdgcn_readfirstlane(dst_wave)), "v"(off), "s"(uniform_ptr(base))
                : "memory", "m0");
 }
+// The same with the non-temporal hint: for data read once whose every byte of a line is
+// copied at once (line-aligned 128-byte code windows of the streaming tiles), so it does not
+// displace what the L2 reuses (measured: streaming MXFP4 mlp1 -2 %; with 64-byte windows,
+// whose line's other half is the next window, +8 %; the matrix-core tiles re-read weight
+// tiles through the L2, +0.7 %).
+static __device__ __forceinline__ void dma16_nt(const void* base, uint32_t off, uint32_t dst_wave) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+               :: "s"(__builtin_amdgcn_readfirstlane(dst_wave)), "v"(off), "s"(uniform_ptr(base))
+               : "memory", "m0");
+}
 // One dword per lane: lane L fills LDS bytes [dst + 4 L, +4) from base + off.
 static __device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t dst_wave) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
@@ -708,7 +718,10 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
     _Pragma("unroll") for (int j = 0; j < PW_C; ++j) {                                           \
       const int i_ = wave + j * NW;                                                              \
       if (FMT != 0 && i_ < NC) {                                                                 \
-        dma16(wbase + (size_t)(w) * CROW, coff[j], codes_l + ((w) % NSB) * CODE_SLOT + cdst[j]);   \
+        if (CROW == 128 && C::STREAM && walign)   /* whole lines, read once */                  \
+          dma16_nt(wbase + (size_t)(w) * CROW, coff[j], codes_l + ((w) % NSB) * CODE_SLOT + cdst[j]); \
+        else                                                                                     \
+          dma16(wbase + (size_t)(w) * CROW, coff[j], codes_l + ((w) % NSB) * CODE_SLOT + cdst[j]); \
         ++issued;                                                                                \
       }                                                                                          \
     }                                                                                            \
