@@ -307,10 +307,10 @@ static __device__ __forceinline__ void dma16(const void* base, uint32_t off, uin
                : "memory", "m0");
 }
 // The same with the non-temporal hint: for data read once whose every byte of a line is
-// copied at once (line-aligned 128-byte code windows of the streaming tiles), so it does not
-// displace what the L2 reuses (measured: streaming MXFP4 mlp1 -2 %; with 64-byte windows,
-// whose line's other half is the next window, +8 %; the matrix-core tiles re-read weight
-// tiles through the L2, +0.7 %).
+// copied at once (streaming tiles: line-aligned bf16 weight rows and 128-byte code windows),
+// so it does not displace what the L2 reuses (measured: streaming MXFP4 mlp1 -2 %; with
+// 64-byte windows, whose line's other half is the next window, +8 %; the matrix-core tiles
+// re-read weight tiles through the L2, +0.7 %).
 static __device__ __forceinline__ void dma16_nt(const void* base, uint32_t off, uint32_t dst_wave) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
                :: "s"(__builtin_amdgcn_readfirstlane(dst_wave)), "v"(off), "s"(uniform_ptr(base))
@@ -606,6 +606,11 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   // code-window shift of a weight row (in 32-byte stages), 0 unless the buffer is aligned
   // to the window; windows start below the row, so copies are relative to w_e - CROW
   const bool walign = WALIGN && (((uintptr_t)p.w) & (CROW - 1)) == 0;
+  // bf16 weight rows are whole 128-byte lines per stage when the buffer is line-aligned (K is
+  // a multiple of 64); streaming tiles read each once and copy them with the non-temporal
+  // hint, which keeps the A rows that every column tile re-reads in the L2 (measured at
+  // T = 256: mlp1 -8 %, mlp2 -9 %)
+  const bool wlines = FMT == 0 && (((uintptr_t)p.w) & 127) == 0;
   const size_t w_e_off = (size_t)(w_e - p.w);
   const uint8_t* const wbase = WALIGN ? w_e - CROW : w_e;
 #define MOE_CSHIFT(wr) (walign ? (int)(((w_e_off + (size_t)(wr) * (K / 2)) >> 5) & (SUPER - 1)) : 0)
@@ -706,7 +711,8 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
                                 : (i_ < A_CPC ? (const void*)p.a : (const void*)p.a_lo);          \
           dma16((const uint8_t*)ab_ + (size_t)(kt) * A_ROWB, goff[j], d_);                       \
         } else {                                                                                 \
-          dma16(w_e + (size_t)(kt) * ROWB, goff[j], d_);                                         \
+          if (C::STREAM && wlines) dma16_nt(w_e + (size_t)(kt) * ROWB, goff[j], d_);             \
+          else dma16(w_e + (size_t)(kt) * ROWB, goff[j], d_);                                    \
         }                                                                                        \
         ++issued;                                                                                \
       }                                                                                          \
