@@ -15,12 +15,12 @@ from _gpu import assert_close, note, upload
 pytestmark = pytest.mark.gpu
 
 
-def experts_vs_oracle(inp, label):
+def experts_vs_oracle(inp, label, weight_offset=0):
     cfg = inp.cfg
     note(f"experts {label}: T={cfg.T} D={cfg.D} E={cfg.E} k={cfg.k} F={cfg.F} fmt={cfg.fmt}")
     ref, r = oracle.moe_forward(inp.x, inp.wr, inp.br, inp.w1, inp.b1, inp.w2, inp.b2,
                                 k=cfg.k, F=cfg.F, fmt=cfg.fmt, return_routing=True)
-    d = upload(inp)
+    d = upload(inp, weight_offset)
     gates = torch.from_numpy(r["gates"].astype(np.float32)).cuda()
     offsets = torch.from_numpy(r["offsets"]).cuda()
     perm = torch.from_numpy(r["perm"]).cuda()
@@ -79,3 +79,18 @@ def test_experts_with_clamped_swiglu():
     nz = (inp.w2 & 0x7FFF) != 0
     inp.w2 = np.where(nz, inp.w2 - np.uint16(6 << 7), inp.w2).astype(np.uint16)
     experts_vs_oracle(inp, "clamped SwiGLU")
+
+
+# Weight buffers 16 or 48 bytes past a line boundary: the streaming tiles then copy code
+# windows from each row's own start (no line alignment) and bf16 rows without the
+# non-temporal hint, and the matrix-core tiles read unaligned windows too.
+@pytest.mark.parametrize("offset", [16, 48])
+@pytest.mark.parametrize("fmt,T,D,E,k,F", [
+    ("bf16", 64, 448, 8, 2, 320),      # streaming tiles
+    ("mxfp4", 64, 448, 8, 2, 320),     # streaming tiles, decode path
+    ("mxfp4", 700, 320, 2, 1, 448),    # matrix-core tiles, scaled engine
+])
+def test_experts_unaligned_weight_buffers(offset, fmt, T, D, E, k, F):
+    base = "C4" if fmt == "mxfp4" else "C2"
+    cfg = get_config(base, name=f"off{T}", T=T, D=D, E=E, k=k, F=F, seed=3000 + T + offset)
+    experts_vs_oracle(make_inputs(cfg), f"weights +{offset} B {fmt} T={T} D={D} E={E} k={k} F={F}", offset)
