@@ -316,13 +316,6 @@ static __device__ __forceinline__ void dma16_nt(const void* base, uint32_t off, 
                :: "s"(__builtin_amdgcn_readfirstlane(dst_wave)), "v"(off), "s"(uniform_ptr(base))
                : "memory", "m0");
 }
-// One dword per lane: lane L fills LDS bytes [dst + 4 L, +4) from base + off.
-static __device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t dst_wave) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
-               :: "s"(__builtin_amdgcn_readfirstlane(dst_wave)), "v"(off), "s"(uniform_ptr(base))
-               : "memory", "m0");
-}
-
 // s_waitcnt vmcnt(N) with the LDS/export counters left alone (gfx9 encoding).
 template <int N>
 static __device__ __forceinline__ void wait_vmcnt() {
