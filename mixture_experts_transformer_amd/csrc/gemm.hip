@@ -1018,6 +1018,10 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
       MX_LOOP(1, acc1);
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[0][j] = acc1[0][j];
+    } else if (MODE == 1 && FM == 4 && rows - wm * C::WTM <= 32) {
+      // a tile's last rows, at most one 32-row block in this wave's share (more variants, or
+      // this one in the three-piece mlp2 loop, would not fit the registers)
+      MX_LOOP(1, acc);
     } else {
       MX_LOOP(FM, acc);
     }
