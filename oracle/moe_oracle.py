@@ -15,6 +15,8 @@ Pages this follows (cited by title and section):
   expert compute, weighted combination).
 * GPT-OSS in Transformers blog (qian.cx), MXFP4 paragraph: E2M1 values (1 sign,
   2 exponent, 1 mantissa bit) with one scale per 32-element block.
+* torchtitan guide, section "StateDict adapter": the load-balancing expert bias
+  (one value per expert, zero when a checkpoint is loaded).
 
 Readings where the pages are silent (each listed with its reason in the design
 notes): softmax over the k selected logits; slots ordered by descending logit
@@ -22,7 +24,9 @@ with ties to the lower expert index; logits are the exact dot product plus bias
 rounded once to fp32; SwiGLU alpha = 1.702 and limit = 7.0; mlp1's output is
 [gate half | linear half]; the gate weight scales mlp2's output including its
 bias; E2M1 exponent bias 1 with the even element in the low nibble and E8M0
-scale 2**(s-127); within an expert, assignments keep ascending order.
+scale 2**(s-127); within an expert, assignments keep ascending order; the
+load-balancing expert bias, when given, is added (fp32) to the logits for the
+selection only, and the gates use the unbiased logits.
 
 No intermediate is rounded: h, y and out are exact up to float64 rounding.
 """
@@ -99,13 +103,18 @@ def router_logits(x: np.ndarray, wr: np.ndarray, br: np.ndarray) -> np.ndarray:
     return l64.astype(np.float32)
 
 
-def select_experts(logits: np.ndarray, k: int) -> np.ndarray:
+def select_experts(logits: np.ndarray, k: int, expert_bias: np.ndarray | None = None) -> np.ndarray:
     """Top-k routing ("gptoss" page, basic parameters: top-4 of 32 experts).
 
     Slot j of token t holds the expert with the j-th largest fp32 logit; equal logits go to
-    the lower expert index first.  Returns int32 [T, k].
+    the lower expert index first.  With a load-balancing expert bias (torchtitan guide,
+    "StateDict adapter": ``expert_bias_E``, one value per expert) the selection key is
+    the fp32 sum logit + bias (one rounding, nearest even) instead.  Returns int32 [T, k].
     """
-    order = np.argsort(-logits.astype(np.float64), axis=1, kind="stable")
+    key = np.asarray(logits, dtype=np.float32)
+    if expert_bias is not None:
+        key = key + np.asarray(expert_bias, dtype=np.float32)[None, :]
+    order = np.argsort(-key.astype(np.float64), axis=1, kind="stable")
     return order[:, :k].astype(np.int32)
 
 
@@ -156,12 +165,14 @@ def expert_forward(xr: np.ndarray, w1e: np.ndarray, b1e: np.ndarray,
     return h @ w2e.T + b2e[None, :]
 
 
-def moe_forward(x, wr, br, w1, b1, w2, b2, k: int, F: int, fmt: str, return_routing: bool = False):
+def moe_forward(x, wr, br, w1, b1, w2, b2, k: int, F: int, fmt: str, return_routing: bool = False,
+                expert_bias: np.ndarray | None = None):
     """The whole block ("gptoss" page, model run flow: route top-k, expert compute,
     weighted combination), in float64 with fp32 logits.
 
     Shapes (storage bits): x [T,D] u16, wr [E,D] u16, br [E] u16, b1 [E,2F] u16, b2 [E,D] u16;
     w1/w2 as in ``expert_weight`` with (rows, K) = (2F, D) and (D, F).
+    ``expert_bias`` (fp32 [E] or None) biases the selection only (``select_experts``).
     Returns out [T,D] float64 (and the routing when ``return_routing``).
     Experts are visited one at a time so the largest layer never holds more than one
     expert's float64 weights.
@@ -170,7 +181,7 @@ def moe_forward(x, wr, br, w1, b1, w2, b2, k: int, F: int, fmt: str, return_rout
     T, D = x.shape
     E = np.asarray(wr).shape[0]
     logits = router_logits(x, wr, br)
-    idx = select_experts(logits, k)
+    idx = select_experts(logits, k, expert_bias)
     g = gate_weights(logits, idx)
     counts, offsets, perm, rowpos = route_assignments(idx, E)
     x64 = bf16_to_f64(x)

@@ -64,13 +64,24 @@ def to_f32(v: float) -> float:
     return struct.unpack("<f", struct.pack("<f", v))[0]
 
 
+def biased_key(l, b):
+    """fp32 logit + fp32 bias rounded once to fp32, one element at a time through Python floats:
+    the float64 sum of two fp32 values rounded again to fp32 equals the correctly rounded fp32
+    sum (53 >= 2*24 + 2 makes the double rounding innocuous for addition)."""
+    l = np.asarray(l, dtype=np.float32)
+    b = np.asarray(b, dtype=np.float32)
+    return np.array([[to_f32(float(l[t, e]) + float(b[e])) for e in range(l.shape[1])]
+                     for t in range(l.shape[0])])
+
+
 def sigmoid_tanh(z):
     """Logistic function through tanh: another route than the oracle's 1/(1+exp(-z))."""
     return 0.5 * (1.0 + np.tanh(0.5 * np.asarray(z, dtype=np.float64)))
 
 
-def dense_reference(x, wr, br, w1, b1, w2, b2, k, F, fmt):
+def dense_reference(x, wr, br, w1, b1, w2, b2, k, F, fmt, ebias=None):
     """Every expert on every token, then a masked softmax mixture: no permutation, no grouping.
+    With ``ebias`` the mask follows the fp32 key logit + bias; the softmax stays on the logits.
 
     Catches: a transposed weight, a dropped bias, gate and linear halves swapped,
     the gate weight applied outside mlp2's bias, a wrong token<->row mapping in the
@@ -93,12 +104,13 @@ def dense_reference(x, wr, br, w1, b1, w2, b2, k, F, fmt):
     l = np.array([[to_f32(float(sum(Fraction(bf16_closed_form(int(a))) * Fraction(bf16_closed_form(int(b)))
                                      for a, b in zip(x[t], wr[e])) + Fraction(bf16_closed_form(int(br[e])))))
                    for e in range(E)] for t in range(T)])
+    sel = l if ebias is None else biased_key(l, ebias)
     mask = np.zeros((T, E), dtype=bool)
     for t in range(T):
         # k largest, ties to the lower index: repeatedly take the first maximum
         avail = list(range(E))
         for _ in range(k):
-            best = max(avail, key=lambda e: (l[t, e], -e))
+            best = max(avail, key=lambda e: (sel[t, e], -e))
             mask[t, best] = True
             avail.remove(best)
     masked = np.where(mask, l, -np.inf)
@@ -238,6 +250,51 @@ def test_topk_constructed_ties_and_duplicate_rows():
         assert order.index(2) < order.index(5)
 
 
+@pytest.mark.parametrize("E,k", [(4, 2), (6, 3), (8, 4), (5, 5)])
+def test_topk_expert_bias_brute_force(E, k):
+    """Load-balancing bias: every k-subset enumerated against the fp32 key logit + bias (ties
+    to the lower index), slots descending by that key, gates the softmax of the unbiased
+    logits over the chosen set (catches the bias left out of the selection, the bias
+    leaking into the gates, a key summed in float64)."""
+    g = np.random.default_rng(100 + E * 10 + k)
+    T = 64
+    logits = (g.integers(-3, 4, (T, E)) * 0.5).astype(np.float32)
+    bias = (g.integers(-2, 3, E) * 0.25).astype(np.float32)     # coarse: many exact key ties
+    idx = select_experts(logits, k, bias)
+    key = biased_key(logits, bias)
+    for t in range(T):
+        kf = lambda e: (float(key[t, e]), -e)
+        best = max(itertools.combinations(range(E), k), key=lambda S: sorted(kf(e) for e in S))
+        assert sorted(idx[t].tolist()) == sorted(best)
+        assert [kf(e) for e in idx[t]] == sorted([kf(e) for e in idx[t]], reverse=True)
+    w = gate_weights(logits, idx)
+    for t in range(T):
+        z = [math.exp(float(logits[t, e])) for e in idx[t]]
+        assert np.allclose(w[t], [v / sum(z) for v in z], rtol=1e-12, atol=0)
+
+
+def test_topk_expert_bias_special_cases():
+    """A zero bias is no bias; a bias that dominates forces its experts in key order while the
+    gates still come from the logits; the key is rounded to fp32 once, so a bias below half
+    an ulp of the logit leaves a tie that the lower index wins."""
+    g = np.random.default_rng(7)
+    l = g.standard_normal((50, 16)).astype(np.float32) * 2
+    for k in (1, 4, 16):
+        assert np.array_equal(select_experts(l, k, np.zeros(16, np.float32)), select_experts(l, k))
+    forced = np.zeros(16, np.float32)
+    forced[[11, 3, 7]] = [3e30, 2e30, 1e30]
+    idx = select_experts(l, 3, forced)
+    assert (idx == np.array([11, 3, 7])).all()
+    w = gate_weights(l, idx)
+    ex = np.exp(l[:, [11, 3, 7]].astype(np.float64))
+    assert np.allclose(w, ex / ex.sum(axis=1, keepdims=True), rtol=1e-12, atol=0)
+    one = np.ones((1, 2), np.float32)
+    half_ulp = np.float32(2.0 ** -24)                       # 1 + 2^-24 rounds (to even) to 1
+    assert select_experts(one, 1, np.array([0, half_ulp], np.float32))[0, 0] == 0
+    assert select_experts(one, 1, np.array([0, 2 * half_ulp], np.float32))[0, 0] == 1
+    assert select_experts(one, 1, np.array([half_ulp, 0], np.float32))[0, 0] == 0
+
+
 def test_gate_weights_properties():
     """Sum to 1, descending, k=1 gives 1, and equal to softmax-over-all renormalised on the
     chosen set (catches softmax over all experts without renormalisation, a wrong sign)."""
@@ -329,6 +386,21 @@ def test_block_equals_dense_masked_mixture(fmt, T, D, E, k, F, seed):
     # the SwiGLU clamps were exercised
     u_max = np.abs(ref).max()
     assert u_max > 0
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp4"])
+def test_block_with_expert_bias_equals_dense_masked_mixture(fmt):
+    """The biased block == the dense mixture masked by the biased key, softmax on the logits;
+    the bias is large enough to change the selection of most tokens."""
+    T, D, E, k, F = 10, 32, 6, 2, 32
+    layer = tiny_layer(11, T, D, E, k, F, fmt)
+    bias = np.random.default_rng(12).standard_normal(E).astype(np.float32) * 2
+    out, r = moe_forward(*layer, k=k, F=F, fmt=fmt, return_routing=True, expert_bias=bias)
+    ref, l, mask = dense_reference(*layer, k=k, F=F, fmt=fmt, ebias=bias)
+    _, _, mask0 = dense_reference(*layer, k=k, F=F, fmt=fmt)
+    assert (mask != mask0).any(axis=1).sum() >= T // 2
+    assert np.array_equal(np.sort(r["idx"], axis=1), np.array([np.flatnonzero(m) for m in mask]))
+    assert np.max(np.abs(out - ref)) <= 1e-12 * np.max(np.abs(ref))
 
 
 def test_block_single_expert_is_dense_swiglu_mlp():
