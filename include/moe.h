@@ -114,6 +114,23 @@ int moe_route(const void* x, const void* router_w, const void* router_b,
               float* logits, int32_t* topk_idx, float* gates,
               int32_t* counts, int32_t* offsets, int32_t* perm);
 
+/* The same with a load-balancing expert bias (torchtitan guide, section "StateDict
+ * adapter": a per-expert bias buffer kept beside the router during training, rebuilt as
+ * zeros when a checkpoint is loaded).  expert_bias is fp32 [E] in device memory.  It moves
+ * the selection only: step 2 ranks the fp32 sums l[t,e] + expert_bias[e] (one rounding,
+ * ties to the lower index; slot j holds the j-th largest sum), while step 3's gates remain
+ * the softmax of the selected unbiased logits, and logits (when not NULL) receives the
+ * unbiased l.  An all-zero bias gives exactly the unbiased calls' results.  expert_bias
+ * must be non-null and 16-byte aligned whenever T > 0. */
+int moe_forward_biased(const void* x, const void* router_w, const void* router_b, const float* expert_bias,
+                       const void* w1, const void* b1, const void* w2, const void* b2,
+                       int64_t T, int64_t D, int64_t E, int64_t k, int64_t F,
+                       int fmt, float* out);
+int moe_route_biased(const void* x, const void* router_w, const void* router_b, const float* expert_bias,
+                     int64_t T, int64_t D, int64_t E, int64_t k,
+                     float* logits, int32_t* topk_idx, float* gates,
+                     int32_t* counts, int32_t* offsets, int32_t* perm);
+
 /* Steps 5-8 on a given routing (expert stage), e.g. the routing of moe_route or of a
  * reference.  gates fp32 [T][k], offsets int32 [E+1] and perm int32 [T*k] must be
  * consistent (as moe_route produces them: perm[offsets[e] .. offsets[e+1]) lists the

@@ -186,9 +186,9 @@ int launch(int stage, const char* name, F&& fn) {
 }
 
 // router -> top-k -> grouping
-int run_route(uint8_t* ws, const Layout& L, const void* x, const void* router_w, const void* router_b, int64_t T,
-              int64_t D, int64_t E, int64_t k, float* logits, int32_t* idx, float* gates, int32_t* counts,
-              int32_t* offsets, int32_t* perm) {
+int run_route(uint8_t* ws, const Layout& L, const void* x, const void* router_w, const void* router_b,
+              const float* ebias, int64_t T, int64_t D, int64_t E, int64_t k, float* logits, int32_t* idx,
+              float* gates, int32_t* counts, int32_t* offsets, int32_t* perm) {
   double* partial = (double*)(ws + L.partial);
   const int ks = moe::router_ksplit(T, D);
   CHECK(launch(moe::ST_ROUTER, "router", [&](hipStream_t st) {
@@ -196,7 +196,8 @@ int run_route(uint8_t* ws, const Layout& L, const void* x, const void* router_w,
                                       partial, st);
   }));
   CHECK(launch(moe::ST_TOPK, "topk", [&](hipStream_t st) {
-    return moe::launch_topk(partial, ks, (const uint16_t*)router_b, (int)T, (int)E, (int)k, logits, idx, gates, st);
+    return moe::launch_topk(partial, ks, (const uint16_t*)router_b, ebias, (int)T, (int)E, (int)k, logits, idx,
+                            gates, st);
   }));
   return launch(moe::ST_PERMUTE, "permute", [&](hipStream_t st) {
     return moe::launch_permute(idx, (int)(T * k), (int)E, (int32_t*)(ws + L.hist), counts, offsets, perm, st);
@@ -237,19 +238,17 @@ int run_experts(const uint8_t* ws, const Layout& L, const void* x, const void* w
   return MOE_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int moe_forward(const void* x, const void* router_w, const void* router_b, const void* w1,
-                const void* b1, const void* w2, const void* b2, int64_t T, int64_t D, int64_t E,
-                int64_t k, int64_t F, int fmt, float* out) {
+// Whole block; ebias is the load-balancing bias when `biased` (then it must be valid).
+int forward_impl(const void* x, const void* router_w, const void* router_b, bool biased, const float* ebias,
+                 const void* w1, const void* b1, const void* w2, const void* b2, int64_t T, int64_t D, int64_t E,
+                 int64_t k, int64_t F, int fmt, float* out) {
   CHECK(check_shapes(T, D, E, k, F, true));
   if (fmt != MOE_FMT_BF16 && fmt != MOE_FMT_MXFP4) return fail(MOE_EFMT, "unknown weight format %d", fmt);
   if (T == 0) return ok();
   CHECK(check_ptr(x, "x"));
   CHECK(check_ptr(router_w, "router_w"));
   CHECK(check_ptr(router_b, "router_b"));
+  if (biased) CHECK(check_ptr(ebias, "expert_bias"));
   CHECK(check_ptr(w1, "w1"));
   CHECK(check_ptr(b1, "b1"));
   CHECK(check_ptr(w2, "w2"));
@@ -263,19 +262,20 @@ int moe_forward(const void* x, const void* router_w, const void* router_b, const
   int32_t* counts = (int32_t*)(ws + L.counts);
   int32_t* offsets = (int32_t*)(ws + L.offsets);
   int32_t* perm = (int32_t*)(ws + L.perm);
-  CHECK(run_route(ws, L, x, router_w, router_b, T, D, E, k, nullptr, idx, gates, counts, offsets, perm));
+  CHECK(run_route(ws, L, x, router_w, router_b, ebias, T, D, E, k, nullptr, idx, gates, counts, offsets, perm));
   CHECK(run_experts(ws, L, x, w1, b1, w2, b2, gates, offsets, perm, T, D, E, k, F, fmt, out));
   return ok();
 }
 
-int moe_route(const void* x, const void* router_w, const void* router_b, int64_t T, int64_t D, int64_t E,
-              int64_t k, float* logits, int32_t* topk_idx, float* gates, int32_t* counts, int32_t* offsets,
-              int32_t* perm) {
+int route_impl(const void* x, const void* router_w, const void* router_b, bool biased, const float* ebias,
+               int64_t T, int64_t D, int64_t E, int64_t k, float* logits, int32_t* topk_idx, float* gates,
+               int32_t* counts, int32_t* offsets, int32_t* perm) {
   CHECK(check_shapes(T, D, E, k, 64, false));
   if (T == 0) return ok();
   CHECK(check_ptr(x, "x"));
   CHECK(check_ptr(router_w, "router_w"));
   CHECK(check_ptr(router_b, "router_b"));
+  if (biased) CHECK(check_ptr(ebias, "expert_bias"));
   CHECK(check_ptr(logits, "logits", true));
   CHECK(check_ptr(topk_idx, "topk_idx"));
   CHECK(check_ptr(gates, "gates"));
@@ -285,8 +285,38 @@ int moe_route(const void* x, const void* router_w, const void* router_b, int64_t
   const Layout L = layout(T, D, E, k, 64, MOE_FMT_BF16, NEED_ROUTE);
   uint8_t* ws = nullptr;
   CHECK(ensure_workspace(L.total, &ws));
-  CHECK(run_route(ws, L, x, router_w, router_b, T, D, E, k, logits, topk_idx, gates, counts, offsets, perm));
+  CHECK(run_route(ws, L, x, router_w, router_b, ebias, T, D, E, k, logits, topk_idx, gates, counts, offsets,
+                  perm));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward(const void* x, const void* router_w, const void* router_b, const void* w1,
+                const void* b1, const void* w2, const void* b2, int64_t T, int64_t D, int64_t E,
+                int64_t k, int64_t F, int fmt, float* out) {
+  return forward_impl(x, router_w, router_b, false, nullptr, w1, b1, w2, b2, T, D, E, k, F, fmt, out);
+}
+
+int moe_forward_biased(const void* x, const void* router_w, const void* router_b, const float* expert_bias,
+                       const void* w1, const void* b1, const void* w2, const void* b2, int64_t T, int64_t D,
+                       int64_t E, int64_t k, int64_t F, int fmt, float* out) {
+  return forward_impl(x, router_w, router_b, true, expert_bias, w1, b1, w2, b2, T, D, E, k, F, fmt, out);
+}
+
+int moe_route(const void* x, const void* router_w, const void* router_b, int64_t T, int64_t D, int64_t E,
+              int64_t k, float* logits, int32_t* topk_idx, float* gates, int32_t* counts, int32_t* offsets,
+              int32_t* perm) {
+  return route_impl(x, router_w, router_b, false, nullptr, T, D, E, k, logits, topk_idx, gates, counts, offsets, perm);
+}
+
+int moe_route_biased(const void* x, const void* router_w, const void* router_b, const float* expert_bias,
+                     int64_t T, int64_t D, int64_t E, int64_t k, float* logits, int32_t* topk_idx, float* gates,
+                     int32_t* counts, int32_t* offsets, int32_t* perm) {
+  return route_impl(x, router_w, router_b, true, expert_bias, T, D, E, k, logits, topk_idx, gates, counts, offsets,
+                    perm);
 }
 
 int moe_experts(const void* x, const void* w1, const void* b1, const void* w2, const void* b2,

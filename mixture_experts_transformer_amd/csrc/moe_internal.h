@@ -24,9 +24,11 @@ int router_ksplit(int64_t T, int64_t D);
 // fp64 partial dot products partial[s][t][e] over the s-th K range.
 hipError_t launch_router_partial(const uint16_t* x, const uint16_t* wr, int T, int D, int E,
                                  int ksplit, double* partial, hipStream_t st);
-// Sum of partials + bias -> fp32 logits, top-k (ties to lower index), softmax gates.
-hipError_t launch_topk(const double* partial, int ksplit, const uint16_t* br, int T, int E, int k,
-                       float* logits, int32_t* idx, float* gates, hipStream_t st);
+// Sum of partials + bias -> fp32 logits, top-k (ties to lower index), softmax gates.  With
+// ebias (fp32 [E], or null) the selection key is the fp32 sum logit + ebias[e]; the gates
+// stay the softmax of the selected logits.
+hipError_t launch_topk(const double* partial, int ksplit, const uint16_t* br, const float* ebias, int T,
+                       int E, int k, float* logits, int32_t* idx, float* gates, hipStream_t st);
 // counts, exclusive offsets and the stable per-expert permutation of the A assignments.
 // hist: workspace of permute_groups(A) * E int32 (unused when permute_groups(A) == 1).
 int permute_groups(int64_t A);

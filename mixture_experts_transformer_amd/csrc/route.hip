@@ -202,10 +202,11 @@ static __device__ __forceinline__ float logit_from_partials(const double* __rest
   return (float)s;
 }
 
-// Top-k of token t by one wave: lane l holds the logits v[i] of experts l + 64 i where
-// live[i].  Writes idx and gates of the token; sel is k floats of this wave's LDS.
-static __device__ __forceinline__ void topk_wave(float (&v)[4], bool (&live)[4], int k, int t,
-                                                 int32_t* __restrict__ idx, float* __restrict__ gates,
+// Top-k of token t by one wave: lane l holds the selection keys v[i] and the logits lv[i]
+// of experts l + 64 i where live[i] (the two are equal without a load-balancing bias).
+// Writes idx and gates of the token; sel is k floats of this wave's LDS.
+static __device__ __forceinline__ void topk_wave(float (&v)[4], const float (&lv)[4], bool (&live)[4], int k,
+                                                 int t, int32_t* __restrict__ idx, float* __restrict__ gates,
                                                  float* sel) {
   constexpr int PER = 4;
   const int lane = threadIdx.x & 63;
@@ -237,21 +238,27 @@ static __device__ __forceinline__ void topk_wave(float (&v)[4], bool (&live)[4],
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) le = min(le, __shfl_xor(le, off));
       ce = le;
-      mv = __shfl(bv, 0);
     }
-    bv = mv;
     be = ce;
+    // the lane holding the winner retires it and records its logit for the gates
 #pragma unroll
     for (int i = 0; i < PER; ++i)
-      if (lane + 64 * i == be) live[i] = false;
-    if (lane == 0) {
-      idx[(size_t)t * k + j] = be;
-      sel[j] = bv;
-    }
+      if (lane + 64 * i == be) {
+        live[i] = false;
+        sel[j] = lv[i];
+      }
+    if (lane == 0) idx[(size_t)t * k + j] = be;
   }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  // gates: softmax over the k selected logits, in fp64
-  const double top = (double)sel[0];
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // gates: softmax over the k selected logits, in fp64, shifted by their largest (the
+  // first slot's unless a bias reordered the selection)
+  float tv = -INFINITY;
+  for (int j = lane; j < k; j += 64) tv = fmaxf(tv, sel[j]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) tv = fmaxf(tv, __shfl_xor(tv, off));
+  const double top = (double)tv;
   double part = 0.0;
   for (int j = lane; j < k; j += 64) part += exp((double)sel[j] - top);
 #pragma unroll
@@ -260,21 +267,21 @@ static __device__ __forceinline__ void topk_wave(float (&v)[4], bool (&live)[4],
     gates[(size_t)t * k + j] = (float)(exp((double)sel[j] - top) / part);
 }
 
-// Top-k and gates of NT tokens at once by one wave, lane e holding expert e's logit v[i]
-// (at most 64 experts; live[i] false for lanes past E and skipped tokens, t[i] < 0).  The
-// same selection as the top-k kernel's, by rank instead of k rounds of wave-wide argmax:
-// each lane counts the experts that beat it (larger logit, or equal and lower index;
-// -0 equals +0, NaN loses to every number), the experts of rank j < k are the token's j-th,
-// and lane j then holds the j-th for the gates.  key/sel_v/sel_e: NT x 64 entries of this
-// wave's LDS each.
+// Top-k and gates of NT tokens at once by one wave, lane e holding expert e's selection key
+// s[i] and logit v[i] (equal without a load-balancing bias; at most 64 experts; live[i]
+// false for lanes past E and skipped tokens, t[i] < 0).  The same selection as the top-k
+// kernel's, by rank instead of k rounds of wave-wide argmax: each lane counts the experts
+// that beat it (larger key, or equal and lower index; -0 equals +0, NaN loses to every
+// number), the experts of rank j < k are the token's j-th, and lane j then holds the j-th
+// for the gates.  key/sel_v/sel_e: NT x 64 entries of this wave's LDS each.
 static __device__ __forceinline__ uint32_t order_key(float v) {
   const uint32_t b = __float_as_uint(v + 0.0f);          // -0 -> +0
   if (v != v) return 0u;                                 // NaN: below everything
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);     // monotone in v, >= 0x007FFFFF
 }
 template <int NT>
-static __device__ __forceinline__ void topk_rank_lanes(const float (&v)[NT], const bool (&live)[NT], const int (&t)[NT],
-                                                       int E, int k, int32_t* __restrict__ idx,
+static __device__ __forceinline__ void topk_rank_lanes(const float (&s)[NT], const float (&v)[NT],
+                                                       const bool (&live)[NT], const int (&t)[NT], int E, int k, int32_t* __restrict__ idx,
                                                        float* __restrict__ gates, uint32_t (*key)[64],
                                                        float (*sel_v)[64], int (*sel_e)[64]) {
   const int lane = threadIdx.x & 63;
@@ -282,7 +289,7 @@ static __device__ __forceinline__ void topk_rank_lanes(const float (&v)[NT], con
   int rank[NT];
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
-    my[i] = live[i] ? order_key(v[i]) : 0u;
+    my[i] = live[i] ? order_key(s[i]) : 0u;
     key[i][lane] = my[i];                                // lanes past E: 0, never beat
     rank[i] = 0;
   }
@@ -307,14 +314,21 @@ static __device__ __forceinline__ void topk_rank_lanes(const float (&v)[NT], con
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // gates: softmax over the k selected logits, in fp64 (lane j < k holds the j-th)
+  // gates: softmax over the k selected logits, in fp64 (lane j < k holds the j-th), shifted
+  // by their largest (the first slot's unless a bias reordered the selection)
   double ex[NT], sum[NT];
   int my_e[NT];
+  float top[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) top[i] = lane < k ? sel_v[i][lane] : -INFINITY;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+    for (int i = 0; i < NT; ++i) top[i] = fmaxf(top[i], __shfl_xor(top[i], off));
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
-    const float top = sel_v[i][0];
     my_e[i] = lane < k ? sel_e[i][lane] : 0;
-    ex[i] = lane < k ? exp((double)sel_v[i][lane] - (double)top) : 0.0;
+    ex[i] = lane < k ? exp((double)sel_v[i][lane] - (double)top[i]) : 0.0;
     sum[i] = ex[i];
   }
 #pragma unroll
@@ -330,8 +344,9 @@ static __device__ __forceinline__ void topk_rank_lanes(const float (&v)[NT], con
 }
 
 __global__ __launch_bounds__(64 * TK_WAVES) void topk_kernel(
-    const double* __restrict__ partial, int ksplit, const uint16_t* __restrict__ br, int T, int E,
-    int k, float* __restrict__ logits, int32_t* __restrict__ idx, float* __restrict__ gates) {
+    const double* __restrict__ partial, int ksplit, const uint16_t* __restrict__ br,
+    const float* __restrict__ ebias, int T, int E, int k, float* __restrict__ logits,
+    int32_t* __restrict__ idx, float* __restrict__ gates) {
   __shared__ float sel_v[TK_WAVES][256];
   __shared__ uint32_t rk_key[TK_WAVES][1][64];
   __shared__ float rk_v[TK_WAVES][1][64];
@@ -349,10 +364,12 @@ __global__ __launch_bounds__(64 * TK_WAVES) void topk_kernel(
       v[0] = logit_from_partials(partial, ksplit, br, T, E, t, lane);
       if (logits) logits[(size_t)t * E + lane] = v[0];
     }
-    topk_rank_lanes<1>(v, live, tt, E, k, idx, gates, rk_key[wave], rk_v[wave], rk_e[wave]);
+    // the load-balancing bias moves the selection only (one fp32 rounding)
+    const float key[1] = {live[0] && ebias ? v[0] + ebias[lane] : v[0]};
+    topk_rank_lanes<1>(key, v, live, tt, E, k, idx, gates, rk_key[wave], rk_v[wave], rk_e[wave]);
     return;
   }
-  float v[4];
+  float v[4], key[4];
   bool live[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {    // E <= 256 = 4 * 64
@@ -363,14 +380,15 @@ __global__ __launch_bounds__(64 * TK_WAVES) void topk_kernel(
       v[i] = logit_from_partials(partial, ksplit, br, T, E, t, e);
       if (logits) logits[(size_t)t * E + e] = v[i];
     }
+    key[i] = live[i] && ebias ? v[i] + ebias[e] : v[i];
   }
-  topk_wave(v, live, k, t, idx, gates, sel_v[wave]);
+  topk_wave(key, v, live, k, t, idx, gates, sel_v[wave]);
 }
 
-hipError_t launch_topk(const double* partial, int ksplit, const uint16_t* br, int T, int E, int k,
-                       float* logits, int32_t* idx, float* gates, hipStream_t st) {
+hipError_t launch_topk(const double* partial, int ksplit, const uint16_t* br, const float* ebias, int T,
+                       int E, int k, float* logits, int32_t* idx, float* gates, hipStream_t st) {
   const dim3 grid((T + TK_WAVES - 1) / TK_WAVES);
-  hipLaunchKernelGGL(topk_kernel, grid, dim3(64 * TK_WAVES), 0, st, partial, ksplit, br, T, E, k,
+  hipLaunchKernelGGL(topk_kernel, grid, dim3(64 * TK_WAVES), 0, st, partial, ksplit, br, ebias, T, E, k,
                      logits, idx, gates);
   return hipGetLastError();
 }

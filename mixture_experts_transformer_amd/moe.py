@@ -25,6 +25,8 @@ _i64 = ctypes.c_int64
 _SIGNATURES = {
     "moe_forward": (ctypes.c_int, [_c_void_p] * 7 + [_i64] * 5 + [ctypes.c_int, _c_void_p]),
     "moe_route": (ctypes.c_int, [_c_void_p] * 3 + [_i64] * 4 + [_c_void_p] * 6),
+    "moe_forward_biased": (ctypes.c_int, [_c_void_p] * 8 + [_i64] * 5 + [ctypes.c_int, _c_void_p]),
+    "moe_route_biased": (ctypes.c_int, [_c_void_p] * 4 + [_i64] * 4 + [_c_void_p] * 6),
     "moe_experts": (ctypes.c_int, [_c_void_p] * 8 + [_i64] * 5 + [ctypes.c_int, _c_void_p]),
     "moe_set_stream": (ctypes.c_int, [_c_void_p]),
     "moe_workspace_bytes": (ctypes.c_size_t, [_i64] * 5 + [ctypes.c_int]),
@@ -105,30 +107,47 @@ def _check_weights(w1, w2, E, D, F, fmt):
         raise ValueError(f"unknown format {fmt!r}")
 
 
+def _check_bias(expert_bias, E):
+    if expert_bias is not None:
+        if expert_bias.dtype != torch.float32 or tuple(expert_bias.shape) != (E,):
+            raise ValueError(f"expert_bias must be float32 [{E}]")
+        _dev(expert_bias, "expert_bias", 4)
+
+
 def forward(x, router_w, router_b, w1, b1, w2, b2, k: int, fmt: str = "bf16",
-            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+            out: Optional[torch.Tensor] = None, expert_bias: Optional[torch.Tensor] = None) -> torch.Tensor:
     """The whole block: returns out fp32 [T, D].  bf16 tensors may be torch.bfloat16 or
-    2-byte integer views of the bits."""
+    2-byte integer views of the bits.  ``expert_bias`` (fp32 [E]) is the load-balancing
+    bias: it moves the top-k selection, not the gates."""
     T, D = x.shape
     E = router_w.shape[0]
     F = b1.shape[-1] // 2
     _dev(x, "x", 2), _dev(router_w, "router_w", 2), _dev(router_b, "router_b", 2)
     _dev(b1, "b1", 2), _dev(b2, "b2", 2)
     _check_weights(w1, w2, E, D, F, fmt)
+    _check_bias(expert_bias, E)
     if out is None:
         out = torch.empty((T, D), dtype=torch.float32, device=x.device)
     _dev(out, "out", 4)
     _bind_stream(x.device)
-    _check(lib().moe_forward(_ptr(x), _ptr(router_w), _ptr(router_b), _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2),
-                             T, D, E, k, F, FMT[fmt], _ptr(out)), "moe_forward")
+    if expert_bias is None:
+        _check(lib().moe_forward(_ptr(x), _ptr(router_w), _ptr(router_b), _ptr(w1), _ptr(b1), _ptr(w2),
+                                 _ptr(b2), T, D, E, k, F, FMT[fmt], _ptr(out)), "moe_forward")
+    else:
+        _check(lib().moe_forward_biased(_ptr(x), _ptr(router_w), _ptr(router_b), _ptr(expert_bias), _ptr(w1),
+                                        _ptr(b1), _ptr(w2), _ptr(b2), T, D, E, k, F, FMT[fmt], _ptr(out)),
+               "moe_forward_biased")
     return out
 
 
-def route(x, router_w, router_b, k: int, want_logits: bool = True) -> dict:
-    """Routing stage: logits (optional), top-k indices, gates, counts, offsets, permutation."""
+def route(x, router_w, router_b, k: int, want_logits: bool = True,
+          expert_bias: Optional[torch.Tensor] = None) -> dict:
+    """Routing stage: logits (optional), top-k indices, gates, counts, offsets, permutation.
+    ``expert_bias`` as in ``forward``."""
     T, D = x.shape
     E = router_w.shape[0]
     _dev(x, "x", 2), _dev(router_w, "router_w", 2), _dev(router_b, "router_b", 2)
+    _check_bias(expert_bias, E)
     dev = x.device
     r = {
         "logits": torch.empty((T, E), dtype=torch.float32, device=dev) if want_logits else None,
@@ -138,10 +157,14 @@ def route(x, router_w, router_b, k: int, want_logits: bool = True) -> dict:
         "offsets": torch.empty((E + 1,), dtype=torch.int32, device=dev),
         "perm": torch.empty((T * k,), dtype=torch.int32, device=dev),
     }
+    outs = (_ptr(r["logits"]), _ptr(r["idx"]), _ptr(r["gates"]), _ptr(r["counts"]), _ptr(r["offsets"]),
+            _ptr(r["perm"]))
     _bind_stream(dev)
-    _check(lib().moe_route(_ptr(x), _ptr(router_w), _ptr(router_b), T, D, E, k, _ptr(r["logits"]),
-                           _ptr(r["idx"]), _ptr(r["gates"]), _ptr(r["counts"]), _ptr(r["offsets"]),
-                           _ptr(r["perm"])), "moe_route")
+    if expert_bias is None:
+        _check(lib().moe_route(_ptr(x), _ptr(router_w), _ptr(router_b), T, D, E, k, *outs), "moe_route")
+    else:
+        _check(lib().moe_route_biased(_ptr(x), _ptr(router_w), _ptr(router_b), _ptr(expert_bias), T, D, E, k,
+                                      *outs), "moe_route_biased")
     return r
 
 

@@ -122,7 +122,9 @@ def gate_weights(logits: np.ndarray, idx: np.ndarray) -> np.ndarray:
     """Softmax over the k selected fp32 logits of each token, in float64 ("gptoss" page lists
     Softmax among the block's functions; the weighted combination uses these weights)."""
     sel = np.take_along_axis(logits.astype(np.float64), idx.astype(np.int64), axis=1)
-    z = np.exp(sel - sel[:, :1])
+    # shifted by the largest selected logit (softmax is shift-invariant); with a selection
+    # bias the first slot need not hold it
+    z = np.exp(sel - sel.max(axis=1, keepdims=True))
     return z / z.sum(axis=1, keepdims=True)
 
 

@@ -9,6 +9,7 @@ from .configs import CONFIGS, Config, get_config  # noqa: F401
 from .generate import (  # noqa: F401
     MoEInputs,
     f32_to_bf16_bits,
+    make_expert_bias,
     make_inputs,
     make_router_inputs,
     make_routing_inputs,

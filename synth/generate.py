@@ -236,3 +236,13 @@ def make_inputs(cfg, router_bias: Optional[np.ndarray] = None, **overrides) -> M
     elif overrides:
         raise TypeError("overrides need a config name")
     return _build(cfg, router_bias)
+
+
+def make_expert_bias(E: int, seed: int, steps_std: float = 300.0, step: float = 1e-3) -> np.ndarray:
+    """A load-balancing expert bias, fp32 [E]: whole numbers of update steps of size ``step``
+    (the torchtitan guide gives load_balance_coeff = 1e-3), the step counts drawn from
+    round(N(0, steps_std)), so the values are k * fp32(step) with many near zero and exact
+    repeats between experts."""
+    n = np.rint(np.random.default_rng(seed).normal(0.0, steps_std, E))
+    return (n.astype(np.float32) * np.float32(step)).astype(np.float32)
+

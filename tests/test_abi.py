@@ -92,6 +92,21 @@ def test_route_and_experts_validate():
     assert lib.moe_experts(P, P, P, P, P, P, P, P, 8, 64, 4, 2, 64, 7, P) == MOE_EFMT
 
 
+def test_biased_entry_points_validate_the_bias():
+    lib = moe.lib()
+    rb = lambda eb, T=8: lib.moe_route_biased(P, P, P, eb, T, 64, 4, 2, None, P, P, P, P, P)
+    fb = lambda eb, T=8: lib.moe_forward_biased(P, P, P, eb, P, P, P, P, T, 64, 4, 2, 64, 0, P)
+    for call in (rb, fb):
+        assert call(None) == MOE_EINVAL
+        assert "expert_bias" in lib.moe_last_error().decode()
+        assert call(BAD) == MOE_EALIGN
+        assert "expert_bias" in lib.moe_last_error().decode()
+        assert call(None, T=0) == MOE_OK
+    # the shape checks come first, as in the unbiased calls
+    assert lib.moe_route_biased(P, P, P, P, 8, 64, 4, 5, None, P, P, P, P, P) == MOE_EINVAL
+    assert lib.moe_forward_biased(P, P, P, P, P, P, P, P, 8, 64, 4, 2, 64, 7, P) == MOE_EFMT
+
+
 def test_workspace_bytes():
     wb = moe.lib().moe_workspace_bytes
     assert wb(0, 2880, 32, 4, 2880, 0) == 0

@@ -293,6 +293,11 @@ def test_topk_expert_bias_special_cases():
     assert select_experts(one, 1, np.array([0, half_ulp], np.float32))[0, 0] == 0
     assert select_experts(one, 1, np.array([0, 2 * half_ulp], np.float32))[0, 0] == 1
     assert select_experts(one, 1, np.array([half_ulp, 0], np.float32))[0, 0] == 0
+    # a bias that puts the smaller of two far-apart logits first: the gates stay finite
+    far = np.array([[-512.0, 512.0, -1024.0]], np.float32)
+    idx = select_experts(far, 2, np.array([4096, 1024, 0], np.float32))
+    assert idx.tolist() == [[0, 1]]
+    assert gate_weights(far, idx).tolist() == [[0.0, 1.0]]
 
 
 def test_gate_weights_properties():

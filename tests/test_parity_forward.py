@@ -12,8 +12,8 @@ import torch
 
 import mixture_experts_transformer_amd as moe
 import oracle
-from synth import get_config, make_inputs
-from _gpu import assert_close, note, upload
+from synth import get_config, make_expert_bias, make_inputs
+from _gpu import DEV, assert_close, note, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -106,3 +106,21 @@ def test_forward_power_of_two_scaling_is_exact(fmt):
     d2 = dict(d, w2=weights(w2s, fmt), b2=u16(b2s))
     out2 = forward(inp, d2)
     assert torch.equal(out2, 2 * out)
+
+
+@pytest.mark.parametrize("name", ["C1", "C2", "X1"])
+def test_forward_with_expert_bias(name):
+    """The biased entry point over the whole block: the bias moves the selection (most tokens
+    at this size) and the gates stay on the unbiased logits."""
+    inp = make_inputs(name)
+    cfg = inp.cfg
+    eb = make_expert_bias(cfg.E, cfg.T)
+    note(f"forward {name} biased: T={cfg.T} E={cfg.E} fmt={cfg.fmt}")
+    d = upload(inp)
+    out = moe.forward(d["x"], d["router_w"], d["router_b"], d["w1"], d["b1"], d["w2"], d["b2"], cfg.k, cfg.fmt,
+                      expert_bias=torch.from_numpy(eb).to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.moe_forward(inp.x, inp.wr, inp.br, inp.w1, inp.b1, inp.w2, inp.b2, k=cfg.k, F=cfg.F,
+                             fmt=cfg.fmt, expert_bias=eb)
+    assert_close(out.cpu().numpy(), ref, f"forward {name} biased")
+

@@ -6,19 +6,21 @@ import torch
 
 import mixture_experts_transformer_amd as moe
 import oracle
-from synth import f32_to_bf16_bits, get_config, make_routing_inputs
-from _gpu import GATE_ABS, note, u16
+from synth import f32_to_bf16_bits, get_config, make_expert_bias, make_routing_inputs
+from _gpu import DEV, GATE_ABS, note, u16
 
 pytestmark = pytest.mark.gpu
 
 
-def run_and_compare(x, wr, br, k, label):
+def run_and_compare(x, wr, br, k, label, ebias=None):
+    """ebias: the load-balancing expert bias (fp32 [E]) for the biased entry point, or None."""
     T, E = x.shape[0], wr.shape[0]
-    note(f"route {label}: T={T} D={x.shape[1]} E={E} k={k}")
-    r = moe.route(u16(x), u16(wr), u16(br), k)
+    note(f"route {label}: T={T} D={x.shape[1]} E={E} k={k}{' biased' if ebias is not None else ''}")
+    eb = None if ebias is None else torch.from_numpy(np.ascontiguousarray(ebias, dtype=np.float32)).to(DEV)
+    r = moe.route(u16(x), u16(wr), u16(br), k, expert_bias=eb)
     torch.cuda.synchronize()
     l_ref = oracle.router_logits(x, wr, br)
-    idx_ref = oracle.select_experts(l_ref, k)
+    idx_ref = oracle.select_experts(l_ref, k, ebias)
     g_ref = oracle.gate_weights(l_ref, idx_ref)
     counts_ref, offsets_ref, perm_ref, _ = oracle.route_assignments(idx_ref, E)
     logits = r["logits"].cpu().numpy()
@@ -32,7 +34,8 @@ def run_and_compare(x, wr, br, k, label):
     assert gerr <= GATE_ABS, f"{label}: gate error {gerr:.3e}"
     # smallest margin between the k-th and (k+1)-th logit: how close the case came to a tie
     if k < E and T:
-        srt = -np.sort(-l_ref.astype(np.float64), axis=1)
+        key = l_ref if ebias is None else l_ref + np.asarray(ebias, np.float32)[None, :]
+        srt = -np.sort(-key.astype(np.float64), axis=1)
         note(f"  min top-k margin {np.min(srt[:, k - 1] - srt[:, k]):.3e}, max gate err {gerr:.2e}")
     return r
 
@@ -119,3 +122,58 @@ def test_route_reused_and_garbage_workspace():
         run_and_compare(*rand_layer(200, 256, 2880, 32), 4, "workspace of 0xFF bytes")
     finally:
         moe.set_workspace(None)
+
+
+# ----------------------------------------------------------- load-balancing expert bias
+@pytest.mark.parametrize("T,D,E,k", [
+    # one expert per lane (E <= 64) and the wave-argmax path (E > 64)
+    (257, 64, 32, 4), (100, 128, 64, 8), (40, 64, 5, 5), (2049, 2880, 32, 4),
+    (129, 192, 100, 6), (64, 64, 256, 16), (1000, 128, 128, 4),
+])
+def test_route_expert_bias(T, D, E, k):
+    x, wr, br = rand_layer(T * 3 + E, T, D, E)
+    eb = make_expert_bias(E, T + E)
+    r = run_and_compare(x, wr, br, k, f"bias T={T} D={D} E={E} k={k}", ebias=eb)
+    if k < E:
+        # the bias moved the selection of some tokens
+        r0 = moe.route(u16(x), u16(wr), u16(br), k)
+        torch.cuda.synchronize()
+        moved = (np.sort(r["idx"].cpu().numpy(), 1) != np.sort(r0["idx"].cpu().numpy(), 1)).any(1).sum()
+        note(f"  {moved} of {T} tokens change experts under the bias")
+        assert moved > 0
+
+
+@pytest.mark.parametrize("E", [40, 80])
+def test_route_expert_bias_ties_and_reordering(E):
+    """Equal logits with a repeating bias: the best bias class wins, lower indices first,
+    gates 1/k; then far-apart logits that the bias puts in increasing order, so the first
+    slot's logit is the smallest and the gate softmax must shift by the largest."""
+    T, D, k = 70, 64, 5
+    x = np.zeros((T, D), dtype=np.uint16)
+    _, wr, _ = rand_layer(3, T, D, E)
+    br = np.full(E, f32_to_bf16_bits(np.float32([0.5]))[0], dtype=np.uint16)
+    eb = (np.arange(E) % 3).astype(np.float32) * np.float32(0.25)
+    r = run_and_compare(x, wr, br, k, f"biased ties E={E}", ebias=eb)
+    assert (r["idx"].cpu().numpy() == np.arange(2, 2 + 3 * k, 3)).all()
+    assert np.allclose(r["gates"].cpu().numpy(), 1.0 / k, atol=1e-7)
+    vals = np.full(E, -1024.0, np.float32)
+    vals[[3, 7, 11]] = [-512.0, 512.0, 0.0]
+    br2 = f32_to_bf16_bits(vals)
+    eb2 = np.zeros(E, np.float32)
+    eb2[[3, 7, 11]] = [8192.0, 1024.0, 4096.0]
+    r2 = run_and_compare(x, wr, br2, 3, f"biased reorder E={E}", ebias=eb2)
+    assert (r2["idx"].cpu().numpy() == np.array([3, 11, 7])).all()
+    g = r2["gates"].cpu().numpy()
+    assert np.isfinite(g).all() and (g[:, 2] == 1.0).all()
+
+
+def test_route_zero_expert_bias_is_bitwise_unbiased():
+    T, D, E, k = 3000, 128, 48, 4
+    x, wr, br = rand_layer(9, T, D, E)
+    note(f"route zero bias: T={T} E={E}")
+    a = moe.route(u16(x), u16(wr), u16(br), k)
+    b = moe.route(u16(x), u16(wr), u16(br), k, expert_bias=torch.zeros(E, dtype=torch.float32, device=DEV))
+    torch.cuda.synchronize()
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
+
