@@ -22,4 +22,5 @@ from .moe_oracle import (  # noqa: F401
     router_logits,
     select_experts,
     swiglu,
+    update_expert_bias,
 )

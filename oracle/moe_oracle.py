@@ -128,6 +128,21 @@ def gate_weights(logits: np.ndarray, idx: np.ndarray) -> np.ndarray:
     return z / z.sum(axis=1, keepdims=True)
 
 
+def update_expert_bias(expert_bias: np.ndarray, counts: np.ndarray, coeff: float) -> np.ndarray:
+    """One load-balancing step of the expert bias (torchtitan guide, "StateDict adapter": a
+    hook registered after the optimizer with load_balance_coeff = 1e-3; the rule is the
+    auxiliary-loss-free balancing of the DeepSeek-V3 report): an expert that received more
+    assignments than the mean lowers its bias by coeff, one that received fewer raises it
+    by coeff, one exactly at the mean keeps it.  fp32 in and out; the step is one fp32
+    rounding of bias + coeff.  Returns the new bias (the input is not modified)."""
+    b = np.asarray(expert_bias, dtype=np.float32)
+    c = np.asarray(counts, dtype=np.int64)
+    mean = c.sum() / c.size                    # exact sign below: |mean - c| >= 1/E when nonzero
+    step = np.sign(mean - c) * float(np.float32(coeff))
+    new = (b.astype(np.float64) + step).astype(np.float32)
+    return np.where(step == 0, b, new)
+
+
 def route_assignments(idx: np.ndarray, E: int):
     """Per-expert counts, int32 offsets and the token permutation (torchtitan guide, grouped GEMM:
     num_tokens_per_expert and its int32 cumulative sum delimit each expert's rows).

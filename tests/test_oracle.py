@@ -24,7 +24,7 @@ import pytest
 import oracle
 from oracle import (SWIGLU_ALPHA, SWIGLU_LIMIT, bf16_to_f64, e2m1_value, expert_weight,
                     gate_weights, moe_forward, mxfp4_decode, route_assignments, router_logits,
-                    select_experts, swiglu)
+                    select_experts, swiglu, update_expert_bias)
 from synth import f32_to_bf16_bits
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -298,6 +298,28 @@ def test_topk_expert_bias_special_cases():
     idx = select_experts(far, 2, np.array([4096, 1024, 0], np.float32))
     assert idx.tolist() == [[0, 1]]
     assert gate_weights(far, idx).tolist() == [[0.0, 1.0]]
+
+
+def test_expert_bias_update():
+    """A hand-worked step, the balanced case, and a brute-force sign against exact rationals
+    (catches a flipped sign, the mean taken over tokens instead of assignments per expert,
+    a step at the mean)."""
+    c = np.float32(1e-3)
+    got = update_expert_bias(np.zeros(4, np.float32), np.array([5, 1, 0, 2]), 1e-3)
+    assert got.tolist() == [float(-c), float(c), float(c), 0.0]          # mean 2
+    b = np.array([0.5, -0.25, 0.0], np.float32)
+    assert np.array_equal(update_expert_bias(b, np.array([7, 7, 7]), 1e-3), b)
+    assert update_expert_bias(np.array([-0.0], np.float32), np.array([3]), 1e-3).tobytes() == \
+        np.array([-0.0], np.float32).tobytes()                              # at the mean: untouched
+    g = np.random.default_rng(21)
+    for E in (2, 5, 32, 256):
+        cnt = g.integers(0, 50, E)
+        b0 = (g.standard_normal(E) * 0.3).astype(np.float32)
+        new = update_expert_bias(b0, cnt, 1e-3)
+        for e in range(E):
+            d = Fraction(int(cnt.sum()), E) - int(cnt[e])
+            want = b0[e] if d == 0 else np.float32(to_f32(float(b0[e]) + (1 if d > 0 else -1) * float(c)))
+            assert new[e].tobytes() == np.float32(want).tobytes()
 
 
 def test_gate_weights_properties():
