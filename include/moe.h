@@ -131,6 +131,16 @@ int moe_route_biased(const void* x, const void* router_w, const void* router_b, 
                      float* logits, int32_t* topk_idx, float* gates,
                      int32_t* counts, int32_t* offsets, int32_t* perm);
 
+/* One load-balancing step of the expert bias, in place (torchtitan guide, section
+ * "StateDict adapter": a hook run after each optimizer step with load_balance_coeff = 1e-3;
+ * the rule is the auxiliary-loss-free balancing of the DeepSeek-V3 report).  counts is int32
+ * [E] (e.g. moe_route's), expert_bias fp32 [E], both device memory; 1 <= E <= 256, coeff
+ * finite.  Expert e's bias becomes expert_bias[e] - coeff if counts[e] exceeds the mean
+ * count, + coeff if it falls below it, and is left untouched at the mean (one fp32
+ * rounding).  Asynchronous on the calling thread's stream; with profiling on, its time
+ * counts under stage 1 (top-k).  Needs no workspace. */
+int moe_update_expert_bias(const int32_t* counts, int64_t E, float coeff, float* expert_bias);
+
 /* Steps 5-8 on a given routing (expert stage), e.g. the routing of moe_route or of a
  * reference.  gates fp32 [T][k], offsets int32 [E+1] and perm int32 [T*k] must be
  * consistent (as moe_route produces them: perm[offsets[e] .. offsets[e+1]) lists the

@@ -17,6 +17,7 @@ from .moe import (  # noqa: F401
     release,
     route,
     set_workspace,
+    update_expert_bias,
     version,
     workspace_bytes,
 )

@@ -7,6 +7,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <cmath>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -317,6 +318,17 @@ int moe_route_biased(const void* x, const void* router_w, const void* router_b, 
                      int32_t* counts, int32_t* offsets, int32_t* perm) {
   return route_impl(x, router_w, router_b, true, expert_bias, T, D, E, k, logits, topk_idx, gates, counts, offsets,
                     perm);
+}
+
+int moe_update_expert_bias(const int32_t* counts, int64_t E, float coeff, float* expert_bias) {
+  if (E < 1 || E > 256) return fail(MOE_EINVAL, "E = %lld must lie in [1, 256]", (long long)E);
+  if (!std::isfinite(coeff)) return fail(MOE_EINVAL, "coeff is not finite");
+  CHECK(check_ptr(counts, "counts"));
+  CHECK(check_ptr(expert_bias, "expert_bias"));
+  CHECK(launch(moe::ST_TOPK, "bias_update", [&](hipStream_t st) {
+    return moe::launch_bias_update(counts, (int)E, coeff, expert_bias, st);
+  }));
+  return ok();
 }
 
 int moe_experts(const void* x, const void* w1, const void* b1, const void* w2, const void* b2,

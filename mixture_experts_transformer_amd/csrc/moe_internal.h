@@ -29,6 +29,8 @@ hipError_t launch_router_partial(const uint16_t* x, const uint16_t* wr, int T, i
 // stay the softmax of the selected logits.
 hipError_t launch_topk(const double* partial, int ksplit, const uint16_t* br, const float* ebias, int T,
                        int E, int k, float* logits, int32_t* idx, float* gates, hipStream_t st);
+// One load-balancing step of the expert bias (fp32 [E], in place) from the counts (int32 [E]).
+hipError_t launch_bias_update(const int32_t* counts, int E, float coeff, float* bias, hipStream_t st);
 // counts, exclusive offsets and the stable per-expert permutation of the A assignments.
 // hist: workspace of permute_groups(A) * E int32 (unused when permute_groups(A) == 1).
 int permute_groups(int64_t A);

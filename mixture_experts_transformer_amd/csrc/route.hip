@@ -393,6 +393,33 @@ hipError_t launch_topk(const double* partial, int ksplit, const uint16_t* br, co
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------- load-balancing bias update
+// One step of the per-expert selection bias from the step's assignment counts: an expert
+// above the mean count lowers its bias by coeff, one below raises it, one at the mean keeps
+// it.  The comparison is exact in integers (sum - E * counts[e] has the sign of
+// mean - counts[e]); the update is one fp32 addition.  One workgroup of 256 lanes, E <= 256.
+__global__ __launch_bounds__(256) void bias_update_kernel(const int32_t* __restrict__ counts, int E, float coeff,
+                                                          float* __restrict__ bias) {
+  __shared__ long long part[4];
+  const int e = threadIdx.x;
+  const long long c = e < E ? (long long)counts[e] : 0;
+  long long sum = c;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+  if ((e & 63) == 0) part[e >> 6] = sum;
+  __syncthreads();
+  const long long total = part[0] + part[1] + part[2] + part[3];
+  if (e < E) {
+    const long long d = total - (long long)E * c;
+    if (d != 0) bias[e] = bias[e] + (d > 0 ? coeff : -coeff);
+  }
+}
+
+hipError_t launch_bias_update(const int32_t* counts, int E, float coeff, float* bias, hipStream_t st) {
+  hipLaunchKernelGGL(bias_update_kernel, dim3(1), dim3(256), 0, st, counts, E, coeff, bias);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------------------ grouping
 constexpr int PM_WAVES = 16;
 constexpr int PM_CHUNK = 2048;        // assignments per workgroup when the grouping is split

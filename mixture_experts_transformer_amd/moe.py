@@ -27,6 +27,7 @@ _SIGNATURES = {
     "moe_route": (ctypes.c_int, [_c_void_p] * 3 + [_i64] * 4 + [_c_void_p] * 6),
     "moe_forward_biased": (ctypes.c_int, [_c_void_p] * 8 + [_i64] * 5 + [ctypes.c_int, _c_void_p]),
     "moe_route_biased": (ctypes.c_int, [_c_void_p] * 4 + [_i64] * 4 + [_c_void_p] * 6),
+    "moe_update_expert_bias": (ctypes.c_int, [_c_void_p, _i64, ctypes.c_float, _c_void_p]),
     "moe_experts": (ctypes.c_int, [_c_void_p] * 8 + [_i64] * 5 + [ctypes.c_int, _c_void_p]),
     "moe_set_stream": (ctypes.c_int, [_c_void_p]),
     "moe_workspace_bytes": (ctypes.c_size_t, [_i64] * 5 + [ctypes.c_int]),
@@ -166,6 +167,19 @@ def route(x, router_w, router_b, k: int, want_logits: bool = True,
         _check(lib().moe_route_biased(_ptr(x), _ptr(router_w), _ptr(router_b), _ptr(expert_bias), T, D, E, k,
                                       *outs), "moe_route_biased")
     return r
+
+
+def update_expert_bias(expert_bias: torch.Tensor, counts: torch.Tensor, coeff: float = 1e-3) -> torch.Tensor:
+    """One load-balancing step of ``expert_bias`` (fp32 [E], updated in place and returned) from
+    the per-expert assignment counts (int32 [E], e.g. ``route(...)["counts"]``)."""
+    E = expert_bias.numel()
+    _check_bias(expert_bias, E)
+    if tuple(counts.shape) != (E,) or counts.dtype != torch.int32:
+        raise ValueError(f"counts must be int32 [{E}]")
+    _dev(counts, "counts", 4)
+    _bind_stream(expert_bias.device)
+    _check(lib().moe_update_expert_bias(_ptr(counts), E, coeff, _ptr(expert_bias)), "moe_update_expert_bias")
+    return expert_bias
 
 
 def experts(x, w1, b1, w2, b2, gates, offsets, perm, k: int, fmt: str = "bf16",

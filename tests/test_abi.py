@@ -107,6 +107,18 @@ def test_biased_entry_points_validate_the_bias():
     assert lib.moe_forward_biased(P, P, P, P, P, P, P, P, 8, 64, 4, 2, 64, 7, P) == MOE_EFMT
 
 
+def test_bias_update_validates():
+    lib = moe.lib()
+    for E in (0, 257, -1):
+        assert lib.moe_update_expert_bias(P, E, 1e-3, P) == MOE_EINVAL
+    for coeff in (float("inf"), float("nan")):
+        assert lib.moe_update_expert_bias(P, 8, coeff, P) == MOE_EINVAL
+    assert lib.moe_update_expert_bias(None, 8, 1e-3, P) == MOE_EINVAL
+    assert lib.moe_update_expert_bias(P, 8, 1e-3, None) == MOE_EINVAL
+    assert lib.moe_update_expert_bias(P, 8, 1e-3, BAD) == MOE_EALIGN
+    assert "expert_bias" in lib.moe_last_error().decode()
+
+
 def test_workspace_bytes():
     wb = moe.lib().moe_workspace_bytes
     assert wb(0, 2880, 32, 4, 2880, 0) == 0

@@ -177,3 +177,51 @@ def test_route_zero_expert_bias_is_bitwise_unbiased():
     for key in a:
         assert torch.equal(a[key], b[key]), key
 
+
+@pytest.mark.parametrize("T,D,E,k", [(512, 256, 32, 4), (300, 128, 100, 6), (64, 64, 256, 8), (40, 64, 1, 1)])
+def test_expert_bias_balancing_loop(T, D, E, k):
+    """Biased routing and the load-balancing update in turn, six steps from a zero bias, on
+    the GPU and in the oracle: every step's routing bit for bit, the bias bit for bit.  The
+    step (0.05, not the training default 1e-3) is large enough to move tokens every step."""
+    x, wr, br = rand_layer(T + 5 * E, T, D, E)
+    note(f"balancing loop T={T} D={D} E={E} k={k}")
+    eb = torch.zeros(E, dtype=torch.float32, device=DEV)
+    eb_ref = np.zeros(E, np.float32)
+    l_ref = oracle.router_logits(x, wr, br)
+    spread = []
+    for step in range(6):
+        r = moe.route(u16(x), u16(wr), u16(br), k, want_logits=False, expert_bias=eb)
+        moe.update_expert_bias(eb, r["counts"], 0.05)
+        torch.cuda.synchronize()
+        idx_ref = oracle.select_experts(l_ref, k, eb_ref)
+        counts_ref = oracle.route_assignments(idx_ref, E)[0]
+        assert np.array_equal(r["idx"].cpu().numpy(), idx_ref), f"step {step}: top-k differs"
+        assert np.array_equal(r["counts"].cpu().numpy(), counts_ref), f"step {step}: counts differ"
+        eb_ref = oracle.update_expert_bias(eb_ref, counts_ref, 0.05)
+        assert eb.cpu().numpy().tobytes() == eb_ref.tobytes(), f"step {step}: bias differs"
+        spread.append(int(counts_ref.max() - counts_ref.min()))
+    note(f"  load spread per step: {spread}")
+    if E > k:
+        assert spread[-1] < spread[0]
+
+
+@pytest.mark.parametrize("E", [1, 7, 64, 200, 256])
+def test_expert_bias_update_direct(E):
+    """Counts with some experts exactly at the mean, a bias with -0 entries and a large
+    coefficient: the new bias bit for bit."""
+    g = np.random.default_rng(E)
+    counts = g.integers(0, 9, E).astype(np.int32)
+    counts[: E // 2] = 4
+    counts[E // 2:] = np.where(np.arange(E - E // 2) % 2 == 0, 2, 6)[: E - E // 2]
+    if (E - E // 2) % 2:
+        counts[-1] = 4                                  # keep the mean at exactly 4
+    bias = (g.standard_normal(E) * 0.1).astype(np.float32)
+    bias[::5] = -0.0
+    for coeff in (1e-3, 0.375, 3e-8):
+        note(f"bias update E={E} coeff={coeff}")
+        eb = torch.from_numpy(bias.copy()).to(DEV)
+        moe.update_expert_bias(eb, torch.from_numpy(counts).to(DEV), coeff)
+        torch.cuda.synchronize()
+        ref = oracle.update_expert_bias(bias, counts, coeff)
+        assert eb.cpu().numpy().tobytes() == ref.tobytes()
+
