@@ -13,11 +13,13 @@ from .moe_oracle import (  # noqa: F401
     SWIGLU_LIMIT,
     bf16_to_f64,
     e2m1_value,
+    e4m3_value,
     expert_forward,
     expert_weight,
     gate_weights,
     moe_forward,
     mxfp4_decode,
+    mxfp8_decode,
     route_assignments,
     router_logits,
     select_experts,

@@ -17,6 +17,9 @@ Pages this follows (cited by title and section):
   2 exponent, 1 mantissa bit) with one scale per 32-element block.
 * torchtitan guide, section "StateDict adapter": the load-balancing expert bias
   (one value per expert, zero when a checkpoint is loaded).
+* torchtitan guide, grouped GEMM section: the grouped product is an overridable seam
+  through which MXFP8 converters inject a scaled grouped GEMM (MXFP8 expert weights:
+  E4M3 elements with one E8M0 scale per 32, as in the OCP Microscaling spec v1.0).
 
 Readings where the pages are silent (each listed with its reason in the design
 notes): softmax over the k selected logits; slots ordered by descending logit
@@ -72,14 +75,48 @@ def mxfp4_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return (q * factor[:, :, None]).reshape(rows, 2 * half)
 
 
+def e4m3_value(code) -> np.ndarray:
+    """Value of an 8-bit E4M3 code (OCP Microscaling v1.0 FP8 E4M3: bit 7 sign, 4 exponent
+    bits with bias 7, 3 mantissa bits; exponent 0 is subnormal, (m / 8) 2^-6; exponent 15
+    with mantissa 7 is NaN and there is no infinity)."""
+    c = np.asarray(code, dtype=np.int64)
+    ex = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(ex == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(ex - 7.0))
+    mag = np.where((ex == 15) & ((c & 7) == 7), np.nan, mag)
+    return np.where(c & 128, -mag, mag)
+
+
+def mxfp8_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """MXFP8 block -> float64: codes uint8 [rows, K] (E4M3, one per element), scales uint8
+    [rows, K/32] (E8M0: 2**(s - 127), 255 = NaN) over 32 consecutive K elements each."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    rows, K = codes.shape
+    q = e4m3_value(codes).reshape(rows, K // 32, 32)
+    s = np.asarray(scales, dtype=np.int64)
+    factor = np.where(s == 255, np.nan, np.ldexp(1.0, s - 127))
+    return (q * factor[:, :, None]).reshape(rows, K)
+
+
 def expert_weight(w: np.ndarray, fmt: str, E: int, rows: int, K: int, e: int) -> np.ndarray:
     """Expert e's weight [rows, K] in float64 from the stored tensor.
 
     bf16: ``w`` is uint16 [E, rows, K].  mxfp4: ``w`` is one uint8 buffer holding the codes
-    [E][rows][K/2] followed by the scales [E][rows][K/32].
+    [E][rows][K/2] followed by the scales [E][rows][K/32].  mxfp8: one uint8 buffer holding
+    the codes [E][rows][K] followed by the scales [E][rows][K/32].
     """
     if fmt == "bf16":
         return bf16_to_f64(np.asarray(w).reshape(E, rows, K)[e])
+    if fmt == "mxfp8":
+        flat = np.asarray(w, dtype=np.uint8).reshape(-1)
+        ncode = rows * K
+        nscale = rows * (K // 32)
+        if flat.size != E * (ncode + nscale):
+            raise ValueError("mxfp8 buffer has the wrong size")
+        codes = flat[e * ncode:(e + 1) * ncode].reshape(rows, K)
+        base = E * ncode
+        scales = flat[base + e * nscale: base + (e + 1) * nscale].reshape(rows, K // 32)
+        return mxfp8_decode(codes, scales)
     if fmt == "mxfp4":
         flat = np.asarray(w, dtype=np.uint8).reshape(-1)
         ncode = rows * (K // 2)

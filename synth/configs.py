@@ -20,7 +20,7 @@ class Config:
     E: int
     k: int
     F: int
-    fmt: str                      # "bf16" or "mxfp4" (expert weights)
+    fmt: str                      # "bf16", "mxfp4" or "mxfp8" (expert weights)
     seed: int
     x_dist: str                   # "normal" (fp32 N(0,1)) or "rmsnorm" (N(0,1) then RMSNorm)
     router_bias: str              # "zero", "normal" (N(0,0.01)) or "zipf" (calibrated to a Zipf load)
@@ -28,7 +28,7 @@ class Config:
     n_empty: int = 0              # experts forced to receive no token (zipf configs only)
     weight_std: float = 0.02      # bf16 weights N(0, weight_std)
     bias_std: float = 0.01        # expert biases N(0, bias_std)
-    scale_exp: Tuple[int, int] = (-8, -4)  # MXFP4: E8M0 exponent drawn uniformly in this closed range
+    scale_exp: Tuple[int, int] = (-8, -4)  # MXFP4/MXFP8: E8M0 exponent drawn uniformly in this closed range
     note: str = ""
 
     @property
@@ -66,6 +66,14 @@ CONFIGS = {
     "X2": Config("X2", T=8192, D=2880, E=32, k=4, F=2880, fmt="mxfp4", seed=7,
                  x_dist="rmsnorm", router_bias="normal",
                  note="MXFP4 at prefill size"),
+    # MXFP8 expert weights (E4M3 codes uniform over the 254 finite ones, RMS ~100, so the
+    # scales sit lower: RMS 0.012 .. 0.1 per block, like the MXFP4 workloads' weights)
+    "Y1": Config("Y1", T=256, D=2880, E=32, k=4, F=2880, fmt="mxfp8", seed=8,
+                 x_dist="rmsnorm", router_bias="normal", scale_exp=(-13, -10),
+                 note="MXFP8 at the decode-like batch"),
+    "Y2": Config("Y2", T=8192, D=2880, E=32, k=4, F=2880, fmt="mxfp8", seed=9,
+                 x_dist="rmsnorm", router_bias="normal", scale_exp=(-13, -10),
+                 note="MXFP8 at prefill size"),
 }
 
 

@@ -9,6 +9,8 @@ draw can run on a thread pool and still give the same bytes on every machine.
 Encodings (these are the storage formats the library reads):
 
 * bf16: the upper 16 bits of the fp32 value after round-to-nearest-even.
+* MXFP8: one uint8 buffer holding the E4M3 codes ``[E][rows][K]`` followed by the
+  E8M0 scale bytes ``[E][rows][K/32]`` (OCP Microscaling spec v1.0).
 * MXFP4 (GPT-OSS-in-Transformers blog, section on MXFP4: 4-bit E2M1 values
   sharing one scale per 32-element block; OCP Microscaling spec v1.0 for the
   E8M0 scale byte): one uint8 buffer holding the codes ``[E][rows][K/2]``
@@ -76,6 +78,28 @@ def _mxfp4_buffer(ss: np.random.SeedSequence, E: int, rows: int, K: int, exp_lo:
     def fill(e):
         g = np.random.default_rng(children[e])
         codes[e] = g.integers(0, 256, ncode, dtype=np.uint8)          # two independent uniform nibbles
+        scales[e] = g.integers(127 + exp_lo, 127 + exp_hi + 1, nscale, dtype=np.uint8)
+
+    with ThreadPoolExecutor(_POOL_THREADS) as ex:
+        list(ex.map(fill, range(E)))
+    return buf
+
+
+def _mxfp8_buffer(ss: np.random.SeedSequence, E: int, rows: int, K: int, exp_lo: int, exp_hi: int) -> np.ndarray:
+    """MXFP8 weights [E][rows][K]: codes [E][rows][K] uniform over the 254 finite E4M3 codes
+    (0x7F and 0xFF, the NaN codes, are skipped), then E8M0 bytes 127+U{exp_lo..exp_hi}."""
+    assert K % 32 == 0
+    children = ss.spawn(E)
+    ncode = rows * K
+    nscale = rows * (K // 32)
+    buf = np.empty(E * (ncode + nscale), dtype=np.uint8)
+    codes = buf[: E * ncode].reshape(E, ncode)
+    scales = buf[E * ncode:].reshape(E, nscale)
+
+    def fill(e):
+        g = np.random.default_rng(children[e])
+        u = g.integers(0, 254, ncode, dtype=np.uint8)                   # index into the finite codes
+        codes[e] = u + (u >= 0x7F)
         scales[e] = g.integers(127 + exp_lo, 127 + exp_hi + 1, nscale, dtype=np.uint8)
 
     with ThreadPoolExecutor(_POOL_THREADS) as ex:
@@ -209,6 +233,10 @@ def _build(cfg: Config, router_bias: Optional[np.ndarray]) -> MoEInputs:
         lo, hi = cfg.scale_exp
         w1 = _mxfp4_buffer(st["w1"], E, 2 * F, D, lo, hi)
         w2 = _mxfp4_buffer(st["w2"], E, D, F, lo, hi)
+    elif cfg.fmt == "mxfp8":
+        lo, hi = cfg.scale_exp
+        w1 = _mxfp8_buffer(st["w1"], E, 2 * F, D, lo, hi)
+        w2 = _mxfp8_buffer(st["w2"], E, D, F, lo, hi)
     else:
         raise ValueError(cfg.fmt)
     b1 = f32_to_bf16_bits(np.random.default_rng(st["b1"]).standard_normal((E, 2 * F), dtype=np.float32)

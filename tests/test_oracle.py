@@ -22,9 +22,9 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle import (SWIGLU_ALPHA, SWIGLU_LIMIT, bf16_to_f64, e2m1_value, expert_weight,
-                    gate_weights, moe_forward, mxfp4_decode, route_assignments, router_logits,
-                    select_experts, swiglu, update_expert_bias)
+from oracle import (SWIGLU_ALPHA, SWIGLU_LIMIT, bf16_to_f64, e2m1_value, e4m3_value, expert_weight,
+                    gate_weights, moe_forward, mxfp4_decode, mxfp8_decode, route_assignments,
+                    router_logits, select_experts, swiglu, update_expert_bias)
 from synth import f32_to_bf16_bits
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -44,6 +44,26 @@ def e2m1_closed_form(code: int) -> float:
     s, e, m = code >> 3, (code >> 1) & 3, code & 1
     v = 0.5 * m if e == 0 else math.ldexp(1.0 + 0.5 * m, e - 1)
     return -v if s else v
+
+
+def e4m3_closed_form(code: int) -> float:
+    s, e, m = code >> 7, (code >> 3) & 15, code & 7
+    if e == 15 and m == 7:
+        return math.nan
+    v = math.ldexp(m / 8.0, -6) if e == 0 else math.ldexp(1.0 + m / 8.0, e - 7)
+    return -v if s else v
+
+
+def mxfp8_elementwise(buf: np.ndarray, E: int, rows: int, K: int, e: int) -> np.ndarray:
+    """Decode MXFP8 expert e element by element from byte addresses."""
+    out = np.empty((rows, K))
+    scale_base = E * rows * K + e * rows * (K // 32)
+    for r in range(rows):
+        for i in range(K):
+            code = int(buf[e * rows * K + r * K + i])
+            s = int(buf[scale_base + r * (K // 32) + i // 32])
+            out[r, i] = e4m3_closed_form(code) * math.ldexp(1.0, s - 127)
+    return out
 
 
 def mxfp4_elementwise(buf: np.ndarray, E: int, rows: int, K: int, e: int) -> np.ndarray:
@@ -129,6 +149,13 @@ def tiny_layer(seed, T, D, E, k, F, fmt, wstd=0.3, bstd=0.2, br_std=0.5):
     if fmt == "bf16":
         w1 = bf(E, 2 * F, D, std=wstd)
         w2 = bf(E, D, F, std=wstd)
+    elif fmt == "mxfp8":
+        def mx8(rows, K):
+            codes = g.integers(0, 256, E * rows * K, dtype=np.uint8)
+            codes[(codes & 0x7F) == 0x7F] -= 1               # no NaN codes
+            scales = g.integers(115, 119, E * rows * K // 32, dtype=np.uint8)
+            return np.concatenate([codes, scales])
+        w1, w2 = mx8(2 * F, D), mx8(D, F)
     else:
         def mx(rows, K):
             codes = g.integers(0, 256, E * rows * K // 2, dtype=np.uint8)
@@ -195,6 +222,49 @@ def test_mxfp4_expert_buffer_layout():
                               mxfp4_elementwise(buf, E, rows, K, e))
     with pytest.raises(ValueError):
         expert_weight(buf[:-1], "mxfp4", E, rows, K, 0)
+
+
+def test_e4m3_all_codes_match_library_and_closed_form():
+    """All 256 E4M3 codes against torch's float8_e4m3fn conversion (a library routine) and
+    the bit-field closed form: bias 7, subnormals (m/8) 2^-6, 0x7F/0xFF NaN, 448 the
+    largest finite (catches a wrong bias, a missing subnormal case, an infinity)."""
+    import torch
+    codes = np.arange(256)
+    got = e4m3_value(codes)
+    lib = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(lib))
+    fin = ~np.isnan(lib)
+    assert np.array_equal(got[fin], lib[fin]) and np.array_equal(np.signbit(got[fin]), np.signbit(lib[fin]))
+    for c in range(256):
+        cf = e4m3_closed_form(c)
+        assert (math.isnan(cf) and math.isnan(got[c])) or cf == got[c]
+    assert np.nanmax(got) == 448.0 and got[1] == 2.0 ** -9 and got[8] == 2.0 ** -6
+    assert np.isnan(got[[0x7F, 0xFF]]).all() and np.isfinite(got[[0x7E, 0xFE]]).all()
+
+
+def test_mxfp8_decode_codes_scales_and_layout():
+    """Every code under every finite E8M0 byte, element i using scale byte i // 32; expert,
+    row and block addressing element by element; 255 = NaN; a short buffer is refused."""
+    codes = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    vals = np.array([e4m3_closed_form(c) for c in range(256)])
+    for s in range(0, 255, 7):
+        sc = np.array([[s, s + 1, s, s + 1, s, s + 1, s, s + 1]], dtype=np.uint8) if s < 254 else \
+            np.full((1, 8), s, dtype=np.uint8)
+        got = mxfp8_decode(codes, sc)[0]
+        want = vals * np.array([math.ldexp(1.0, int(sc[0, i // 32]) - 127) for i in range(256)])
+        assert np.array_equal(np.isnan(got), np.isnan(want))
+        assert np.array_equal(got[~np.isnan(want)], want[~np.isnan(want)]), s
+    assert np.isnan(mxfp8_decode(codes, np.full((1, 8), 255, dtype=np.uint8))).all()
+    g = np.random.default_rng(8)
+    E, rows, K = 3, 5, 64
+    buf = np.concatenate([g.integers(0, 256, E * rows * K, dtype=np.uint8),
+                          g.integers(100, 150, E * rows * K // 32, dtype=np.uint8)])
+    for e in range(E):
+        a = expert_weight(buf, "mxfp8", E, rows, K, e)
+        b = mxfp8_elementwise(buf, E, rows, K, e)
+        assert np.array_equal(np.isnan(a), np.isnan(b)) and np.array_equal(a[~np.isnan(a)], b[~np.isnan(b)])
+    with pytest.raises(ValueError):
+        expert_weight(buf[:-1], "mxfp8", E, rows, K, 0)
 
 
 # ------------------------------------------------------------------------------- router and top-k
@@ -399,7 +469,7 @@ def test_swiglu_gate_is_gelu_like():
 
 
 # ------------------------------------------------------------------------------- whole block
-@pytest.mark.parametrize("fmt", ["bf16", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp4", "mxfp8"])
 @pytest.mark.parametrize("T,D,E,k,F,seed", [(12, 32, 4, 2, 32, 0), (9, 64, 6, 3, 64, 1), (5, 32, 3, 3, 32, 2)])
 def test_block_equals_dense_masked_mixture(fmt, T, D, E, k, F, seed):
     """Permuted/grouped oracle == every-expert-on-every-token masked softmax mixture (1e-12)."""
@@ -480,10 +550,10 @@ def test_block_k_equals_E_is_full_softmax_mixture():
     assert np.max(np.abs(out - ref)) <= 1e-12 * np.max(np.abs(ref))
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp4", "mxfp8"])
 def test_block_power_of_two_scaling_is_exact(fmt):
-    """W2, b2 scaled by 2 (bf16: exponent field + 1; mxfp4: every W2 scale byte + 1, b2 x 2)
-    scales out by exactly 2."""
+    """W2, b2 scaled by 2 (bf16: exponent field + 1; mxfp4/mxfp8: every W2 scale byte + 1,
+    b2 x 2) scales out by exactly 2."""
     T, D, E, k, F = 16, 64, 4, 2, 64
     x, wr, br, w1, b1, w2, b2 = tiny_layer(9, T, D, E, k, F, fmt)
     out = moe_forward(x, wr, br, w1, b1, w2, b2, k=k, F=F, fmt=fmt)
@@ -492,7 +562,7 @@ def test_block_power_of_two_scaling_is_exact(fmt):
         w2s = np.where((w2 & 0x7FFF) != 0, w2 + np.uint16(1 << 7), w2).astype(np.uint16)
     else:
         w2s = w2.copy()
-        n = E * D * (F // 2)
+        n = E * D * (F // 2 if fmt == "mxfp4" else F)
         w2s[n:] += 1
     out2 = moe_forward(x, wr, br, w1, b1, w2s, b2s, k=k, F=F, fmt=fmt)
     assert np.array_equal(out2, 2 * out)

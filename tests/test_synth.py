@@ -49,6 +49,21 @@ def test_bf16_weight_distribution():
     assert abs(b.std() - 0.01) < 1e-3
 
 
+def test_mxfp8_weight_buffer():
+    """Codes uniform over the 254 finite E4M3 codes (no NaN code), scale bytes in the
+    configured range, buffer = codes then scales."""
+    cfg = get_config("Y1", E=2, T=8, D=256, F=256)
+    inp = make_inputs(cfg)
+    n = 2 * (2 * 256) * 256
+    codes, scales = inp.w1[:n], inp.w1[n:]
+    assert inp.w1.size == n + n // 32
+    assert not np.isin(codes, [0x7F, 0xFF]).any()
+    hist = np.bincount(codes, minlength=256)
+    assert hist.max() < 2.0 * n / 254 and (hist > 0).sum() == 254
+    lo, hi = cfg.scale_exp
+    assert scales.min() == 127 + lo and scales.max() == 127 + hi
+
+
 def test_zipf_plan_targets():
     for name in ("C3", "C5"):
         cfg = CONFIGS[name]
