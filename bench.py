@@ -54,20 +54,23 @@ def algorithmic(cfg, counts):
     the router, x (bf16) and out (fp32).  Per kernel, mlp1 reads x (bf16; on the scaled
     engine its two fp8 pieces, the same two bytes per element) and writes h, mlp2 reads h
     and writes y (fp32); h is bf16 (bf16 weights), a bf16 pair (MXFP4, few rows) or three
-    fp8 pieces and one scale dword per 32 elements (scaled engine).
+    fp8 pieces and one scale dword per 32 elements (scaled engine); MXFP8 weights are one
+    byte per element plus one scale byte per 32 and carry h as a bf16 pair.
     """
     T, D, E, k, F = cfg.T, cfg.D, cfg.E, cfg.k, cfg.F
     A = T * k
     touched = int(np.count_nonzero(counts))
     if cfg.fmt == "bf16":
         w1_e, w2_e = 2 * F * D * 2, D * F * 2
+    elif cfg.fmt == "mxfp8":
+        w1_e, w2_e = 2 * F * (D + D // 32), D * (F + F // 32)
     else:
         w1_e, w2_e = 2 * F * (D // 2 + D // 32), D * (F // 2 + F // 32)
     b1_e, b2_e = 2 * F * 2, D * 2
     if mx_engine(cfg):
         hbytes = A * (3 * F + ((F // 32 + 7) // 8 * 8) * 4)
     else:
-        hbytes = A * F * 2 * (2 if cfg.fmt == "mxfp4" else 1)
+        hbytes = A * F * 2 * (1 if cfg.fmt == "bf16" else 2)
     flops = T * (2 * D * E + 6 * k * D * F)
     step_bytes = touched * (w1_e + b1_e + w2_e + b2_e) + E * D * 2 + E * 2 + T * D * 2 + T * D * 4
     mlp1_bytes = touched * (w1_e + b1_e) + T * D * 2 + hbytes
@@ -186,7 +189,7 @@ def bench_workload(name, steps, warmup, with_cpu):
     # issues each flop once per activation piece (x: 2, h: 3)
     mx = mx_engine(cfg)
     peak_t = FP8_PEAK_TFLOPS if mx else BF16_PEAK_TFLOPS
-    pieces = (2 if dom == "mlp1" else 3) if mx else (2 if (cfg.fmt == "mxfp4" and dom == "mlp2") else 1)
+    pieces = (2 if dom == "mlp1" else 3) if mx else (2 if (cfg.fmt != "bf16" and dom == "mlp2") else 1)
     hbm_bound = alg[dom]["flops"] * pieces / alg[dom]["bytes"] < peak_t * 1e12 / (HBM_PEAK_GBS * 1e9)
     if hbm_bound:
         achieved = alg[dom]["bytes"] / avg_s / 1e9
@@ -249,7 +252,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="C2", help="C2 (default), C3, C4, C5, X1, X2")
+    ap.add_argument("--workload", default="C2", help="C2 (default), C3, C4, C5, X1, X2, Y1, Y2")
     ap.add_argument("--all", action="store_true", help="one line per target workload: C2 C3 X1 X2")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",

@@ -37,6 +37,16 @@
  * [2, 252] so every decoded weight is an exact normal bf16 value; other bytes
  * are outside the contract (not checked on the device).
  *
+ * MXFP8 weights (fmt 2: E4M3 elements, 1 sign / 4 exponent bits with bias 7 / 3 mantissa
+ * bits, no infinity, 0x7F and 0xFF NaN, one E8M0 scale per 32 elements, OCP Microscaling
+ * spec v1.0; the torchtitan guide's grouped GEMM section names MXFP8 converters as the
+ * users of its scaled grouped-GEMM seam): one uint8 buffer per matrix, the codes
+ * [E][rows][K] (one byte per element) then the scale bytes [E][rows][K/32].  Scale bytes
+ * must lie in [10, 246] and codes must not be NaN, so every decoded weight is an exact
+ * normal bf16 (not checked on the device).  Decoded to bf16 and multiplied on the bf16
+ * matrix instructions at every token count, h carried into mlp2 as a bf16 pair as for
+ * MXFP4 at small token counts.
+ *
  * Numerics: every product is accumulated in fp32 on the matrix cores except the
  * router (fp64).  The bf16 path rounds h to bf16 once.  With MXFP4 weights, small
  * token counts carry h as a bf16 pair (hi + lo, 16 significant bits) into mlp2;
@@ -77,6 +87,7 @@ extern "C" {
 
 #define MOE_FMT_BF16 0
 #define MOE_FMT_MXFP4 1
+#define MOE_FMT_MXFP8 2
 
 /* GPT-OSS SwiGLU constants: the torchtitan guide names alpha and limit but prints no
  * value; these are the published GPT-OSS defaults (alpha = 1.702 is the sigmoid
@@ -94,9 +105,11 @@ extern "C" {
 /* Whole block (steps 1-8).
  *   x        bf16 [T][D]
  *   router_w bf16 [E][D]             router_b bf16 [E]
- *   w1       fmt 0: bf16 [E][2F][D]; fmt 1: MXFP4 buffer (codes [E][2F][D/2], scales [E][2F][D/32])
+ *   w1       fmt 0: bf16 [E][2F][D]; fmt 1: MXFP4 buffer (codes [E][2F][D/2], scales [E][2F][D/32]);
+ *            fmt 2: MXFP8 buffer (codes [E][2F][D], scales [E][2F][D/32])
  *   b1       bf16 [E][2F]            ([0,F) gate half, [F,2F) linear half)
- *   w2       fmt 0: bf16 [E][D][F];  fmt 1: MXFP4 buffer (codes [E][D][F/2],  scales [E][D][F/32])
+ *   w2       fmt 0: bf16 [E][D][F];  fmt 1: MXFP4 buffer (codes [E][D][F/2],  scales [E][D][F/32]);
+ *            fmt 2: MXFP8 buffer (codes [E][D][F], scales [E][D][F/32])
  *   b2       bf16 [E][D]
  *   out      fp32 [T][D] (written)
  */

@@ -12,6 +12,7 @@ from .moe import (  # noqa: F401
     forward,
     lib,
     mxfp4_bytes,
+    mxfp8_bytes,
     profile_enable,
     profile_read,
     release,

@@ -126,6 +126,9 @@ struct Tile {
 #ifndef MOE_S_SUPER2
 #define MOE_S_SUPER2 2              // mlp2 (64-byte code segments, but three workgroups per CU)
 #endif
+#ifndef MOE_S_SUPER8
+#define MOE_S_SUPER8 2              // MXFP8 (64 code bytes per row and stage: 128-byte windows)
+#endif
 #ifndef MOE_S_WPE
 #define MOE_S_WPE 1                 // streaming tiles: waves per SIMD the registers must allow
 #endif
@@ -148,7 +151,7 @@ template <int MODE, int FMT> using SmallTile =
     Tile<MOE_S_BM, (MODE == 1 ? (FMT == 0 ? MOE_S_BN1 : MOE_S_BN14) : (FMT == 0 ? MOE_S_BN2 : MOE_S_BN24)),
          MOE_S_WM, (MODE == 1 ? (FMT == 0 ? MOE_S_WN : MOE_S_WN4) : (FMT == 0 ? MOE_S_WN2 : MOE_S_WN24)),
          (FMT == 0 ? (MODE == 1 ? MOE_S_NS : MOE_S_NS2) : (MODE == 1 ? MOE_S_NS4 : MOE_S_NSH)), 64,
-         MOE_S_STREAM != 0, (FMT == 1 ? (MODE == 1 ? MOE_S_SUPER1 : MOE_S_SUPER2) : 4),
+         MOE_S_STREAM != 0, (FMT == 1 ? (MODE == 1 ? MOE_S_SUPER1 : MOE_S_SUPER2) : (FMT == 3 ? MOE_S_SUPER8 : 4)),
          (FMT == 0 ? MOE_S_WPE : MOE_S_WPE4)>;
 template <int MODE, int FMT> struct LargeTileSel {   // bf16 weights
   using type = Tile<MOE_L_BM, MOE_L_BN, MOE_L_WM, MOE_L_WN, MOE_L_NS, MOE_L_BK, false>;
@@ -179,6 +182,14 @@ template <> struct LargeTileSel<1, 2> {
 };
 template <> struct LargeTileSel<2, 2> {
   using type = Tile<256, 256, MOE_LX2_WM, MOE_LX2_WN, MOE_LX_NS, 64, false, MOE_LX2_SUPER>;
+};
+// MXFP8 decoded to bf16 on matrix-core tiles (128-byte code windows: 64 KB of codes per
+// 256 weight rows); mlp2's h arrives as a bf16 pair, so its tile takes 128 rows to fit
+template <> struct LargeTileSel<1, 3> {
+  using type = Tile<256, 256, MOE_L_WM, MOE_L_WN, 2, 64, false, 2>;
+};
+template <> struct LargeTileSel<2, 3> {
+  using type = Tile<128, 256, MOE_L_WM, MOE_L_WN, 2, 64, false, 2>;
 };
 template <int MODE, int FMT> using LargeTile = typename LargeTileSel<MODE, FMT>::type;
 
@@ -344,6 +355,17 @@ static __device__ __forceinline__ int code_swz(int r) {
 
 // Decode 8 MXFP4 codes (one dword: element 2i in the low nibble of byte i) times the
 // power-of-two scale into one bf16x8 matrix-core operand.
+// Decode 8 MXFP8 codes (E4M3, element i in byte i of c0 c1) times a power-of-two scale:
+// E4M3 has 3 mantissa bits, so with the scale bytes of the contract every value is an
+// exact normal bf16.
+static __device__ __forceinline__ bf16x8 decode_fp8x8(uint32_t c0, uint32_t c1, float scale) {
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c0, scale, false);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c0, scale, true);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1, scale, false);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1, scale, true);
+  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
 static __device__ __forceinline__ bf16x8 decode_fp4x8(uint32_t codes, float scale) {
   const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0);
   const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1);
@@ -437,9 +459,11 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, CPR = C::CPR, NS = C::NS, NW = C::NW;
   constexpr int FM = C::FM, FN = C::FN;
   constexpr bool MX = FMT == 2;                             // scaled MFMA on fp8 pieces
+  constexpr bool DEC = FMT == 1 || FMT == 3;                // codes decoded to bf16 (MXFP4, MXFP8)
+  constexpr int CBS = FMT == 3 ? 64 : 32;                   // code bytes per row and stage
   constexpr int KS = MX ? 1 : BK / 16;                      // MFMA K steps per stage
   // A parts: bf16 (1), h hi + lo (2), or fp8 pieces (x: 2, h: 3)
-  constexpr int AP = MX ? (MODE == 1 ? 2 : 3) : ((MODE == 2 && FMT == 1) ? 2 : 1);
+  constexpr int AP = MX ? (MODE == 1 ? 2 : 3) : ((MODE == 2 && DEC) ? 2 : 1);
   constexpr int ROWB = CPR * 16;                            // bytes per bf16 row segment
   constexpr int APL = MX ? 1 : AP;                          // A parts in LDS (pieces share rows)
   constexpr int A_CPR = MX ? 4 * AP : CPR;                  // 16-byte chunks per A row per stage
@@ -453,7 +477,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   // a slot is refilled NS - 1 steps ahead of its first use, after the barrier that ends
   // the last use of its previous super-stage
   static_assert(FMT == 0 || SUPER * (NSB - 1) > NS - 2, "code ring too short for the stage ring");
-  constexpr int CROW = 32 * SUPER;                          // code bytes per row per super-stage
+  constexpr int CROW = CBS * SUPER;                         // code bytes per row per super-stage
   constexpr int CCH = CROW / 16;                            // 16-byte code chunks per row
   constexpr int B_STAGE_BYTES = (FMT == 0) ? BN * ROWB : 0;  // bf16 B tile (MXFP4: none)
   constexpr int STAGE = APL * A_BYTES + B_STAGE_BYTES;
@@ -505,7 +529,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   constexpr int EP_P = C::WTN / 2;
   // (scaled-MFMA engine, mlp1: fp32 [32][32 pairs], one MXFP8 block of h per row)
   constexpr int EP_S = (MODE == 1) ? (MX ? 4 * EP_P + 16 : 2 * EP_P + 8) : 4 * C::WTN + 32;
-  constexpr int EP_REG = 32 * EP_S * ((MODE == 1 && FMT == 1) ? 2 : 1);
+  constexpr int EP_REG = 32 * EP_S * ((MODE == 1 && DEC) ? 2 : 1);
   static_assert(!(MX && MODE == 1) || EP_P % 32 == 0, "whole 32-element blocks of h per wave and row");
   static_assert(NW * EP_REG <= SMEM, "epilogue slices exceed the operand ring");
   constexpr int ROWTAB = (MODE == 2) ? BM * 8 : 0;          // mlp2: assignment and gate per tile row
@@ -593,8 +617,8 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   if (FMT == 0) {
     w_e = p.w + (size_t)e * p.N * K * 2;
   } else {
-    w_e = p.w + (size_t)e * p.N * (K / 2);
-    s_e_off = (size_t)p.E * p.N * (K / 2) + (size_t)e * p.N * (K / 32);
+    w_e = p.w + (size_t)e * p.N * (K / 64 * CBS);
+    s_e_off = (size_t)p.E * p.N * (K / 64 * CBS) + (size_t)e * p.N * (K / 32);
   }
   // scale records: offsets relative to 32 bytes before the expert's scales (a record can
   // start up to 24 bytes before a row's first scale byte)
@@ -610,7 +634,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   const bool wlines = FMT == 0 && (((uintptr_t)p.w) & 127) == 0;
   const size_t w_e_off = (size_t)(w_e - p.w);
   const uint8_t* const wbase = WALIGN ? w_e - CROW : w_e;
-#define MOE_CSHIFT(wr) (walign ? (int)(((w_e_off + (size_t)(wr) * (K / 2)) >> 5) & (SUPER - 1)) : 0)
+#define MOE_CSHIFT(wr) (walign ? (int)(((w_e_off + (size_t)(wr) * (K / 64 * CBS)) / CBS) & (SUPER - 1)) : 0)
   // start of super-stage w's 16-byte scale record of a row whose scales are [rs, re)
   // (offsets relative to the expert's scales): the super-stage's bytes end at
   // rs + 2 SUPER (w + 1), the record at the 4-aligned address at or past the earlier end
@@ -672,7 +696,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
       const int r = i * (1024 / CROW) + lane / CCH;
       const int c = (lane % CCH) ^ code_swz<CCH>(r);
       const int wr = MOE_WROW(r);
-      coff[j] = (uint32_t)((size_t)wr * (K / 2) + (WALIGN ? CROW - 32 * MOE_CSHIFT(wr) : 0) + c * 16);
+      coff[j] = (uint32_t)((size_t)wr * (K / 64 * CBS) + (WALIGN ? CROW - CBS * MOE_CSHIFT(wr) : 0) + c * 16);
       cdst[j] = i * 1024;
     } else if (i < NC + NASC) {
       constexpr int CPS = ASL_ROW / 16;                    // chunks per row
@@ -812,11 +836,12 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   // this lane's scale byte of fragment j for stage kt (K block kg) in the scale ring
 #define MOE_SCALE_AT(kt_, j_)                                                                    \
   ((uint32_t)wsc_lds[(((kt_) / SUPER) % NSB) * SCW_SLOT + sidx[j_] + 2 * ((kt_) % SUPER)])
-  // this lane's 32 codes of fragment j for stage kt in the code ring
-#define MOE_CODES_AT(kt_, j_)                                                                    \
+  // this lane's 32 codes of fragment j for stage kt in the code ring: 16-byte chunk h_ of
+  // them (MXFP4: one chunk; MXFP8: two)
+#define MOE_CODES_AT(kt_, j_, h_)                                                                \
   ([&]() {                                                                                       \
     const int t_ = (kt_) + csh[j_];                                                              \
-    const int c_ = 2 * (t_ % SUPER) + kg;                                                        \
+    const int c_ = (CBS / 16) * (t_ % SUPER) + (CBS / 32) * kg + (h_);                           \
     return codes_lds + ((t_ / SUPER) % NSB) * CODE_SLOT + brow[j_] * CROW +                      \
            ((c_ ^ code_swz<CCH>(brow[j_])) << 4);                                               \
   }())
@@ -832,12 +857,15 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   bf16x8 fa[2][AP][FM];
   bf16x8 fb[2][FN];
   u32x4 q4[FN];                             // MXFP4: this lane's 32 codes per fragment
+  u32x4 q8[FN];                             // MXFP8: the second 16 of them (q4 the first)
   float scl[FN];
 #define MOE_LOAD_FRAGS(buf, ks_, sa_, sb_, FA)                                                   \
   do {                                                                                           \
     const int cc_ = kg * KS + (ks_);        /* chunk (8 K elements) this lane feeds */           \
     _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                             \
       if (FMT == 0) fb[buf][j] = *(const bf16x8*)((sb_) + swz<CPR>(brow[j], cc_));                \
+      else if (FMT == 3) fb[buf][j] = (ks_) < 2 ? decode_fp8x8(q4[j][2 * (ks_)], q4[j][2 * (ks_) + 1], scl[j]) \
+                                    : decode_fp8x8(q8[j][2 * (ks_) - 4], q8[j][2 * (ks_) - 3], scl[j]); \
       else fb[buf][j] = decode_fp4x8(q4[j][ks_], scl[j]);                                        \
     }                                                                                            \
     _Pragma("unroll") for (int pa = 0; pa < AP; ++pa)                                            \
@@ -875,11 +903,12 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
                                                                                                  \
       const uint8_t* sa = smem + slot * STAGE;                                                   \
       const uint8_t* sb = sa + AP * A_BYTES;                                                     \
-      if (FMT == 1) {                                                                            \
+      if (DEC) {                                                                                 \
         if (UNR == 1 || u_ == 0) MOE_SCALE_LAST(kt);                                             \
   _Pragma("unroll")                                                                              \
         for (int j = 0; j < FN; ++j) {                                                           \
-          q4[j] = *(const u32x4*)MOE_CODES_AT(kt, j);                                            \
+          q4[j] = *(const u32x4*)MOE_CODES_AT(kt, j, 0);                                         \
+          if (FMT == 3) q8[j] = *(const u32x4*)MOE_CODES_AT(kt, j, 1);                           \
           const uint32_t sc = MOE_SCALE_AT(kt, j);                                               \
           scl[j] = __uint_as_float(sc << 23);                                                    \
         }                                                                                        \
@@ -976,7 +1005,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
       uint32_t sbv[FN];                                                                          \
       if (UNR == 1 || u_ == 0) MOE_SCALE_LAST(kt);                                               \
       _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                           \
-        const i32x4 q = *(const i32x4*)MOE_CODES_AT(kt, j);                                      \
+        const i32x4 q = *(const i32x4*)MOE_CODES_AT(kt, j, 0);                                      \
         fb[j] = __builtin_shufflevector(q, q, 0, 1, 2, 3, -1, -1, -1, -1);                       \
         sbv[j] = MOE_SCALE_AT(kt, j);                                                            \
       }                                                                                          \
@@ -1099,7 +1128,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
             const __bf16 hi = (__bf16)hv;                  // round to nearest even
             __bf16* d = (__bf16*)(ep + r * EP_S) + j * 16 + pl;
             d[0] = hi;
-            if (FMT == 1) d[32 * EP_S / 2] = (__bf16)(hv - (float)hi);
+            if (DEC) d[32 * EP_S / 2] = (__bf16)(hv - (float)hi);
           }
         }
       }
@@ -1151,7 +1180,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
         if (idx < 32 * CH && rl < rows && f0 < p.F) {
           const size_t at = (size_t)(gbase + rl) * p.F + f0;
           *(uint2*)(p.h + at) = *(const uint2*)(ep + r * EP_S + c * 8);
-          if (FMT == 1) *(uint2*)(p.h_lo + at) = *(const uint2*)(ep + 32 * EP_S + r * EP_S + c * 8);
+          if (DEC) *(uint2*)(p.h_lo + at) = *(const uint2*)(ep + 32 * EP_S + r * EP_S + c * 8);
         }
       }
     }
@@ -1221,6 +1250,11 @@ static hipError_t launch_any(const GemmArgs& g, int fmt, int cfg, int64_t A, hip
   if (fmt == 2) return launch_gemm<MODE, 2, LargeTile<MODE, 2>>(g, A, st);
   if (fmt == 0)
     return cfg == 0 ? launch_gemm<MODE, 0, SmallTile<MODE, 0>>(g, A, st) : launch_gemm<MODE, 0, LargeTile<MODE, 0>>(g, A, st);
+  // MXFP8 (kernel format 3) decodes to bf16: matrix-core tiles at many rows per expert,
+  // streaming tiles otherwise
+  if (fmt == 3)
+    return cfg != 0 ? launch_gemm<MODE, 3, LargeTile<MODE, 3>>(g, A, st)
+                    : launch_gemm<MODE, 3, SmallTile<MODE, 3>>(g, A, st);
   // MXFP4 on matrix-core tiles runs on the scaled engine (fmt 2)
   if (cfg != 0) return hipErrorInvalidValue;
   return launch_gemm<MODE, 1, SmallTile<MODE, 1>>(g, A, st);
@@ -1231,6 +1265,10 @@ static hipError_t launch_any(const GemmArgs& g, int fmt, int cfg, int64_t A, hip
 // h per wave) measured slower there.
 bool mx_engine(int fmt, int cfg) { return fmt == 1 && cfg == 1; }
 
+// Kernel format of a weight format (0 bf16, 1 MXFP4, 2 MXFP8) and tile configuration:
+// 0 bf16, 1 MXFP4 decoded, 2 MXFP4 on the scaled engine, 3 MXFP8 decoded.
+static int kernel_format(int fmt, int cfg) { return fmt == 2 ? 3 : (mx_engine(fmt, cfg) ? 2 : fmt); }
+
 hipError_t launch_mlp1(const ExpertArgs& a, int cfg, hipStream_t st) {
   GemmArgs g{};
   g.a = a.x; g.a_lo = nullptr; g.perm = a.perm; g.offsets = a.offsets; g.gates = a.gates;
@@ -1240,7 +1278,7 @@ hipError_t launch_mlp1(const ExpertArgs& a, int cfg, hipStream_t st) {
   g.E = a.E; g.k = a.k; g.K = a.D; g.N = 2 * a.F; g.F = a.F;
   const int64_t A = (int64_t)a.T * a.k;
   g.A = (int)A;
-  return launch_any<1>(g, mx_engine(a.fmt, cfg) ? 2 : a.fmt, cfg, A, st);
+  return launch_any<1>(g, kernel_format(a.fmt, cfg), cfg, A, st);
 }
 
 hipError_t launch_mlp2(const ExpertArgs& a, int cfg, hipStream_t st) {
@@ -1251,7 +1289,7 @@ hipError_t launch_mlp2(const ExpertArgs& a, int cfg, hipStream_t st) {
   g.E = a.E; g.k = a.k; g.K = a.F; g.N = a.D; g.F = a.F;
   const int64_t A = (int64_t)a.T * a.k;
   g.A = (int)A;
-  return launch_any<2>(g, mx_engine(a.fmt, cfg) ? 2 : a.fmt, cfg, A, st);
+  return launch_any<2>(g, kernel_format(a.fmt, cfg), cfg, A, st);
 }
 
 // ------------------------------------------------------------------------------ fp8 pieces

@@ -60,6 +60,8 @@ struct Layout {
   size_t h = 0, h_lo = 0, xq = 0, xs = 0, hq = 0, hs = 0, y = 0, total = 0;
 };
 
+bool valid_fmt(int fmt) { return fmt == MOE_FMT_BF16 || fmt == MOE_FMT_MXFP4 || fmt == MOE_FMT_MXFP8; }
+
 enum Need { NEED_ROUTE = 1, NEED_EXPERTS = 2, NEED_ROUTE_OUTPUTS = 4 };
 
 Layout layout(int64_t T, int64_t D, int64_t E, int64_t k, int64_t F, int fmt, int need) {
@@ -90,7 +92,7 @@ Layout layout(int64_t T, int64_t D, int64_t E, int64_t k, int64_t F, int fmt, in
       L.hs = take(A * (size_t)moe::mx_scale_stride((int)F) * 4);
     } else {
       L.h = take(A * (size_t)F * 2);
-      if (fmt == MOE_FMT_MXFP4) L.h_lo = take(A * (size_t)F * 2);
+      if (fmt != MOE_FMT_BF16) L.h_lo = take(A * (size_t)F * 2);
     }
     L.y = take(A * (size_t)D * 4);
   }
@@ -219,7 +221,7 @@ int run_experts(const uint8_t* ws, const Layout& L, const void* x, const void* w
   ea.offsets = offsets;
   ea.perm = perm;
   ea.h = (uint16_t*)(ws + L.h);
-  ea.h_lo = fmt == MOE_FMT_MXFP4 ? (uint16_t*)(ws + L.h_lo) : nullptr;
+  ea.h_lo = fmt != MOE_FMT_BF16 ? (uint16_t*)(ws + L.h_lo) : nullptr;
   ea.y = (float*)(ws + L.y);
   ea.xq = (uint8_t*)(ws + L.xq);
   ea.xs = (uint32_t*)(ws + L.xs);
@@ -244,7 +246,7 @@ int forward_impl(const void* x, const void* router_w, const void* router_b, bool
                  const void* w1, const void* b1, const void* w2, const void* b2, int64_t T, int64_t D, int64_t E,
                  int64_t k, int64_t F, int fmt, float* out) {
   CHECK(check_shapes(T, D, E, k, F, true));
-  if (fmt != MOE_FMT_BF16 && fmt != MOE_FMT_MXFP4) return fail(MOE_EFMT, "unknown weight format %d", fmt);
+  if (!valid_fmt(fmt)) return fail(MOE_EFMT, "unknown weight format %d", fmt);
   if (T == 0) return ok();
   CHECK(check_ptr(x, "x"));
   CHECK(check_ptr(router_w, "router_w"));
@@ -335,7 +337,7 @@ int moe_experts(const void* x, const void* w1, const void* b1, const void* w2, c
                 const float* gates, const int32_t* offsets, const int32_t* perm, int64_t T, int64_t D,
                 int64_t E, int64_t k, int64_t F, int fmt, float* out) {
   CHECK(check_shapes(T, D, E, k, F, true));
-  if (fmt != MOE_FMT_BF16 && fmt != MOE_FMT_MXFP4) return fail(MOE_EFMT, "unknown weight format %d", fmt);
+  if (!valid_fmt(fmt)) return fail(MOE_EFMT, "unknown weight format %d", fmt);
   if (T == 0) return ok();
   CHECK(check_ptr(x, "x"));
   CHECK(check_ptr(w1, "w1"));
@@ -360,7 +362,7 @@ int moe_set_stream(void* hip_stream) {
 
 size_t moe_workspace_bytes(int64_t T, int64_t D, int64_t E, int64_t k, int64_t F, int fmt) {
   if (check_shapes(T, D, E, k, F, true) != MOE_OK) return 0;
-  if (fmt != MOE_FMT_BF16 && fmt != MOE_FMT_MXFP4) return 0;
+  if (!valid_fmt(fmt)) return 0;
   if (T == 0) return 0;
   return layout(T, D, E, k, F, fmt, NEED_ROUTE | NEED_ROUTE_OUTPUTS | NEED_EXPERTS).total;
 }

@@ -15,7 +15,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
-FMT = {"bf16": 0, "mxfp4": 1}
+FMT = {"bf16": 0, "mxfp4": 1, "mxfp8": 2}
 STAGES = ("router", "topk", "permute", "mlp1", "mlp2", "combine", "split")
 
 _c_void_p = ctypes.c_void_p
@@ -88,6 +88,11 @@ def _bind_stream(device: torch.device) -> None:
     _check(lib().moe_set_stream(torch.cuda.current_stream(device).cuda_stream), "moe_set_stream")
 
 
+def mxfp8_bytes(E: int, rows: int, K: int) -> int:
+    """Bytes of an MXFP8 weight buffer: codes [E][rows][K] then scales [E][rows][K/32]."""
+    return E * rows * (K + K // 32)
+
+
 def mxfp4_bytes(E: int, rows: int, K: int) -> int:
     """Bytes of an MXFP4 weight buffer: codes [E][rows][K/2] then scales [E][rows][K/32]."""
     return E * rows * (K // 2 + K // 32)
@@ -103,6 +108,12 @@ def _check_weights(w1, w2, E, D, F, fmt):
             raise ValueError("mxfp4 weights are uint8 buffers")
         if w1.numel() != mxfp4_bytes(E, 2 * F, D) or w2.numel() != mxfp4_bytes(E, D, F):
             raise ValueError("mxfp4 weight buffers have the wrong size")
+        _dev(w1, "w1"), _dev(w2, "w2")
+    elif fmt == "mxfp8":
+        if w1.dtype != torch.uint8 or w2.dtype != torch.uint8:
+            raise ValueError("mxfp8 weights are uint8 buffers")
+        if w1.numel() != mxfp8_bytes(E, 2 * F, D) or w2.numel() != mxfp8_bytes(E, D, F):
+            raise ValueError("mxfp8 weight buffers have the wrong size")
         _dev(w1, "w1"), _dev(w2, "w2")
     else:
         raise ValueError(f"unknown format {fmt!r}")

@@ -33,7 +33,8 @@ def test_library_exports_every_declared_function():
 def test_header_constants_match_binding():
     src = open(HEADER).read()
     assert re.search(r"#define MOE_FMT_BF16 0\b", src) and re.search(r"#define MOE_FMT_MXFP4 1\b", src)
-    assert moe.FMT == {"bf16": 0, "mxfp4": 1}
+    assert re.search(r"#define MOE_FMT_MXFP8 2\b", src)
+    assert moe.FMT == {"bf16": 0, "mxfp4": 1, "mxfp8": 2}
     assert "#define MOE_SWIGLU_ALPHA 1.702f" in src and "#define MOE_SWIGLU_LIMIT 7.0f" in src
     assert re.search(r"#define MOE_NUM_STAGES 7\b", src) and len(moe.STAGES) == 7
 
@@ -55,7 +56,7 @@ def fwd(T=8, D=64, E=4, k=2, F=64, fmt=0, ptrs=None):
 @pytest.mark.parametrize("kw,code", [
     (dict(T=-1), MOE_EINVAL), (dict(D=0), MOE_EINVAL), (dict(D=96), MOE_EINVAL), (dict(F=32), MOE_EINVAL),
     (dict(E=0), MOE_EINVAL), (dict(E=257, k=2), MOE_EINVAL), (dict(k=0), MOE_EINVAL), (dict(k=5, E=4), MOE_EINVAL),
-    (dict(T=2**30, k=2), MOE_EINVAL), (dict(fmt=2), MOE_EFMT), (dict(fmt=-1), MOE_EFMT),
+    (dict(T=2**30, k=2), MOE_EINVAL), (dict(fmt=3), MOE_EFMT), (dict(fmt=-1), MOE_EFMT),
     (dict(T=2**24, D=64), MOE_EINVAL), (dict(T=2**22, D=64, k=4, E=4, F=64), MOE_EINVAL),
     (dict(D=2**15, F=2**15, T=1), MOE_EINVAL),
 ])
@@ -90,6 +91,7 @@ def test_route_and_experts_validate():
     assert lib.moe_route(P, P, P, 8, 64, 4, 2, BAD, P, P, P, P, P) == MOE_EALIGN
     assert lib.moe_experts(P, P, P, P, P, P, P, None, 8, 64, 4, 2, 64, 0, P) == MOE_EINVAL
     assert lib.moe_experts(P, P, P, P, P, P, P, P, 8, 64, 4, 2, 64, 7, P) == MOE_EFMT
+    assert lib.moe_experts(P, P, P, P, P, P, P, P, 8, 64, 4, 2, 64, 3, P) == MOE_EFMT
 
 
 def test_biased_entry_points_validate_the_bias():

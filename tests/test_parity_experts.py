@@ -30,16 +30,19 @@ def experts_vs_oracle(inp, label, weight_offset=0):
     return r
 
 
-@pytest.mark.parametrize("name", ["C1", "C2", "X1"])
+@pytest.mark.parametrize("name", ["C1", "C2", "X1", "Y1"])
 def test_experts_workloads(name):
     experts_vs_oracle(make_inputs(name), name)
+
+
+BASE = {"bf16": "C2", "mxfp4": "C4", "mxfp8": "Y1"}   # workload whose weight recipe a case takes
 
 
 # shapes chosen to cover both tile configurations (streaming 64x128 when T*k < 128*E, else
 # 256x256), row tails inside a tile, column tails of mlp1 (F not a multiple of the tile's
 # pair count: 64 or 128) and of mlp2 (D not a multiple of the tile width: 128 or 256),
 # single-K-step and multi-step reductions, and the degenerate layers
-@pytest.mark.parametrize("fmt", ["bf16", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp4", "mxfp8"])
 @pytest.mark.parametrize("T,D,E,k,F", [
     (37, 128, 5, 2, 192),       # streaming tiles, ragged groups, mlp1 pair tail (192 = 128 + 64)
     (300, 64, 3, 3, 64),        # k = E, one K step
@@ -51,14 +54,14 @@ def test_experts_workloads(name):
     (200, 128, 256, 8, 128),    # 256 experts, most of them empty
 ])
 def test_experts_ragged_shapes(fmt, T, D, E, k, F):
-    base = "C4" if fmt == "mxfp4" else "C2"
+    base = BASE[fmt]
     cfg = get_config(base, name=f"rag{T}", T=T, D=D, E=E, k=k, F=F, seed=1000 + T)
     experts_vs_oracle(make_inputs(cfg), f"ragged {fmt} T={T} D={D} E={E} k={k} F={F}")
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp4", "mxfp8"])
 def test_experts_with_empty_experts(fmt):
-    base = "C4" if fmt == "mxfp4" else "C2"
+    base = BASE[fmt]
     cfg = get_config(base, name="empty", T=600, D=128, E=16, k=2, F=128, seed=77)
     inp = make_inputs(cfg)
     neg = f32_to_bf16_bits(np.float32([-64.0]))[0]
@@ -89,8 +92,9 @@ def test_experts_with_clamped_swiglu():
     ("bf16", 64, 448, 8, 2, 320),      # streaming tiles
     ("mxfp4", 64, 448, 8, 2, 320),     # streaming tiles, decode path
     ("mxfp4", 700, 320, 2, 1, 448),    # matrix-core tiles, scaled engine
+    ("mxfp8", 64, 448, 8, 2, 320),     # MXFP8 decode path
 ])
 def test_experts_unaligned_weight_buffers(offset, fmt, T, D, E, k, F):
-    base = "C4" if fmt == "mxfp4" else "C2"
+    base = BASE[fmt]
     cfg = get_config(base, name=f"off{T}", T=T, D=D, E=E, k=k, F=F, seed=3000 + T + offset)
     experts_vs_oracle(make_inputs(cfg), f"weights +{offset} B {fmt} T={T} D={D} E={E} k={k} F={F}", offset)

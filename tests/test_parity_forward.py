@@ -26,7 +26,7 @@ def forward(inp, d=None):
     return out
 
 
-@pytest.mark.parametrize("name", ["C1", "C2", "X1"])
+@pytest.mark.parametrize("name", ["C1", "C2", "X1", "Y1"])
 def test_forward_full(name):
     inp = make_inputs(name)
     cfg = inp.cfg
@@ -52,7 +52,7 @@ def pick_sample(name, idx, E, n):
     return np.unique(np.concatenate([g.choice(cand, size=min(n, cand.size), replace=False)] + tail))
 
 
-@pytest.mark.parametrize("name,n", [("C3", 256), ("C4", 256), ("X2", 256), ("C5", 128)])
+@pytest.mark.parametrize("name,n", [("C3", 256), ("C4", 256), ("X2", 256), ("C5", 128), ("Y2", 256)])
 def test_forward_large_sampled(name, n):
     inp = make_inputs(name)
     cfg = inp.cfg
