@@ -34,6 +34,12 @@
 //   bytes as its B scales unchanged; the activations enter as fp8 E4M3 pieces with their
 //   own block scales (x: two pieces from the split kernel, h: three pieces written by
 //   mlp1's epilogue), so no weight is ever decoded.
+//
+// MXFP8 weights (E4M3 elements with the same block scales; the torchtitan guide's grouped
+// GEMM section names MXFP8 converters as users of the scaled grouped-GEMM seam) are
+// decoded like MXFP4 ones, with v_cvt_scalef32_pk_bf16_fp8 (E4M3 has 3 mantissa bits: exact
+// in bf16 for scale bytes in [10, 246]), on streaming tiles and on matrix-core tiles alike;
+// h goes into mlp2 as a bf16 pair there too.
 #include "moe_internal.h"
 
 namespace moe {
