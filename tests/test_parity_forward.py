@@ -74,7 +74,7 @@ def test_forward_large_sampled(name, n):
     assert_close(got[sample], ref, f"forward {name} ({sample.size} sampled tokens)")
 
 
-@pytest.mark.parametrize("name", ["C3", "C4"])
+@pytest.mark.parametrize("name", ["C3", "C4", "Y2"])
 def test_forward_is_bitwise_deterministic(name):
     inp = make_inputs(name)
     d = upload(inp)
@@ -84,11 +84,11 @@ def test_forward_is_bitwise_deterministic(name):
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp4", "mxfp8"])
 def test_forward_power_of_two_scaling_is_exact(fmt):
-    """W2, b2 doubled (bf16: exponent + 1; MXFP4: every W2 scale byte + 1, b2 doubled) doubles
-    the output bit for bit: scaling by 2 commutes with every rounding on the path."""
-    base = "C4" if fmt == "mxfp4" else "C2"
+    """W2, b2 doubled (bf16: exponent + 1; MXFP4/MXFP8: every W2 scale byte + 1, b2 doubled)
+    doubles the output bit for bit: scaling by 2 commutes with every rounding on the path."""
+    base = {"bf16": "C2", "mxfp4": "C4", "mxfp8": "Y1"}[fmt]
     cfg = get_config(base, name="scale", T=1024, E=8, seed=31)
     inp = make_inputs(cfg)
     d = upload(inp)
@@ -101,14 +101,14 @@ def test_forward_power_of_two_scaling_is_exact(fmt):
         w2s = np.where(nzw, inp.w2 + np.uint16(1 << 7), inp.w2).astype(np.uint16)
     else:
         w2s = inp.w2.copy()
-        w2s[cfg.E * cfg.D * cfg.F // 2:] += 1
+        w2s[cfg.E * cfg.D * (cfg.F // 2 if fmt == "mxfp4" else cfg.F):] += 1
     from _gpu import u16, weights
     d2 = dict(d, w2=weights(w2s, fmt), b2=u16(b2s))
     out2 = forward(inp, d2)
     assert torch.equal(out2, 2 * out)
 
 
-@pytest.mark.parametrize("name", ["C1", "C2", "X1"])
+@pytest.mark.parametrize("name", ["C1", "C2", "X1", "Y1"])
 def test_forward_with_expert_bias(name):
     """The biased entry point over the whole block: the bias moves the selection (most tokens
     at this size) and the gates stay on the unbiased logits."""
