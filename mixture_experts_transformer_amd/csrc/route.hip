@@ -40,12 +40,12 @@ constexpr int RT_PD = 4;              // chunks whose loads are in flight (up to
 #define RT_TARGET_WAVES 2048
 #endif
 #ifndef RT_MIN_CHUNKS
-#define RT_MIN_CHUNKS 6
+#define RT_MIN_CHUNKS 3
 #endif
 int router_ksplit(int64_t T, int64_t D) {
   const int64_t chunks = D / RT_CHUNK;
   const int64_t tiles = (T + 15) / 16;
-  // aim at ~2048 waves in flight; keep >= 6 chunks per split so the top-k kernel's
+  // aim at ~2048 waves in flight; keep >= 3 chunks per split so the top-k kernel's
   // sum over splits stays short
   int64_t ks = (RT_TARGET_WAVES + tiles - 1) / tiles;
   int64_t maxks = chunks / RT_MIN_CHUNKS > 0 ? chunks / RT_MIN_CHUNKS : 1;
