@@ -70,6 +70,9 @@
  *     synchronisation.  Outputs are fully overwritten and must not alias inputs.
  *   - Return value: MOE_OK (0) or a negative MOE_E* status; on failure nothing
  *     has been launched and moe_last_error() describes the problem.
+ *   - Graph capture: a call enqueues kernels only (no allocation, memset, copy or
+ *     synchronisation) once the workspace fits its shape, so after one eager call of the
+ *     same shape (or with moe_set_workspace) it can be captured into a HIP graph.
  *   - The library-owned workspace is shared by all calls of the process and is
  *     reused between calls: calls that run concurrently on different streams
  *     race on it.  Serialise them, or give each stream its own workspace with
