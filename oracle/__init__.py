@@ -26,3 +26,4 @@ from .moe_oracle import (  # noqa: F401
     swiglu,
     update_expert_bias,
 )
+from .moe_backward import forward_fixed_routing, moe_backward, swiglu_backward  # noqa: F401,E402
