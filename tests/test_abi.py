@@ -140,3 +140,36 @@ def test_workspace_bytes():
 def test_set_workspace_rejects_misaligned():
     assert moe.lib().moe_set_workspace(0x1010, 4096) == MOE_EALIGN
     assert moe.lib().moe_set_workspace(None, 0) == MOE_OK
+
+
+def test_plain_c_program_links_and_calls_the_library(tmp_path):
+    """The header is plain C (C99, no C++): a C program includes it, links libmoe.so, and
+    gets the host-side validation and zero-token results without a GPU."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "use.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include "moe.h"
+int main(void) {
+  int rc = 0;
+  if (moe_forward(0, 0, 0, 0, 0, 0, 0, 0, 64, 4, 2, 64, MOE_FMT_MXFP8, 0) != MOE_OK) rc |= 1;
+  if (moe_forward(0, 0, 0, 0, 0, 0, 0, 8, 64, 4, 5, 64, MOE_FMT_BF16, 0) != MOE_EINVAL) rc |= 2;
+  if (moe_update_expert_bias(0, 300, 1e-3f, 0) != MOE_EINVAL) rc |= 4;
+  if (moe_workspace_bytes(0, 64, 4, 2, 64, MOE_FMT_BF16) != 0) rc |= 8;
+  printf("%s\n", moe_version());
+  return rc;
+}
+''')
+    lib_dir = os.path.dirname(moe.LIB_PATH)
+    exe = tmp_path / "use"
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), str(src),
+                        "-L", lib_dir, "-l:libmoe.so", f"-Wl,-rpath,{lib_dir}", "-o", str(exe)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
+    assert "gfx950" in r.stdout
