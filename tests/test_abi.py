@@ -173,3 +173,26 @@ int main(void) {
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
     assert "gfx950" in r.stdout
+
+
+def test_product_path_never_touches_the_oracle():
+    """The package (binding and kernels) imports nothing from oracle/ and has no CPU fallback:
+    its sources never name the oracle package, and importing it leaves oracle unloaded.
+    The oracle in turn imports nothing from the package."""
+    import subprocess
+    import sys
+    pkg = os.path.join(ROOT, "mixture_experts_transformer_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
+                assert "import oracle" not in text and "from oracle" not in text, f
+    for f in os.listdir(os.path.join(ROOT, "oracle")):
+        if f.endswith(".py"):
+            assert "mixture_experts_transformer_amd" not in open(os.path.join(ROOT, "oracle", f)).read(), f
+    code = ("import sys, mixture_experts_transformer_amd as m; m.lib(); "
+            "print('oracle' in sys.modules)")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert r.stdout.strip() == "False"
