@@ -1,9 +1,11 @@
 """Throughput of the GPT-OSS MoE block on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload C2] [--all]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload C2] [--all] [--no-targets]
 
 One step = one moe_forward over one batch of synthetic tokens (router, top-k, grouping,
-mlp1 + SwiGLU, mlp2 + gate, combine).  Inputs are resident in device memory before the
+mlp1 + SwiGLU, mlp2 + gate, combine).  The default line is the 256-token bf16 layer (C2);
+it also carries, under "targets", the same measurement of the other target layers: bf16 at
+8192 tokens with a Zipf load (C3) and MXFP4 weights at 256 and 8192 tokens (X1, X2).  Inputs are resident in device memory before the
 timed region.  The expert weights are rotated over several device copies so no step finds
 the previous step's weights in the 256 MB Infinity Cache, as consecutive MoE layers of a
 model would not.  Prints one JSON line (per workload with --all).
@@ -84,9 +86,14 @@ def cpu_baseline(inp, n_tokens, min_seconds=10.0):
     """Time the oracle on the first n_tokens of the workload (float64 NumPy on host cores),
     repeating the forward until at least min_seconds have elapsed."""
     import oracle
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        pools = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        threads = max([p.get("num_threads", 1) for p in pools] or [os.cpu_count() or 1])
+        if pools:
+            p = pools[0]
+            blas = f"{p.get('internal_api', '?')} {p.get('version', '?')} ({p.get('architecture', '?')})"
     except Exception:
         threads = os.cpu_count() or 1
     cfg = inp.cfg
@@ -100,8 +107,21 @@ def cpu_baseline(inp, n_tokens, min_seconds=10.0):
         if dt >= min_seconds:
             break
     return {"value": round(reps * n_tokens / dt, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(), "blas": blas,
             "sample": f"first {n_tokens} of the {cfg.T} tokens of workload {cfg.name}, float64 forward "
                       f"repeated {reps} times ({dt:.1f} s)"}
+
+
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), or the platform string."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
 
 
 def source_key():
@@ -247,6 +267,18 @@ def bench_workload(name, steps, warmup, with_cpu):
     return res
 
 
+TARGETS = ("C3", "X1", "X2")     # the other target workloads: bf16 at 8192 tokens, MXFP4 at 256 and 8192
+
+
+def target_summary(res):
+    """The fields of a target workload's measurement that go into the headline line."""
+    keep = ("value", "unit", "ms_per_step", "steps", "warmup", "dtype", "step_tflops", "step_mfma_frac",
+            "step_fp8_peak_frac", "step_fp4_peak_frac", "step_hbm_gbs", "step_hbm_frac", "kernel_us", "roofline")
+    out = {k: res[k] for k in keep if k in res}
+    out["workload"] = res["config"]["workload"]
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -254,6 +286,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="C2", help="C2 (default), C3, C4, C5, X1, X2, Y1, Y2")
     ap.add_argument("--all", action="store_true", help="one line per target workload: C2 C3 X1 X2")
+    ap.add_argument("--no-targets", action="store_true",
+                    help="time only --workload (by default the C2 line also carries C3, X1 and X2 under 'targets')")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device copies of MIB MiB (reference for the HBM byte counters)")
@@ -275,10 +309,19 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
         return
-    names = ["C2", "C3", "X1", "X2"] if args.all else [args.workload]
-    for i, name in enumerate(names):
-        res = bench_workload(name, args.steps, args.warmup, with_cpu=(not args.no_cpu) and i == 0)
-        print(json.dumps(res), flush=True)
+    if args.all:
+        for i, name in enumerate(["C2", *TARGETS]):
+            res = bench_workload(name, args.steps, args.warmup, with_cpu=(not args.no_cpu) and i == 0)
+            print(json.dumps(res), flush=True)
+        return
+    res = bench_workload(args.workload, args.steps, args.warmup, with_cpu=not args.no_cpu)
+    if args.workload == "C2" and not args.no_targets:
+        # the headline workload's line also carries the other target workloads, each timed the
+        # same way (own warm-up, K timed steps between synchronisations, then an event pass)
+        res["targets"] = {}
+        for name in TARGETS:
+            res["targets"][name] = target_summary(bench_workload(name, args.steps, args.warmup, with_cpu=False))
+    print(json.dumps(res), flush=True)
 
 
 if __name__ == "__main__":

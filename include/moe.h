@@ -72,11 +72,16 @@
  *     has been launched and moe_last_error() describes the problem.
  *   - Graph capture: a call enqueues kernels only (no allocation, memset, copy or
  *     synchronisation) once the workspace fits its shape, so after one eager call of the
- *     same shape (or with moe_set_workspace) it can be captured into a HIP graph.
- *   - The library-owned workspace is shared by all calls of the process and is
- *     reused between calls: calls that run concurrently on different streams
- *     race on it.  Serialise them, or give each stream its own workspace with
- *     moe_set_workspace.
+ *     same shape (or with moe_set_workspace) it can be captured into a HIP graph.  A call
+ *     on a capturing stream that would have to grow the library-owned workspace fails
+ *     with MOE_ENOMEM.  Once a call has been captured, the library-owned buffer it used is
+ *     never freed before moe_release: a later, larger call allocates a new one and keeps
+ *     the old one, so captured graphs stay valid.  moe_release, and freeing or reusing a
+ *     caller workspace (moe_set_workspace), invalidate the graphs captured on it.
+ *   - Workspace: a thread that called moe_set_workspace uses its own caller-owned buffer;
+ *     every other thread shares the library-owned one, reused from call to call.  Calls
+ *     that run concurrently (other threads, other streams) on the same buffer race on it:
+ *     serialise them, or give each thread its own buffer with moe_set_workspace.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -158,11 +163,15 @@ int moe_route_biased(const void* x, const void* router_w, const void* router_b, 
 int moe_update_expert_bias(const int32_t* counts, int64_t E, float coeff, float* expert_bias);
 
 /* Steps 5-8 on a given routing (expert stage), e.g. the routing of moe_route or of a
- * reference.  gates fp32 [T][k], offsets int32 [E+1] and perm int32 [T*k] must be
- * consistent (as moe_route produces them: perm[offsets[e] .. offsets[e+1]) lists the
- * assignments t*k+j routed to expert e); inconsistent routing is outside the contract.
- * The token and slot of a row come from its assignment id, so top-k indices are not
- * needed.  Other arguments as in moe_forward. */
+ * reference: the stage isolation of the "gptoss" re-implementation page, section 测试说明
+ * (testing notes: each layer can be verified on the reference's inputs rather than on its
+ * own upstream output).  gates fp32 [T][k], offsets int32 [E+1] and perm int32 [T*k] must
+ * be consistent (as moe_route produces them: perm[offsets[e] .. offsets[e+1]) lists the
+ * assignments t*k+j routed to expert e); inconsistent routing is outside the contract, but
+ * rows outside [0, T*k) are skipped, never dereferenced.  The expert of a row is the group
+ * it sits in and its token and slot come from its assignment id, so the top-k index array
+ * would repeat what offsets and perm already say: it is not an argument.  Other arguments
+ * as in moe_forward. */
 int moe_experts(const void* x, const void* w1, const void* b1, const void* w2, const void* b2,
                 const float* gates, const int32_t* offsets, const int32_t* perm,
                 int64_t T, int64_t D, int64_t E, int64_t k, int64_t F,
@@ -174,15 +183,19 @@ int moe_set_stream(void* hip_stream);
 /* Device bytes of workspace a moe_forward call of this shape needs (0 for T == 0). */
 size_t moe_workspace_bytes(int64_t T, int64_t D, int64_t E, int64_t k, int64_t F, int fmt);
 
-/* Use caller-owned device memory as the workspace (256-byte aligned).  Calls whose need
- * exceeds `bytes` fail with MOE_ENOMEM.  Passing NULL returns to the library-owned
- * workspace, which grows on demand with hipMalloc and is kept until moe_release. */
+/* Use caller-owned device memory as the calling thread's workspace (256-byte aligned) for
+ * its later calls; other threads are not affected.  Calls whose need exceeds `bytes` fail
+ * with MOE_ENOMEM before launching anything.  Passing NULL returns the thread to the shared
+ * library-owned workspace, which grows on demand with hipMalloc and is kept until
+ * moe_release. */
 int moe_set_workspace(void* dev_ptr, size_t bytes);
 
 /* Message for the calling thread's last failing call ("" if none). */
 const char* moe_last_error(void);
 
-/* Free the library-owned workspace and profiling events. */
+/* Free the library-owned workspace (with the buffers kept for captured graphs) and the
+ * profiling events, and return the calling thread to the library-owned workspace.  Must not
+ * run while work that uses the workspace is queued or a captured graph may still replay. */
 void moe_release(void);
 
 /* Kernel timing (tracing): while enabled, every launch is bracketed by HIP events on the

@@ -2,7 +2,9 @@
 
     python -m mixture_experts_transformer_amd.build [--verbose]
 
-Every HIP source under ``csrc/`` is compiled for gfx950 only.  Packed-fp32 VALU
+Every HIP source under ``csrc/`` is compiled for gfx950 only.  The copies of the grouped GEMM
+load M0 in inline assembly; the build checks the generated assembly (``check_m0``) and fails
+rather than ship a library in which anything else uses M0.  Packed-fp32 VALU
 instructions are disabled for device code (``-packed-fp32-ops``); the host pass prints a
 harmless warning that it does not know the feature.
 """
@@ -25,6 +27,45 @@ def hipcc() -> str:
     return path if os.path.exists(path) else "hipcc"
 
 
+def device_asm(src: str) -> str:
+    """gfx950 assembly of one HIP source (device code only), compiled as the library is."""
+    import tempfile
+    with tempfile.TemporaryDirectory() as d:
+        out = os.path.join(d, "k.s")
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-S", "--cuda-device-only",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-I", os.path.join(os.path.dirname(HERE), "include"), os.path.join(CSRC, src), "-o", out]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc -S {src} failed ({r.returncode}):\n{r.stderr[-4000:]}")
+        return open(out).read()
+
+
+# Sources whose kernels issue the direct global->LDS copies (inline assembly that loads M0
+# without the compiler preserving it).
+M0_SOURCES = ["gemm.hip"]
+
+
+def check_m0(src: str) -> int:
+    """The LDS copies load M0 in inline assembly that the compiler does not preserve; that is
+    sound only while nothing else in the generated code uses M0.  Raise if any use of M0 in
+    the gfx950 assembly of `src` is not 's_mov_b32 m0, sN' directly followed by 's_nop 0' and
+    a global_load_lds copy.  Returns the number of copies checked."""
+    import re
+    lines = [l.split(";")[0].strip() for l in device_asm(src).splitlines()]
+    lines = [l for l in lines if l and not l.startswith(".")]
+    uses = [i for i, l in enumerate(lines) if re.search(r"\bm0\b", l)]
+    if not uses:
+        raise RuntimeError(f"{src}: expected the LDS copies to set M0")
+    for i in uses:
+        if not re.fullmatch(r"s_mov_b32 m0, s\d+", lines[i]):
+            raise RuntimeError(f"{src}: M0 used other than by an LDS copy: {lines[i]!r}")
+        nxt = lines[i + 1:i + 3]
+        if len(nxt) < 2 or nxt[0] != "s_nop 0" or not nxt[1].startswith("global_load_lds_dword"):
+            raise RuntimeError(f"{src}: M0 set but not consumed by a copy: {lines[i:i + 3]!r}")
+    return len(uses)
+
+
 def build(verbose: bool = False) -> str:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     tmp = LIB + ".tmp"
@@ -42,6 +83,11 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{msgs}")
     if msgs.strip() and verbose:
         print(msgs)
+    # the library ships only if the copies' M0 handling holds in the code just generated
+    for s in M0_SOURCES:
+        n = check_m0(s)
+        if verbose:
+            print(f"M0 check {s}: {n} copies, no other use", flush=True)
     os.replace(tmp, LIB)
     return LIB
 

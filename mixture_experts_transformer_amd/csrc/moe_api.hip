@@ -20,13 +20,25 @@ namespace {
 thread_local std::string g_err;
 thread_local hipStream_t g_stream = nullptr;
 
+// Library-owned workspace, shared by the threads that have not set their own.  Once a call
+// has run on a capturing stream, captured graphs may hold its address: from then on a
+// larger buffer does not free the old one (it is retired, kept until moe_release), so the
+// graphs stay valid.
 struct Workspace {
   std::mutex mu;
   void* ptr = nullptr;
   size_t size = 0;
-  bool user = false;
+  bool pinned = false;                     // a captured graph may use ptr
+  std::vector<void*> retired;              // earlier buffers captured graphs may still use
 };
 Workspace g_ws;
+
+// Caller-owned workspace of the calling thread (moe_set_workspace).
+struct UserWorkspace {
+  void* ptr = nullptr;
+  size_t size = 0;
+};
+thread_local UserWorkspace t_user_ws;
 
 struct Profiler {
   std::mutex mu;
@@ -129,19 +141,37 @@ int check_ptr(const void* p, const char* name, bool nullable = false) {
   } while (0)
 
 int ensure_workspace(size_t bytes, uint8_t** base) {
-  std::lock_guard<std::mutex> lk(g_ws.mu);
-  if (g_ws.user) {
-    if (g_ws.size < bytes)
-      return fail(MOE_ENOMEM, "caller workspace holds %zu bytes, the call needs %zu", g_ws.size, bytes);
-    *base = (uint8_t*)g_ws.ptr;
+  if (t_user_ws.ptr) {
+    if (t_user_ws.size < bytes)
+      return fail(MOE_ENOMEM, "caller workspace holds %zu bytes, the call needs %zu", t_user_ws.size, bytes);
+    *base = (uint8_t*)t_user_ws.ptr;
     return MOE_OK;
   }
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (g_stream && hipStreamIsCapturing(g_stream, &cs) != hipSuccess)
+    return fail(MOE_EHIP, "hipStreamIsCapturing failed");
+  const bool capturing = cs != hipStreamCaptureStatusNone;
+  std::lock_guard<std::mutex> lk(g_ws.mu);
   if (g_ws.size < bytes) {
+    if (capturing)
+      return fail(MOE_ENOMEM,
+                  "the stream is capturing and the workspace holds %zu bytes, the call needs %zu: run one "
+                  "call of this shape eagerly first, or set a workspace with moe_set_workspace",
+                  g_ws.size, bytes);
     if (g_ws.ptr) {
-      hipError_t e = hipFree(g_ws.ptr);   // waits for queued work that may still use it
+      if (g_ws.pinned) {
+        g_ws.retired.push_back(g_ws.ptr);  // a captured graph may still replay into it
+      } else {
+        hipError_t e = hipFree(g_ws.ptr);  // waits for queued work that may still use it
+        if (e != hipSuccess) {
+          g_ws.ptr = nullptr;
+          g_ws.size = 0;
+          return fail(MOE_EHIP, "hipFree(workspace): %s", hipGetErrorString(e));
+        }
+      }
       g_ws.ptr = nullptr;
       g_ws.size = 0;
-      if (e != hipSuccess) return fail(MOE_EHIP, "hipFree(workspace): %s", hipGetErrorString(e));
+      g_ws.pinned = false;
     }
     const size_t want = align256(bytes + bytes / 4);
     void* p = nullptr;
@@ -153,6 +183,7 @@ int ensure_workspace(size_t bytes, uint8_t** base) {
     g_ws.ptr = p;
     g_ws.size = want;
   }
+  if (capturing) g_ws.pinned = true;
   *base = (uint8_t*)g_ws.ptr;
   return MOE_OK;
 }
@@ -181,10 +212,25 @@ int launch(int stage, const char* name, F&& fn) {
       prof = true;
     }
   }
-  if (prof && hipEventRecord(a, st) != hipSuccess) return fail(MOE_EHIP, "hipEventRecord failed");
+  // a failed launch leaves no pair behind: its stop event would never be recorded
+  auto unrecord = [&]() {
+    if (!prof) return;
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    if (g_prof.used > 0 && g_prof.start[g_prof.used - 1] == a) --g_prof.used;
+  };
+  if (prof && hipEventRecord(a, st) != hipSuccess) {
+    unrecord();
+    return fail(MOE_EHIP, "hipEventRecord failed");
+  }
   hipError_t e = fn(st);
-  if (e != hipSuccess) return fail(MOE_EHIP, "%s launch failed: %s", name, hipGetErrorString(e));
-  if (prof && hipEventRecord(b, st) != hipSuccess) return fail(MOE_EHIP, "hipEventRecord failed");
+  if (e != hipSuccess) {
+    unrecord();
+    return fail(MOE_EHIP, "%s launch failed: %s", name, hipGetErrorString(e));
+  }
+  if (prof && hipEventRecord(b, st) != hipSuccess) {
+    unrecord();
+    return fail(MOE_EHIP, "hipEventRecord failed");
+  }
   return MOE_OK;
 }
 
@@ -368,16 +414,10 @@ size_t moe_workspace_bytes(int64_t T, int64_t D, int64_t E, int64_t k, int64_t F
 }
 
 int moe_set_workspace(void* dev_ptr, size_t bytes) {
-  std::lock_guard<std::mutex> lk(g_ws.mu);
   if (dev_ptr && (((uintptr_t)dev_ptr) & 255))
     return fail(MOE_EALIGN, "workspace %p is not 256-byte aligned", dev_ptr);
-  if (!g_ws.user && g_ws.ptr) {
-    hipError_t e = hipFree(g_ws.ptr);
-    if (e != hipSuccess) return fail(MOE_EHIP, "hipFree(workspace): %s", hipGetErrorString(e));
-  }
-  g_ws.ptr = dev_ptr;
-  g_ws.size = dev_ptr ? bytes : 0;
-  g_ws.user = dev_ptr != nullptr;
+  t_user_ws.ptr = dev_ptr;
+  t_user_ws.size = dev_ptr ? bytes : 0;
   return ok();
 }
 
@@ -386,11 +426,14 @@ const char* moe_last_error(void) { return g_err.c_str(); }
 void moe_release(void) {
   {
     std::lock_guard<std::mutex> lk(g_ws.mu);
-    if (!g_ws.user && g_ws.ptr) (void)hipFree(g_ws.ptr);
+    if (g_ws.ptr) (void)hipFree(g_ws.ptr);
+    for (void* p : g_ws.retired) (void)hipFree(p);
+    g_ws.retired.clear();
     g_ws.ptr = nullptr;
     g_ws.size = 0;
-    g_ws.user = false;
+    g_ws.pinned = false;
   }
+  t_user_ws = UserWorkspace{};
   std::lock_guard<std::mutex> lk(g_prof.mu);
   for (auto e : g_prof.start) (void)hipEventDestroy(e);
   for (auto e : g_prof.stop) (void)hipEventDestroy(e);
@@ -411,10 +454,15 @@ int moe_profile_read(double* ms, int64_t* launches) {
   double acc[MOE_NUM_STAGES] = {0};
   int64_t cnt[MOE_NUM_STAGES] = {0};
   for (size_t i = 0; i < g_prof.used; ++i) {
-    if (hipEventSynchronize(g_prof.stop[i]) != hipSuccess) return fail(MOE_EHIP, "hipEventSynchronize failed");
+    if (hipEventSynchronize(g_prof.stop[i]) != hipSuccess) {
+      g_prof.used = 0;
+      return fail(MOE_EHIP, "hipEventSynchronize failed");
+    }
     float t = 0.f;
-    if (hipEventElapsedTime(&t, g_prof.start[i], g_prof.stop[i]) != hipSuccess)
+    if (hipEventElapsedTime(&t, g_prof.start[i], g_prof.stop[i]) != hipSuccess) {
+      g_prof.used = 0;
       return fail(MOE_EHIP, "hipEventElapsedTime failed");
+    }
     acc[g_prof.stage[i]] += t;
     cnt[g_prof.stage[i]] += 1;
   }

@@ -196,3 +196,59 @@ def test_product_path_never_touches_the_oracle():
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT, timeout=300)
     assert r.returncode == 0, r.stderr[-2000:]
     assert r.stdout.strip() == "False"
+
+
+def test_too_small_caller_workspace_is_enomem():
+    """A caller workspace smaller than the call needs fails with MOE_ENOMEM before any HIP call
+    (the addresses are fake: nothing is launched), naming both sizes."""
+    lib = moe.lib()
+    MOE_ENOMEM = -4
+    T, D, E, k, F = 256, 2880, 32, 4, 2880
+    need = lib.moe_workspace_bytes(T, D, E, k, F, 0)
+    assert need > 4096
+    assert lib.moe_set_workspace(0x100000, 4096) == MOE_OK
+    try:
+        assert fwd(T=T, D=D, E=E, k=k, F=F) == MOE_ENOMEM
+        msg = lib.moe_last_error().decode()
+        assert "4096" in msg and str(need) in msg
+        assert lib.moe_route(P, P, P, T, D, E, k, None, P, P, P, P, P) == MOE_ENOMEM
+        assert lib.moe_experts(P, P, P, P, P, P, P, P, T, D, E, k, F, 1, P) == MOE_ENOMEM
+        assert lib.moe_forward_biased(P, P, P, P, P, P, P, P, T, D, E, k, F, 2, P) == MOE_ENOMEM
+    finally:
+        assert lib.moe_set_workspace(None, 0) == MOE_OK
+
+
+def test_caller_workspace_is_per_thread():
+    """moe_set_workspace binds the calling thread only: two threads with buffers of different
+    sizes each see their own size in the MOE_ENOMEM message."""
+    import threading
+    lib = moe.lib()
+    MOE_ENOMEM = -4
+    seen = {}
+
+    def worker(size):
+        assert lib.moe_set_workspace(0x200000, size) == MOE_OK
+        try:
+            rc = fwd(T=256, D=2880, E=32, k=4, F=2880)
+            seen[size] = (rc, lib.moe_last_error().decode())
+        finally:
+            lib.moe_set_workspace(None, 0)
+
+    for size in (4096, 8192):
+        th = threading.Thread(target=worker, args=(size,))
+        th.start()
+        th.join()
+    assert lib.moe_set_workspace(0x300000, 1 << 20) == MOE_OK
+    try:
+        ths = [threading.Thread(target=worker, args=(s,)) for s in (12288, 16384)]
+        for th in ths:
+            th.start()
+        for th in ths:
+            th.join()
+        rc = fwd(T=256, D=2880, E=32, k=4, F=2880)       # this thread keeps its own 1 MiB
+        assert rc == MOE_ENOMEM and f"holds {1 << 20} bytes" in lib.moe_last_error().decode()
+    finally:
+        lib.moe_set_workspace(None, 0)
+    for size in (4096, 8192, 12288, 16384):
+        rc, msg = seen[size]
+        assert rc == MOE_ENOMEM and f"holds {size} bytes" in msg, (size, msg)

@@ -57,3 +57,49 @@ def test_forward_graph_replays_match_eager(base, T, E, biased):
         torch.cuda.synchronize()
         assert torch.equal(mid, ref2)
     del g
+
+
+def test_graph_survives_a_larger_eager_call():
+    """A graph captured while the library-owned workspace was small keeps replaying correctly
+    after an eager call of a larger shape grew the workspace: the captured buffer is retired,
+    not freed, until moe_release."""
+    base = "C2"
+    small = get_config(base, name="graph-small", T=64, E=8, D=512, F=512, seed=6101)
+    large = get_config(base, name="graph-large", T=4096, E=8, D=512, F=512, seed=6102)
+    ds, dl = upload(make_inputs(small)), upload(make_inputs(large))
+    note("graph capture, then a larger eager call, then replay")
+
+    def fwd(dd, cfg, out=None):
+        return moe.forward(dd["x"], dd["router_w"], dd["router_b"], dd["w1"], dd["b1"], dd["w2"], dd["b2"],
+                           cfg.k, cfg.fmt, out=out)
+
+    torch.cuda.synchronize()
+    moe.release()                                # start from an empty library-owned workspace
+    ref = fwd(ds, small)
+    torch.cuda.synchronize()
+    assert moe.workspace_bytes(64, 512, 8, 4, 512) < moe.workspace_bytes(4096, 512, 8, 4, 512)
+    out_g = torch.empty_like(ref)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fwd(ds, small, out_g)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        fwd(ds, small, out_g)
+    torch.cuda.synchronize()
+    big = fwd(dl, large)                         # grows the workspace (the old one is kept)
+    torch.cuda.synchronize()
+    big_ref = big.clone()
+    for rep in range(3):
+        out_g.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, ref), f"replay {rep} after the larger call differs"
+        again = fwd(dl, large)
+        torch.cuda.synchronize()
+        assert torch.equal(again, big_ref)
+    del g
+    torch.cuda.synchronize()
+    moe.release()

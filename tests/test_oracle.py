@@ -139,8 +139,9 @@ def dense_reference(x, wr, br, w1, b1, w2, b2, k, F, fmt, ebias=None):
     return np.einsum("te,ted->td", gh, Y), l, mask
 
 
-def tiny_layer(seed, T, D, E, k, F, fmt, wstd=0.3, bstd=0.2, br_std=0.5):
-    """Small random layer (bits), with weights large enough that SwiGLU clamps engage."""
+def tiny_layer(seed, T, D, E, k, F, fmt, wstd=0.3, bstd=0.2, br_std=0.5, mx8_scales=(115, 119)):
+    """Small random layer (bits).  With MXFP4 weights the SwiGLU clamps engage; bf16 and MXFP8
+    layers engage them when wstd or mx8_scales (E8M0 bytes drawn in [lo, hi)) are raised."""
     g = np.random.default_rng(seed)
     bf = lambda *s, std=1.0: f32_to_bf16_bits(g.standard_normal(s).astype(np.float32) * np.float32(std))
     x = bf(T, D)
@@ -153,7 +154,7 @@ def tiny_layer(seed, T, D, E, k, F, fmt, wstd=0.3, bstd=0.2, br_std=0.5):
         def mx8(rows, K):
             codes = g.integers(0, 256, E * rows * K, dtype=np.uint8)
             codes[(codes & 0x7F) == 0x7F] -= 1               # no NaN codes
-            scales = g.integers(115, 119, E * rows * K // 32, dtype=np.uint8)
+            scales = g.integers(mx8_scales[0], mx8_scales[1], E * rows * K // 32, dtype=np.uint8)
             return np.concatenate([codes, scales])
         w1, w2 = mx8(2 * F, D), mx8(D, F)
     else:
@@ -472,17 +473,23 @@ def test_swiglu_gate_is_gelu_like():
 @pytest.mark.parametrize("fmt", ["bf16", "mxfp4", "mxfp8"])
 @pytest.mark.parametrize("T,D,E,k,F,seed", [(12, 32, 4, 2, 32, 0), (9, 64, 6, 3, 64, 1), (5, 32, 3, 3, 32, 2)])
 def test_block_equals_dense_masked_mixture(fmt, T, D, E, k, F, seed):
-    """Permuted/grouped oracle == every-expert-on-every-token masked softmax mixture (1e-12)."""
-    layer = tiny_layer(seed, T, D, E, k, F, fmt)
+    """Permuted/grouped oracle == every-expert-on-every-token masked softmax mixture (1e-12), on
+    layers whose weights put some SwiGLU inputs past the clamps."""
+    layer = tiny_layer(seed, T, D, E, k, F, fmt, wstd=5.0 / np.sqrt(D), mx8_scales=(119, 123))
     out, r = moe_forward(*layer, k=k, F=F, fmt=fmt, return_routing=True)
     ref, l, mask = dense_reference(*layer, k=k, F=F, fmt=fmt)
     assert np.array_equal(r["logits"], l.astype(np.float32))
     assert np.array_equal(np.sort(r["idx"], axis=1), np.array([np.flatnonzero(m) for m in mask]))
     scale = np.max(np.abs(ref))
     assert np.max(np.abs(out - ref)) <= 1e-12 * scale
-    # the SwiGLU clamps were exercised
-    u_max = np.abs(ref).max()
-    assert u_max > 0
+    # the SwiGLU clamps were exercised on the routed pairs: some gate input above the limit,
+    # some linear input past it on each side
+    xf = bf16_to_f64(layer[0])
+    W1 = np.stack([expert_weight(layer[3], fmt, E, 2 * F, D, e) for e in range(E)])
+    u = np.einsum("td,egd->teg", xf, W1) + bf16_to_f64(layer[4]).reshape(E, 2 * F)[None]
+    routed = u[mask]                                   # [T*k, 2F]
+    assert (routed[:, :F] > SWIGLU_LIMIT).any()
+    assert (routed[:, F:] > SWIGLU_LIMIT).any() and (routed[:, F:] < -SWIGLU_LIMIT).any()
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "mxfp4"])
