@@ -126,6 +126,23 @@ int moe_forward(const void* x, const void* router_w, const void* router_b,
                 int64_t T, int64_t D, int64_t E, int64_t k, int64_t F,
                 int fmt, float* out);
 
+/* moe_forward for callers that cannot allocate device memory: code being captured into a
+ * HIP graph, tight serving loops, harnesses that forbid hipMalloc.  Same arguments, same
+ * kernels and bitwise the same result as moe_forward, but the intermediates live in a fixed
+ * scratch array of MOE_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends, instead of the workspace: no hipMalloc, hipFree or allocating call
+ * is made.  A shape whose intermediates exceed the scratch (moe_workspace_bytes) fails with
+ * MOE_ENOMEM before any launch; at the 20B shape (D = F = 2880, 32 experts, top-4) that is
+ * above 873 tokens with bf16 weights and above 671 with MXFP4 or MXFP8 ones.  All calls on one GPU share its scratch
+ * array: calls that overlap in time on that GPU (other streams, other threads) race on it and
+ * must be serialised.  Nothing in the scratch needs to start at zero; it keeps the last call's
+ * intermediates.  Not timed by moe_profile_*. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_forward_noalloc(const void* x, const void* router_w, const void* router_b,
+                        const void* w1, const void* b1, const void* w2, const void* b2,
+                        int64_t T, int64_t D, int64_t E, int64_t k, int64_t F,
+                        int fmt, float* out);
+
 /* Steps 1-4 only (routing stage; its integer outputs are exact).
  *   logits   fp32 [T][E] or NULL     topk_idx int32 [T][k]    gates fp32 [T][k]
  *   counts   int32 [E]               offsets  int32 [E+1]     perm  int32 [T*k]

@@ -10,6 +10,7 @@ from .moe import (  # noqa: F401
     MoEError,
     experts,
     forward,
+    forward_noalloc,
     lib,
     mxfp4_bytes,
     mxfp8_bytes,

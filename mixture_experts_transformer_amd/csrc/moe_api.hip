@@ -19,6 +19,7 @@ namespace {
 
 thread_local std::string g_err;
 thread_local hipStream_t g_stream = nullptr;
+thread_local bool t_noalloc = false;       // inside moe_forward_noalloc: no event bracketing
 
 // Library-owned workspace, shared by the threads that have not set their own.  Once a call
 // has run on a capturing stream, captured graphs may hold its address: from then on a
@@ -32,6 +33,19 @@ struct Workspace {
   std::vector<void*> retired;              // earlier buffers captured graphs may still use
 };
 Workspace g_ws;
+
+// Scratch of the allocation-free entry point: a file-scope device array, one copy per GPU
+// that loads the library, held until the process ends.  In host code `scratch` names a
+// host-side stand-in, never the device memory: its device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and only that
+// address is passed to kernels.
+__device__ __attribute__((aligned(256))) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+struct ScratchTable {
+  std::mutex mu;
+  std::vector<uint8_t*> ptr;               // per device ordinal; null until looked up
+};
+ScratchTable g_scratch;
 
 // Caller-owned workspace of the calling thread (moe_set_workspace).
 struct UserWorkspace {
@@ -196,7 +210,7 @@ int launch(int stage, const char* name, F&& fn) {
   bool prof = false;
   {
     std::lock_guard<std::mutex> lk(g_prof.mu);
-    if (g_prof.on) {
+    if (g_prof.on && !t_noalloc) {
       if (g_prof.used == g_prof.start.size()) {
         hipEvent_t s0, s1;
         if (hipEventCreate(&s0) != hipSuccess || hipEventCreate(&s1) != hipSuccess)
@@ -287,10 +301,29 @@ int run_experts(const uint8_t* ws, const Layout& L, const void* x, const void* w
   return MOE_OK;
 }
 
+// Device address of the current device's scratch array (looked up on the first call on
+// that device).
+int scratch_ptr(uint8_t** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) return fail(MOE_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(g_scratch.mu);
+  if ((size_t)dev >= g_scratch.ptr.size()) g_scratch.ptr.resize((size_t)dev + 1, nullptr);
+  if (!g_scratch.ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MOE_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch.ptr[dev] = (uint8_t*)p;
+  }
+  *out = g_scratch.ptr[dev];
+  return MOE_OK;
+}
+
 // Whole block; ebias is the load-balancing bias when `biased` (then it must be valid).
 int forward_impl(const void* x, const void* router_w, const void* router_b, bool biased, const float* ebias,
                  const void* w1, const void* b1, const void* w2, const void* b2, int64_t T, int64_t D, int64_t E,
-                 int64_t k, int64_t F, int fmt, float* out) {
+                 int64_t k, int64_t F, int fmt, float* out, bool noalloc = false) {
   CHECK(check_shapes(T, D, E, k, F, true));
   if (!valid_fmt(fmt)) return fail(MOE_EFMT, "unknown weight format %d", fmt);
   if (T == 0) return ok();
@@ -305,7 +338,16 @@ int forward_impl(const void* x, const void* router_w, const void* router_b, bool
   CHECK(check_ptr(out, "out"));
   const Layout L = layout(T, D, E, k, F, fmt, NEED_ROUTE | NEED_ROUTE_OUTPUTS | NEED_EXPERTS);
   uint8_t* ws = nullptr;
-  CHECK(ensure_workspace(L.total, &ws));
+  if (noalloc) {
+    if (L.total > MOE_NOALLOC_SCRATCH_BYTES)
+      return fail(MOE_ENOMEM,
+                  "moe_forward_noalloc: this shape needs %zu bytes of scratch, the fixed scratch holds %zu "
+                  "(use moe_forward, or fewer tokens)",
+                  L.total, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+    CHECK(scratch_ptr(&ws));
+  } else {
+    CHECK(ensure_workspace(L.total, &ws));
+  }
   int32_t* idx = (int32_t*)(ws + L.idx);
   float* gates = (float*)(ws + L.gates);
   int32_t* counts = (int32_t*)(ws + L.counts);
@@ -347,6 +389,15 @@ int moe_forward(const void* x, const void* router_w, const void* router_b, const
                 const void* b1, const void* w2, const void* b2, int64_t T, int64_t D, int64_t E,
                 int64_t k, int64_t F, int fmt, float* out) {
   return forward_impl(x, router_w, router_b, false, nullptr, w1, b1, w2, b2, T, D, E, k, F, fmt, out);
+}
+
+int moe_forward_noalloc(const void* x, const void* router_w, const void* router_b, const void* w1,
+                        const void* b1, const void* w2, const void* b2, int64_t T, int64_t D, int64_t E,
+                        int64_t k, int64_t F, int fmt, float* out) {
+  t_noalloc = true;
+  const int rc = forward_impl(x, router_w, router_b, false, nullptr, w1, b1, w2, b2, T, D, E, k, F, fmt, out, true);
+  t_noalloc = false;
+  return rc;
 }
 
 int moe_forward_biased(const void* x, const void* router_w, const void* router_b, const float* expert_bias,

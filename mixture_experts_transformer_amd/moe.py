@@ -25,6 +25,7 @@ _i64 = ctypes.c_int64
 _SIGNATURES = {
     "moe_forward": (ctypes.c_int, [_c_void_p] * 7 + [_i64] * 5 + [ctypes.c_int, _c_void_p]),
     "moe_route": (ctypes.c_int, [_c_void_p] * 3 + [_i64] * 4 + [_c_void_p] * 6),
+    "moe_forward_noalloc": (ctypes.c_int, [_c_void_p] * 7 + [_i64] * 5 + [ctypes.c_int, _c_void_p]),
     "moe_forward_biased": (ctypes.c_int, [_c_void_p] * 8 + [_i64] * 5 + [ctypes.c_int, _c_void_p]),
     "moe_route_biased": (ctypes.c_int, [_c_void_p] * 4 + [_i64] * 4 + [_c_void_p] * 6),
     "moe_update_expert_bias": (ctypes.c_int, [_c_void_p, _i64, ctypes.c_float, _c_void_p]),
@@ -149,6 +150,26 @@ def forward(x, router_w, router_b, w1, b1, w2, b2, k: int, fmt: str = "bf16",
         _check(lib().moe_forward_biased(_ptr(x), _ptr(router_w), _ptr(router_b), _ptr(expert_bias), _ptr(w1),
                                         _ptr(b1), _ptr(w2), _ptr(b2), T, D, E, k, F, FMT[fmt], _ptr(out)),
                "moe_forward_biased")
+    return out
+
+
+def forward_noalloc(x, router_w, router_b, w1, b1, w2, b2, k: int, fmt: str = "bf16",
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``forward`` through ``moe_forward_noalloc``: the library allocates nothing (its
+    intermediates live in a fixed per-GPU scratch array; shapes that do not fit raise
+    ``MoEError`` with MOE_ENOMEM).  Pass ``out`` to allocate nothing here either."""
+    T, D = x.shape
+    E = router_w.shape[0]
+    F = b1.shape[-1] // 2
+    _dev(x, "x", 2), _dev(router_w, "router_w", 2), _dev(router_b, "router_b", 2)
+    _dev(b1, "b1", 2), _dev(b2, "b2", 2)
+    _check_weights(w1, w2, E, D, F, fmt)
+    if out is None:
+        out = torch.empty((T, D), dtype=torch.float32, device=x.device)
+    _dev(out, "out", 4)
+    _bind_stream(x.device)
+    _check(lib().moe_forward_noalloc(_ptr(x), _ptr(router_w), _ptr(router_b), _ptr(w1), _ptr(b1), _ptr(w2),
+                                     _ptr(b2), T, D, E, k, F, FMT[fmt], _ptr(out)), "moe_forward_noalloc")
     return out
 
 
