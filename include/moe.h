@@ -194,6 +194,41 @@ int moe_experts(const void* x, const void* w1, const void* b1, const void* w2, c
                 int64_t T, int64_t D, int64_t E, int64_t k, int64_t F,
                 int fmt, float* out);
 
+/* Gradients of the block (bf16 expert weights only), with the routing of the forward held
+ * fixed: the torchtitan guide's grouped GEMM section trains this block and unit-tests the
+ * gradient of its SwiGLU variant.  The top-k selection is piecewise constant, so gradients
+ * reach the router through the softmax gates only, and never the load-balancing bias.
+ * Readings: a clamp passes the gradient where its input lies inside the closed interval
+ * (gate <= LIMIT; -LIMIT <= linear <= LIMIT); the logits are differentiated as exact reals.
+ *   inputs   x, router_w, w1, b1, w2, b2 as in moe_forward (fmt must be MOE_FMT_BF16; the
+ *            router bias is not needed); topk_idx int32 [T][k], gates fp32 [T][k], offsets
+ *            int32 [E+1], perm int32 [T*k]: the routing of the forward as moe_route returns it;
+ *            dout fp32 [T][D], the gradient of the loss with respect to out.
+ *   outputs  (fp32, fully overwritten) dx [T][D], d_router_w [E][D], d_router_b [E],
+ *            dw1 [E][2F][D], db1 [E][2F], dw2 [E][D][F], db2 [E][D].
+ * Per assignment a = t*k + j with expert e and gate g, u = x W1[e]^T + b1[e] is recomputed;
+ * dz = g dout[t] gives dW2[e] += dz^T h and db2[e] += dz; du = SwiGLU'(u) (dz W2[e]) gives
+ * dW1[e] += du^T x[t], db1[e] += du and dx[t] += du W1[e]; dg = <dout[t], h W2[e]^T + b2[e]>;
+ * the softmax over the selected logits gives dl = g (dg - sum_j g_j dg_j), then
+ * d_router_w[e] += dl x[t], d_router_b[e] += dl and dx[t] += dl router_w[e].  The matrix
+ * products run on the bf16 matrix cores with fp32 accumulation: dout enters the product with
+ * W2 as a bf16 pair (hi + lo, about 16 significant bits), while dz, du and h enter theirs
+ * rounded to bf16, which bounds the relative error of each gradient near 2^-9; every sum has
+ * a fixed order, so the result is bitwise reproducible.  With
+ * T = 0 the parameter gradients are set to zero.  Uses moe_backward_workspace_bytes of
+ * workspace (the same workspace rules as the forward).  Timed as stage 7 by moe_profile_*. */
+int moe_backward(const void* x, const void* router_w, const void* w1, const void* b1,
+                 const void* w2, const void* b2,
+                 const int32_t* topk_idx, const float* gates, const int32_t* offsets, const int32_t* perm,
+                 const float* dout,
+                 int64_t T, int64_t D, int64_t E, int64_t k, int64_t F, int fmt,
+                 float* dx, float* d_router_w, float* d_router_b,
+                 float* dw1, float* db1, float* dw2, float* db2);
+
+/* Device bytes of workspace a moe_backward call of this shape needs (0 for T == 0 or a
+ * format the backward does not take). */
+size_t moe_backward_workspace_bytes(int64_t T, int64_t D, int64_t E, int64_t k, int64_t F, int fmt);
+
 /* Stream for the calling thread's subsequent calls (a hipStream_t; NULL = default stream). */
 int moe_set_stream(void* hip_stream);
 
@@ -219,9 +254,10 @@ void moe_release(void);
  * call's stream, and each kernel's summed device time and launch count accumulate per
  * stage.  Stages: 0 router, 1 top-k, 2 permute, 3 mlp1, 4 mlp2, 5 combine, 6 split (the
  * fp8 pieces of the activations that the scaled matrix-core engine reads; MXFP4 weights
- * at large token counts only).  moe_profile_read synchronises on the recorded events; it
- * fills ms[7] and launches[7] (either may be NULL) and resets the counters. */
-#define MOE_NUM_STAGES 7
+ * at large token counts only), 7 backward (a whole moe_backward call).  moe_profile_read
+ * synchronises on the recorded events; it fills ms[8] and launches[8] (either may be NULL)
+ * and resets the counters. */
+#define MOE_NUM_STAGES 8
 int moe_profile_enable(int on);
 int moe_profile_read(double* ms, int64_t* launches);
 

@@ -8,6 +8,8 @@ from .moe import (  # noqa: F401
     LIB_PATH,
     STAGES,
     MoEError,
+    backward,
+    backward_workspace_bytes,
     experts,
     forward,
     forward_noalloc,

@@ -17,7 +17,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["route.hip", "gemm.hip", "moe_api.hip"]
+SOURCES = ["route.hip", "gemm.hip", "backward.hip", "moe_api.hip"]
 ARCH = "gfx950"
 
 

@@ -1,0 +1,732 @@
+// Backward of the GPT-OSS MoE block on gfx950 (bf16 expert weights), with the top-k
+// selection of the forward held fixed.
+//
+// torchtitan GPT-OSS guide, section "Grouped matrix multiplication": the block is trained,
+// and the gradient of its SwiGLU variant is unit tested against a reference.  The selection
+// is piecewise constant in the inputs, so gradients reach the router only through the
+// softmax gates.  Per assignment a = t*k + j (expert e, gate g, row p of e's group):
+//
+//   u  = x[t] W1[e]^T + b1[e]                          (recomputed: grouped GEMM, K = D)
+//   dh' = dout[t] W2[e]                                 (grouped GEMM, K = D; ungated)
+//   dg[a] = <dh', h(u)> + <dout[t], b2[e]>              (= <dout[t], z[a]>, z the ungated mlp2 output)
+//   du = SwiGLU'(u) * (g dh')                           (in that GEMM's epilogue)
+//   dx[t] += du W1[e]                                   (grouped GEMM, K = 2F)
+//   dW2[e] = sum_p (g dout[t])^T h,  dW1[e] = sum_p du^T x[t]   (per-expert GEMMs, K = rows)
+//   db2[e] = sum_p g dout[t],  db1[e] = sum_p du
+//   router: dl = g (dg - sum_j g_j dg_j) on the selected experts; dWr[e] = sum dl x[t],
+//   dbr[e] = sum dl, dx[t] += sum_j dl_j Wr[e_j].
+//
+// Every matrix product runs on v_mfma_f32_32x32x16_bf16 in one kernel (bwd_gemm_kernel)
+// whose operands are K-contiguous rows: the weights are transposed once per call for the
+// two products that contract over their other dimension, and the activations that the
+// weight-gradient products contract over their rows are written transposed, per expert, in
+// a layout whose expert blocks are padded to 64 rows with zeros.  No float atomics: every
+// sum runs in a fixed order, so the gradients are bitwise reproducible.
+#include "device_common.h"
+
+namespace moe {
+
+namespace {
+
+constexpr float BW_ALPHA = 1.702f;
+constexpr float BW_LIMIT = 7.0f;
+constexpr float BW_NEG_ALPHA_LOG2E = -BW_ALPHA * 1.4426950408889634f;
+
+// ------------------------------------------------------------------------------ GEMM tile
+// 256 x 128 outputs per workgroup, 8 waves in a 4 x 2 grid of 64 x 64, K in steps of 64
+// (whole 128-byte row segments per stage), two LDS stages filled through registers.
+constexpr int BG_BM = 256, BG_BN = 128, BG_BK = 64, BG_CPR = BG_BK / 8;
+constexpr int BG_WAVES_M = 4, BG_WAVES_N = 2, BG_NW = BG_WAVES_M * BG_WAVES_N, BG_THREADS = 64 * BG_NW;
+constexpr int BG_WTM = BG_BM / BG_WAVES_M, BG_WTN = BG_BN / BG_WAVES_N;
+constexpr int BG_FM = BG_WTM / 32, BG_FN = BG_WTN / 32;
+constexpr int BG_A_BYTES = BG_BM * BG_BK * 2;
+constexpr int BG_B_BYTES = BG_BN * BG_BK * 2;
+constexpr int BG_STAGE = BG_A_BYTES + BG_B_BYTES;
+constexpr int BG_ALD = BG_BM * BG_CPR / BG_THREADS;   // 16-byte A chunks per thread and stage
+constexpr int BG_BLD = BG_BN * BG_CPR / BG_THREADS;   // B chunks
+static_assert(BG_ALD * BG_THREADS == BG_BM * BG_CPR && BG_BLD * BG_THREADS == BG_BN * BG_CPR, "load split");
+
+enum BwdMode { BW_RECOMP = 0, BW_DGRAD2 = 1, BW_DGRAD1 = 2, BW_WGRAD = 3 };
+
+struct BwdGemmArgs {
+  const int32_t* offsets;   // [E+1] group offsets of the routed rows (grouped modes)
+  const int32_t* perm;      // [A] assignment of each routed row
+  const float* gates;       // [A] gate of each assignment
+  const int32_t* poff;      // [E+1] padded column offsets (weight-gradient mode)
+  const uint16_t* a;        // A operand rows (bf16, K contiguous), lda elements apart
+  const uint16_t* b;        // B operand rows, ldb elements apart; grouped modes: expert e's
+  int64_t b_expert;         //   rows start b_expert elements after expert e - 1's
+  int lda, ldb;
+  int E, k, A, K, M, N, F;
+  int n_tiles, m_tiles;
+  int kwrap;                // dgrad2: K stages after which B's K offset starts again (A = [hi | lo])
+  const uint16_t* bias;     // recompute: b1 [E][N]
+  float* c;                 // recompute: u [A][N]; dgrad1: [A][N] at slot rows; wgrad: [E][M][N]
+  const float* u;           // dgrad2: u [A][2F]
+  uint16_t* h;              // dgrad2: h [A][F]
+  uint16_t* du;             // dgrad2: du [A][2F]
+  float* dgpart;            // dgrad2: [n_tiles][A] partial <dh', h> per column tile
+};
+
+// MODE selects the operands and the epilogue:
+//   BW_RECOMP  A = x rows gathered by token, B = W1[e] rows (K = D): u = acc + b1 -> c (fp32)
+//   BW_DGRAD2  A = dout rows gathered by token as a bf16 pair [hi | lo] (K = 2D), B = W2^T[e]
+//              rows read twice (K offset modulo D): dh' = acc to about 16 significant bits of
+//              dout; writes h, du (bf16) and the per-tile partial <dh', h>
+//   BW_DGRAD1  A = du rows in place, B = W1^T[e] rows (K = 2F): acc -> c at the slot row
+//   BW_WGRAD   per expert: A = rows of a transposed activation, B = rows of another (K =
+//              the expert's padded row count): acc -> dW[e]
+//
+// Matrix-core mapping as in the forward's grouped GEMM: in MFMA step ks of a stage, lane l
+// feeds row l & 31 and the 8 K elements of chunk 4 (l >> 5) + ks of each operand, and output
+// register q of lane l is C[8 (q >> 2) + 4 (l >> 5) + (q & 3)][l & 31].
+template <int MODE>
+__global__ __launch_bounds__(BG_THREADS, 1) void bwd_gemm_kernel(BwdGemmArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BG_STAGE];
+  __shared__ int tab_a[BG_BM];
+  __shared__ float tab_g[BG_BM];
+  __shared__ float red[BG_WAVES_N][BG_BM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / BG_WAVES_N, wn = wave % BG_WAVES_N;
+  const int kg = lane >> 5;
+
+  // ---- which tile: the tiles that exist, XCD x (block ids congruent to x mod 8) taking the
+  // x-th eighth of them, in groups of four row tiles so neighbouring workgroups share rows
+  int e = 0, row0 = 0, rows = 0, gbase = 0, m0 = 0, n_tile = 0, K = p.K;
+  {
+    constexpr int GM = 4;
+    int total, mt_total;
+    TileScan ts;
+    if (MODE == BW_WGRAD) {
+      mt_total = p.E * p.m_tiles;
+    } else {
+      ts = tile_scan<BG_BM>(p.offsets, p.E);
+      mt_total = ts.total;
+    }
+    total = mt_total * p.n_tiles;
+    const int share = (total + 7) >> 3;
+    const int xl = blockIdx.x >> 3;
+    const int lin = (blockIdx.x & 7) * share + xl;
+    if (xl >= share || lin >= total) return;
+    const int gsize = GM * p.n_tiles;
+    const int g = lin / gsize;
+    const int first_m = g * GM;
+    const int gm = min(mt_total - first_m, GM);
+    const int m_tile = first_m + (lin % gsize) % gm;
+    n_tile = (lin % gsize) / gm;
+    if (MODE == BW_WGRAD) {
+      e = m_tile / p.m_tiles;
+      m0 = (m_tile % p.m_tiles) * BG_BM;
+      rows = min(BG_BM, p.M - m0);
+      K = p.poff[e + 1] - p.poff[e];
+    } else {
+      int cnt;
+      if (!tile_lookup<BG_BM>(ts, p.offsets, m_tile, e, row0, cnt)) return;
+      gbase = p.offsets[e] + row0;
+      rows = min(BG_BM, cnt - row0);
+      if (gbase < 0 || rows <= 0 || gbase + rows > p.A) return;
+    }
+  }
+  const int n0 = n_tile * BG_BN;
+  const int nk = K / BG_BK;
+
+  // routed rows of the tile: assignment and gate (grouped modes)
+  if (MODE != BW_WGRAD && tid < BG_BM) {
+    int a = -1;
+    float g = 0.f;
+    if (tid < rows) {
+      a = p.perm[gbase + tid];
+      a = ((unsigned)a < (unsigned)p.A) ? a : -1;
+      if (MODE == BW_DGRAD2 && a >= 0) g = p.gates[a];
+    }
+    tab_a[tid] = a;
+    tab_g[tid] = g;
+  }
+
+  // ---- this thread's copy rows: chunk c of tile rows (tid / CPR) + (THREADS / CPR) j
+  const int cch = tid % BG_CPR;
+  const uint16_t* arow[BG_ALD];
+  const uint16_t* brow[BG_BLD];
+  int ar[BG_ALD], br[BG_BLD];
+#pragma unroll
+  for (int j = 0; j < BG_ALD; ++j) {
+    const int r = tid / BG_CPR + (BG_THREADS / BG_CPR) * j;
+    ar[j] = r;
+    int64_t src;
+    if (MODE == BW_WGRAD) {
+      src = (int64_t)min(m0 + r, p.M - 1) * p.lda + p.poff[e];
+    } else {
+      const int rc = min(r, rows - 1);
+      if (MODE == BW_DGRAD1) {
+        src = (int64_t)(gbase + rc) * p.lda;
+      } else {
+        int asg = p.perm[gbase + rc];
+        asg = ((unsigned)asg < (unsigned)p.A) ? asg : 0;
+        src = (int64_t)(asg / p.k) * p.lda;
+      }
+    }
+    arow[j] = p.a + src + cch * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < BG_BLD; ++j) {
+    const int r = tid / BG_CPR + (BG_THREADS / BG_CPR) * j;
+    br[j] = r;
+    const int n = min(n0 + r, p.N - 1);
+    if (MODE == BW_WGRAD) brow[j] = p.b + (int64_t)n * p.ldb + p.poff[e] + cch * 8;
+    else brow[j] = p.b + (int64_t)e * p.b_expert + (int64_t)n * p.ldb + cch * 8;
+  }
+
+  f32x16 acc[BG_FM][BG_FN];
+#pragma unroll
+  for (int i = 0; i < BG_FM; ++i)
+#pragma unroll
+    for (int j = 0; j < BG_FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  // stage kt of this thread's rows into registers, and registers into LDS slot s (macros, not
+  // lambdas: a call that is not inlined would leave the staging arrays in memory)
+  u32x4 ra[BG_ALD], rb[BG_BLD];
+#define BW_GLOAD(kt)                                                                             \
+  do {                                                                                           \
+    const int ko_ = (kt) * BG_BK;                                                                \
+    const int kb_ = MODE == BW_DGRAD2 ? ((kt) % p.kwrap) * BG_BK : ko_;                          \
+    _Pragma("unroll") for (int j = 0; j < BG_ALD; ++j) ra[j] = *(const u32x4*)(arow[j] + ko_);   \
+    _Pragma("unroll") for (int j = 0; j < BG_BLD; ++j) rb[j] = *(const u32x4*)(brow[j] + kb_);   \
+  } while (0)
+#define BW_LSTORE(slot)                                                                          \
+  do {                                                                                           \
+    uint8_t* s_ = smem + (slot) * BG_STAGE;                                                      \
+    _Pragma("unroll") for (int j = 0; j < BG_ALD; ++j)                                           \
+      *(u32x4*)(s_ + swz<BG_CPR>(ar[j], cch)) = ra[j];                                           \
+    _Pragma("unroll") for (int j = 0; j < BG_BLD; ++j)                                           \
+      *(u32x4*)(s_ + BG_A_BYTES + swz<BG_CPR>(br[j], cch)) = rb[j];                              \
+  } while (0)
+
+  // a wave whose 64 rows are all padding skips its matrix instructions
+  const bool active = wm * BG_WTM < rows;
+  const int arow0 = wm * BG_WTM + (lane & 31);
+  const int brow0 = wn * BG_WTN + (lane & 31);
+  if (nk > 0) {
+    BW_GLOAD(0);
+    BW_LSTORE(0);
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    __syncthreads();                       // stage kt landed; stage kt + 1's slot is free
+    if (kt + 1 < nk) BW_GLOAD(kt + 1);
+    if (active) {
+      const uint8_t* sa = smem + (kt & 1) * BG_STAGE;
+      const uint8_t* sb = sa + BG_A_BYTES;
+#pragma unroll
+      for (int ks = 0; ks < BG_BK / 16; ++ks) {
+        const int cc = kg * (BG_BK / 16) + ks;
+        bf16x8 fa[BG_FM], fb[BG_FN];
+#pragma unroll
+        for (int i = 0; i < BG_FM; ++i) fa[i] = *(const bf16x8*)(sa + swz<BG_CPR>(arow0 + 32 * i, cc));
+#pragma unroll
+        for (int j = 0; j < BG_FN; ++j) fb[j] = *(const bf16x8*)(sb + swz<BG_CPR>(brow0 + 32 * j, cc));
+#pragma unroll
+        for (int i = 0; i < BG_FM; ++i)
+#pragma unroll
+          for (int j = 0; j < BG_FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    if (kt + 1 < nk) BW_LSTORE((kt + 1) & 1);
+  }
+#undef BW_GLOAD
+#undef BW_LSTORE
+  __syncthreads();                         // tab_a / tab_g visible (also when nk == 0)
+
+  // ---- epilogue.  Row rr of the tile for register q of fragment i; column cc for fragment j.
+  if (MODE == BW_RECOMP) {
+#pragma unroll
+    for (int j = 0; j < BG_FN; ++j) {
+      const int n = n0 + wn * BG_WTN + 32 * j + (lane & 31);
+      if (n >= p.N) continue;
+      const float bv = bf16_to_f32(p.bias[(int64_t)e * p.N + n]);
+#pragma unroll
+      for (int i = 0; i < BG_FM; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int rr = wm * BG_WTM + 32 * i + 8 * (q >> 2) + 4 * kg + (q & 3);
+          if (rr < rows) p.c[(int64_t)(gbase + rr) * p.N + n] = acc[i][j][q] + bv;
+        }
+    }
+  } else if (MODE == BW_DGRAD1) {
+#pragma unroll
+    for (int j = 0; j < BG_FN; ++j) {
+      const int n = n0 + wn * BG_WTN + 32 * j + (lane & 31);
+      if (n >= p.N) continue;
+#pragma unroll
+      for (int i = 0; i < BG_FM; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int rr = wm * BG_WTM + 32 * i + 8 * (q >> 2) + 4 * kg + (q & 3);
+          if (rr < rows) {
+            const int a = tab_a[rr];
+            if (a >= 0) p.c[(int64_t)a * p.N + n] = acc[i][j][q];
+          }
+        }
+    }
+  } else if (MODE == BW_WGRAD) {
+    float* const dst = p.c + (int64_t)e * p.M * p.N;
+#pragma unroll
+    for (int j = 0; j < BG_FN; ++j) {
+      const int n = n0 + wn * BG_WTN + 32 * j + (lane & 31);
+      if (n >= p.N) continue;
+#pragma unroll
+      for (int i = 0; i < BG_FM; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int rr = wm * BG_WTM + 32 * i + 8 * (q >> 2) + 4 * kg + (q & 3);
+          if (rr < rows) dst[(int64_t)(m0 + rr) * p.N + n] = acc[i][j][q];
+        }
+    }
+  } else {
+    // dgrad2: acc = dh'[row][f] = dout[t] . W2[e][:, f]; the clamped SwiGLU of u gives h and
+    // its two partial derivatives, du = SwiGLU' * g dh', and each row's <dh', h> over this
+    // tile's columns (summed across lanes and waves in a fixed order)
+    const int F = p.F;
+    const int64_t ldu = 2 * (int64_t)F;
+    float rs[BG_FM][16];
+#pragma unroll
+    for (int i = 0; i < BG_FM; ++i)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) rs[i][q] = 0.f;
+#pragma unroll
+    for (int j = 0; j < BG_FN; ++j) {
+      const int f = n0 + wn * BG_WTN + 32 * j + (lane & 31);
+      if (f >= F) continue;
+#pragma unroll
+      for (int i = 0; i < BG_FM; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int rr = wm * BG_WTM + 32 * i + 8 * (q >> 2) + 4 * kg + (q & 3);
+          if (rr >= rows) continue;
+          const int64_t prow = gbase + rr;
+          const float ug = p.u[prow * ldu + f];
+          const float ul = p.u[prow * ldu + F + f];
+          const float gc = fminf(ug, BW_LIMIT);
+          const float lc = fminf(fmaxf(ul, -BW_LIMIT), BW_LIMIT);
+          // sigmoid(ALPHA gc) = 1 / (1 + 2^(-ALPHA log2(e) gc))
+          const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(gc * BW_NEG_ALPHA_LOG2E));
+          const float hv = gc * s * (lc + 1.0f);
+          const float dhp = acc[i][j][q];
+          rs[i][q] += dhp * hv;
+          const float dh = tab_g[rr] * dhp;
+          const float dgc = s + BW_ALPHA * gc * s * (1.0f - s);      // d(gc sigma(ALPHA gc)) / d gc
+          const float dug = (ug <= BW_LIMIT) ? dh * dgc * (lc + 1.0f) : 0.f;
+          const float dul = (ul >= -BW_LIMIT && ul <= BW_LIMIT) ? dh * gc * s : 0.f;
+          const __bf16 hb = (__bf16)hv, gb = (__bf16)dug, lb = (__bf16)dul;
+          p.h[prow * F + f] = *(const uint16_t*)&hb;
+          p.du[prow * ldu + f] = *(const uint16_t*)&gb;
+          p.du[prow * ldu + F + f] = *(const uint16_t*)&lb;
+        }
+    }
+    // row sums over the 32 columns a lane half holds, then across the two column waves
+#pragma unroll
+    for (int i = 0; i < BG_FM; ++i)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        float v = rs[i][q];
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 8);
+        v += __shfl_xor(v, 4);
+        v += __shfl_xor(v, 2);
+        v += __shfl_xor(v, 1);
+        if ((lane & 31) == 0) red[wn][wm * BG_WTM + 32 * i + 8 * (q >> 2) + 4 * kg + (q & 3)] = v;
+      }
+    __syncthreads();
+    if (tid < BG_BM && tid < rows) {
+      const int a = tab_a[tid];
+      float v = red[0][tid];
+#pragma unroll
+      for (int w = 1; w < BG_WAVES_N; ++w) v += red[w][tid];
+      if (a >= 0) p.dgpart[(int64_t)n_tile * p.A + a] = v;
+    }
+  }
+}
+
+template <int MODE>
+hipError_t launch_bwd_gemm(BwdGemmArgs g, int64_t max_row_tiles, hipStream_t st) {
+  const int64_t tiles = (MODE == BW_WGRAD ? (int64_t)g.E * g.m_tiles : max_row_tiles) * g.n_tiles;
+  const int64_t blocks = (tiles + 7) / 8 * 8;
+  hipLaunchKernelGGL(bwd_gemm_kernel<MODE>, dim3((unsigned)blocks), dim3(BG_THREADS), 0, st, g);
+  return hipGetLastError();
+}
+
+int64_t row_tiles_bound(int64_t A, int E) {
+  int64_t m = (A + (int64_t)E * (BG_BM - 1)) / BG_BM;
+  return m > A ? A : m;
+}
+
+// ------------------------------------------------------------------------------ routing helpers
+// Padded column offsets of the experts in the transposed activations: expert e's rows
+// occupy columns [poff[e], poff[e + 1]), its count rounded up to a multiple of 64.
+__global__ __launch_bounds__(256) void pad_offsets_kernel(const int32_t* __restrict__ offsets, int E,
+                                                          int32_t* __restrict__ poff) {
+  __shared__ int s[257];
+  const int tid = threadIdx.x;
+  if (tid < E) {
+    const int c = offsets[tid + 1] - offsets[tid];
+    s[tid + 1] = (max(c, 0) + BG_BK - 1) / BG_BK * BG_BK;
+  }
+  if (tid == 0) s[0] = 0;
+  __syncthreads();
+  if (tid == 0)
+    for (int i = 1; i <= E; ++i) s[i] += s[i - 1];
+  __syncthreads();
+  for (int i = tid; i <= E; i += 256) poff[i] = s[i];
+}
+
+// padmap[col] = routed row p in column col of the transposed layout, or -1 for padding.
+__global__ __launch_bounds__(256) void pad_map_kernel(const int32_t* __restrict__ offsets,
+                                                      const int32_t* __restrict__ poff, int E, int ldt,
+                                                      int32_t* __restrict__ padmap) {
+  const int col = blockIdx.x * 256 + threadIdx.x;
+  if (col >= ldt) return;
+  int lo = 0, hi = E;                      // the expert e with poff[e] <= col < poff[e + 1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (poff[mid] <= col) lo = mid;
+    else hi = mid;
+  }
+  int v = -1;
+  if (col < poff[E]) {
+    const int r = col - poff[lo];
+    if (r < offsets[lo + 1] - offsets[lo]) v = offsets[lo] + r;
+  }
+  padmap[col] = v;
+}
+
+// ------------------------------------------------------------------------------ conversions
+// fp32 rows [rows][D] -> bf16 pairs [rows][2D]: the first D the nearest bf16 (hi), the next D
+// the nearest bf16 of what hi leaves (lo), so hi + lo holds about 16 significant bits.
+static __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const __bf16 x = (__bf16)a, y = (__bf16)b;
+  return (uint32_t)*(const uint16_t*)&x | ((uint32_t)*(const uint16_t*)&y << 16);
+}
+__global__ __launch_bounds__(256) void f32_to_bf16_pair_kernel(const float4* __restrict__ src, int64_t rows,
+                                                               int D4, uint2* __restrict__ dst) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * D4) return;
+  const int64_t r = i / D4;
+  const int c = (int)(i - r * D4);
+  const float4 v = src[i];
+  const float h0 = (float)(__bf16)v.x, h1 = (float)(__bf16)v.y, h2 = (float)(__bf16)v.z, h3 = (float)(__bf16)v.w;
+  uint2* const row = dst + r * 2 * D4;
+  row[c] = uint2{pack_bf16x2(h0, h1), pack_bf16x2(h2, h3)};
+  row[D4 + c] = uint2{pack_bf16x2(v.x - h0, v.y - h1), pack_bf16x2(v.z - h2, v.w - h3)};
+}
+
+// Transpose of each of B matrices [R][C] (bf16) into [C][R], 64 x 64 tiles through LDS.
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src, int R, int C,
+                                                             uint16_t* __restrict__ dst) {
+  __shared__ uint16_t t[64][65];
+  const int64_t b = blockIdx.z;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const uint16_t* s = src + b * R * (int64_t)C;
+  uint16_t* d = dst + b * R * (int64_t)C;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int r = ty; r < 64; r += 4)
+    if (r0 + r < R && c0 + tx < C) t[r][tx] = s[(int64_t)(r0 + r) * C + c0 + tx];
+  __syncthreads();
+  for (int c = ty; c < 64; c += 4)
+    if (c0 + c < C && r0 + tx < R) d[(int64_t)(c0 + c) * R + r0 + tx] = t[tx][c];
+}
+
+// Transposed, expert-padded copy of routed rows: dst[c][col] = scale(col) src[row(col)][c]
+// for the C columns of the rows, zero where padmap[col] < 0.  SRC_TOKEN: the source row is
+// the token of the routed row's assignment (x, dout), else the routed row itself (du, h).
+// GATE: scaled by the assignment's gate (dz = g dout).  SRC_F32: fp32 source.
+template <bool SRC_TOKEN, bool GATE, bool SRC_F32>
+__global__ __launch_bounds__(256) void gather_transpose_kernel(const void* __restrict__ src, int C, int ld_src,
+                                                               const int32_t* __restrict__ padmap,
+                                                               const int32_t* __restrict__ perm,
+                                                               const float* __restrict__ gates, int k, int A,
+                                                               int ldt, uint16_t* __restrict__ dst) {
+  __shared__ uint16_t t[64][65];
+  const int col0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int r = ty; r < 64; r += 4) {        // r: column of the padded layout (a routed row)
+    const int col = col0 + r;
+    float v = 0.f;
+    const int prow = col < ldt ? padmap[col] : -1;
+    if (prow >= 0 && c0 + tx < C) {
+      int64_t srow = prow;
+      float sc = 1.f;
+      if (SRC_TOKEN || GATE) {
+        int a = perm[prow];
+        a = ((unsigned)a < (unsigned)A) ? a : 0;
+        if (SRC_TOKEN) srow = a / k;
+        if (GATE) sc = gates[a];
+      }
+      if (SRC_F32) v = ((const float*)src)[srow * ld_src + c0 + tx] * sc;
+      else v = bf16_to_f32(((const uint16_t*)src)[srow * ld_src + c0 + tx]) * sc;
+    }
+    const __bf16 bv = (__bf16)v;
+    t[r][tx] = *(const uint16_t*)&bv;
+  }
+  __syncthreads();
+  for (int c = ty; c < 64; c += 4)
+    if (c0 + c < C && col0 + tx < ldt) dst[(int64_t)(c0 + c) * ldt + col0 + tx] = t[tx][c];
+}
+
+// ------------------------------------------------------------------------------ router
+// One wave per token: dg_j = sum over column tiles of <dh', h> + <dout[t], b2[e_j]>, then
+// the softmax backward over the k selected logits, dl_j = g_j (dg_j - sum_i g_i dg_i).
+// Lane l keeps dg_j for the slots j = l + 64 m (k <= 256).
+__global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict__ dgpart, int n_tiles,
+                                                         const float* __restrict__ dout,
+                                                         const uint16_t* __restrict__ b2,
+                                                         const int32_t* __restrict__ idx,
+                                                         const float* __restrict__ gates, int T, int D, int E,
+                                                         int k, float* __restrict__ dl) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T) return;
+  const int A = T * k;
+  float mine[4] = {0.f, 0.f, 0.f, 0.f};
+  float sgd = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int a = t * k + j;
+    const int e = min(max(idx[a], 0), E - 1);
+    float v = 0.f;
+    for (int d = lane; d < D; d += 64) v += dout[(int64_t)t * D + d] * bf16_to_f32(b2[(int64_t)e * D + d]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    float s = 0.f;
+    for (int nt = 0; nt < n_tiles; ++nt) s += dgpart[(int64_t)nt * A + a];
+    const float d_g = s + v;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      if (j == lane + 64 * m) mine[m] = d_g;
+    sgd += gates[a] * d_g;
+  }
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int j = lane + 64 * m;
+    if (j < k) dl[t * k + j] = gates[t * k + j] * (mine[m] - sgd);
+  }
+}
+
+// Per expert, sums over its routed rows.  The rows are split into EX_CHUNKS fixed chunks in
+// group order; pass 1 sums each chunk per column, pass 2 adds the chunks in order:
+//   dwr[e][d] = sum dl x[t][d];  db2[e][d] = sum g dout[t][d];  db1[e][c] = sum du[p][c].
+constexpr int EX_CHUNKS = 32;
+__global__ __launch_bounds__(256) void expert_partial_kernel(const int32_t* __restrict__ offsets,
+                                                             const int32_t* __restrict__ perm,
+                                                             const float* __restrict__ gates,
+                                                             const float* __restrict__ dl,
+                                                             const uint16_t* __restrict__ x,
+                                                             const float* __restrict__ dout,
+                                                             const uint16_t* __restrict__ du, int D, int F, int k,
+                                                             int A, int E, float* __restrict__ pw,
+                                                             float* __restrict__ pb2, float* __restrict__ pb1) {
+  const int e = blockIdx.y, r = blockIdx.z;
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int G = 2 * F;
+  const int p0 = offsets[e], cnt = offsets[e + 1] - p0;
+  const int len = (cnt + EX_CHUNKS - 1) / EX_CHUNKS;
+  const int lo = p0 + min(cnt, r * len), hi = p0 + min(cnt, (r + 1) * len);
+  const int64_t slot = (int64_t)r * E + e;
+  if (c < D) {
+    float sw = 0.f, sb = 0.f;
+#pragma unroll 4
+    for (int pp = lo; pp < hi; ++pp) {
+      int a = perm[pp];
+      a = ((unsigned)a < (unsigned)A) ? a : 0;
+      const int64_t t = a / k;
+      sw += dl[a] * bf16_to_f32(x[t * D + c]);
+      sb += gates[a] * dout[t * D + c];
+    }
+    pw[slot * D + c] = sw;
+    pb2[slot * D + c] = sb;
+  }
+  if (c < G) {
+    float s = 0.f;
+#pragma unroll 4
+    for (int pp = lo; pp < hi; ++pp) s += bf16_to_f32(du[(int64_t)pp * G + c]);
+    pb1[slot * G + c] = s;
+  }
+}
+
+__global__ __launch_bounds__(256) void expert_reduce_kernel(const float* __restrict__ pw,
+                                                            const float* __restrict__ pb2,
+                                                            const float* __restrict__ pb1, int D, int F, int E,
+                                                            float* __restrict__ dwr, float* __restrict__ db2,
+                                                            float* __restrict__ db1) {
+  const int e = blockIdx.y;
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int G = 2 * F;
+  if (c < D) {
+    float sw = 0.f, sb = 0.f;
+    for (int r = 0; r < EX_CHUNKS; ++r) {
+      sw += pw[((int64_t)r * E + e) * D + c];
+      sb += pb2[((int64_t)r * E + e) * D + c];
+    }
+    dwr[(int64_t)e * D + c] = sw;
+    db2[(int64_t)e * D + c] = sb;
+  }
+  if (c < G) {
+    float s = 0.f;
+    for (int r = 0; r < EX_CHUNKS; ++r) s += pb1[((int64_t)r * E + e) * G + c];
+    db1[(int64_t)e * G + c] = s;
+  }
+}
+
+// dbr[e] = sum of dl over the expert's rows: 256 threads stride the rows, then a fixed tree.
+__global__ __launch_bounds__(256) void router_bias_grad_kernel(const int32_t* __restrict__ offsets,
+                                                               const int32_t* __restrict__ perm,
+                                                               const float* __restrict__ dl, int A,
+                                                               float* __restrict__ dbr) {
+  __shared__ float s[256];
+  const int e = blockIdx.x, tid = threadIdx.x;
+  float v = 0.f;
+  for (int pp = offsets[e] + tid; pp < offsets[e + 1]; pp += 256) {
+    int a = perm[pp];
+    a = ((unsigned)a < (unsigned)A) ? a : 0;
+    v += dl[a];
+  }
+  s[tid] = v;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) s[tid] += s[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) dbr[e] = s[0];
+}
+
+// dx[t][d] = sum_j dxs[t k + j][d] + sum_j dl[t k + j] Wr[e_j][d], slots in order.
+__global__ __launch_bounds__(256) void dx_combine_kernel(const float* __restrict__ dxs,
+                                                         const float* __restrict__ dl,
+                                                         const int32_t* __restrict__ idx,
+                                                         const uint16_t* __restrict__ wr, int T, int D, int E,
+                                                         int k, float* __restrict__ dx) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)T * D) return;
+  const int64_t t = i / D;
+  const int d = (int)(i - t * D);
+  float s = 0.f;
+  for (int j = 0; j < k; ++j) s += dxs[(t * k + j) * D + d];
+  for (int j = 0; j < k; ++j) {
+    const int64_t a = t * k + j;
+    const int e = min(max(idx[a], 0), E - 1);
+    s += dl[a] * bf16_to_f32(wr[(int64_t)e * D + d]);
+  }
+  dx[i] = s;
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0.f;
+}
+
+unsigned blocks_for(int64_t n, int per = 256) { return (unsigned)((n + per - 1) / per); }
+
+#define BW_CHECK(expr)                          \
+  do {                                          \
+    const hipError_t e_ = (expr);               \
+    if (e_ != hipSuccess) return e_;            \
+  } while (0)
+
+}  // namespace
+
+int bwd_padded_cols(int64_t A, int64_t E) {
+  const int64_t v = A + E * (BG_BK - 1);
+  return (int)((v + 63) / 64 * 64);
+}
+int bwd_f_tiles(int64_t F) { return (int)((F + BG_BN - 1) / BG_BN); }
+int bwd_sum_chunks() { return EX_CHUNKS; }
+
+hipError_t launch_backward(const BwdArgs& b, hipStream_t st) {
+  const int T = b.T, D = b.D, E = b.E, k = b.k, F = b.F, G = 2 * F;
+  const int A = T * k;
+  const int ldt = bwd_padded_cols(A, E);
+  // 1. padded layout of the routed rows per expert
+  hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(256), 0, st, b.offsets, E, b.poff);
+  BW_CHECK(hipGetLastError());
+  hipLaunchKernelGGL(pad_map_kernel, dim3(blocks_for(ldt)), dim3(256), 0, st, b.offsets, b.poff, E, ldt, b.padmap);
+  BW_CHECK(hipGetLastError());
+  // 2. dout as bf16 pairs [T][hi D | lo D] (A operand of mlp2's input gradient)
+  hipLaunchKernelGGL(f32_to_bf16_pair_kernel, dim3(blocks_for((int64_t)T * D / 4)), dim3(256), 0, st,
+                     (const float4*)b.dout, (int64_t)T, D / 4, (uint2*)b.dout16);
+  BW_CHECK(hipGetLastError());
+  // 3. the weights along their other dimension: W1^T [E][D][2F], W2^T [E][F][D]
+  hipLaunchKernelGGL(transpose_bf16_kernel, dim3(blocks_for(D, 64), blocks_for(G, 64), E), dim3(256), 0, st,
+                     b.w1, G, D, b.w1t);
+  BW_CHECK(hipGetLastError());
+  hipLaunchKernelGGL(transpose_bf16_kernel, dim3(blocks_for(F, 64), blocks_for(D, 64), E), dim3(256), 0, st,
+                     b.w2, D, F, b.w2t);
+  BW_CHECK(hipGetLastError());
+  // 4. transposed, padded x and dz = g dout (operands of the weight gradients)
+  hipLaunchKernelGGL((gather_transpose_kernel<true, false, false>), dim3(ldt / 64, blocks_for(D, 64)), dim3(256), 0,
+                     st, (const void*)b.x, D, D, b.padmap, b.perm, b.gates, k, A, ldt, b.xT);
+  BW_CHECK(hipGetLastError());
+  hipLaunchKernelGGL((gather_transpose_kernel<true, true, true>), dim3(ldt / 64, blocks_for(D, 64)), dim3(256), 0,
+                     st, (const void*)b.dout, D, D, b.padmap, b.perm, b.gates, k, A, ldt, b.dzT);
+  BW_CHECK(hipGetLastError());
+
+  const int64_t mt = row_tiles_bound(A, E);
+  BwdGemmArgs g{};
+  g.offsets = b.offsets; g.perm = b.perm; g.gates = b.gates; g.poff = b.poff;
+  g.E = E; g.k = k; g.A = A; g.F = F;
+  // 5. recompute u = x W1^T + b1
+  g.a = b.x; g.lda = D; g.b = b.w1; g.ldb = D; g.b_expert = (int64_t)G * D;
+  g.K = D; g.N = G; g.n_tiles = (G + BG_BN - 1) / BG_BN;
+  g.bias = b.b1; g.c = b.u;
+  BW_CHECK(launch_bwd_gemm<BW_RECOMP>(g, mt, st));
+  // 6. dh' = dout W2[e], SwiGLU backward -> h, du, partial dg
+  g.a = b.dout16; g.lda = 2 * D; g.b = b.w2t; g.ldb = D; g.b_expert = (int64_t)F * D;
+  g.K = 2 * D; g.kwrap = D / BG_BK; g.N = F; g.n_tiles = bwd_f_tiles(F);
+  g.u = b.u; g.h = b.h; g.du = b.du; g.dgpart = b.dgpart; g.c = nullptr; g.bias = nullptr;
+  BW_CHECK(launch_bwd_gemm<BW_DGRAD2>(g, mt, st));
+  // 7. dx contributions du W1[e] at the slot rows
+  g.a = b.du; g.lda = G; g.b = b.w1t; g.ldb = G; g.b_expert = (int64_t)D * G;
+  g.K = G; g.N = D; g.n_tiles = (D + BG_BN - 1) / BG_BN; g.c = b.dxs;
+  BW_CHECK(launch_bwd_gemm<BW_DGRAD1>(g, mt, st));
+  // 8. transposed, padded h and du
+  hipLaunchKernelGGL((gather_transpose_kernel<false, false, false>), dim3(ldt / 64, blocks_for(F, 64)), dim3(256), 0,
+                     st, (const void*)b.h, F, F, b.padmap, b.perm, b.gates, k, A, ldt, b.hT);
+  BW_CHECK(hipGetLastError());
+  hipLaunchKernelGGL((gather_transpose_kernel<false, false, false>), dim3(ldt / 64, blocks_for(G, 64)), dim3(256), 0,
+                     st, (const void*)b.du, G, G, b.padmap, b.perm, b.gates, k, A, ldt, b.duT);
+  BW_CHECK(hipGetLastError());
+  // 9. weight gradients per expert: dW2[e] = dz^T h, dW1[e] = du^T x
+  BwdGemmArgs w{};
+  w.poff = b.poff; w.E = E; w.k = k; w.A = A;
+  w.a = b.dzT; w.lda = ldt; w.b = b.hT; w.ldb = ldt; w.M = D; w.N = F;
+  w.m_tiles = (D + BG_BM - 1) / BG_BM; w.n_tiles = (F + BG_BN - 1) / BG_BN; w.c = b.dw2;
+  BW_CHECK(launch_bwd_gemm<BW_WGRAD>(w, 0, st));
+  w.a = b.duT; w.b = b.xT; w.M = G; w.N = D;
+  w.m_tiles = (G + BG_BM - 1) / BG_BM; w.n_tiles = (D + BG_BN - 1) / BG_BN; w.c = b.dw1;
+  BW_CHECK(launch_bwd_gemm<BW_WGRAD>(w, 0, st));
+  // 10. router: dg and the softmax backward, then the per-expert sums and dx
+  hipLaunchKernelGGL(router_bwd_kernel, dim3(blocks_for(T, 4)), dim3(256), 0, st, b.dgpart, bwd_f_tiles(F), b.dout,
+                     b.b2, b.idx, b.gates, T, D, E, k, b.dl);
+  BW_CHECK(hipGetLastError());
+  const unsigned wblk = blocks_for(G > D ? G : D);
+  hipLaunchKernelGGL(expert_partial_kernel, dim3(wblk, E, EX_CHUNKS), dim3(256), 0, st, b.offsets, b.perm, b.gates,
+                     b.dl, b.x, b.dout, b.du, D, F, k, A, E, b.part_w, b.part_b2, b.part_b1);
+  BW_CHECK(hipGetLastError());
+  hipLaunchKernelGGL(expert_reduce_kernel, dim3(wblk, E), dim3(256), 0, st, b.part_w, b.part_b2, b.part_b1, D, F, E,
+                     b.dwr, b.db2, b.db1);
+  BW_CHECK(hipGetLastError());
+  hipLaunchKernelGGL(router_bias_grad_kernel, dim3(E), dim3(256), 0, st, b.offsets, b.perm, b.dl, A, b.dbr);
+  BW_CHECK(hipGetLastError());
+  hipLaunchKernelGGL(dx_combine_kernel, dim3(blocks_for((int64_t)T * D)), dim3(256), 0, st, b.dxs, b.dl, b.idx,
+                     b.wr, T, D, E, k, b.dx);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks_for(n)), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
+
+}  // namespace moe

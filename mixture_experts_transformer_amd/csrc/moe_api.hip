@@ -126,6 +126,45 @@ Layout layout(int64_t T, int64_t D, int64_t E, int64_t k, int64_t F, int fmt, in
   return L;
 }
 
+// Backward workspace (moe_backward), one allocation.
+struct BwdLayout {
+  size_t poff = 0, padmap = 0, dout16 = 0, w1t = 0, w2t = 0, xT = 0, dzT = 0, u = 0, h = 0, du = 0;
+  size_t dgpart = 0, dxs = 0, hT = 0, duT = 0, dl = 0, part_w = 0, part_b2 = 0, part_b1 = 0, total = 0;
+};
+
+BwdLayout bwd_layout(int64_t T, int64_t D, int64_t E, int64_t k, int64_t F) {
+  BwdLayout L;
+  const size_t A = (size_t)T * (size_t)k, G = 2 * (size_t)F;
+  const size_t ldt = (size_t)moe::bwd_padded_cols((int64_t)A, E);
+  const size_t ch = (size_t)moe::bwd_sum_chunks();
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  L.poff = take(((size_t)E + 1) * 4);
+  L.padmap = take(ldt * 4);
+  L.dout16 = take((size_t)T * D * 4);
+  L.w1t = take((size_t)E * G * D * 2);
+  L.w2t = take((size_t)E * F * D * 2);
+  L.xT = take((size_t)D * ldt * 2);
+  L.dzT = take((size_t)D * ldt * 2);
+  L.u = take(A * G * 4);
+  L.h = take(A * F * 2);
+  L.du = take(A * G * 2);
+  L.dgpart = take((size_t)moe::bwd_f_tiles(F) * A * 4);
+  L.dxs = take(A * D * 4);
+  L.hT = take((size_t)F * ldt * 2);
+  L.duT = take(G * ldt * 2);
+  L.dl = take(A * 4);
+  L.part_w = take(ch * E * D * 4);
+  L.part_b2 = take(ch * E * D * 4);
+  L.part_b1 = take(ch * E * G * 4);
+  L.total = off;
+  return L;
+}
+
 int check_shapes(int64_t T, int64_t D, int64_t E, int64_t k, int64_t F, bool with_f) {
   if (T < 0) return fail(MOE_EINVAL, "T = %lld must be >= 0", (long long)T);
   if (D <= 0 || D % 64 != 0) return fail(MOE_EINVAL, "D = %lld must be a positive multiple of 64", (long long)D);
@@ -452,6 +491,74 @@ int moe_experts(const void* x, const void* w1, const void* b1, const void* w2, c
   return ok();
 }
 
+int moe_backward(const void* x, const void* router_w, const void* w1, const void* b1, const void* w2,
+                 const void* b2, const int32_t* topk_idx, const float* gates, const int32_t* offsets,
+                 const int32_t* perm, const float* dout, int64_t T, int64_t D, int64_t E, int64_t k, int64_t F,
+                 int fmt, float* dx, float* d_router_w, float* d_router_b, float* dw1, float* db1, float* dw2,
+                 float* db2) {
+  CHECK(check_shapes(T, D, E, k, F, true));
+  if (!valid_fmt(fmt)) return fail(MOE_EFMT, "unknown weight format %d", fmt);
+  if (fmt != MOE_FMT_BF16) return fail(MOE_EFMT, "moe_backward takes bf16 expert weights only (fmt %d)", fmt);
+  CHECK(check_ptr(d_router_w, "d_router_w"));
+  CHECK(check_ptr(d_router_b, "d_router_b"));
+  CHECK(check_ptr(dw1, "dw1"));
+  CHECK(check_ptr(db1, "db1"));
+  CHECK(check_ptr(dw2, "dw2"));
+  CHECK(check_ptr(db2, "db2"));
+  if (T == 0) {
+    // no token: every parameter gradient is zero (dx has no element)
+    const int64_t G = 2 * F;
+    const struct { float* p; int64_t n; } z[] = {{d_router_w, E * D}, {d_router_b, E}, {dw1, E * G * D},
+                                                   {db1, E * G}, {dw2, E * D * F}, {db2, E * D}};
+    CHECK(launch(moe::ST_BACKWARD, "backward zero", [&](hipStream_t st) {
+      for (const auto& zz : z) {
+        const hipError_t e = moe::launch_fill_zero(zz.p, zz.n, st);
+        if (e != hipSuccess) return e;
+      }
+      return hipSuccess;
+    }));
+    return ok();
+  }
+  CHECK(check_ptr(x, "x"));
+  CHECK(check_ptr(router_w, "router_w"));
+  CHECK(check_ptr(w1, "w1"));
+  CHECK(check_ptr(b1, "b1"));
+  CHECK(check_ptr(w2, "w2"));
+  CHECK(check_ptr(b2, "b2"));
+  CHECK(check_ptr(topk_idx, "topk_idx"));
+  CHECK(check_ptr(gates, "gates"));
+  CHECK(check_ptr(offsets, "offsets"));
+  CHECK(check_ptr(perm, "perm"));
+  CHECK(check_ptr(dout, "dout"));
+  CHECK(check_ptr(dx, "dx"));
+  if (T * k + E * 63 + 64 >= ((int64_t)1 << 31))
+    return fail(MOE_EINVAL, "T*k = %lld is too large for the backward's padded layout", (long long)(T * k));
+  const BwdLayout L = bwd_layout(T, D, E, k, F);
+  uint8_t* ws = nullptr;
+  CHECK(ensure_workspace(L.total, &ws));
+  moe::BwdArgs b{};
+  b.x = (const uint16_t*)x; b.wr = (const uint16_t*)router_w;
+  b.w1 = (const uint16_t*)w1; b.b1 = (const uint16_t*)b1; b.w2 = (const uint16_t*)w2; b.b2 = (const uint16_t*)b2;
+  b.idx = topk_idx; b.gates = gates; b.offsets = offsets; b.perm = perm; b.dout = dout;
+  b.dx = dx; b.dwr = d_router_w; b.dbr = d_router_b; b.dw1 = dw1; b.db1 = db1; b.dw2 = dw2; b.db2 = db2;
+  b.poff = (int32_t*)(ws + L.poff); b.padmap = (int32_t*)(ws + L.padmap);
+  b.dout16 = (uint16_t*)(ws + L.dout16); b.w1t = (uint16_t*)(ws + L.w1t); b.w2t = (uint16_t*)(ws + L.w2t);
+  b.xT = (uint16_t*)(ws + L.xT); b.dzT = (uint16_t*)(ws + L.dzT); b.u = (float*)(ws + L.u);
+  b.h = (uint16_t*)(ws + L.h); b.du = (uint16_t*)(ws + L.du); b.dgpart = (float*)(ws + L.dgpart);
+  b.dxs = (float*)(ws + L.dxs); b.hT = (uint16_t*)(ws + L.hT); b.duT = (uint16_t*)(ws + L.duT);
+  b.dl = (float*)(ws + L.dl); b.part_w = (float*)(ws + L.part_w); b.part_b2 = (float*)(ws + L.part_b2);
+  b.part_b1 = (float*)(ws + L.part_b1);
+  b.T = (int)T; b.D = (int)D; b.E = (int)E; b.k = (int)k; b.F = (int)F;
+  CHECK(launch(moe::ST_BACKWARD, "backward", [&](hipStream_t st) { return moe::launch_backward(b, st); }));
+  return ok();
+}
+
+size_t moe_backward_workspace_bytes(int64_t T, int64_t D, int64_t E, int64_t k, int64_t F, int fmt) {
+  if (check_shapes(T, D, E, k, F, true) != MOE_OK) return 0;
+  if (fmt != MOE_FMT_BF16 || T == 0) return 0;
+  return bwd_layout(T, D, E, k, F).total;
+}
+
 int moe_set_stream(void* hip_stream) {
   g_stream = (hipStream_t)hip_stream;
   return ok();
@@ -528,7 +635,8 @@ int moe_profile_read(double* ms, int64_t* launches) {
 const char* moe_version(void) {
   return "moe-mi355x gfx950: router fp64-MFMA, top-k wave argmax, grouped GEMM v_mfma_f32_32x32x16_bf16 "
          "(streaming tile 64x128; matrix-core tile 256x256) and, for MXFP4 on matrix-core tiles, "
-         "v_mfma_scale_f32_32x32x64_f8f6f4 on fp8 activation pieces; combine fp32";
+         "v_mfma_scale_f32_32x32x64_f8f6f4 on fp8 activation pieces; combine fp32; backward (bf16) "
+         "grouped GEMM 256x128 v_mfma_f32_32x32x16_bf16";
 }
 
 }  // extern "C"

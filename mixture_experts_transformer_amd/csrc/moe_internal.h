@@ -15,7 +15,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-enum Stage { ST_ROUTER = 0, ST_TOPK = 1, ST_PERMUTE = 2, ST_MLP1 = 3, ST_MLP2 = 4, ST_COMBINE = 5, ST_SPLIT = 6 };
+enum Stage {
+  ST_ROUTER = 0, ST_TOPK = 1, ST_PERMUTE = 2, ST_MLP1 = 3, ST_MLP2 = 4, ST_COMBINE = 5, ST_SPLIT = 6,
+  ST_BACKWARD = 7
+};
 
 // ---------------------------------------------------------------- routing
 // Number of K splits the router uses for T tokens of width D (>= 1).
@@ -74,5 +77,50 @@ hipError_t launch_mx_split(const uint16_t* src, int64_t rows, int K, uint8_t* q,
 hipError_t launch_mlp1(const ExpertArgs& a, int cfg, hipStream_t st);
 hipError_t launch_mlp2(const ExpertArgs& a, int cfg, hipStream_t st);
 hipError_t launch_combine(const float* y, int T, int D, int k, float* out, hipStream_t st);
+
+// ---------------------------------------------------------------- backward
+// Gradients of the block for bf16 expert weights with the routing of the forward held
+// fixed (inputs as moe_backward takes them; workspace arrays as laid out by the ABI layer).
+struct BwdArgs {
+  const uint16_t* x;        // [T][D]
+  const uint16_t* wr;       // [E][D]
+  const uint16_t* w1;       // [E][2F][D]
+  const uint16_t* b1;       // [E][2F]
+  const uint16_t* w2;       // [E][D][F]
+  const uint16_t* b2;       // [E][D]
+  const int32_t* idx;       // [A] expert of each assignment
+  const float* gates;       // [A]
+  const int32_t* offsets;   // [E+1]
+  const int32_t* perm;      // [A]
+  const float* dout;        // [T][D]
+  float *dx, *dwr, *dbr, *dw1, *db1, *dw2, *db2;   // outputs (fp32)
+  // workspace
+  int32_t* poff;            // [E+1] padded column offsets per expert
+  int32_t* padmap;          // [ldt] routed row of each padded column, -1 for padding
+  uint16_t* dout16;         // [T][2D] bf16 pairs: hi then lo
+  uint16_t* w1t;            // [E][D][2F]
+  uint16_t* w2t;            // [E][F][D]
+  uint16_t* xT;             // [D][ldt]
+  uint16_t* dzT;            // [D][ldt]
+  float* u;                 // [A][2F] recomputed mlp1 output (routed-row order)
+  uint16_t* h;              // [A][F]
+  uint16_t* du;             // [A][2F]
+  float* dgpart;            // [bwd_f_tiles(F)][A]
+  float* dxs;               // [A][D] slot rows
+  uint16_t* hT;             // [F][ldt]
+  uint16_t* duT;            // [2F][ldt]
+  float* dl;                // [A] gradient of the selected logits
+  float *part_w, *part_b2;  // [bwd_sum_chunks()][E][D]
+  float* part_b1;           // [bwd_sum_chunks()][E][2F]
+  int T, D, E, k, F;
+};
+// Columns of the transposed, expert-padded activation layout (a multiple of 64).
+int bwd_padded_cols(int64_t A, int64_t E);
+// Column tiles over F of the input-gradient product of mlp2.
+int bwd_f_tiles(int64_t F);
+// Fixed row chunks of the per-expert sums.
+int bwd_sum_chunks();
+hipError_t launch_backward(const BwdArgs& b, hipStream_t st);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 
 }  // namespace moe

@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 FMT = {"bf16": 0, "mxfp4": 1, "mxfp8": 2}
-STAGES = ("router", "topk", "permute", "mlp1", "mlp2", "combine", "split")
+STAGES = ("router", "topk", "permute", "mlp1", "mlp2", "combine", "split", "backward")
 
 _c_void_p = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -30,6 +30,8 @@ _SIGNATURES = {
     "moe_route_biased": (ctypes.c_int, [_c_void_p] * 4 + [_i64] * 4 + [_c_void_p] * 6),
     "moe_update_expert_bias": (ctypes.c_int, [_c_void_p, _i64, ctypes.c_float, _c_void_p]),
     "moe_experts": (ctypes.c_int, [_c_void_p] * 8 + [_i64] * 5 + [ctypes.c_int, _c_void_p]),
+    "moe_backward": (ctypes.c_int, [_c_void_p] * 11 + [_i64] * 5 + [ctypes.c_int] + [_c_void_p] * 7),
+    "moe_backward_workspace_bytes": (ctypes.c_size_t, [_i64] * 5 + [ctypes.c_int]),
     "moe_set_stream": (ctypes.c_int, [_c_void_p]),
     "moe_workspace_bytes": (ctypes.c_size_t, [_i64] * 5 + [ctypes.c_int]),
     "moe_set_workspace": (ctypes.c_int, [_c_void_p, ctypes.c_size_t]),
@@ -231,6 +233,37 @@ def experts(x, w1, b1, w2, b2, gates, offsets, perm, k: int, fmt: str = "bf16",
     _check(lib().moe_experts(_ptr(x), _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(gates), _ptr(offsets),
                              _ptr(perm), T, D, E, k, F, FMT[fmt], _ptr(out)), "moe_experts")
     return out
+
+
+def backward(x, router_w, w1, b1, w2, b2, routing: dict, dout, k: int, fmt: str = "bf16") -> dict:
+    """Gradients of the block (``moe_backward``) for the routing of a forward (``route``'s dict:
+    idx, gates, offsets, perm) and the output gradient ``dout`` (fp32 [T, D]).  Returns fp32
+    dx, dwr, dbr, dw1, db1, dw2, db2 (each the shape of its input)."""
+    T, D = x.shape
+    E = router_w.shape[0]
+    F = b1.shape[-1] // 2
+    _dev(x, "x", 2), _dev(router_w, "router_w", 2), _dev(b1, "b1", 2), _dev(b2, "b2", 2)
+    _check_weights(w1, w2, E, D, F, fmt)
+    _dev(dout, "dout", 4)
+    if tuple(dout.shape) != (T, D):
+        raise ValueError(f"dout must be [{T}, {D}]")
+    for n in ("idx", "gates", "offsets", "perm"):
+        _dev(routing[n], n, 4)
+    dev = x.device
+    f32 = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)
+    g = {"dx": f32(T, D), "dwr": f32(E, D), "dbr": f32(E), "dw1": f32(E, 2 * F, D), "db1": f32(E, 2 * F),
+         "dw2": f32(E, D, F), "db2": f32(E, D)}
+    _bind_stream(dev)
+    _check(lib().moe_backward(_ptr(x), _ptr(router_w), _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2),
+                              _ptr(routing["idx"]), _ptr(routing["gates"]), _ptr(routing["offsets"]),
+                              _ptr(routing["perm"]), _ptr(dout), T, D, E, k, F, FMT[fmt],
+                              _ptr(g["dx"]), _ptr(g["dwr"]), _ptr(g["dbr"]), _ptr(g["dw1"]), _ptr(g["db1"]),
+                              _ptr(g["dw2"]), _ptr(g["db2"])), "moe_backward")
+    return g
+
+
+def backward_workspace_bytes(T: int, D: int, E: int, k: int, F: int, fmt: str = "bf16") -> int:
+    return int(lib().moe_backward_workspace_bytes(T, D, E, k, F, FMT[fmt]))
 
 
 def workspace_bytes(T: int, D: int, E: int, k: int, F: int, fmt: str = "bf16") -> int:

@@ -26,4 +26,5 @@ from .moe_oracle import (  # noqa: F401
     swiglu,
     update_expert_bias,
 )
-from .moe_backward import forward_fixed_routing, moe_backward, swiglu_backward  # noqa: F401,E402
+from .moe_backward import (forward_fixed_routing, moe_backward, moe_backward_grouped,  # noqa: F401,E402
+                           swiglu_backward)

@@ -107,3 +107,73 @@ def moe_backward(x, wr, br, w1, b1, w2, b2, idx, dout, F: int) -> dict:
     dbr = dl.sum(axis=0)
     dx += dl @ wr
     return dict(dx=dx, dwr=dwr, dbr=dbr, dw1=dw1, db1=db1, dw2=dw2, db2=db2)
+
+
+def moe_backward_grouped(x, wr, br, w1, b1, w2, b2, idx, dout, k: int, F: int, fmt: str,
+                         weight_experts=None) -> dict:
+    """The gradients of ``moe_backward`` from the stored bits (as ``moe_forward`` takes them:
+    x [T,D], wr [E,D], br [E], b1, b2 as bf16 bits; w1/w2 in ``fmt``), computed one expert
+    at a time over the tokens routed to it (torchtitan guide, grouped GEMM section: each
+    expert's rows form one group), so layers of the 20B shape fit in host memory.
+
+    Same readings as ``moe_backward`` (selection idx [T, k] fixed, clamps pass the gradient
+    on the closed interval, logits exact reals).  dx, dwr, dbr are returned whole; dw1, db1,
+    dw2, db2 only for the experts in ``weight_experts`` (all when None), as dicts
+    {e: array}.  Per expert e with routed rows R (tokens t_r, slots j_r, gates g_r):
+    U = X_R W1[e]^T + b1[e], H = swiglu(U), Z = H W2[e]^T + b2[e]; dg_r = <dout[t_r], Z_r>;
+    dZ = g dout[t_R]; dW2 = dZ^T H, db2 = sum dZ; dU = swiglu_backward(U, dZ W2[e]);
+    dW1 = dU^T X_R, db1 = sum dU, dx[t_r] += dU_r W1[e]; then the softmax backward over
+    the selected logits and the router's products, as in ``moe_backward``.
+    """
+    from .moe_oracle import bf16_to_f64, expert_weight, swiglu
+
+    x64 = bf16_to_f64(np.asarray(x))
+    T, D = x64.shape
+    wr64 = bf16_to_f64(np.asarray(wr))
+    E = wr64.shape[0]
+    br64 = bf16_to_f64(np.asarray(br))
+    b1_64 = bf16_to_f64(np.asarray(b1)).reshape(E, 2 * F)
+    b2_64 = bf16_to_f64(np.asarray(b2)).reshape(E, D)
+    idx = np.asarray(idx, dtype=np.int64)
+    dout = np.asarray(dout, dtype=np.float64)
+    logits = x64 @ wr64.T + br64[None, :]
+    sel = np.take_along_axis(logits, idx, axis=1)
+    z = np.exp(sel - sel.max(axis=1, keepdims=True))
+    g = z / z.sum(axis=1, keepdims=True)
+    want = set(range(E)) if weight_experts is None else set(int(e) for e in weight_experts)
+    dx = np.zeros_like(x64)
+    dg = np.zeros((T, k))
+    dw1, db1, dw2, db2 = {}, {}, {}, {}
+    flat = idx.reshape(-1)
+    for e in range(E):
+        a = np.flatnonzero(flat == e)                     # assignments t*k + j routed to e
+        if e in want:
+            dw1[e] = np.zeros((2 * F, D))
+            db1[e] = np.zeros(2 * F)
+            dw2[e] = np.zeros((D, F))
+            db2[e] = np.zeros(D)
+        if a.size == 0:
+            continue
+        t, j = a // k, a % k
+        w1e = expert_weight(w1, fmt, E, 2 * F, D, e)
+        w2e = expert_weight(w2, fmt, E, D, F, e)
+        xr = x64[t]
+        U = xr @ w1e.T + b1_64[e][None, :]
+        H = swiglu(U, F)
+        Z = H @ w2e.T + b2_64[e][None, :]
+        dg[t, j] = np.einsum("rd,rd->r", dout[t], Z)
+        dZ = g[t, j][:, None] * dout[t]
+        dU = swiglu_backward(U, dZ @ w2e, F)
+        np.add.at(dx, t, dU @ w1e)
+        if e in want:
+            dw2[e] = dZ.T @ H
+            db2[e] = dZ.sum(axis=0)
+            dw1[e] = dU.T @ xr
+            db1[e] = dU.sum(axis=0)
+    dsel = g * (dg - (g * dg).sum(axis=1, keepdims=True))
+    dl = np.zeros((T, E))
+    np.put_along_axis(dl, idx, dsel, axis=1)
+    dwr = dl.T @ x64
+    dbr = dl.sum(axis=0)
+    dx += dl @ wr64
+    return dict(dx=dx, dwr=dwr, dbr=dbr, dw1=dw1, db1=db1, dw2=dw2, db2=db2)

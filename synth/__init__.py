@@ -8,6 +8,7 @@ of the block's own arithmetic (no router product, no top-k, no expert MLP).
 from .configs import CONFIGS, Config, get_config  # noqa: F401
 from .generate import (  # noqa: F401
     MoEInputs,
+    make_dout,
     f32_to_bf16_bits,
     make_expert_bias,
     make_inputs,

@@ -274,3 +274,9 @@ def make_expert_bias(E: int, seed: int, steps_std: float = 300.0, step: float = 
     n = np.rint(np.random.default_rng(seed).normal(0.0, steps_std, E))
     return (n.astype(np.float32) * np.float32(step)).astype(np.float32)
 
+
+
+def make_dout(T: int, D: int, seed: int, std: float = 1.0) -> np.ndarray:
+    """A seeded output gradient for the backward, fp32 [T, D] drawn from N(0, std^2)."""
+    return (np.random.default_rng(np.random.SeedSequence([seed, 0x6D6F65]))
+            .standard_normal((T, D), dtype=np.float32) * np.float32(std))

@@ -36,7 +36,7 @@ def test_header_constants_match_binding():
     assert re.search(r"#define MOE_FMT_MXFP8 2\b", src)
     assert moe.FMT == {"bf16": 0, "mxfp4": 1, "mxfp8": 2}
     assert "#define MOE_SWIGLU_ALPHA 1.702f" in src and "#define MOE_SWIGLU_LIMIT 7.0f" in src
-    assert re.search(r"#define MOE_NUM_STAGES 7\b", src) and len(moe.STAGES) == 7
+    assert re.search(r"#define MOE_NUM_STAGES 8\b", src) and len(moe.STAGES) == 8
 
 
 def test_version_string():
@@ -252,3 +252,31 @@ def test_caller_workspace_is_per_thread():
     for size in (4096, 8192, 12288, 16384):
         rc, msg = seen[size]
         assert rc == MOE_ENOMEM and f"holds {size} bytes" in msg, (size, msg)
+
+
+def test_backward_validates():
+    """moe_backward: bf16 weights only (MOE_EFMT otherwise), shape and pointer checks first,
+    and no workspace size for formats it does not take."""
+    lib = moe.lib()
+    bw = lambda fmt=0, T=8, ptrs=None: lib.moe_backward(*(ptrs or [P] * 11), T, 64, 4, 2, 64, fmt,
+                                                       *([P] * 7))
+    assert bw(fmt=1) == MOE_EFMT and "bf16" in lib.moe_last_error().decode()
+    assert bw(fmt=2) == MOE_EFMT
+    assert bw(fmt=9) == MOE_EFMT
+    assert lib.moe_backward(*([P] * 11), 8, 96, 4, 2, 64, 0, *([P] * 7)) == MOE_EINVAL
+    for which in range(11):
+        ptrs = [P] * 11
+        ptrs[which] = None
+        assert bw(ptrs=ptrs) == MOE_EINVAL, which
+        ptrs[which] = BAD
+        assert bw(ptrs=ptrs) == MOE_EALIGN, which
+    assert lib.moe_backward_workspace_bytes(256, 2880, 32, 4, 2880, 1) == 0
+    assert lib.moe_backward_workspace_bytes(0, 2880, 32, 4, 2880, 0) == 0
+    need = lib.moe_backward_workspace_bytes(256, 2880, 32, 4, 2880, 0)
+    # the transposed weights alone are one copy of both expert matrices
+    assert need > 32 * 3 * 2880 * 2880 * 2
+    assert lib.moe_set_workspace(0x100000, 4096) == MOE_OK
+    try:
+        assert lib.moe_backward(*([P] * 11), 256, 2880, 32, 4, 2880, 0, *([P] * 7)) == -4
+    finally:
+        lib.moe_set_workspace(None, 0)

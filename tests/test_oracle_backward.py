@@ -111,3 +111,44 @@ def test_backward_exact_properties():
     u2 = np.array([[0.5, 1.0, 9.0, -7.5]])
     du2 = swiglu_backward(u2, np.ones((1, 2)), 2)
     assert du2[0, 2] == 0.0 and du2[0, 3] == 0.0          # both linear inputs past +-limit
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp4"])
+@pytest.mark.parametrize("T,D,E,k,F,seed", [(10, 32, 5, 2, 32, 0), (8, 64, 5, 4, 32, 1), (12, 32, 6, 3, 64, 2)])
+def test_grouped_backward_equals_loop_backward(fmt, T, D, E, k, F, seed):
+    """The per-expert batched form from stored bits == the per-assignment loop on the decoded
+    arrays (1e-12 relative), including a subset of experts for the weight gradients and an
+    expert that receives no token (its weight gradients are zero)."""
+    from synth import f32_to_bf16_bits
+    from oracle import bf16_to_f64, expert_weight, moe_backward_grouped, router_logits
+    g = np.random.default_rng(100 + seed)
+    bf = lambda *s, std=1.0: f32_to_bf16_bits(g.standard_normal(s).astype(np.float32) * np.float32(std))
+    x = bf(T, D)
+    wr = bf(E, D, std=0.3)
+    br = bf(E, std=0.5)
+    br[E - 1] = f32_to_bf16_bits(np.array([-64.0], dtype=np.float32))[0]     # expert E-1 gets no token
+    if fmt == "bf16":
+        w1, w2 = bf(E, 2 * F, D, std=4.0 / np.sqrt(D)), bf(E, D, F, std=0.3)
+    else:
+        def mx(rows, K):
+            return np.concatenate([g.integers(0, 256, E * rows * K // 2, dtype=np.uint8),
+                                   g.integers(123, 128, E * rows * K // 32, dtype=np.uint8)])
+        w1, w2 = mx(2 * F, D), mx(D, F)
+    b1, b2 = bf(E, 2 * F, std=0.2), bf(E, D, std=0.2)
+    idx = select_experts(router_logits(x, wr, br), k).astype(np.int64)
+    assert not (idx == E - 1).any()
+    dout = g.standard_normal((T, D))
+    dec = [bf16_to_f64(x), bf16_to_f64(wr), bf16_to_f64(br),
+           np.stack([expert_weight(w1, fmt, E, 2 * F, D, e) for e in range(E)]), bf16_to_f64(b1).reshape(E, 2 * F),
+           np.stack([expert_weight(w2, fmt, E, D, F, e) for e in range(E)]), bf16_to_f64(b2).reshape(E, D)]
+    ref = moe_backward(*dec, idx, dout, F)
+    sub = [0, E - 1, E // 2]
+    got = moe_backward_grouped(x, wr, br, w1, b1, w2, b2, idx, dout, k, F, fmt, weight_experts=sub)
+    close = lambda a, b: np.max(np.abs(a - b)) <= 1e-12 * max(1.0, np.abs(b).max())
+    for n in ("dx", "dwr", "dbr"):
+        assert close(got[n], ref[n]), n
+    for n in ("dw1", "db1", "dw2", "db2"):
+        assert sorted(got[n]) == sorted(set(sub)), n
+        for e in got[n]:
+            assert close(got[n][e], ref[n][e]), (n, e)
+    assert not got["dw1"][E - 1].any() and not got["db2"][E - 1].any()
