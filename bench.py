@@ -267,6 +267,58 @@ def bench_workload(name, steps, warmup, with_cpu):
     return res
 
 
+def bench_backward(name, steps, warmup):
+    """Time moe_backward (bf16 expert weights) on a workload's layer and routing: the gradient
+    of every input and parameter for a seeded output gradient, the routing held fixed.
+
+    Algorithmic work per token (the gradient math, not the recomputation of mlp1's output
+    that the backward does instead of keeping it): flops 12 k D F + 4 D E (each forward
+    product twice: input and weight gradients); bytes: the touched experts' weights read
+    once and their fp32 gradients written once, plus x, dout and dx."""
+    import torch
+    import mixture_experts_transformer_amd as moe
+    from synth import get_config, make_dout, make_inputs
+
+    cfg = get_config(name)
+    if cfg.fmt != "bf16":
+        raise ValueError("the backward takes bf16 expert weights")
+    inp = make_inputs(name)
+    dev = torch.device("cuda:0")
+    t16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+    x, wr, br, b1, b2 = t16(inp.x), t16(inp.wr), t16(inp.br), t16(inp.b1), t16(inp.b2)
+    w1, w2 = t16(inp.w1), t16(inp.w2)
+    dout = torch.from_numpy(make_dout(cfg.T, cfg.D, seed=cfg.seed)).to(dev)
+    r = moe.route(x, wr, br, cfg.k, want_logits=False)
+    touched = int(np.count_nonzero(r["counts"].cpu().numpy()))
+    T, D, E, k, F = cfg.T, cfg.D, cfg.E, cfg.k, cfg.F
+    flops = T * (12 * k * D * F + 4 * D * E)
+    issued = T * (18 * k * D * F + 4 * D * E)      # + mlp1 recomputed, dout as a bf16 pair
+    byts = touched * (3 * D * F * (2 + 4) + 2 * F * (2 + 4) + D * (2 + 4)) + E * D * (2 + 4) + T * D * (2 + 4 + 4)
+
+    def step():
+        moe.backward(x, wr, w1, b1, w2, b2, r, dout, k)
+
+    log(f"[bench] {name} backward: warmup {warmup} steps")
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    s = ms / 1e3
+    log(f"[bench] {name} backward: {ms * 1e3:.1f} us/step")
+    res = {"workload": f"{name}: T={T} D={D} E={E} k={k} F={F} bf16, gradients of x, router, w1, b1, w2, b2",
+           "ms_per_step": round(ms, 4), "tokens_per_s": round(T / s, 1),
+           "tflops": round(flops / s / 1e12, 2), "mfma_frac": round(flops / s / 1e12 / BF16_PEAK_TFLOPS, 4),
+           "issued_mfma_frac": round(issued / s / 1e12 / BF16_PEAK_TFLOPS, 4),
+           "hbm_gbs": round(byts / s / 1e9, 1), "hbm_frac": round(byts / s / 1e9 / HBM_PEAK_GBS, 4)}
+    del w1, w2
+    torch.cuda.empty_cache()
+    return res
+
+
 TARGETS = ("C3", "X1", "X2")     # the other target workloads: bf16 at 8192 tokens, MXFP4 at 256 and 8192
 
 
@@ -289,6 +341,7 @@ def main():
     ap.add_argument("--no-targets", action="store_true",
                     help="time only --workload (by default the C2 line also carries C3, X1 and X2 under 'targets')")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--backward", action="store_true", help="time only moe_backward on --workload (bf16)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device copies of MIB MiB (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -309,6 +362,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
         return
+    if args.backward:
+        print(json.dumps(bench_backward(args.workload, args.steps, args.warmup)), flush=True)
+        return
     if args.all:
         for i, name in enumerate(["C2", *TARGETS]):
             res = bench_workload(name, args.steps, args.warmup, with_cpu=(not args.no_cpu) and i == 0)
@@ -321,6 +377,7 @@ def main():
         res["targets"] = {}
         for name in TARGETS:
             res["targets"][name] = target_summary(bench_workload(name, args.steps, args.warmup, with_cpu=False))
+        res["backward"] = {name: bench_backward(name, args.steps, args.warmup) for name in ("C2", "C3")}
     print(json.dumps(res), flush=True)
 
 

@@ -52,7 +52,8 @@ struct BwdGemmArgs {
   const int32_t* offsets;   // [E+1] group offsets of the routed rows (grouped modes)
   const int32_t* perm;      // [A] assignment of each routed row
   const float* gates;       // [A] gate of each assignment
-  const int32_t* poff;      // [E+1] padded column offsets (weight-gradient mode)
+  const int32_t* poff;      // [E+1] padded column offsets, then [E] the experts by decreasing
+                            //   padded row count (weight-gradient mode)
   const uint16_t* a;        // A operand rows (bf16, K contiguous), lda elements apart
   const uint16_t* b;        // B operand rows, ldb elements apart; grouped modes: expert e's
   int64_t b_expert;         //   rows start b_expert elements after expert e - 1's
@@ -107,10 +108,18 @@ __global__ __launch_bounds__(BG_THREADS, 1) void bwd_gemm_kernel(BwdGemmArgs p) 
       mt_total = ts.total;
     }
     total = mt_total * p.n_tiles;
-    const int share = (total + 7) >> 3;
-    const int xl = blockIdx.x >> 3;
-    const int lin = (blockIdx.x & 7) * share + xl;
-    if (xl >= share || lin >= total) return;
+    int lin;
+    if (MODE == BW_WGRAD) {
+      // the experts' weight-gradient tiles cost their row counts: largest experts first
+      // (dispatched first and spread over every XCD), so the Zipf head does not trail
+      lin = blockIdx.x;
+      if (lin >= total) return;
+    } else {
+      const int share = (total + 7) >> 3;
+      const int xl = blockIdx.x >> 3;
+      lin = (blockIdx.x & 7) * share + xl;
+      if (xl >= share || lin >= total) return;
+    }
     const int gsize = GM * p.n_tiles;
     const int g = lin / gsize;
     const int first_m = g * GM;
@@ -118,7 +127,8 @@ __global__ __launch_bounds__(BG_THREADS, 1) void bwd_gemm_kernel(BwdGemmArgs p) 
     const int m_tile = first_m + (lin % gsize) % gm;
     n_tile = (lin % gsize) / gm;
     if (MODE == BW_WGRAD) {
-      e = m_tile / p.m_tiles;
+      // the expert of rank m_tile / m_tiles in decreasing padded row count
+      e = p.poff[p.E + 1 + m_tile / p.m_tiles];
       m0 = (m_tile % p.m_tiles) * BG_BM;
       rows = min(BG_BM, p.M - m0);
       K = p.poff[e + 1] - p.poff[e];
@@ -187,58 +197,72 @@ __global__ __launch_bounds__(BG_THREADS, 1) void bwd_gemm_kernel(BwdGemmArgs p) 
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-  // stage kt of this thread's rows into registers, and registers into LDS slot s (macros, not
-  // lambdas: a call that is not inlined would leave the staging arrays in memory)
-  u32x4 ra[BG_ALD], rb[BG_BLD];
-#define BW_GLOAD(kt)                                                                             \
+  // Stage kt of this thread's rows into register set R, and register set R into LDS slot s
+  // (macros, not lambdas: a call that is not inlined would leave the staging arrays in
+  // memory).  Two register sets: the loads of stage kt + 2 are issued before stage kt is
+  // multiplied and stored to LDS only after stage kt + 1 is, so two stages of matrix work
+  // cover their latency.
+  u32x4 ra0[BG_ALD], rb0[BG_BLD], ra1[BG_ALD], rb1[BG_BLD];
+#define BW_GLOAD(kt, RA, RB)                                                                     \
   do {                                                                                           \
     const int ko_ = (kt) * BG_BK;                                                                \
     const int kb_ = MODE == BW_DGRAD2 ? ((kt) % p.kwrap) * BG_BK : ko_;                          \
-    _Pragma("unroll") for (int j = 0; j < BG_ALD; ++j) ra[j] = *(const u32x4*)(arow[j] + ko_);   \
-    _Pragma("unroll") for (int j = 0; j < BG_BLD; ++j) rb[j] = *(const u32x4*)(brow[j] + kb_);   \
+    _Pragma("unroll") for (int j = 0; j < BG_ALD; ++j) RA[j] = *(const u32x4*)(arow[j] + ko_);   \
+    _Pragma("unroll") for (int j = 0; j < BG_BLD; ++j) RB[j] = *(const u32x4*)(brow[j] + kb_);   \
   } while (0)
-#define BW_LSTORE(slot)                                                                          \
+#define BW_LSTORE(slot, RA, RB)                                                                  \
   do {                                                                                           \
     uint8_t* s_ = smem + (slot) * BG_STAGE;                                                      \
     _Pragma("unroll") for (int j = 0; j < BG_ALD; ++j)                                           \
-      *(u32x4*)(s_ + swz<BG_CPR>(ar[j], cch)) = ra[j];                                           \
+      *(u32x4*)(s_ + swz<BG_CPR>(ar[j], cch)) = RA[j];                                           \
     _Pragma("unroll") for (int j = 0; j < BG_BLD; ++j)                                           \
-      *(u32x4*)(s_ + BG_A_BYTES + swz<BG_CPR>(br[j], cch)) = rb[j];                              \
+      *(u32x4*)(s_ + BG_A_BYTES + swz<BG_CPR>(br[j], cch)) = RB[j];                              \
   } while (0)
-
   // a wave whose 64 rows are all padding skips its matrix instructions
   const bool active = wm * BG_WTM < rows;
   const int arow0 = wm * BG_WTM + (lane & 31);
   const int brow0 = wn * BG_WTN + (lane & 31);
+#define BW_COMPUTE(slot)                                                                         \
+  do {                                                                                           \
+    if (active) {                                                                                \
+      const uint8_t* sa = smem + (slot) * BG_STAGE;                                              \
+      const uint8_t* sb = sa + BG_A_BYTES;                                                       \
+      _Pragma("unroll") for (int ks = 0; ks < BG_BK / 16; ++ks) {                                \
+        const int cc = kg * (BG_BK / 16) + ks;                                                   \
+        bf16x8 fa[BG_FM], fb[BG_FN];                                                             \
+        _Pragma("unroll") for (int i = 0; i < BG_FM; ++i)                                        \
+          fa[i] = *(const bf16x8*)(sa + swz<BG_CPR>(arow0 + 32 * i, cc));                        \
+        _Pragma("unroll") for (int j = 0; j < BG_FN; ++j)                                        \
+          fb[j] = *(const bf16x8*)(sb + swz<BG_CPR>(brow0 + 32 * j, cc));                        \
+        _Pragma("unroll") for (int i = 0; i < BG_FM; ++i)                                        \
+        _Pragma("unroll") for (int j = 0; j < BG_FN; ++j)                                        \
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0); \
+      }                                                                                          \
+    }                                                                                            \
+  } while (0)
+  // The loads are unconditional (past the last stage they fetch the last stage again): with
+  // loads under a condition the compiler's wait counts assume the newest loads may be the
+  // ones a store needs, and the stores then wait for everything in flight.
   if (nk > 0) {
-    BW_GLOAD(0);
-    BW_LSTORE(0);
-  }
-  for (int kt = 0; kt < nk; ++kt) {
-    __syncthreads();                       // stage kt landed; stage kt + 1's slot is free
-    if (kt + 1 < nk) BW_GLOAD(kt + 1);
-    if (active) {
-      const uint8_t* sa = smem + (kt & 1) * BG_STAGE;
-      const uint8_t* sb = sa + BG_A_BYTES;
-#pragma unroll
-      for (int ks = 0; ks < BG_BK / 16; ++ks) {
-        const int cc = kg * (BG_BK / 16) + ks;
-        bf16x8 fa[BG_FM], fb[BG_FN];
-#pragma unroll
-        for (int i = 0; i < BG_FM; ++i) fa[i] = *(const bf16x8*)(sa + swz<BG_CPR>(arow0 + 32 * i, cc));
-#pragma unroll
-        for (int j = 0; j < BG_FN; ++j) fb[j] = *(const bf16x8*)(sb + swz<BG_CPR>(brow0 + 32 * j, cc));
-#pragma unroll
-        for (int i = 0; i < BG_FM; ++i)
-#pragma unroll
-          for (int j = 0; j < BG_FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-      }
+    BW_GLOAD(0, ra0, rb0);
+    BW_LSTORE(0, ra0, rb0);
+    BW_GLOAD(min(1, nk - 1), ra1, rb1);
+    for (int kt = 0; kt < nk; kt += 2) {
+      // even stage kt in slot 0; stage kt + 1 in flight in set 1
+      __syncthreads();
+      BW_GLOAD(min(kt + 2, nk - 1), ra0, rb0);
+      BW_COMPUTE(0);
+      BW_LSTORE(1, ra1, rb1);
+      // odd stage kt + 1 in slot 1; stage kt + 2 in flight in set 0
+      __syncthreads();
+      BW_GLOAD(min(kt + 3, nk - 1), ra1, rb1);
+      if (kt + 1 < nk) BW_COMPUTE(1);
+      BW_LSTORE(0, ra0, rb0);
     }
-    if (kt + 1 < nk) BW_LSTORE((kt + 1) & 1);
   }
 #undef BW_GLOAD
 #undef BW_LSTORE
+#undef BW_COMPUTE
   __syncthreads();                         // tab_a / tab_g visible (also when nk == 0)
 
   // ---- epilogue.  Row rr of the tile for register q of fragment i; column cc for fragment j.
@@ -366,7 +390,9 @@ int64_t row_tiles_bound(int64_t A, int E) {
 
 // ------------------------------------------------------------------------------ routing helpers
 // Padded column offsets of the experts in the transposed activations: expert e's rows
-// occupy columns [poff[e], poff[e + 1]), its count rounded up to a multiple of 64.
+// occupy columns [poff[e], poff[e + 1]), its count rounded up to a multiple of 64.  Then
+// poff[E + 1 + r] = the expert of rank r by decreasing padded count (ties: lower index), the
+// order in which the weight-gradient tiles are dispatched.
 __global__ __launch_bounds__(256) void pad_offsets_kernel(const int32_t* __restrict__ offsets, int E,
                                                           int32_t* __restrict__ poff) {
   __shared__ int s[257];
@@ -376,6 +402,13 @@ __global__ __launch_bounds__(256) void pad_offsets_kernel(const int32_t* __restr
     s[tid + 1] = (max(c, 0) + BG_BK - 1) / BG_BK * BG_BK;
   }
   if (tid == 0) s[0] = 0;
+  __syncthreads();
+  if (tid < E) {
+    const int kc = s[tid + 1];
+    int rk = 0;
+    for (int o = 0; o < E; ++o) rk += (s[o + 1] > kc || (s[o + 1] == kc && o < tid)) ? 1 : 0;
+    poff[E + 1 + rk] = tid;
+  }
   __syncthreads();
   if (tid == 0)
     for (int i = 1; i <= E; ++i) s[i] += s[i - 1];
@@ -423,40 +456,55 @@ __global__ __launch_bounds__(256) void f32_to_bf16_pair_kernel(const float4* __r
   row[D4 + c] = uint2{pack_bf16x2(v.x - h0, v.y - h1), pack_bf16x2(v.z - h2, v.w - h3)};
 }
 
-// Transpose of each of B matrices [R][C] (bf16) into [C][R], 64 x 64 tiles through LDS.
+// 64 x 64 bf16 tiles through LDS with 16-byte global accesses: phase 1 puts tile row r
+// (8-element chunks) in LDS row r, phase 2 writes output row c as eight 8-element chunks,
+// each gathered from one LDS column.  Row stride 72 elements keeps LDS rows 16-byte aligned.
+constexpr int TP_LD = 72;
+static __device__ __forceinline__ void tile_out(const uint16_t (*t)[TP_LD], int c, int ch, uint16_t* dst) {
+  u32x4 v;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    v[q] = (uint32_t)t[ch * 8 + 2 * q][c] | ((uint32_t)t[ch * 8 + 2 * q + 1][c] << 16);
+  *(u32x4*)dst = v;
+}
+
+// Transpose of each of B matrices [R][C] (bf16) into [C][R]; R and C multiples of 64.
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src, int R, int C,
                                                              uint16_t* __restrict__ dst) {
-  __shared__ uint16_t t[64][65];
+  __shared__ __attribute__((aligned(16))) uint16_t t[64][TP_LD];
   const int64_t b = blockIdx.z;
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
   const uint16_t* s = src + b * R * (int64_t)C;
   uint16_t* d = dst + b * R * (int64_t)C;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int r = ty; r < 64; r += 4)
-    if (r0 + r < R && c0 + tx < C) t[r][tx] = s[(int64_t)(r0 + r) * C + c0 + tx];
+  for (int i = threadIdx.x; i < 512; i += 256) {
+    const int r = i >> 3, ch = i & 7;
+    *(u32x4*)&t[r][ch * 8] = *(const u32x4*)(s + (int64_t)(r0 + r) * C + c0 + ch * 8);
+  }
   __syncthreads();
-  for (int c = ty; c < 64; c += 4)
-    if (c0 + c < C && r0 + tx < R) d[(int64_t)(c0 + c) * R + r0 + tx] = t[tx][c];
+  for (int i = threadIdx.x; i < 512; i += 256) {
+    const int c = i >> 3, ch = i & 7;
+    tile_out(t, c, ch, d + (int64_t)(c0 + c) * R + r0 + ch * 8);
+  }
 }
 
 // Transposed, expert-padded copy of routed rows: dst[c][col] = scale(col) src[row(col)][c]
-// for the C columns of the rows, zero where padmap[col] < 0.  SRC_TOKEN: the source row is
-// the token of the routed row's assignment (x, dout), else the routed row itself (du, h).
-// GATE: scaled by the assignment's gate (dz = g dout).  SRC_F32: fp32 source.
+// for the C columns of the rows (C a multiple of 64), zero where padmap[col] < 0.
+// SRC_TOKEN: the source row is the token of the routed row's assignment (x, dout), else the
+// routed row itself (du, h).  GATE: scaled by the assignment's gate (dz = g dout).  SRC_F32:
+// fp32 source.
 template <bool SRC_TOKEN, bool GATE, bool SRC_F32>
 __global__ __launch_bounds__(256) void gather_transpose_kernel(const void* __restrict__ src, int C, int ld_src,
                                                                const int32_t* __restrict__ padmap,
                                                                const int32_t* __restrict__ perm,
                                                                const float* __restrict__ gates, int k, int A,
                                                                int ldt, uint16_t* __restrict__ dst) {
-  __shared__ uint16_t t[64][65];
+  __shared__ __attribute__((aligned(16))) uint16_t t[64][TP_LD];
   const int col0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int r = ty; r < 64; r += 4) {        // r: column of the padded layout (a routed row)
-    const int col = col0 + r;
-    float v = 0.f;
-    const int prow = col < ldt ? padmap[col] : -1;
-    if (prow >= 0 && c0 + tx < C) {
+  for (int i = threadIdx.x; i < 512; i += 256) {
+    const int r = i >> 3, ch = i & 7;          // r: column of the padded layout (a routed row)
+    const int prow = padmap[col0 + r];
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (prow >= 0) {
       int64_t srow = prow;
       float sc = 1.f;
       if (SRC_TOKEN || GATE) {
@@ -465,15 +513,29 @@ __global__ __launch_bounds__(256) void gather_transpose_kernel(const void* __res
         if (SRC_TOKEN) srow = a / k;
         if (GATE) sc = gates[a];
       }
-      if (SRC_F32) v = ((const float*)src)[srow * ld_src + c0 + tx] * sc;
-      else v = bf16_to_f32(((const uint16_t*)src)[srow * ld_src + c0 + tx]) * sc;
+      if (SRC_F32) {
+        const float* sp = (const float*)src + srow * ld_src + c0 + ch * 8;
+        const f32x4 lo = *(const f32x4*)sp, hi = *(const f32x4*)(sp + 4);
+        v[0] = pack_bf16x2(lo[0] * sc, lo[1] * sc);
+        v[1] = pack_bf16x2(lo[2] * sc, lo[3] * sc);
+        v[2] = pack_bf16x2(hi[0] * sc, hi[1] * sc);
+        v[3] = pack_bf16x2(hi[2] * sc, hi[3] * sc);
+      } else {
+        v = *(const u32x4*)((const uint16_t*)src + srow * ld_src + c0 + ch * 8);
+        if (GATE) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            v[q] = pack_bf16x2(bf16_to_f32(v[q] & 0xFFFFu) * sc, bf16_to_f32(v[q] >> 16) * sc);
+        }
+      }
     }
-    const __bf16 bv = (__bf16)v;
-    t[r][tx] = *(const uint16_t*)&bv;
+    *(u32x4*)&t[r][ch * 8] = v;
   }
   __syncthreads();
-  for (int c = ty; c < 64; c += 4)
-    if (c0 + c < C && col0 + tx < ldt) dst[(int64_t)(c0 + c) * ldt + col0 + tx] = t[tx][c];
+  for (int i = threadIdx.x; i < 512; i += 256) {
+    const int c = i >> 3, ch = i & 7;
+    tile_out(t, c, ch, dst + (int64_t)(c0 + c) * ldt + col0 + ch * 8);
+  }
 }
 
 // ------------------------------------------------------------------------------ router

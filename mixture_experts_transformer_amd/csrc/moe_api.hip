@@ -143,7 +143,7 @@ BwdLayout bwd_layout(int64_t T, int64_t D, int64_t E, int64_t k, int64_t F) {
     off += align256(bytes);
     return at;
   };
-  L.poff = take(((size_t)E + 1) * 4);
+  L.poff = take((2 * (size_t)E + 1) * 4);
   L.padmap = take(ldt * 4);
   L.dout16 = take((size_t)T * D * 4);
   L.w1t = take((size_t)E * G * D * 2);

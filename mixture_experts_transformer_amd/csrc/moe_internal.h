@@ -95,7 +95,8 @@ struct BwdArgs {
   const float* dout;        // [T][D]
   float *dx, *dwr, *dbr, *dw1, *db1, *dw2, *db2;   // outputs (fp32)
   // workspace
-  int32_t* poff;            // [E+1] padded column offsets per expert
+  int32_t* poff;            // [E+1] padded column offsets per expert, then [E] the experts by
+                            //   decreasing padded row count
   int32_t* padmap;          // [ldt] routed row of each padded column, -1 for padding
   uint16_t* dout16;         // [T][2D] bf16 pairs: hi then lo
   uint16_t* w1t;            // [E][D][2F]

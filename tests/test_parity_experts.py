@@ -84,6 +84,25 @@ def test_experts_with_clamped_swiglu():
     experts_vs_oracle(inp, "clamped SwiGLU")
 
 
+@pytest.mark.parametrize("fmt,T", [("mxfp4", 200), ("mxfp4", 2000), ("mxfp8", 200), ("mxfp8", 2000)])
+def test_experts_with_clamped_swiglu_mx(fmt, T):
+    """The same for MX weights, on the streaming tiles (200 tokens) and the matrix-core tiles
+    (2000 tokens: the scaled fp8 x fp4 engine for MXFP4): block scales raised until mlp1's
+    outputs pass the limit on both sides; every W2 scale byte lowered by 4 (exact: a power of
+    two) so the output keeps a moderate size."""
+    E, D, F = 4, 256, 128
+    scale = (-3, -1) if fmt == "mxfp4" else (-8, -6)
+    cfg = get_config(BASE[fmt], name=f"clamp{fmt}{T}", T=T, D=D, E=E, k=2, F=F, seed=9 + T, scale_exp=scale)
+    inp = make_inputs(cfg)
+    u = oracle.bf16_to_f64(inp.x) @ oracle.expert_weight(inp.w1, fmt, E, 2 * F, D, 0).T
+    assert (u[:, :F] > 7).mean() > 0.1 and (u[:, F:] < -7).mean() > 0.1 and (u[:, F:] > 7).mean() > 0.1
+    w2 = inp.w2.copy()
+    codes = E * D * (F // 2 if fmt == "mxfp4" else F)
+    w2[codes:] -= 4
+    inp.w2 = w2
+    experts_vs_oracle(inp, f"clamped SwiGLU {fmt} T={T}")
+
+
 # Weight buffers 16 or 48 bytes past a line boundary: the streaming tiles then copy code
 # windows from each row's own start (no line alignment) and bf16 rows without the
 # non-temporal hint, and the matrix-core tiles read unaligned windows too.

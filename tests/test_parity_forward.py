@@ -3,9 +3,9 @@
 Small workloads are compared on every output.  At the large ones the integer routing is
 compared in full (through moe_route, same kernels as moe_forward) and the fp32 output on a
 sample of tokens the oracle evaluates on its own: a token's output depends only on its
-own row, so the oracle runs the block on the sampled rows alone.  The C5 sample is drawn
-from tokens whose experts lie in a bounded set (the most loaded experts plus some of the
-least loaded) to keep the oracle's MXFP4 decoding to a few experts."""
+own row, so the oracle runs the block on the sampled rows alone.  The C5 sample takes, for
+every live expert, the first token routed to it, plus random tokens, so every expert's tiles
+(the Zipf head, the middle and the tail, on the scaled matrix-core engine) are compared."""
 import numpy as np
 import pytest
 import torch
@@ -43,16 +43,13 @@ def pick_sample(name, idx, E, n):
         return np.sort(g.choice(T, size=n, replace=False))
     counts = np.bincount(idx.reshape(-1), minlength=E)
     live = np.flatnonzero(counts)
-    order = live[np.argsort(-counts[live], kind="stable")]
-    allowed = set(order[:10].tolist()) | set(order[-4:].tolist())
-    ok = np.array([set(row.tolist()) <= allowed for row in idx])
-    cand = np.flatnonzero(ok)
-    # every allowed tail expert appears in the sample when some token reaches it
-    tail = [np.flatnonzero(ok & (idx == e).any(axis=1))[:2] for e in order[-4:]]
-    return np.unique(np.concatenate([g.choice(cand, size=min(n, cand.size), replace=False)] + tail))
+    first = [int(np.flatnonzero((idx == e).any(axis=1))[0]) for e in live]
+    sample = np.unique(np.concatenate([np.array(first), g.choice(T, size=n, replace=False)]))
+    assert np.array_equal(np.unique(idx[sample]), live)      # every live expert is compared
+    return sample
 
 
-@pytest.mark.parametrize("name,n", [("C3", 256), ("C4", 256), ("X2", 256), ("C5", 128), ("Y2", 256)])
+@pytest.mark.parametrize("name,n", [("C3", 256), ("C4", 256), ("X2", 256), ("C5", 64), ("Y2", 256)])
 def test_forward_large_sampled(name, n):
     inp = make_inputs(name)
     cfg = inp.cfg
@@ -74,7 +71,7 @@ def test_forward_large_sampled(name, n):
     assert_close(got[sample], ref, f"forward {name} ({sample.size} sampled tokens)")
 
 
-@pytest.mark.parametrize("name", ["C3", "C4", "Y2"])
+@pytest.mark.parametrize("name", ["C2", "C3", "C4", "C5", "X1", "X2", "Y2"])
 def test_forward_is_bitwise_deterministic(name):
     inp = make_inputs(name)
     d = upload(inp)
