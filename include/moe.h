@@ -211,10 +211,11 @@ int moe_experts(const void* x, const void* w1, const void* b1, const void* w2, c
  * dW1[e] += du^T x[t], db1[e] += du and dx[t] += du W1[e]; dg = <dout[t], h W2[e]^T + b2[e]>;
  * the softmax over the selected logits gives dl = g (dg - sum_j g_j dg_j), then
  * d_router_w[e] += dl x[t], d_router_b[e] += dl and dx[t] += dl router_w[e].  The matrix
- * products run on the bf16 matrix cores with fp32 accumulation: dout enters the product with
- * W2 as a bf16 pair (hi + lo, about 16 significant bits), while dz, du and h enter theirs
- * rounded to bf16, which bounds the relative error of each gradient near 2^-9; every sum has
- * a fixed order, so the result is bitwise reproducible.  With
+ * products run on the bf16 matrix cores with fp32 accumulation (the products over routed rows
+ * on the forward's grouped GEMM kernels, the weights transposed once per call): dout enters
+ * the product with W2 as a bf16 pair (hi + lo, about 16 significant bits), while dz, du and h
+ * enter theirs rounded to bf16, which bounds the relative error of each gradient near 2^-9;
+ * every sum has a fixed order, so the result is bitwise reproducible.  With
  * T = 0 the parameter gradients are set to zero.  Uses moe_backward_workspace_bytes of
  * workspace (the same workspace rules as the forward).  Timed as stage 7 by moe_profile_*. */
 int moe_backward(const void* x, const void* router_w, const void* w1, const void* b1,

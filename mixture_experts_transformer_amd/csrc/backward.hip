@@ -6,22 +6,24 @@
 // is piecewise constant in the inputs, so gradients reach the router only through the
 // softmax gates.  Per assignment a = t*k + j (expert e, gate g, row p of e's group):
 //
-//   u  = x[t] W1[e]^T + b1[e]                          (recomputed: grouped GEMM, K = D)
-//   dh' = dout[t] W2[e]                                 (grouped GEMM, K = D; ungated)
+//   u  = x[t] W1[e]^T + b1[e]                          (recomputed: the forward's mlp1 kernel)
+//   dh' = dout[t] W2[e]                                 (the forward's mlp2 kernel on W2^T)
 //   dg[a] = <dh', h(u)> + <dout[t], b2[e]>              (= <dout[t], z[a]>, z the ungated mlp2 output)
-//   du = SwiGLU'(u) * (g dh')                           (in that GEMM's epilogue)
-//   dx[t] += du W1[e]                                   (grouped GEMM, K = 2F)
+//   du = SwiGLU'(u) * (g dh')
+//   dx[t] += du W1[e]                                   (the forward's mlp2 kernel on W1^T)
 //   dW2[e] = sum_p (g dout[t])^T h,  dW1[e] = sum_p du^T x[t]   (per-expert GEMMs, K = rows)
 //   db2[e] = sum_p g dout[t],  db1[e] = sum_p du
 //   router: dl = g (dg - sum_j g_j dg_j) on the selected experts; dWr[e] = sum dl x[t],
 //   dbr[e] = sum dl, dx[t] += sum_j dl_j Wr[e_j].
 //
-// Every matrix product runs on v_mfma_f32_32x32x16_bf16 in one kernel (bwd_gemm_kernel)
-// whose operands are K-contiguous rows: the weights are transposed once per call for the
-// two products that contract over their other dimension, and the activations that the
-// weight-gradient products contract over their rows are written transposed, per expert, in
-// a layout whose expert blocks are padded to 64 rows with zeros.  No float atomics: every
-// sum runs in a fixed order, so the gradients are bitwise reproducible.
+// The three products over routed rows are the forward's grouped GEMMs (grouped_gemm_kernel):
+// mlp1 with an epilogue that stores u instead of h, and mlp2 with unit gates and zero biases
+// for dh' and for du W1 (their weights transposed once per call; dout enters as a bf16 pair,
+// the K dimension doubled: [hi | lo] against [W2^T | W2^T]).  The weight gradients contract
+// over an expert's rows, so their operands are written transposed, per expert, in a layout
+// whose expert blocks are padded to 64 rows with zeros, and multiplied by bwd_gemm_kernel.
+// Everything runs on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  No float atomics:
+// every sum runs in a fixed order, so the gradients are bitwise reproducible.
 #include "device_common.h"
 
 namespace moe {
@@ -33,10 +35,11 @@ constexpr float BW_LIMIT = 7.0f;
 constexpr float BW_NEG_ALPHA_LOG2E = -BW_ALPHA * 1.4426950408889634f;
 
 // ------------------------------------------------------------------------------ GEMM tile
-// 256 x 128 outputs per workgroup, 8 waves in a 4 x 2 grid of 64 x 64, K in steps of 64
-// (whole 128-byte row segments per stage), two LDS stages filled through registers.
-constexpr int BG_BM = 256, BG_BN = 128, BG_BK = 64, BG_CPR = BG_BK / 8;
-constexpr int BG_WAVES_M = 4, BG_WAVES_N = 2, BG_NW = BG_WAVES_M * BG_WAVES_N, BG_THREADS = 64 * BG_NW;
+// Weight-gradient tiles: 256 x 128 outputs per workgroup, 8 waves in a 4 x 2 grid of 64 x 64,
+// K in steps of 64 (whole 128-byte row segments per stage), two LDS stages filled through
+// registers.
+constexpr int BG_BM = 256, BG_BN = 256, BG_BK = 64, BG_CPR = BG_BK / 8;
+constexpr int BG_WAVES_M = 2, BG_WAVES_N = 4, BG_NW = BG_WAVES_M * BG_WAVES_N, BG_THREADS = 64 * BG_NW;
 constexpr int BG_WTM = BG_BM / BG_WAVES_M, BG_WTN = BG_BN / BG_WAVES_N;
 constexpr int BG_FM = BG_WTM / 32, BG_FN = BG_WTN / 32;
 constexpr int BG_A_BYTES = BG_BM * BG_BK * 2;
@@ -46,47 +49,26 @@ constexpr int BG_ALD = BG_BM * BG_CPR / BG_THREADS;   // 16-byte A chunks per th
 constexpr int BG_BLD = BG_BN * BG_CPR / BG_THREADS;   // B chunks
 static_assert(BG_ALD * BG_THREADS == BG_BM * BG_CPR && BG_BLD * BG_THREADS == BG_BN * BG_CPR, "load split");
 
-enum BwdMode { BW_RECOMP = 0, BW_DGRAD2 = 1, BW_DGRAD1 = 2, BW_WGRAD = 3 };
-
 struct BwdGemmArgs {
-  const int32_t* offsets;   // [E+1] group offsets of the routed rows (grouped modes)
-  const int32_t* perm;      // [A] assignment of each routed row
-  const float* gates;       // [A] gate of each assignment
   const int32_t* poff;      // [E+1] padded column offsets, then [E] the experts by decreasing
-                            //   padded row count (weight-gradient mode)
+                            //   padded row count
   const uint16_t* a;        // A operand rows (bf16, K contiguous), lda elements apart
-  const uint16_t* b;        // B operand rows, ldb elements apart; grouped modes: expert e's
-  int64_t b_expert;         //   rows start b_expert elements after expert e - 1's
+  const uint16_t* b;        // B operand rows, ldb elements apart
   int lda, ldb;
-  int E, k, A, K, M, N, F;
+  int E, M, N;
   int n_tiles, m_tiles;
-  int kwrap;                // dgrad2: K stages after which B's K offset starts again (A = [hi | lo])
-  const uint16_t* bias;     // recompute: b1 [E][N]
-  float* c;                 // recompute: u [A][N]; dgrad1: [A][N] at slot rows; wgrad: [E][M][N]
-  const float* u;           // dgrad2: u [A][2F]
-  uint16_t* h;              // dgrad2: h [A][F]
-  uint16_t* du;             // dgrad2: du [A][2F]
-  float* dgpart;            // dgrad2: [n_tiles][A] partial <dh', h> per column tile
+  float* c;                 // [E][M][N]
 };
 
-// MODE selects the operands and the epilogue:
-//   BW_RECOMP  A = x rows gathered by token, B = W1[e] rows (K = D): u = acc + b1 -> c (fp32)
-//   BW_DGRAD2  A = dout rows gathered by token as a bf16 pair [hi | lo] (K = 2D), B = W2^T[e]
-//              rows read twice (K offset modulo D): dh' = acc to about 16 significant bits of
-//              dout; writes h, du (bf16) and the per-tile partial <dh', h>
-//   BW_DGRAD1  A = du rows in place, B = W1^T[e] rows (K = 2F): acc -> c at the slot row
-//   BW_WGRAD   per expert: A = rows of a transposed activation, B = rows of another (K =
-//              the expert's padded row count): acc -> dW[e]
+// Per-expert weight gradient C[e] = A_e B_e^T: A_e = rows of a transposed activation and B_e
+// rows of another, both restricted to expert e's padded columns [poff[e], poff[e + 1]) (the
+// K of the product: the expert's rows, zero past its count).
 //
 // Matrix-core mapping as in the forward's grouped GEMM: in MFMA step ks of a stage, lane l
 // feeds row l & 31 and the 8 K elements of chunk 4 (l >> 5) + ks of each operand, and output
 // register q of lane l is C[8 (q >> 2) + 4 (l >> 5) + (q & 3)][l & 31].
-template <int MODE>
 __global__ __launch_bounds__(BG_THREADS, 1) void bwd_gemm_kernel(BwdGemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BG_STAGE];
-  __shared__ int tab_a[BG_BM];
-  __shared__ float tab_g[BG_BM];
-  __shared__ float red[BG_WAVES_N][BG_BM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -94,67 +76,30 @@ __global__ __launch_bounds__(BG_THREADS, 1) void bwd_gemm_kernel(BwdGemmArgs p) 
   const int wm = wave / BG_WAVES_N, wn = wave % BG_WAVES_N;
   const int kg = lane >> 5;
 
-  // ---- which tile: the tiles that exist, XCD x (block ids congruent to x mod 8) taking the
-  // x-th eighth of them, in groups of four row tiles so neighbouring workgroups share rows
-  int e = 0, row0 = 0, rows = 0, gbase = 0, m0 = 0, n_tile = 0, K = p.K;
+  // ---- which tile: the tiles cost their expert's row count, so the largest experts go
+  // first (dispatched first and spread over every XCD) and the Zipf head does not trail;
+  // in groups of four row tiles so neighbouring workgroups share operand rows
+  int e, m0, n_tile, rows;
   {
     constexpr int GM = 4;
-    int total, mt_total;
-    TileScan ts;
-    if (MODE == BW_WGRAD) {
-      mt_total = p.E * p.m_tiles;
-    } else {
-      ts = tile_scan<BG_BM>(p.offsets, p.E);
-      mt_total = ts.total;
-    }
-    total = mt_total * p.n_tiles;
-    int lin;
-    if (MODE == BW_WGRAD) {
-      // the experts' weight-gradient tiles cost their row counts: largest experts first
-      // (dispatched first and spread over every XCD), so the Zipf head does not trail
-      lin = blockIdx.x;
-      if (lin >= total) return;
-    } else {
-      const int share = (total + 7) >> 3;
-      const int xl = blockIdx.x >> 3;
-      lin = (blockIdx.x & 7) * share + xl;
-      if (xl >= share || lin >= total) return;
-    }
+    const int mt_total = p.E * p.m_tiles;
+    const int total = mt_total * p.n_tiles;
+    const int lin = blockIdx.x;
+    if (lin >= total) return;
     const int gsize = GM * p.n_tiles;
     const int g = lin / gsize;
     const int first_m = g * GM;
     const int gm = min(mt_total - first_m, GM);
     const int m_tile = first_m + (lin % gsize) % gm;
     n_tile = (lin % gsize) / gm;
-    if (MODE == BW_WGRAD) {
-      // the expert of rank m_tile / m_tiles in decreasing padded row count
-      e = p.poff[p.E + 1 + m_tile / p.m_tiles];
-      m0 = (m_tile % p.m_tiles) * BG_BM;
-      rows = min(BG_BM, p.M - m0);
-      K = p.poff[e + 1] - p.poff[e];
-    } else {
-      int cnt;
-      if (!tile_lookup<BG_BM>(ts, p.offsets, m_tile, e, row0, cnt)) return;
-      gbase = p.offsets[e] + row0;
-      rows = min(BG_BM, cnt - row0);
-      if (gbase < 0 || rows <= 0 || gbase + rows > p.A) return;
-    }
+    // the expert of rank m_tile / m_tiles in decreasing padded row count
+    e = p.poff[p.E + 1 + m_tile / p.m_tiles];
+    m0 = (m_tile % p.m_tiles) * BG_BM;
+    rows = min(BG_BM, p.M - m0);
   }
+  const int K = p.poff[e + 1] - p.poff[e];
   const int n0 = n_tile * BG_BN;
   const int nk = K / BG_BK;
-
-  // routed rows of the tile: assignment and gate (grouped modes)
-  if (MODE != BW_WGRAD && tid < BG_BM) {
-    int a = -1;
-    float g = 0.f;
-    if (tid < rows) {
-      a = p.perm[gbase + tid];
-      a = ((unsigned)a < (unsigned)p.A) ? a : -1;
-      if (MODE == BW_DGRAD2 && a >= 0) g = p.gates[a];
-    }
-    tab_a[tid] = a;
-    tab_g[tid] = g;
-  }
 
   // ---- this thread's copy rows: chunk c of tile rows (tid / CPR) + (THREADS / CPR) j
   const int cch = tid % BG_CPR;
@@ -165,28 +110,13 @@ __global__ __launch_bounds__(BG_THREADS, 1) void bwd_gemm_kernel(BwdGemmArgs p) 
   for (int j = 0; j < BG_ALD; ++j) {
     const int r = tid / BG_CPR + (BG_THREADS / BG_CPR) * j;
     ar[j] = r;
-    int64_t src;
-    if (MODE == BW_WGRAD) {
-      src = (int64_t)min(m0 + r, p.M - 1) * p.lda + p.poff[e];
-    } else {
-      const int rc = min(r, rows - 1);
-      if (MODE == BW_DGRAD1) {
-        src = (int64_t)(gbase + rc) * p.lda;
-      } else {
-        int asg = p.perm[gbase + rc];
-        asg = ((unsigned)asg < (unsigned)p.A) ? asg : 0;
-        src = (int64_t)(asg / p.k) * p.lda;
-      }
-    }
-    arow[j] = p.a + src + cch * 8;
+    arow[j] = p.a + (int64_t)min(m0 + r, p.M - 1) * p.lda + p.poff[e] + cch * 8;
   }
 #pragma unroll
   for (int j = 0; j < BG_BLD; ++j) {
     const int r = tid / BG_CPR + (BG_THREADS / BG_CPR) * j;
     br[j] = r;
-    const int n = min(n0 + r, p.N - 1);
-    if (MODE == BW_WGRAD) brow[j] = p.b + (int64_t)n * p.ldb + p.poff[e] + cch * 8;
-    else brow[j] = p.b + (int64_t)e * p.b_expert + (int64_t)n * p.ldb + cch * 8;
+    brow[j] = p.b + (int64_t)min(n0 + r, p.N - 1) * p.ldb + p.poff[e] + cch * 8;
   }
 
   f32x16 acc[BG_FM][BG_FN];
@@ -206,9 +136,8 @@ __global__ __launch_bounds__(BG_THREADS, 1) void bwd_gemm_kernel(BwdGemmArgs p) 
 #define BW_GLOAD(kt, RA, RB)                                                                     \
   do {                                                                                           \
     const int ko_ = (kt) * BG_BK;                                                                \
-    const int kb_ = MODE == BW_DGRAD2 ? ((kt) % p.kwrap) * BG_BK : ko_;                          \
     _Pragma("unroll") for (int j = 0; j < BG_ALD; ++j) RA[j] = *(const u32x4*)(arow[j] + ko_);   \
-    _Pragma("unroll") for (int j = 0; j < BG_BLD; ++j) RB[j] = *(const u32x4*)(brow[j] + kb_);   \
+    _Pragma("unroll") for (int j = 0; j < BG_BLD; ++j) RB[j] = *(const u32x4*)(brow[j] + ko_);   \
   } while (0)
 #define BW_LSTORE(slot, RA, RB)                                                                  \
   do {                                                                                           \
@@ -263,129 +192,27 @@ __global__ __launch_bounds__(BG_THREADS, 1) void bwd_gemm_kernel(BwdGemmArgs p) 
 #undef BW_GLOAD
 #undef BW_LSTORE
 #undef BW_COMPUTE
-  __syncthreads();                         // tab_a / tab_g visible (also when nk == 0)
 
-  // ---- epilogue.  Row rr of the tile for register q of fragment i; column cc for fragment j.
-  if (MODE == BW_RECOMP) {
+  // ---- epilogue: row rr of the tile for register q of fragment i, column for fragment j
+  float* const dst = p.c + (int64_t)e * p.M * p.N;
 #pragma unroll
-    for (int j = 0; j < BG_FN; ++j) {
-      const int n = n0 + wn * BG_WTN + 32 * j + (lane & 31);
-      if (n >= p.N) continue;
-      const float bv = bf16_to_f32(p.bias[(int64_t)e * p.N + n]);
-#pragma unroll
-      for (int i = 0; i < BG_FM; ++i)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int rr = wm * BG_WTM + 32 * i + 8 * (q >> 2) + 4 * kg + (q & 3);
-          if (rr < rows) p.c[(int64_t)(gbase + rr) * p.N + n] = acc[i][j][q] + bv;
-        }
-    }
-  } else if (MODE == BW_DGRAD1) {
-#pragma unroll
-    for (int j = 0; j < BG_FN; ++j) {
-      const int n = n0 + wn * BG_WTN + 32 * j + (lane & 31);
-      if (n >= p.N) continue;
-#pragma unroll
-      for (int i = 0; i < BG_FM; ++i)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int rr = wm * BG_WTM + 32 * i + 8 * (q >> 2) + 4 * kg + (q & 3);
-          if (rr < rows) {
-            const int a = tab_a[rr];
-            if (a >= 0) p.c[(int64_t)a * p.N + n] = acc[i][j][q];
-          }
-        }
-    }
-  } else if (MODE == BW_WGRAD) {
-    float* const dst = p.c + (int64_t)e * p.M * p.N;
-#pragma unroll
-    for (int j = 0; j < BG_FN; ++j) {
-      const int n = n0 + wn * BG_WTN + 32 * j + (lane & 31);
-      if (n >= p.N) continue;
-#pragma unroll
-      for (int i = 0; i < BG_FM; ++i)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int rr = wm * BG_WTM + 32 * i + 8 * (q >> 2) + 4 * kg + (q & 3);
-          if (rr < rows) dst[(int64_t)(m0 + rr) * p.N + n] = acc[i][j][q];
-        }
-    }
-  } else {
-    // dgrad2: acc = dh'[row][f] = dout[t] . W2[e][:, f]; the clamped SwiGLU of u gives h and
-    // its two partial derivatives, du = SwiGLU' * g dh', and each row's <dh', h> over this
-    // tile's columns (summed across lanes and waves in a fixed order)
-    const int F = p.F;
-    const int64_t ldu = 2 * (int64_t)F;
-    float rs[BG_FM][16];
-#pragma unroll
-    for (int i = 0; i < BG_FM; ++i)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) rs[i][q] = 0.f;
-#pragma unroll
-    for (int j = 0; j < BG_FN; ++j) {
-      const int f = n0 + wn * BG_WTN + 32 * j + (lane & 31);
-      if (f >= F) continue;
-#pragma unroll
-      for (int i = 0; i < BG_FM; ++i)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int rr = wm * BG_WTM + 32 * i + 8 * (q >> 2) + 4 * kg + (q & 3);
-          if (rr >= rows) continue;
-          const int64_t prow = gbase + rr;
-          const float ug = p.u[prow * ldu + f];
-          const float ul = p.u[prow * ldu + F + f];
-          const float gc = fminf(ug, BW_LIMIT);
-          const float lc = fminf(fmaxf(ul, -BW_LIMIT), BW_LIMIT);
-          // sigmoid(ALPHA gc) = 1 / (1 + 2^(-ALPHA log2(e) gc))
-          const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(gc * BW_NEG_ALPHA_LOG2E));
-          const float hv = gc * s * (lc + 1.0f);
-          const float dhp = acc[i][j][q];
-          rs[i][q] += dhp * hv;
-          const float dh = tab_g[rr] * dhp;
-          const float dgc = s + BW_ALPHA * gc * s * (1.0f - s);      // d(gc sigma(ALPHA gc)) / d gc
-          const float dug = (ug <= BW_LIMIT) ? dh * dgc * (lc + 1.0f) : 0.f;
-          const float dul = (ul >= -BW_LIMIT && ul <= BW_LIMIT) ? dh * gc * s : 0.f;
-          const __bf16 hb = (__bf16)hv, gb = (__bf16)dug, lb = (__bf16)dul;
-          p.h[prow * F + f] = *(const uint16_t*)&hb;
-          p.du[prow * ldu + f] = *(const uint16_t*)&gb;
-          p.du[prow * ldu + F + f] = *(const uint16_t*)&lb;
-        }
-    }
-    // row sums over the 32 columns a lane half holds, then across the two column waves
+  for (int j = 0; j < BG_FN; ++j) {
+    const int n = n0 + wn * BG_WTN + 32 * j + (lane & 31);
+    if (n >= p.N) continue;
 #pragma unroll
     for (int i = 0; i < BG_FM; ++i)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        float v = rs[i][q];
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 8);
-        v += __shfl_xor(v, 4);
-        v += __shfl_xor(v, 2);
-        v += __shfl_xor(v, 1);
-        if ((lane & 31) == 0) red[wn][wm * BG_WTM + 32 * i + 8 * (q >> 2) + 4 * kg + (q & 3)] = v;
+        const int rr = wm * BG_WTM + 32 * i + 8 * (q >> 2) + 4 * kg + (q & 3);
+        if (rr < rows) dst[(int64_t)(m0 + rr) * p.N + n] = acc[i][j][q];
       }
-    __syncthreads();
-    if (tid < BG_BM && tid < rows) {
-      const int a = tab_a[tid];
-      float v = red[0][tid];
-#pragma unroll
-      for (int w = 1; w < BG_WAVES_N; ++w) v += red[w][tid];
-      if (a >= 0) p.dgpart[(int64_t)n_tile * p.A + a] = v;
-    }
   }
 }
 
-template <int MODE>
-hipError_t launch_bwd_gemm(BwdGemmArgs g, int64_t max_row_tiles, hipStream_t st) {
-  const int64_t tiles = (MODE == BW_WGRAD ? (int64_t)g.E * g.m_tiles : max_row_tiles) * g.n_tiles;
-  const int64_t blocks = (tiles + 7) / 8 * 8;
-  hipLaunchKernelGGL(bwd_gemm_kernel<MODE>, dim3((unsigned)blocks), dim3(BG_THREADS), 0, st, g);
+hipError_t launch_wgrad(BwdGemmArgs g, hipStream_t st) {
+  const int64_t tiles = (int64_t)g.E * g.m_tiles * g.n_tiles;
+  hipLaunchKernelGGL(bwd_gemm_kernel, dim3((unsigned)tiles), dim3(BG_THREADS), 0, st, g);
   return hipGetLastError();
-}
-
-int64_t row_tiles_bound(int64_t A, int E) {
-  int64_t m = (A + (int64_t)E * (BG_BM - 1)) / BG_BM;
-  return m > A ? A : m;
 }
 
 // ------------------------------------------------------------------------------ routing helpers
@@ -437,23 +264,82 @@ __global__ __launch_bounds__(256) void pad_map_kernel(const int32_t* __restrict_
 }
 
 // ------------------------------------------------------------------------------ conversions
-// fp32 rows [rows][D] -> bf16 pairs [rows][2D]: the first D the nearest bf16 (hi), the next D
-// the nearest bf16 of what hi leaves (lo), so hi + lo holds about 16 significant bits.
 static __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   const __bf16 x = (__bf16)a, y = (__bf16)b;
   return (uint32_t)*(const uint16_t*)&x | ((uint32_t)*(const uint16_t*)&y << 16);
 }
-__global__ __launch_bounds__(256) void f32_to_bf16_pair_kernel(const float4* __restrict__ src, int64_t rows,
-                                                               int D4, uint2* __restrict__ dst) {
+// dout rows in routed order as bf16 pairs: out[p] = [hi D | lo D] of dout[token of perm[p]], hi
+// the nearest bf16 and lo the nearest bf16 of what hi leaves (hi + lo: about 16 significant
+// bits), the A operand of dh' = dout W2 on the K-doubled [W2^T | W2^T].
+__global__ __launch_bounds__(256) void gather_dout_pair_kernel(const float4* __restrict__ dout,
+                                                               const int32_t* __restrict__ perm, int A, int k,
+                                                               int D4, uint2* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= rows * D4) return;
-  const int64_t r = i / D4;
-  const int c = (int)(i - r * D4);
-  const float4 v = src[i];
+  if (i >= (int64_t)A * D4) return;
+  const int64_t p = i / D4;
+  const int c = (int)(i - p * D4);
+  int a = perm[p];
+  a = ((unsigned)a < (unsigned)A) ? a : 0;
+  const float4 v = dout[(int64_t)(a / k) * D4 + c];
   const float h0 = (float)(__bf16)v.x, h1 = (float)(__bf16)v.y, h2 = (float)(__bf16)v.z, h3 = (float)(__bf16)v.w;
-  uint2* const row = dst + r * 2 * D4;
+  uint2* const row = out + p * 2 * D4;
   row[c] = uint2{pack_bf16x2(h0, h1), pack_bf16x2(h2, h3)};
   row[D4 + c] = uint2{pack_bf16x2(v.x - h0, v.y - h1), pack_bf16x2(v.z - h2, v.w - h3)};
+}
+
+__global__ __launch_bounds__(256) void fill_f32_kernel(float* __restrict__ p, int64_t n, float v) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// The clamped SwiGLU's backward on routed row p (one workgroup per row): from u (fp32, gate
+// half then linear half) and dh' (fp32, the ungated mlp2 input gradient at slot row a =
+// perm[p]), h = gc sigmoid(ALPHA gc) (lc + 1) with gc = min(gate, LIMIT), lc = clamp(lin);
+// du_gate = g dh' (sigmoid + ALPHA gc sigmoid (1 - sigmoid)) (lc + 1) where gate <= LIMIT,
+// du_lin = g dh' gc sigmoid where -LIMIT <= lin <= LIMIT; writes h and du (bf16) and
+// dg[a] = sum_f dh' h (fixed-order tree over the workgroup).
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float* __restrict__ u, const float* __restrict__ dhp,
+                                                         const int32_t* __restrict__ perm,
+                                                         const float* __restrict__ gates, int A, int F,
+                                                         uint16_t* __restrict__ h, uint16_t* __restrict__ du,
+                                                         float* __restrict__ dg) {
+  __shared__ float red[256];
+  const int64_t p = blockIdx.x;
+  int a = perm[p];
+  a = ((unsigned)a < (unsigned)A) ? a : 0;
+  const float g = gates[a];
+  const float* const ur = u + p * 2 * F;
+  const float* const dr = dhp + (int64_t)a * F;
+  float s = 0.f;
+  for (int f = threadIdx.x * 4; f < F; f += 1024) {
+    const f32x4 ug4 = *(const f32x4*)(ur + f), ul4 = *(const f32x4*)(ur + F + f);
+    const f32x4 d4 = *(const f32x4*)(dr + f);
+    float hv[4], dgv[4], dlv[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float ug = ug4[c], ul = ul4[c];
+      const float gc = fminf(ug, BW_LIMIT);
+      const float lc = fminf(fmaxf(ul, -BW_LIMIT), BW_LIMIT);
+      // sigmoid(ALPHA gc) = 1 / (1 + 2^(-ALPHA log2(e) gc))
+      const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(gc * BW_NEG_ALPHA_LOG2E));
+      hv[c] = gc * sg * (lc + 1.0f);
+      s += d4[c] * hv[c];
+      const float dh = g * d4[c];
+      const float dgc = sg + BW_ALPHA * gc * sg * (1.0f - sg);    // d(gc sigmoid(ALPHA gc)) / d gc
+      dgv[c] = (ug <= BW_LIMIT) ? dh * dgc * (lc + 1.0f) : 0.f;
+      dlv[c] = (ul >= -BW_LIMIT && ul <= BW_LIMIT) ? dh * gc * sg : 0.f;
+    }
+    *(uint2*)(h + p * F + f) = uint2{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
+    *(uint2*)(du + p * 2 * F + f) = uint2{pack_bf16x2(dgv[0], dgv[1]), pack_bf16x2(dgv[2], dgv[3])};
+    *(uint2*)(du + p * 2 * F + F + f) = uint2{pack_bf16x2(dlv[0], dlv[1]), pack_bf16x2(dlv[2], dlv[3])};
+  }
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) dg[a] = red[0];
 }
 
 // 64 x 64 bf16 tiles through LDS with 16-byte global accesses: phase 1 puts tile row r
@@ -468,14 +354,17 @@ static __device__ __forceinline__ void tile_out(const uint16_t (*t)[TP_LD], int 
   *(u32x4*)dst = v;
 }
 
-// Transpose of each of B matrices [R][C] (bf16) into [C][R]; R and C multiples of 64.
+// Transpose of each of B matrices [R][C] (bf16) into [C][R] (R and C multiples of 64); with
+// DUP the output rows are [C][2R], the transposed row written twice, side by side.
+template <bool DUP>
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src, int R, int C,
                                                              uint16_t* __restrict__ dst) {
   __shared__ __attribute__((aligned(16))) uint16_t t[64][TP_LD];
+  constexpr int W = DUP ? 2 : 1;
   const int64_t b = blockIdx.z;
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
   const uint16_t* s = src + b * R * (int64_t)C;
-  uint16_t* d = dst + b * R * (int64_t)C;
+  uint16_t* d = dst + b * W * R * (int64_t)C;
   for (int i = threadIdx.x; i < 512; i += 256) {
     const int r = i >> 3, ch = i & 7;
     *(u32x4*)&t[r][ch * 8] = *(const u32x4*)(s + (int64_t)(r0 + r) * C + c0 + ch * 8);
@@ -483,7 +372,9 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __r
   __syncthreads();
   for (int i = threadIdx.x; i < 512; i += 256) {
     const int c = i >> 3, ch = i & 7;
-    tile_out(t, c, ch, d + (int64_t)(c0 + c) * R + r0 + ch * 8);
+    uint16_t* const o = d + (int64_t)(c0 + c) * W * R + r0 + ch * 8;
+    tile_out(t, c, ch, o);
+    if (DUP) tile_out(t, c, ch, o + R);
   }
 }
 
@@ -539,10 +430,10 @@ __global__ __launch_bounds__(256) void gather_transpose_kernel(const void* __res
 }
 
 // ------------------------------------------------------------------------------ router
-// One wave per token: dg_j = sum over column tiles of <dh', h> + <dout[t], b2[e_j]>, then
+// One wave per token: dg_j = <dh', h> (from the SwiGLU backward) + <dout[t], b2[e_j]>, then
 // the softmax backward over the k selected logits, dl_j = g_j (dg_j - sum_i g_i dg_i).
 // Lane l keeps dg_j for the slots j = l + 64 m (k <= 256).
-__global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict__ dgpart, int n_tiles,
+__global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict__ dgh,
                                                          const float* __restrict__ dout,
                                                          const uint16_t* __restrict__ b2,
                                                          const int32_t* __restrict__ idx,
@@ -561,9 +452,7 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
     for (int d = lane; d < D; d += 64) v += dout[(int64_t)t * D + d] * bf16_to_f32(b2[(int64_t)e * D + d]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-    float s = 0.f;
-    for (int nt = 0; nt < n_tiles; ++nt) s += dgpart[(int64_t)nt * A + a];
-    const float d_g = s + v;
+    const float d_g = dgh[a] + v;
 #pragma unroll
     for (int m = 0; m < 4; ++m)
       if (j == lane + 64 * m) mine[m] = d_g;
@@ -663,24 +552,31 @@ __global__ __launch_bounds__(256) void router_bias_grad_kernel(const int32_t* __
   if (tid == 0) dbr[e] = s[0];
 }
 
-// dx[t][d] = sum_j dxs[t k + j][d] + sum_j dl[t k + j] Wr[e_j][d], slots in order.
-__global__ __launch_bounds__(256) void dx_combine_kernel(const float* __restrict__ dxs,
+// dx[t][d] = sum_j dxs[t k + j][d] + sum_j dl[t k + j] Wr[e_j][d], slots in order; four
+// columns per thread (dxs rows are ld_dxs floats apart).
+__global__ __launch_bounds__(256) void dx_combine_kernel(const float* __restrict__ dxs, int ld_dxs,
                                                          const float* __restrict__ dl,
                                                          const int32_t* __restrict__ idx,
                                                          const uint16_t* __restrict__ wr, int T, int D, int E,
                                                          int k, float* __restrict__ dx) {
+  const int D4 = D / 4;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (int64_t)T * D) return;
-  const int64_t t = i / D;
-  const int d = (int)(i - t * D);
-  float s = 0.f;
-  for (int j = 0; j < k; ++j) s += dxs[(t * k + j) * D + d];
+  if (i >= (int64_t)T * D4) return;
+  const int64_t t = i / D4;
+  const int d = (int)(i - t * D4) * 4;
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < k; ++j) s += *(const f32x4*)(dxs + (t * k + j) * ld_dxs + d);
   for (int j = 0; j < k; ++j) {
     const int64_t a = t * k + j;
     const int e = min(max(idx[a], 0), E - 1);
-    s += dl[a] * bf16_to_f32(wr[(int64_t)e * D + d]);
+    const float g = dl[a];
+    const uint2 w = *(const uint2*)(wr + (int64_t)e * D + d);
+    s[0] += g * bf16_to_f32(w.x & 0xFFFFu);
+    s[1] += g * bf16_to_f32(w.x >> 16);
+    s[2] += g * bf16_to_f32(w.y & 0xFFFFu);
+    s[3] += g * bf16_to_f32(w.y >> 16);
   }
-  dx[i] = s;
+  *(f32x4*)(dx + t * D + d) = s;
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
@@ -702,27 +598,29 @@ int bwd_padded_cols(int64_t A, int64_t E) {
   const int64_t v = A + E * (BG_BK - 1);
   return (int)((v + 63) / 64 * 64);
 }
-int bwd_f_tiles(int64_t F) { return (int)((F + BG_BN - 1) / BG_BN); }
 int bwd_sum_chunks() { return EX_CHUNKS; }
 
 hipError_t launch_backward(const BwdArgs& b, hipStream_t st) {
   const int T = b.T, D = b.D, E = b.E, k = b.k, F = b.F, G = 2 * F;
   const int A = T * k;
   const int ldt = bwd_padded_cols(A, E);
-  // 1. padded layout of the routed rows per expert
+  const int DF = D > F ? D : F;
+  // 1. padded layout of the routed rows per expert (weight gradients)
   hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(256), 0, st, b.offsets, E, b.poff);
   BW_CHECK(hipGetLastError());
   hipLaunchKernelGGL(pad_map_kernel, dim3(blocks_for(ldt)), dim3(256), 0, st, b.offsets, b.poff, E, ldt, b.padmap);
   BW_CHECK(hipGetLastError());
-  // 2. dout as bf16 pairs [T][hi D | lo D] (A operand of mlp2's input gradient)
-  hipLaunchKernelGGL(f32_to_bf16_pair_kernel, dim3(blocks_for((int64_t)T * D / 4)), dim3(256), 0, st,
-                     (const float4*)b.dout, (int64_t)T, D / 4, (uint2*)b.dout16);
+  // 2. unit gates and zero biases for the forward's mlp2 kernel used as a plain grouped GEMM
+  hipLaunchKernelGGL(fill_f32_kernel, dim3(blocks_for(A)), dim3(256), 0, st, b.ones, (int64_t)A, 1.0f);
   BW_CHECK(hipGetLastError());
-  // 3. the weights along their other dimension: W1^T [E][D][2F], W2^T [E][F][D]
-  hipLaunchKernelGGL(transpose_bf16_kernel, dim3(blocks_for(D, 64), blocks_for(G, 64), E), dim3(256), 0, st,
+  hipLaunchKernelGGL(fill_f32_kernel, dim3(blocks_for((int64_t)E * DF / 2)), dim3(256), 0, st, (float*)b.zeros,
+                     (int64_t)E * DF / 2, 0.0f);
+  BW_CHECK(hipGetLastError());
+  // 3. the weights along their other dimension: W1^T [E][D][2F], W2^T twice [E][F][2D]
+  hipLaunchKernelGGL(transpose_bf16_kernel<false>, dim3(blocks_for(D, 64), blocks_for(G, 64), E), dim3(256), 0, st,
                      b.w1, G, D, b.w1t);
   BW_CHECK(hipGetLastError());
-  hipLaunchKernelGGL(transpose_bf16_kernel, dim3(blocks_for(F, 64), blocks_for(D, 64), E), dim3(256), 0, st,
+  hipLaunchKernelGGL(transpose_bf16_kernel<true>, dim3(blocks_for(F, 64), blocks_for(D, 64), E), dim3(256), 0, st,
                      b.w2, D, F, b.w2t);
   BW_CHECK(hipGetLastError());
   // 4. transposed, padded x and dz = g dout (operands of the weight gradients)
@@ -732,44 +630,48 @@ hipError_t launch_backward(const BwdArgs& b, hipStream_t st) {
   hipLaunchKernelGGL((gather_transpose_kernel<true, true, true>), dim3(ldt / 64, blocks_for(D, 64)), dim3(256), 0,
                      st, (const void*)b.dout, D, D, b.padmap, b.perm, b.gates, k, A, ldt, b.dzT);
   BW_CHECK(hipGetLastError());
+  // 5. dout rows in routed order as bf16 pairs
+  hipLaunchKernelGGL(gather_dout_pair_kernel, dim3(blocks_for((int64_t)A * D / 4)), dim3(256), 0, st,
+                     (const float4*)b.dout, b.perm, A, k, D / 4, (uint2*)b.dout_perm);
+  BW_CHECK(hipGetLastError());
 
-  const int64_t mt = row_tiles_bound(A, E);
-  BwdGemmArgs g{};
-  g.offsets = b.offsets; g.perm = b.perm; g.gates = b.gates; g.poff = b.poff;
-  g.E = E; g.k = k; g.A = A; g.F = F;
-  // 5. recompute u = x W1^T + b1
-  g.a = b.x; g.lda = D; g.b = b.w1; g.ldb = D; g.b_expert = (int64_t)G * D;
-  g.K = D; g.N = G; g.n_tiles = (G + BG_BN - 1) / BG_BN;
-  g.bias = b.b1; g.c = b.u;
-  BW_CHECK(launch_bwd_gemm<BW_RECOMP>(g, mt, st));
-  // 6. dh' = dout W2[e], SwiGLU backward -> h, du, partial dg
-  g.a = b.dout16; g.lda = 2 * D; g.b = b.w2t; g.ldb = D; g.b_expert = (int64_t)F * D;
-  g.K = 2 * D; g.kwrap = D / BG_BK; g.N = F; g.n_tiles = bwd_f_tiles(F);
-  g.u = b.u; g.h = b.h; g.du = b.du; g.dgpart = b.dgpart; g.c = nullptr; g.bias = nullptr;
-  BW_CHECK(launch_bwd_gemm<BW_DGRAD2>(g, mt, st));
-  // 7. dx contributions du W1[e] at the slot rows
-  g.a = b.du; g.lda = G; g.b = b.w1t; g.ldb = G; g.b_expert = (int64_t)D * G;
-  g.K = G; g.N = D; g.n_tiles = (D + BG_BN - 1) / BG_BN; g.c = b.dxs;
-  BW_CHECK(launch_bwd_gemm<BW_DGRAD1>(g, mt, st));
-  // 8. transposed, padded h and du
+  const int cfg = expert_tile_config(A, E);
+  // 6. recompute u = x W1^T + b1 (the forward's mlp1, storing u)
+  ExpertArgs f{};
+  f.x = b.x; f.w1 = b.w1; f.b1 = b.b1; f.gates = b.gates; f.offsets = b.offsets; f.perm = b.perm;
+  f.u_out = b.u; f.T = T; f.D = D; f.E = E; f.k = k; f.F = F; f.fmt = 0;
+  BW_CHECK(launch_mlp1(f, cfg, st));
+  // 7. dh' = [dout hi | lo] [W2^T | W2^T]^T at the slot rows (the forward's mlp2: K = 2D, N = F)
+  ExpertArgs m{};
+  m.h = b.dout_perm; m.w2 = b.w2t; m.b2 = b.zeros; m.gates = b.ones; m.offsets = b.offsets; m.perm = b.perm;
+  m.y = b.dxs; m.T = T; m.D = F; m.E = E; m.k = k; m.F = 2 * D; m.fmt = 0;
+  BW_CHECK(launch_mlp2(m, cfg, st));
+  // 8. the SwiGLU backward: h, du, dg (dh' sits in dxs until step 9 overwrites it)
+  hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)A), dim3(256), 0, st, b.u, b.dxs, b.perm, b.gates, A, F, b.h,
+                     b.du, b.dgsum);
+  BW_CHECK(hipGetLastError());
+  // 9. dx contributions du W1[e] at the slot rows (the forward's mlp2: K = 2F, N = D)
+  m.h = b.du; m.w2 = b.w1t; m.y = b.dxs; m.D = D; m.F = G;
+  BW_CHECK(launch_mlp2(m, cfg, st));
+  // 10. transposed, padded h and du
   hipLaunchKernelGGL((gather_transpose_kernel<false, false, false>), dim3(ldt / 64, blocks_for(F, 64)), dim3(256), 0,
                      st, (const void*)b.h, F, F, b.padmap, b.perm, b.gates, k, A, ldt, b.hT);
   BW_CHECK(hipGetLastError());
   hipLaunchKernelGGL((gather_transpose_kernel<false, false, false>), dim3(ldt / 64, blocks_for(G, 64)), dim3(256), 0,
                      st, (const void*)b.du, G, G, b.padmap, b.perm, b.gates, k, A, ldt, b.duT);
   BW_CHECK(hipGetLastError());
-  // 9. weight gradients per expert: dW2[e] = dz^T h, dW1[e] = du^T x
+  // 11. weight gradients per expert: dW2[e] = dz^T h, dW1[e] = du^T x
   BwdGemmArgs w{};
-  w.poff = b.poff; w.E = E; w.k = k; w.A = A;
+  w.poff = b.poff; w.E = E;
   w.a = b.dzT; w.lda = ldt; w.b = b.hT; w.ldb = ldt; w.M = D; w.N = F;
   w.m_tiles = (D + BG_BM - 1) / BG_BM; w.n_tiles = (F + BG_BN - 1) / BG_BN; w.c = b.dw2;
-  BW_CHECK(launch_bwd_gemm<BW_WGRAD>(w, 0, st));
+  BW_CHECK(launch_wgrad(w, st));
   w.a = b.duT; w.b = b.xT; w.M = G; w.N = D;
   w.m_tiles = (G + BG_BM - 1) / BG_BM; w.n_tiles = (D + BG_BN - 1) / BG_BN; w.c = b.dw1;
-  BW_CHECK(launch_bwd_gemm<BW_WGRAD>(w, 0, st));
-  // 10. router: dg and the softmax backward, then the per-expert sums and dx
-  hipLaunchKernelGGL(router_bwd_kernel, dim3(blocks_for(T, 4)), dim3(256), 0, st, b.dgpart, bwd_f_tiles(F), b.dout,
-                     b.b2, b.idx, b.gates, T, D, E, k, b.dl);
+  BW_CHECK(launch_wgrad(w, st));
+  // 12. router: dg and the softmax backward, then the per-expert sums and dx
+  hipLaunchKernelGGL(router_bwd_kernel, dim3(blocks_for(T, 4)), dim3(256), 0, st, b.dgsum, b.dout, b.b2, b.idx,
+                     b.gates, T, D, E, k, b.dl);
   BW_CHECK(hipGetLastError());
   const unsigned wblk = blocks_for(G > D ? G : D);
   hipLaunchKernelGGL(expert_partial_kernel, dim3(wblk, E, EX_CHUNKS), dim3(256), 0, st, b.offsets, b.perm, b.gates,
@@ -780,8 +682,8 @@ hipError_t launch_backward(const BwdArgs& b, hipStream_t st) {
   BW_CHECK(hipGetLastError());
   hipLaunchKernelGGL(router_bias_grad_kernel, dim3(E), dim3(256), 0, st, b.offsets, b.perm, b.dl, A, b.dbr);
   BW_CHECK(hipGetLastError());
-  hipLaunchKernelGGL(dx_combine_kernel, dim3(blocks_for((int64_t)T * D)), dim3(256), 0, st, b.dxs, b.dl, b.idx,
-                     b.wr, T, D, E, k, b.dx);
+  hipLaunchKernelGGL(dx_combine_kernel, dim3(blocks_for((int64_t)T * D / 4)), dim3(256), 0, st, b.dxs, D, b.dl,
+                     b.idx, b.wr, T, D, E, k, b.dx);
   return hipGetLastError();
 }
 

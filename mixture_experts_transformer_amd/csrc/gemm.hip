@@ -211,6 +211,8 @@ struct GemmArgs {
   const uint8_t* w;         // weights (bf16 or MXFP4 buffer)
   const uint16_t* bias;     // [E][N]
   uint16_t* h;              // mlp1 output
+  float* u_out;             // mlp1, bf16 weights: when set, the pre-activation u [A][2F] (fp32,
+                            //   gate half then linear half) is stored instead of h
   uint16_t* h_lo;
   uint8_t* h8;              // mlp1 output for the scaled-MFMA engine: three fp8 pieces of h
   uint32_t* h8s;            //   and their scales
@@ -1041,6 +1043,29 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
       bl[j] = (f < p.F) ? bf16_to_f32(bias[p.F + f]) : 0.f;
     }
     constexpr int CH = EP_P / 4;                           // 8-byte chunks per slice row
+    if constexpr (FMT == 0) {
+      if (p.u_out) {
+        // the backward's recomputation of the pre-activation: u itself, fp32, no SwiGLU
+        const size_t ldu = 2 * (size_t)p.F;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[i][j][q]),
+                                                               __float_as_uint(acc[i][j][q + 8]), false, false);
+              const int rl = wm * C::WTM + i * 32 + 8 * (q >> 2) + rlane + (q & 3);
+              const int f = f_wave + j * 16 + pl;
+              if (rl < rows && f < p.F) {
+                float* const d = p.u_out + (size_t)(gbase + rl) * ldu + f;
+                d[0] = __uint_as_float(sw[0]) + bg[j];
+                d[p.F] = __uint_as_float(sw[1]) + bl[j];
+              }
+            }
+        return;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -1209,7 +1234,7 @@ hipError_t launch_mlp1(const ExpertArgs& a, int cfg, hipStream_t st) {
   g.a = a.x; g.a_lo = nullptr; g.perm = a.perm; g.offsets = a.offsets; g.gates = a.gates;
   g.a8 = a.xq; g.a8s = a.xs; g.a8s_stride = mx_scale_stride(a.D);
   g.h8 = a.hq; g.h8s = a.hs; g.h8s_stride = mx_scale_stride(a.F);
-  g.w = (const uint8_t*)a.w1; g.bias = a.b1; g.h = a.h; g.h_lo = a.h_lo; g.y = nullptr;
+  g.w = (const uint8_t*)a.w1; g.bias = a.b1; g.h = a.h; g.h_lo = a.h_lo; g.y = nullptr; g.u_out = a.u_out;
   g.E = a.E; g.k = a.k; g.K = a.D; g.N = 2 * a.F; g.F = a.F;
   const int64_t A = (int64_t)a.T * a.k;
   g.A = (int)A;

@@ -61,6 +61,8 @@ struct ExpertArgs {
   uint32_t* hs;             // [A][mx_scale_stride(F)]
   float* y;                 // [A][D] fp32, row a = assignment id
   float* out;               // [T][D] fp32
+  float* u_out;             // mlp1 with bf16 weights: store the pre-activation u [A][2F] (fp32)
+                            //   instead of h (the backward's recomputation); null otherwise
   int T, D, E, k, F, fmt;
 };
 
@@ -98,16 +100,18 @@ struct BwdArgs {
   int32_t* poff;            // [E+1] padded column offsets per expert, then [E] the experts by
                             //   decreasing padded row count
   int32_t* padmap;          // [ldt] routed row of each padded column, -1 for padding
-  uint16_t* dout16;         // [T][2D] bf16 pairs: hi then lo
+  uint16_t* dout_perm;      // [A][2D] dout rows in routed order, bf16 pairs: hi then lo
   uint16_t* w1t;            // [E][D][2F]
-  uint16_t* w2t;            // [E][F][D]
+  uint16_t* w2t;            // [E][F][2D]: W2^T twice along K
+  float* ones;              // [A] unit gates
+  uint16_t* zeros;          // [E][max(D, F)] zero biases
   uint16_t* xT;             // [D][ldt]
   uint16_t* dzT;            // [D][ldt]
   float* u;                 // [A][2F] recomputed mlp1 output (routed-row order)
   uint16_t* h;              // [A][F]
   uint16_t* du;             // [A][2F]
-  float* dgpart;            // [bwd_f_tiles(F)][A]
-  float* dxs;               // [A][D] slot rows
+  float* dgsum;             // [A] <dh', h> per assignment
+  float* dxs;               // [A][max(D, F)] slot rows: dh' first, then the dx contributions
   uint16_t* hT;             // [F][ldt]
   uint16_t* duT;            // [2F][ldt]
   float* dl;                // [A] gradient of the selected logits
@@ -117,8 +121,6 @@ struct BwdArgs {
 };
 // Columns of the transposed, expert-padded activation layout (a multiple of 64).
 int bwd_padded_cols(int64_t A, int64_t E);
-// Column tiles over F of the input-gradient product of mlp2.
-int bwd_f_tiles(int64_t F);
 // Fixed row chunks of the per-expert sums.
 int bwd_sum_chunks();
 hipError_t launch_backward(const BwdArgs& b, hipStream_t st);

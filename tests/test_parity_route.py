@@ -18,6 +18,7 @@ def run_and_compare(x, wr, br, k, label, ebias=None):
     note(f"route {label}: T={T} D={x.shape[1]} E={E} k={k}{' biased' if ebias is not None else ''}")
     eb = None if ebias is None else torch.from_numpy(np.ascontiguousarray(ebias, dtype=np.float32)).to(DEV)
     r = moe.route(u16(x), u16(wr), u16(br), k, expert_bias=eb)
+    rf = moe.route(u16(x), u16(wr), u16(br), k, want_logits=False, expert_bias=eb)   # as the forward calls it
     torch.cuda.synchronize()
     l_ref = oracle.router_logits(x, wr, br)
     idx_ref = oracle.select_experts(l_ref, k, ebias)
@@ -26,12 +27,15 @@ def run_and_compare(x, wr, br, k, label, ebias=None):
     logits = r["logits"].cpu().numpy()
     nbad = int(np.sum(logits.view(np.uint32) != l_ref.view(np.uint32)))
     assert nbad == 0, f"{label}: {nbad} logits differ from the oracle's fp32 rounding"
-    assert np.array_equal(r["idx"].cpu().numpy(), idx_ref), f"{label}: top-k indices differ"
-    assert np.array_equal(r["counts"].cpu().numpy(), counts_ref), f"{label}: counts differ"
-    assert np.array_equal(r["offsets"].cpu().numpy(), offsets_ref), f"{label}: offsets differ"
-    assert np.array_equal(r["perm"].cpu().numpy(), perm_ref), f"{label}: permutation differs"
-    gerr = np.max(np.abs(r["gates"].cpu().numpy().astype(np.float64) - g_ref)) if T else 0.0
-    assert gerr <= GATE_ABS, f"{label}: gate error {gerr:.3e}"
+    gerr = 0.0
+    for path, rr in (("with logits", r), ("without logits", rf)):
+        assert np.array_equal(rr["idx"].cpu().numpy(), idx_ref), f"{label} ({path}): top-k indices differ"
+        assert np.array_equal(rr["counts"].cpu().numpy(), counts_ref), f"{label} ({path}): counts differ"
+        assert np.array_equal(rr["offsets"].cpu().numpy(), offsets_ref), f"{label} ({path}): offsets differ"
+        assert np.array_equal(rr["perm"].cpu().numpy(), perm_ref), f"{label} ({path}): permutation differs"
+        ge = np.max(np.abs(rr["gates"].cpu().numpy().astype(np.float64) - g_ref)) if T else 0.0
+        assert ge <= GATE_ABS, f"{label} ({path}): gate error {ge:.3e}"
+        gerr = max(gerr, ge)
     # smallest margin between the k-th and (k+1)-th logit: how close the case came to a tie
     if k < E and T:
         key = l_ref if ebias is None else l_ref + np.asarray(ebias, np.float32)[None, :]
@@ -85,6 +89,20 @@ def test_route_duplicated_router_rows():
         wr[b] = wr[a]
         br[b] = br[a]
     run_and_compare(x, wr, br, k, "duplicated rows")
+
+
+def test_route_near_ties_resolved_exactly():
+    """Router rows that differ from another expert's in one element by one bf16 ulp: logits
+    a few fp32 ulps apart, whose order the exact fp64 router must still get right."""
+    T, D, E, k = 512, 2880, 32, 4
+    x, wr, br = rand_layer(5, T, D, E, bias_std=0.0)
+    g = np.random.default_rng(6)
+    for a, b in [(0, 1), (4, 5), (8, 9), (12, 13), (20, 21), (30, 31)]:
+        wr[b] = wr[a]
+        d = int(g.integers(0, D))
+        wr[b, d] = wr[a, d] + np.uint16(1)         # one ulp in one element
+        br[b] = br[a]
+    run_and_compare(x, wr, br, k, "near ties (one-ulp router rows)")
 
 
 def test_route_empty_experts_at_edges():
