@@ -1,5 +1,6 @@
 """GPU routing stage vs the oracle: logits, top-k indices, counts, offsets and the
-permutation must match bit for bit; gates to 1e-6 absolute."""
+permutation must match bit for bit; gates to 1e-6 absolute.  Every case runs both ways: with
+logits requested and without, as the forward calls it."""
 import numpy as np
 import pytest
 import torch
@@ -72,8 +73,9 @@ def test_route_ragged_shapes(T, D, E, k):
     run_and_compare(*rand_layer(T * 7 + E, T, D, E), k, f"ragged T={T} D={D} E={E} k={k}")
 
 
-def test_route_exact_ties_go_to_lower_index():
-    T, D, E, k = 70, 64, 40, 5
+@pytest.mark.parametrize("T", [70, 2048])
+def test_route_exact_ties_go_to_lower_index(T):
+    D, E, k = 64, 40, 5
     x = np.zeros((T, D), dtype=np.uint16)
     _, wr, _ = rand_layer(1, T, D, E)
     br = np.full(E, f32_to_bf16_bits(np.float32([0.5]))[0], dtype=np.uint16)
@@ -82,8 +84,9 @@ def test_route_exact_ties_go_to_lower_index():
     assert np.allclose(r["gates"].cpu().numpy(), 1.0 / k, atol=1e-7)
 
 
-def test_route_duplicated_router_rows():
-    T, D, E, k = 200, 128, 12, 4
+@pytest.mark.parametrize("T", [200, 8192])
+def test_route_duplicated_router_rows(T):
+    D, E, k = 128, 12, 4
     x, wr, br = rand_layer(2, T, D, E, bias_std=0.0)
     for a, b in [(0, 1), (3, 9), (10, 11)]:
         wr[b] = wr[a]
@@ -91,10 +94,11 @@ def test_route_duplicated_router_rows():
     run_and_compare(x, wr, br, k, "duplicated rows")
 
 
-def test_route_near_ties_resolved_exactly():
+@pytest.mark.parametrize("T", [512, 4096])
+def test_route_near_ties_resolved_exactly(T):
     """Router rows that differ from another expert's in one element by one bf16 ulp: logits
-    a few fp32 ulps apart, whose order the exact fp64 router must still get right."""
-    T, D, E, k = 512, 2880, 32, 4
+    a few fp32 ulps apart, whose order the fp64 router must still get right."""
+    D, E, k = 2880, 32, 4
     x, wr, br = rand_layer(5, T, D, E, bias_std=0.0)
     g = np.random.default_rng(6)
     for a, b in [(0, 1), (4, 5), (8, 9), (12, 13), (20, 21), (30, 31)]:
