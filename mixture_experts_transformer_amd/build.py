@@ -1,6 +1,7 @@
 """Build the gfx950 shared library ``libmoe.so`` in-tree with hipcc.
 
     python -m mixture_experts_transformer_amd.build [--verbose]
+    python -m mixture_experts_transformer_amd.build --host-sanitized <out.so>
 
 Every HIP source under ``csrc/`` is compiled for gfx950 only.  The copies of the grouped GEMM
 load M0 in inline assembly; the build checks the generated assembly (``check_m0``) and fails
@@ -92,5 +93,27 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_host_sanitized(out: str) -> str:
+    """A copy of the library whose host code (argument checks, workspace and stream handling,
+    error strings, profiling) is built with AddressSanitizer and UndefinedBehaviorSanitizer,
+    for exercising the C ABI on a machine without a GPU.  The device code is built as usual
+    (the sanitizers apply to the host pass only); a program that loads this copy must itself
+    be linked with the same compiler's sanitizer runtime (clang -fsanitize=address,undefined)."""
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O1", "-g", "-std=c++17", "-fPIC", "-shared",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-fno-omit-frame-pointer",
+           "-Xarch_host", "-fsanitize=address",
+           "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined",
+           "-I", os.path.join(os.path.dirname(HERE), "include"), "-o", out] + srcs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitized host build failed ({r.returncode}):\n{r.stderr[-4000:]}")
+    return out
+
+
 if __name__ == "__main__":
-    print(build(verbose="--verbose" in sys.argv))
+    if "--host-sanitized" in sys.argv:
+        print(build_host_sanitized(sys.argv[sys.argv.index("--host-sanitized") + 1]))
+    else:
+        print(build(verbose="--verbose" in sys.argv))

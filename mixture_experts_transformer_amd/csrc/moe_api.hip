@@ -175,7 +175,9 @@ int check_shapes(int64_t T, int64_t D, int64_t E, int64_t k, int64_t F, bool wit
     return fail(MOE_EINVAL, "F = %lld must be a positive multiple of 64", (long long)F);
   if (E < 1 || E > 256) return fail(MOE_EINVAL, "E = %lld must be in [1, 256]", (long long)E);
   if (k < 1 || k > E) return fail(MOE_EINVAL, "k = %lld must be in [1, E = %lld]", (long long)k, (long long)E);
-  if (T * k >= ((int64_t)1 << 31)) return fail(MOE_EINVAL, "T*k = %lld must be < 2^31", (long long)(T * k));
+  // bound T before forming a product with it (k <= E <= 256, so T*k cannot overflow after this)
+  if (T >= ((int64_t)1 << 31) || T * k >= ((int64_t)1 << 31))
+    return fail(MOE_EINVAL, "T*k = %lld*%lld must be < 2^31", (long long)T, (long long)k);
   if (D >= ((int64_t)1 << 24) || (with_f && F >= ((int64_t)1 << 24)))
     return fail(MOE_EINVAL, "D and F must be < 2^24");
   // the expert kernels address rows of x, h and one expert's weights with 32-bit offsets
@@ -644,7 +646,8 @@ const char* moe_version(void) {
   return "moe-mi355x gfx950: router fp64-MFMA, top-k wave argmax, grouped GEMM v_mfma_f32_32x32x16_bf16 "
          "(streaming tile 64x128; matrix-core tile 256x256) and, for MXFP4 on matrix-core tiles, "
          "v_mfma_scale_f32_32x32x64_f8f6f4 on fp8 activation pieces; combine fp32; backward (bf16) "
-         "grouped GEMM 256x128 v_mfma_f32_32x32x16_bf16";
+         "recomputation and input gradients on the forward's grouped GEMM, weight gradients on 256x256 "
+         "v_mfma_f32_32x32x16_bf16 tiles";
 }
 
 }  // extern "C"
