@@ -72,130 +72,38 @@ struct Tile {
   static_assert((BM * CPR) % 64 == 0 && (BN * CPR) % 64 == 0, "copy granularity");
 };
 
-// Tile shapes.  Few rows per expert (weight streaming, full 128-byte row segments per
-// stage) and many rows (matrix-core bound).  The defaults below are the tuned shapes; the
-// macros let a build try others without touching the kernel.
-#ifndef MOE_S_BM
-#define MOE_S_BM 64
-#endif
-#ifndef MOE_S_BN1
-#define MOE_S_BN1 128
-#endif
-#ifndef MOE_S_BN2
-#define MOE_S_BN2 128
-#endif
-#ifndef MOE_S_WM
-#define MOE_S_WM 1
-#endif
-#ifndef MOE_S_WN
-#define MOE_S_WN 4
-#endif
-#ifndef MOE_S_NS
-#define MOE_S_NS 2
-#endif
-#ifndef MOE_S_NS4
-#define MOE_S_NS4 2
-#endif
-#ifndef MOE_S_STREAM
-#define MOE_S_STREAM 1
-#endif
-#ifndef MOE_L_BM
-#define MOE_L_BM 256
-#endif
-#ifndef MOE_L_BN
-#define MOE_L_BN 256
-#endif
-#ifndef MOE_L_WM
-#define MOE_L_WM 2
-#endif
-#ifndef MOE_L_WN
-#define MOE_L_WN 4
-#endif
-#ifndef MOE_L_NS
-#define MOE_L_NS 2
-#endif
-#ifndef MOE_S_NSH
-#define MOE_S_NSH 2
-#endif
-#ifndef MOE_L_BK
-#define MOE_L_BK 64
-#endif
-#ifndef MOE_S_WN2
-#define MOE_S_WN2 MOE_S_WN          // waves across the streaming mlp2 tile
-#endif
-#ifndef MOE_S_NS2
-#define MOE_S_NS2 2                 // stages of the streaming mlp2 tile, bf16 weights
-#endif
-#ifndef MOE_S_SUPER1
-#define MOE_S_SUPER1 4              // code super-stage of the streaming MXFP4 tiles: mlp1
-#endif
-#ifndef MOE_S_SUPER2
-#define MOE_S_SUPER2 2              // mlp2 (64-byte code segments, but three workgroups per CU)
-#endif
-#ifndef MOE_S_SUPER8
-#define MOE_S_SUPER8 2              // MXFP8 (64 code bytes per row and stage: 128-byte windows)
-#endif
-#ifndef MOE_S_WPE
-#define MOE_S_WPE 1                 // streaming tiles: waves per SIMD the registers must allow
-#endif
-#ifndef MOE_S_WPE4
-#define MOE_S_WPE4 4                //   with MXFP4 weights (register cap: measured a few percent faster)
-#endif
-#ifndef MOE_S_BN14
-#define MOE_S_BN14 MOE_S_BN1        // streaming tile width with MXFP4 weights: mlp1
-#endif
-#ifndef MOE_S_BN24
-#define MOE_S_BN24 MOE_S_BN2        //   mlp2
-#endif
-#ifndef MOE_S_WN4
-#define MOE_S_WN4 MOE_S_WN          // waves across the streaming MXFP4 tiles: mlp1
-#endif
-#ifndef MOE_S_WN24
-#define MOE_S_WN24 MOE_S_WN2        //   mlp2
-#endif
+// Tile shapes (the measured choices).
+//
+// Streaming tiles serve few routed rows per expert, where the weights' HBM stream bounds the
+// loop: 64 routed rows x 128 weight rows, four waves side by side along the weight rows, two
+// LDS stages of K = 64 (full 128-byte bf16 row segments).  With decoded formats (MXFP4,
+// MXFP8) the registers are capped for four waves per SIMD, which measured a few percent
+// faster; SUPER, the K steps whose codes one copy brings in, is 4 for MXFP4 mlp1 (32-byte
+// code segments) and 2 for MXFP4 mlp2 (three workgroups per CU) and for MXFP8 (64 code bytes
+// per row and stage: 128-byte windows).
 template <int MODE, int FMT> using SmallTile =
-    Tile<MOE_S_BM, (MODE == 1 ? (FMT == 0 ? MOE_S_BN1 : MOE_S_BN14) : (FMT == 0 ? MOE_S_BN2 : MOE_S_BN24)),
-         MOE_S_WM, (MODE == 1 ? (FMT == 0 ? MOE_S_WN : MOE_S_WN4) : (FMT == 0 ? MOE_S_WN2 : MOE_S_WN24)),
-         (FMT == 0 ? (MODE == 1 ? MOE_S_NS : MOE_S_NS2) : (MODE == 1 ? MOE_S_NS4 : MOE_S_NSH)), 64,
-         MOE_S_STREAM != 0, (FMT == 1 ? (MODE == 1 ? MOE_S_SUPER1 : MOE_S_SUPER2) : (FMT == 3 ? MOE_S_SUPER8 : 4)),
-         (FMT == 0 ? MOE_S_WPE : MOE_S_WPE4)>;
+    Tile<64, 128, 1, 4, 2, 64, true, (FMT == 0 || (FMT == 1 && MODE == 1)) ? 4 : 2, FMT == 0 ? 1 : 4>;
+
+// Matrix-core tiles serve many routed rows per expert: 256 x 256 outputs on eight waves
+// (2 x 4, 128 x 64 each), two LDS stages of K = 64.
 template <int MODE, int FMT> struct LargeTileSel {   // bf16 weights
-  using type = Tile<MOE_L_BM, MOE_L_BN, MOE_L_WM, MOE_L_WN, MOE_L_NS, MOE_L_BK, false>;
+  using type = Tile<256, 256, 2, 4, 2, 64, false>;
 };
-#ifndef MOE_LX_NS
-#define MOE_LX_NS 2                 // scaled-MFMA engine (fp8 activation pieces x MXFP4)
-#endif
-#ifndef MOE_LX_SUPER
-#define MOE_LX_SUPER 4
-#endif
-#ifndef MOE_LX2_SUPER
-#define MOE_LX2_SUPER 2             // mlp2 (three pieces of h per stage: LDS)
-#endif
-#ifndef MOE_LX_WM
-#define MOE_LX_WM 2
-#endif
-#ifndef MOE_LX_WN
-#define MOE_LX_WN 4
-#endif
-#ifndef MOE_LX2_WM
-#define MOE_LX2_WM MOE_LX_WM
-#endif
-#ifndef MOE_LX2_WN
-#define MOE_LX2_WN MOE_LX_WN
-#endif
+// the scaled-MFMA engine (fp8 activation pieces x MXFP4); mlp2 reads three pieces of h per
+// stage, so its code super-stage is halved to fit LDS
 template <> struct LargeTileSel<1, 2> {
-  using type = Tile<256, 256, MOE_LX_WM, MOE_LX_WN, MOE_LX_NS, 64, false, MOE_LX_SUPER>;
+  using type = Tile<256, 256, 2, 4, 2, 64, false, 4>;
 };
 template <> struct LargeTileSel<2, 2> {
-  using type = Tile<256, 256, MOE_LX2_WM, MOE_LX2_WN, MOE_LX_NS, 64, false, MOE_LX2_SUPER>;
+  using type = Tile<256, 256, 2, 4, 2, 64, false, 2>;
 };
-// MXFP8 decoded to bf16 on matrix-core tiles (128-byte code windows: 64 KB of codes per
-// 256 weight rows); mlp2's h arrives as a bf16 pair, so its tile takes 128 rows to fit
+// MXFP8 decoded to bf16 (128-byte code windows: 64 KB of codes per 256 weight rows); mlp2's
+// h arrives as a bf16 pair, so its tile takes 128 rows to fit
 template <> struct LargeTileSel<1, 3> {
-  using type = Tile<256, 256, MOE_L_WM, MOE_L_WN, 2, 64, false, 2>;
+  using type = Tile<256, 256, 2, 4, 2, 64, false, 2>;
 };
 template <> struct LargeTileSel<2, 3> {
-  using type = Tile<128, 256, MOE_L_WM, MOE_L_WN, 2, 64, false, 2>;
+  using type = Tile<128, 256, 2, 4, 2, 64, false, 2>;
 };
 template <int MODE, int FMT> using LargeTile = typename LargeTileSel<MODE, FMT>::type;
 
