@@ -268,12 +268,13 @@ static __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   const __bf16 x = (__bf16)a, y = (__bf16)b;
   return (uint32_t)*(const uint16_t*)&x | ((uint32_t)*(const uint16_t*)&y << 16);
 }
-// dout rows in routed order as bf16 pairs: out[p] = [hi D | lo D] of dout[token of perm[p]], hi
-// the nearest bf16 and lo the nearest bf16 of what hi leaves (hi + lo: about 16 significant
-// bits), the A operand of dh' = dout W2 on the K-doubled [W2^T | W2^T].
+// dout rows in routed order as bf16 pairs: hi[p] and lo[p] of dout[token of perm[p]], hi the
+// nearest bf16 and lo the nearest bf16 of what hi leaves (hi + lo: about 16 significant bits),
+// the two parts of the A operand of dh' = dout W2^T.
 __global__ __launch_bounds__(256) void gather_dout_pair_kernel(const float4* __restrict__ dout,
                                                                const int32_t* __restrict__ perm, int A, int k,
-                                                               int D4, uint2* __restrict__ out) {
+                                                               int D4, uint2* __restrict__ hi,
+                                                               uint2* __restrict__ lo) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (int64_t)A * D4) return;
   const int64_t p = i / D4;
@@ -282,9 +283,8 @@ __global__ __launch_bounds__(256) void gather_dout_pair_kernel(const float4* __r
   a = ((unsigned)a < (unsigned)A) ? a : 0;
   const float4 v = dout[(int64_t)(a / k) * D4 + c];
   const float h0 = (float)(__bf16)v.x, h1 = (float)(__bf16)v.y, h2 = (float)(__bf16)v.z, h3 = (float)(__bf16)v.w;
-  uint2* const row = out + p * 2 * D4;
-  row[c] = uint2{pack_bf16x2(h0, h1), pack_bf16x2(h2, h3)};
-  row[D4 + c] = uint2{pack_bf16x2(v.x - h0, v.y - h1), pack_bf16x2(v.z - h2, v.w - h3)};
+  hi[i] = uint2{pack_bf16x2(h0, h1), pack_bf16x2(h2, h3)};
+  lo[i] = uint2{pack_bf16x2(v.x - h0, v.y - h1), pack_bf16x2(v.z - h2, v.w - h3)};
 }
 
 __global__ __launch_bounds__(256) void fill_f32_kernel(float* __restrict__ p, int64_t n, float v) {
@@ -352,30 +352,6 @@ static __device__ __forceinline__ void tile_out(const uint16_t (*t)[TP_LD], int 
   for (int q = 0; q < 4; ++q)
     v[q] = (uint32_t)t[ch * 8 + 2 * q][c] | ((uint32_t)t[ch * 8 + 2 * q + 1][c] << 16);
   *(u32x4*)dst = v;
-}
-
-// Transpose of each of B matrices [R][C] (bf16) into [C][R] (R and C multiples of 64); with
-// DUP the output rows are [C][2R], the transposed row written twice, side by side.
-template <bool DUP>
-__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src, int R, int C,
-                                                             uint16_t* __restrict__ dst) {
-  __shared__ __attribute__((aligned(16))) uint16_t t[64][TP_LD];
-  constexpr int W = DUP ? 2 : 1;
-  const int64_t b = blockIdx.z;
-  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  const uint16_t* s = src + b * R * (int64_t)C;
-  uint16_t* d = dst + b * W * R * (int64_t)C;
-  for (int i = threadIdx.x; i < 512; i += 256) {
-    const int r = i >> 3, ch = i & 7;
-    *(u32x4*)&t[r][ch * 8] = *(const u32x4*)(s + (int64_t)(r0 + r) * C + c0 + ch * 8);
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < 512; i += 256) {
-    const int c = i >> 3, ch = i & 7;
-    uint16_t* const o = d + (int64_t)(c0 + c) * W * R + r0 + ch * 8;
-    tile_out(t, c, ch, o);
-    if (DUP) tile_out(t, c, ch, o + R);
-  }
 }
 
 // Transposed, expert-padded copy of routed rows: dst[c][col] = scale(col) src[row(col)][c]
@@ -616,51 +592,47 @@ hipError_t launch_backward(const BwdArgs& b, hipStream_t st) {
   hipLaunchKernelGGL(fill_f32_kernel, dim3(blocks_for((int64_t)E * DF / 2)), dim3(256), 0, st, (float*)b.zeros,
                      (int64_t)E * DF / 2, 0.0f);
   BW_CHECK(hipGetLastError());
-  // 3. the weights along their other dimension: W1^T [E][D][2F], W2^T twice [E][F][2D]
-  hipLaunchKernelGGL(transpose_bf16_kernel<false>, dim3(blocks_for(D, 64), blocks_for(G, 64), E), dim3(256), 0, st,
-                     b.w1, G, D, b.w1t);
-  BW_CHECK(hipGetLastError());
-  hipLaunchKernelGGL(transpose_bf16_kernel<true>, dim3(blocks_for(F, 64), blocks_for(D, 64), E), dim3(256), 0, st,
-                     b.w2, D, F, b.w2t);
-  BW_CHECK(hipGetLastError());
-  // 4. transposed, padded x and dz = g dout (operands of the weight gradients)
+  // 3. transposed, padded x and dz = g dout (operands of the weight gradients)
   hipLaunchKernelGGL((gather_transpose_kernel<true, false, false>), dim3(ldt / 64, blocks_for(D, 64)), dim3(256), 0,
                      st, (const void*)b.x, D, D, b.padmap, b.perm, b.gates, k, A, ldt, b.xT);
   BW_CHECK(hipGetLastError());
   hipLaunchKernelGGL((gather_transpose_kernel<true, true, true>), dim3(ldt / 64, blocks_for(D, 64)), dim3(256), 0,
                      st, (const void*)b.dout, D, D, b.padmap, b.perm, b.gates, k, A, ldt, b.dzT);
   BW_CHECK(hipGetLastError());
-  // 5. dout rows in routed order as bf16 pairs
+  // 4. dout rows in routed order as bf16 pairs
+  uint16_t* const dout_lo = b.dout_perm + (int64_t)A * D;
   hipLaunchKernelGGL(gather_dout_pair_kernel, dim3(blocks_for((int64_t)A * D / 4)), dim3(256), 0, st,
-                     (const float4*)b.dout, b.perm, A, k, D / 4, (uint2*)b.dout_perm);
+                     (const float4*)b.dout, b.perm, A, k, D / 4, (uint2*)b.dout_perm, (uint2*)dout_lo);
   BW_CHECK(hipGetLastError());
 
   const int cfg = expert_tile_config(A, E);
-  // 6. recompute u = x W1^T + b1 (the forward's mlp1, storing u)
+  // 5. recompute u = x W1^T + b1 (the forward's mlp1, storing u)
   ExpertArgs f{};
   f.x = b.x; f.w1 = b.w1; f.b1 = b.b1; f.gates = b.gates; f.offsets = b.offsets; f.perm = b.perm;
   f.u_out = b.u; f.T = T; f.D = D; f.E = E; f.k = k; f.F = F; f.fmt = 0;
   BW_CHECK(launch_mlp1(f, cfg, st));
-  // 7. dh' = [dout hi | lo] [W2^T | W2^T]^T at the slot rows (the forward's mlp2: K = 2D, N = F)
+  // 6. dh' = (dout hi + lo) W2 at the slot rows: the forward's mlp2 with K = D, N = F, reading
+  // W2 [E][D][F] as stored, both parts of A against each staged tile of W2
   ExpertArgs m{};
-  m.h = b.dout_perm; m.w2 = b.w2t; m.b2 = b.zeros; m.gates = b.ones; m.offsets = b.offsets; m.perm = b.perm;
-  m.y = b.dxs; m.T = T; m.D = F; m.E = E; m.k = k; m.F = 2 * D; m.fmt = 0;
+  m.h = b.dout_perm; m.h_lo = dout_lo; m.w2 = b.w2; m.b2 = b.zeros; m.gates = b.ones; m.offsets = b.offsets;
+  m.perm = b.perm; m.y = b.dxs; m.T = T; m.D = F; m.E = E; m.k = k; m.F = D; m.fmt = 0; m.w2_kn_rows = D;
   BW_CHECK(launch_mlp2(m, cfg, st));
-  // 8. the SwiGLU backward: h, du, dg (dh' sits in dxs until step 9 overwrites it)
+  // 7. the SwiGLU backward: h, du, dg (dh' sits in dxs until step 8 overwrites it)
   hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)A), dim3(256), 0, st, b.u, b.dxs, b.perm, b.gates, A, F, b.h,
                      b.du, b.dgsum);
   BW_CHECK(hipGetLastError());
-  // 9. dx contributions du W1[e] at the slot rows (the forward's mlp2: K = 2F, N = D)
-  m.h = b.du; m.w2 = b.w1t; m.y = b.dxs; m.D = D; m.F = G;
+  // 8. dx contributions du W1[e] at the slot rows: the forward's mlp2 with K = 2F, N = D,
+  // reading W1 [E][2F][D] as stored
+  m.h = b.du; m.h_lo = nullptr; m.w2 = b.w1; m.y = b.dxs; m.D = D; m.F = G; m.w2_kn_rows = G;
   BW_CHECK(launch_mlp2(m, cfg, st));
-  // 10. transposed, padded h and du
+  // 9. transposed, padded h and du
   hipLaunchKernelGGL((gather_transpose_kernel<false, false, false>), dim3(ldt / 64, blocks_for(F, 64)), dim3(256), 0,
                      st, (const void*)b.h, F, F, b.padmap, b.perm, b.gates, k, A, ldt, b.hT);
   BW_CHECK(hipGetLastError());
   hipLaunchKernelGGL((gather_transpose_kernel<false, false, false>), dim3(ldt / 64, blocks_for(G, 64)), dim3(256), 0,
                      st, (const void*)b.du, G, G, b.padmap, b.perm, b.gates, k, A, ldt, b.duT);
   BW_CHECK(hipGetLastError());
-  // 11. weight gradients per expert: dW2[e] = dz^T h, dW1[e] = du^T x
+  // 10. weight gradients per expert: dW2[e] = dz^T h, dW1[e] = du^T x
   BwdGemmArgs w{};
   w.poff = b.poff; w.E = E;
   w.a = b.dzT; w.lda = ldt; w.b = b.hT; w.ldb = ldt; w.M = D; w.N = F;
@@ -669,7 +641,7 @@ hipError_t launch_backward(const BwdArgs& b, hipStream_t st) {
   w.a = b.duT; w.b = b.xT; w.M = G; w.N = D;
   w.m_tiles = (G + BG_BM - 1) / BG_BM; w.n_tiles = (D + BG_BN - 1) / BG_BN; w.c = b.dw1;
   BW_CHECK(launch_wgrad(w, st));
-  // 12. router: dg and the softmax backward, then the per-expert sums and dx
+  // 11. router: dg and the softmax backward, then the per-expert sums and dx
   hipLaunchKernelGGL(router_bwd_kernel, dim3(blocks_for(T, 4)), dim3(256), 0, st, b.dgsum, b.dout, b.b2, b.idx,
                      b.gates, T, D, E, k, b.dl);
   BW_CHECK(hipGetLastError());

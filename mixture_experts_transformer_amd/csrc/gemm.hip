@@ -82,7 +82,8 @@ struct Tile {
 // code segments) and 2 for MXFP4 mlp2 (three workgroups per CU) and for MXFP8 (64 code bytes
 // per row and stage: 128-byte windows).
 template <int MODE, int FMT> using SmallTile =
-    Tile<64, 128, 1, 4, 2, 64, true, (FMT == 0 || (FMT == 1 && MODE == 1)) ? 4 : 2, FMT == 0 ? 1 : 4>;
+    Tile<64, 128, 1, 4, 2, 64, true, (FMT == 0 || FMT >= 4 || (FMT == 1 && MODE == 1)) ? 4 : 2,
+         (FMT == 0 || FMT >= 4) ? 1 : 4>;
 
 // Matrix-core tiles serve many routed rows per expert: 256 x 256 outputs on eight waves
 // (2 x 4, 128 x 64 each), two LDS stages of K = 64.
@@ -105,6 +106,10 @@ template <> struct LargeTileSel<1, 3> {
 template <> struct LargeTileSel<2, 3> {
   using type = Tile<128, 256, 2, 4, 2, 64, false, 2>;
 };
+// bf16 weights stored [K][N] with A as a bf16 pair (the backward's dout W2^T): 128 rows, as above
+template <> struct LargeTileSel<2, 5> {
+  using type = Tile<128, 256, 2, 4, 2, 64, false>;
+};
 template <int MODE, int FMT> using LargeTile = typename LargeTileSel<MODE, FMT>::type;
 
 struct GemmArgs {
@@ -126,12 +131,26 @@ struct GemmArgs {
   uint32_t* h8s;            //   and their scales
   int h8s_stride;
   float* y;                 // mlp2 output
+  int bt_rows;              // kernel format 4 (bf16 weights stored [rows][N], N contiguous): rows
+                            //   per expert; K step k reads stored row k mod bt_rows
   int E, k, K, N, F;
   int A;                    // routed rows (T * k)
   int n_tiles, max_m_tiles;
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+// Transposing LDS read (ds_read_b64_tr_b16, gfx950), lane layout measured on the GPU: in
+// each group of 16 lanes, lane s loads 4 consecutive 16-bit values from its own address and
+// lane i of the group receives value i % 4 of lanes i / 4, 4 + i / 4, 8 + i / 4, 12 + i / 4.
+// With lane s of a group addressing stored row r0 + s / 4, columns c0 + 4 (s % 4) .. + 3 of a
+// [K][N] tile, lane i receives column c0 + i of rows r0 .. r0 + 3: four K values of one
+// output column, as the matrix instruction's B operand wants them.
+static __device__ __forceinline__ i16x4 lds_read_tr16(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+}
 
 // Direct global -> LDS copies.  They are written as inline assembly: the copies have no
 // register results, their completion is waited for explicitly (vmcnt) before the barrier
@@ -302,13 +321,18 @@ static __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
 template <int MODE, int FMT, class C>
 __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmArgs p) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, CPR = C::CPR, NS = C::NS, NW = C::NW;
+  // formats 4 and 5: bf16 weights stored [K][N] (N contiguous), staged as such and read into
+  // the matrix-core operand with transposing LDS reads; otherwise as format 0.  Format 5 takes
+  // A as a bf16 pair (a + a_lo), both parts against each staged weight tile.
+  constexpr bool BT = FMT == 4 || FMT == 5;
+  constexpr int WF = BT ? 0 : FMT;
   constexpr int FM = C::FM, FN = C::FN;
   constexpr bool MX = FMT == 2;                             // scaled MFMA on fp8 pieces
   constexpr bool DEC = FMT == 1 || FMT == 3;                // codes decoded to bf16 (MXFP4, MXFP8)
   constexpr int CBS = FMT == 3 ? 64 : 32;                   // code bytes per row and stage
   constexpr int KS = MX ? 1 : BK / 16;                      // MFMA K steps per stage
   // A parts: bf16 (1), h hi + lo (2), or fp8 pieces (x: 2, h: 3)
-  constexpr int AP = MX ? (MODE == 1 ? 2 : 3) : ((MODE == 2 && DEC) ? 2 : 1);
+  constexpr int AP = MX ? (MODE == 1 ? 2 : 3) : ((MODE == 2 && (DEC || FMT == 5)) ? 2 : 1);
   constexpr int ROWB = CPR * 16;                            // bytes per bf16 row segment
   constexpr int APL = MX ? 1 : AP;                          // A parts in LDS (pieces share rows)
   constexpr int A_CPR = MX ? 4 * AP : CPR;                  // 16-byte chunks per A row per stage
@@ -316,23 +340,23 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   constexpr int A_CPC = BM * A_CPR / 64;                    // A copies per part and stage
   constexpr int A_BYTES = BM * A_ROWB;                      // per A part per stage
   static_assert((BM * A_CPR) % 64 == 0, "A stage must tile the copy instructions");
-  static_assert(FMT == 0 || BK == 64, "MXFP4 staging assumes 64-wide K steps");
+  static_assert(WF == 0 || BK == 64, "MXFP4 staging assumes 64-wide K steps");
   constexpr int SUPER = C::SUPER;                           // stages per MXFP4 code super-stage
   constexpr int NSB = 2;                                    // code super-stage slots
   // a slot is refilled NS - 1 steps ahead of its first use, after the barrier that ends
   // the last use of its previous super-stage
-  static_assert(FMT == 0 || SUPER * (NSB - 1) > NS - 2, "code ring too short for the stage ring");
+  static_assert(WF == 0 || SUPER * (NSB - 1) > NS - 2, "code ring too short for the stage ring");
   constexpr int CROW = CBS * SUPER;                         // code bytes per row per super-stage
   constexpr int CCH = CROW / 16;                            // 16-byte code chunks per row
-  constexpr int B_STAGE_BYTES = (FMT == 0) ? BN * ROWB : 0;  // bf16 B tile (MXFP4: none)
+  constexpr int B_STAGE_BYTES = (WF == 0) ? BN * ROWB : 0;  // bf16 B tile (MXFP4: none)
   constexpr int STAGE = APL * A_BYTES + B_STAGE_BYTES;
   constexpr int CODE_SLOT = BN * CROW;
-  constexpr int CODE_BYTES = (FMT != 0) ? NSB * CODE_SLOT : 0;
+  constexpr int CODE_BYTES = (WF != 0) ? NSB * CODE_SLOT : 0;
   constexpr int ROWS_PER_CP = 1024 / ROWB;                  // bf16 B rows per copy instruction
   constexpr int NA = APL * A_CPC;                           // per stage: A copies
-  constexpr int NBS = (FMT == 0) ? BN / ROWS_PER_CP : 0;    // per stage: B copies
+  constexpr int NBS = (WF == 0) ? BN / ROWS_PER_CP : 0;    // per stage: B copies
   constexpr int NG = NA + NBS;                              // copies per stage group
-  constexpr int NC = (FMT != 0) ? BN * CROW / 1024 : 0;     // copies per code super-stage
+  constexpr int NC = (WF != 0) ? BN * CROW / 1024 : 0;     // copies per code super-stage
   // scaled-MFMA engine: A scale dwords (two per row and stage) in a ring of super-stages
   // beside the codes, 8 SUPER bytes per row, chunks swizzled by row bit 3
   constexpr int ASL_ROW = MX ? 8 * SUPER : 16;
@@ -344,28 +368,28 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   // last scale byte and the row's last one (a super-stage needs 2 SUPER <= 8 of them, so the
   // record covers them; stopping at the row keeps the last row's records inside the weight
   // buffer, whose size is a multiple of 4); one copy covers 64 rows
-  constexpr int SCW_SLOT = (FMT != 0) ? BN * 16 : 0;
+  constexpr int SCW_SLOT = (WF != 0) ? BN * 16 : 0;
   constexpr int SCW_BYTES = NSB * SCW_SLOT;
-  constexpr int NSW = (FMT != 0) ? BN / 64 : 0;             // scale copies per window
+  constexpr int NSW = (WF != 0) ? BN / 64 : 0;             // scale copies per window
   constexpr int NCT = NC + NASC + NSW;
-  static_assert(FMT == 0 || (SUPER % 2 == 0 && SUPER <= 4), "scale records: even windows of <= 8 scale bytes");
+  static_assert(WF == 0 || (SUPER % 2 == 0 && SUPER <= 4), "scale records: even windows of <= 8 scale bytes");
   // with four-stage code super-stages the K loop is unrolled over one, which makes the
   // stage slot and the super-stage boundaries compile-time constants (measured: a few
   // percent there; elsewhere it costs registers, spills in the three-piece mlp2 tile)
-  constexpr int UNR = (FMT != 0 && SUPER >= 4 && SUPER % NS == 0) ? SUPER : 1;
+  constexpr int UNR = (WF != 0 && SUPER >= 4 && SUPER % NS == 0) ? SUPER : 1;
   // Code windows aligned to their own size (64 or 128 bytes per row): each row's windows
   // start at the boundary at or below its codes (a row starts 32 s bytes past one when its
   // length is not a multiple of the window), so every 64-byte sector or 128-byte line is
   // fetched by one window instead of two.  Row r's stage kt then sits at position
   // kt + s(r) of the row's window sequence.  The windows need their own issue schedule
   // (below), which fits a two-stage ring.
-  constexpr bool WALIGN = FMT != 0 && (CROW == 64 || CROW == 128) && NS == 2;
+  constexpr bool WALIGN = WF != 0 && (CROW == 64 || CROW == 128) && NS == 2;
   static_assert(!MX || (SUPER >= 2 && 1024 % ASL_ROW == 0), "A scale super-stage granularity");
   constexpr int PW_G = (NG + NW - 1) / NW;
   constexpr int PW_C = (NCT + NW - 1) / NW + (NCT == 0 ? 1 : 0);
   constexpr int PN = BN / 2;                                // mlp1: pairs per tile
   static_assert(BN % 32 == 0 && (BM * CPR) % 64 == 0 && (BN * CPR) % 64 == 0, "copy granularity");
-  static_assert(FMT == 0 || BN % 64 == 0, "scale copies cover 64 rows");
+  static_assert(WF == 0 || BN % 64 == 0, "scale copies cover 64 rows");
 
   constexpr int SMEM = NS * STAGE + CODE_BYTES + ASL_BYTES + SCW_BYTES;
   // epilogue slices (per wave, 32 output rows): mlp1 bf16 [32][pairs] (+ lo part), row
@@ -459,7 +483,9 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
 
   const uint8_t* w_e;
   size_t s_e_off = 0;                       // byte offset of expert e's scales in p.w
-  if (FMT == 0) {
+  if (BT) {
+    w_e = p.w + (size_t)e * p.bt_rows * p.N * 2;
+  } else if (WF == 0) {
     w_e = p.w + (size_t)e * p.N * K * 2;
   } else {
     w_e = p.w + (size_t)e * p.N * (K / 64 * CBS);
@@ -476,7 +502,8 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   // a multiple of 64); streaming tiles read each once and copy them with the non-temporal
   // hint, which keeps the A rows that every column tile re-reads in the L2 (measured at
   // T = 256: mlp1 -8 %, mlp2 -9 %)
-  const bool wlines = FMT == 0 && (((uintptr_t)p.w) & 127) == 0;
+  const bool wlines = WF == 0 && (((uintptr_t)p.w) & 127) == 0;
+  const int bt_kt = BT ? p.bt_rows / 64 : 1;  // format 4: K steps before the stored rows repeat
   const size_t w_e_off = (size_t)(w_e - p.w);
   const uint8_t* const wbase = WALIGN ? w_e - CROW : w_e;
 #define MOE_CSHIFT(wr) (walign ? (int)(((w_e_off + (size_t)(wr) * (K / 64 * CBS)) / CBS) & (SUPER - 1)) : 0)
@@ -520,7 +547,16 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
       gdst[j] = part * A_BYTES + ii * 1024;
     } else if (i < NG) {
       const int ii = i - NA;
-      if (FMT == 0) {
+      if (BT) {
+        // stored rows of the stage's 64 K values, BN columns each (16-byte chunks XOR-swizzled
+        // by 4 (row & 3), so the transposing reads of four rows hit disjoint banks); columns
+        // past the matrix edge copy valid ones (never stored)
+        constexpr int RCH = BN / 8;
+        const int r = ii * (64 / RCH) + lane / RCH;
+        const int c = (lane % RCH) ^ (4 * (r & 3));
+        goff[j] = (uint32_t)(((size_t)r * p.N + min(n_tile * BN + 8 * c, p.N - 8)) * 2);
+        gdst[j] = APL * A_BYTES + ii * 1024;
+      } else if (WF == 0) {
         const int r = ii * ROWS_PER_CP + lane / CPR;
         const int c = swz_pos<CPR>(r, lane % CPR);
         goff[j] = (uint32_t)(((size_t)MOE_WROW(r) * K + c * 8) * 2);
@@ -537,7 +573,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
     coff[j] = 0;
     cdst[j] = 0;
     cre[j] = 0;
-    if (FMT != 0 && i < NC) {
+    if (WF != 0 && i < NC) {
       const int r = i * (1024 / CROW) + lane / CCH;
       const int c = (lane % CCH) ^ code_swz<CCH>(r);
       const int wr = MOE_WROW(r);
@@ -577,8 +613,10 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
                                 : (i_ < A_CPC ? (const void*)p.a : (const void*)p.a_lo);          \
           dma16((const uint8_t*)ab_ + (size_t)(kt) * A_ROWB, goff[j], d_);                       \
         } else {                                                                                 \
-          if (C::STREAM && wlines) dma16_nt(w_e + (size_t)(kt) * ROWB, goff[j], d_);             \
-          else dma16(w_e + (size_t)(kt) * ROWB, goff[j], d_);                                    \
+          const uint8_t* ws_ = BT ? w_e + (size_t)((kt) % bt_kt) * 64 * p.N * 2                  \
+                                  : w_e + (size_t)(kt) * ROWB;                                   \
+          if (C::STREAM && wlines) dma16_nt(ws_, goff[j], d_);                                   \
+          else dma16(ws_, goff[j], d_);                                                          \
         }                                                                                        \
         ++issued;                                                                                \
       }                                                                                          \
@@ -589,7 +627,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   do {                                                                                           \
     _Pragma("unroll") for (int j = 0; j < PW_C; ++j) {                                           \
       const int i_ = wave + j * NW;                                                              \
-      if (FMT != 0 && i_ < NC) {                                                                 \
+      if (WF != 0 && i_ < NC) {                                                                 \
         if (CROW == 128 && C::STREAM && walign)   /* whole lines, read once */                  \
           dma16_nt(wbase + (size_t)(w) * CROW, coff[j], codes_l + ((w) % NSB) * CODE_SLOT + cdst[j]); \
         else                                                                                     \
@@ -620,7 +658,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   // w - 2's slot is free, ahead of the group of stage S (w - 1) + 1, its first use.
 #define MOE_ISSUE(kt)                                                                            \
   do {                                                                                           \
-    if (FMT != 0 && (kt) % SUPER == 0) {                                                         \
+    if (WF != 0 && (kt) % SUPER == 0) {                                                         \
       if (!WALIGN) MOE_ISSUE_WIN((kt) / SUPER);                                                  \
       MOE_ISSUE_ASC((kt) / SUPER);                                                               \
     }                                                                                            \
@@ -661,7 +699,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
     csh[j] = 0;
     sidx[j] = 0;
     if (WALIGN) csh[j] = MOE_CSHIFT(MOE_WROW(brow[j]));
-    if (FMT != 0) {
+    if (WF != 0) {
       const int rs = MOE_WROW(brow[j]) * (K / 32);
       sidx[j] = brow[j] * 16 + rs - MOE_SCW_START(rs, 1 << 30, 0) + kg;
     }
@@ -671,7 +709,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   const int sk_last = (nk - 1) / SUPER;
 #define MOE_SCALE_LAST(kt_)                                                                      \
   do {                                                                                           \
-    if (FMT != 0 && (kt_) == SUPER * sk_last) {                                                  \
+    if (WF != 0 && (kt_) == SUPER * sk_last) {                                                  \
       _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                           \
         const int rs_ = MOE_WROW(brow[j]) * (K / 32);                                            \
         sidx[j] += MOE_SCW_START(rs_, 1 << 30, sk_last) - MOE_SCW_START(rs_, rs_ + K / 32, sk_last); \
@@ -708,7 +746,15 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   do {                                                                                           \
     const int cc_ = kg * KS + (ks_);        /* chunk (8 K elements) this lane feeds */           \
     _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                             \
-      if (FMT == 0) fb[buf][j] = *(const bf16x8*)((sb_) + swz<CPR>(brow[j], cc_));                \
+      if (BT) {                                                                                  \
+        const int s_ = lane & 15;                                                                \
+        const int col_ = wn * C::WTN + j * 32 + 16 * ((lane >> 4) & 1) + 4 * (s_ & 3);           \
+        const uint8_t* p_ = (sb_) + (32 * kg + 8 * (ks_) + (s_ >> 2)) * (2 * BN) +              \
+                            ((((col_ >> 3) ^ (4 * (s_ >> 2))) << 4) | ((col_ & 7) * 2));         \
+        const i16x4 t0_ = lds_read_tr16(p_);                                                     \
+        const i16x4 t1_ = lds_read_tr16(p_ + 4 * (2 * BN));                                      \
+        fb[buf][j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0_, t1_, 0, 1, 2, 3, 4, 5, 6, 7)); \
+      } else if (WF == 0) fb[buf][j] = *(const bf16x8*)((sb_) + swz<CPR>(brow[j], cc_));         \
       else if (FMT == 3) fb[buf][j] = (ks_) < 2 ? decode_fp8x8(q4[j][2 * (ks_)], q4[j][2 * (ks_) + 1], scl[j]) \
                                     : decode_fp8x8(q8[j][2 * (ks_) - 4], q8[j][2 * (ks_) - 3], scl[j]); \
       else fb[buf][j] = decode_fp4x8(q4[j][ks_], scl[j]);                                        \
@@ -727,7 +773,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   // one scheduling group per MFMA step: the next step's LDS reads ahead of this step's MFMAs
 #define MOE_SCHED(FA)                                                                            \
   do {                                                                                           \
-    __builtin_amdgcn_sched_group_barrier(0x100, (FMT == 0 ? FN : 0) + AP * (FA), 0);             \
+    __builtin_amdgcn_sched_group_barrier(0x100, (WF == 0 ? (BT ? 2 : 1) * FN : 0) + AP * (FA), 0); \
     __builtin_amdgcn_sched_group_barrier(0x008, AP * (FA) * FN, 0);                              \
   } while (0)
 
@@ -1118,6 +1164,15 @@ static hipError_t launch_any(const GemmArgs& g, int fmt, int cfg, int64_t A, hip
   if (fmt == 2) return launch_gemm<MODE, 2, LargeTile<MODE, 2>>(g, A, st);
   if (fmt == 0)
     return cfg == 0 ? launch_gemm<MODE, 0, SmallTile<MODE, 0>>(g, A, st) : launch_gemm<MODE, 0, LargeTile<MODE, 0>>(g, A, st);
+  if constexpr (MODE == 2) {
+    // bf16 weights stored [K][N] (the backward's products with W2 and W1 as stored)
+    if (fmt == 4)
+      return cfg == 0 ? launch_gemm<MODE, 4, SmallTile<MODE, 4>>(g, A, st)
+                      : launch_gemm<MODE, 4, LargeTile<MODE, 4>>(g, A, st);
+    if (fmt == 5)
+      return cfg == 0 ? launch_gemm<MODE, 5, SmallTile<MODE, 5>>(g, A, st)
+                      : launch_gemm<MODE, 5, LargeTile<MODE, 5>>(g, A, st);
+  }
   // MXFP8 (kernel format 3) decodes to bf16: matrix-core tiles at many rows per expert,
   // streaming tiles otherwise
   if (fmt == 3)
@@ -1155,8 +1210,13 @@ hipError_t launch_mlp2(const ExpertArgs& a, int cfg, hipStream_t st) {
   g.a8 = a.hq; g.a8s = a.hs; g.a8s_stride = mx_scale_stride(a.F);
   g.w = (const uint8_t*)a.w2; g.bias = a.b2; g.h = nullptr; g.h_lo = nullptr; g.y = a.y;
   g.E = a.E; g.k = a.k; g.K = a.F; g.N = a.D; g.F = a.F;
+  g.bt_rows = a.w2_kn_rows;
   const int64_t A = (int64_t)a.T * a.k;
   g.A = (int)A;
+  if (a.w2_kn_rows > 0) {
+    if (a.fmt != 0 || a.w2_kn_rows % 64 != 0) return hipErrorInvalidValue;
+    return launch_any<2>(g, a.h_lo ? 5 : 4, cfg, A, st);
+  }
   return launch_any<2>(g, kernel_format(a.fmt, cfg), cfg, A, st);
 }
 

@@ -128,7 +128,7 @@ Layout layout(int64_t T, int64_t D, int64_t E, int64_t k, int64_t F, int fmt, in
 
 // Backward workspace (moe_backward), one allocation.
 struct BwdLayout {
-  size_t poff = 0, padmap = 0, dout_perm = 0, w1t = 0, w2t = 0, ones = 0, zeros = 0, xT = 0, dzT = 0, u = 0;
+  size_t poff = 0, padmap = 0, dout_perm = 0, ones = 0, zeros = 0, xT = 0, dzT = 0, u = 0;
   size_t h = 0, du = 0, dgsum = 0, dxs = 0, hT = 0, duT = 0, dl = 0, part_w = 0, part_b2 = 0, part_b1 = 0;
   size_t total = 0;
 };
@@ -147,8 +147,6 @@ BwdLayout bwd_layout(int64_t T, int64_t D, int64_t E, int64_t k, int64_t F) {
   L.poff = take((2 * (size_t)E + 1) * 4);
   L.padmap = take(ldt * 4);
   L.dout_perm = take(A * 2 * D * 2);
-  L.w1t = take((size_t)E * G * D * 2);
-  L.w2t = take((size_t)E * F * 2 * D * 2);
   L.ones = take(A * 4);
   L.zeros = take((size_t)E * DF * 2);
   L.xT = take((size_t)D * ldt * 2);
@@ -538,8 +536,8 @@ int moe_backward(const void* x, const void* router_w, const void* w1, const void
   CHECK(check_ptr(dx, "dx"));
   if (T * k + E * 63 + 64 >= ((int64_t)1 << 31))
     return fail(MOE_EINVAL, "T*k = %lld is too large for the backward's padded layout", (long long)(T * k));
-  // the grouped GEMMs address a routed row and one expert's weights with 32-bit byte offsets,
-  // and the backward's take K = 2D and 2F
+  // the grouped GEMMs address a routed row (the backward's have K = 2D and 2F) and one
+  // expert's weights (W1: 4 D F bytes) with 32-bit byte offsets; kept with a factor 4 margin
   if (T * k * 2 * (D > F ? D : F) >= ((int64_t)1 << 30) || 4 * D * F >= ((int64_t)1 << 30))
     return fail(MOE_EINVAL, "T*k*2*max(D, F) and 4*D*F must each be < 2^30 for the backward");
   const BwdLayout L = bwd_layout(T, D, E, k, F);
@@ -551,7 +549,7 @@ int moe_backward(const void* x, const void* router_w, const void* w1, const void
   b.idx = topk_idx; b.gates = gates; b.offsets = offsets; b.perm = perm; b.dout = dout;
   b.dx = dx; b.dwr = d_router_w; b.dbr = d_router_b; b.dw1 = dw1; b.db1 = db1; b.dw2 = dw2; b.db2 = db2;
   b.poff = (int32_t*)(ws + L.poff); b.padmap = (int32_t*)(ws + L.padmap);
-  b.dout_perm = (uint16_t*)(ws + L.dout_perm); b.w1t = (uint16_t*)(ws + L.w1t); b.w2t = (uint16_t*)(ws + L.w2t);
+  b.dout_perm = (uint16_t*)(ws + L.dout_perm);
   b.ones = (float*)(ws + L.ones); b.zeros = (uint16_t*)(ws + L.zeros);
   b.xT = (uint16_t*)(ws + L.xT); b.dzT = (uint16_t*)(ws + L.dzT); b.u = (float*)(ws + L.u);
   b.h = (uint16_t*)(ws + L.h); b.du = (uint16_t*)(ws + L.du); b.dgsum = (float*)(ws + L.dgsum);

@@ -63,6 +63,10 @@ struct ExpertArgs {
   float* out;               // [T][D] fp32
   float* u_out;             // mlp1 with bf16 weights: store the pre-activation u [A][2F] (fp32)
                             //   instead of h (the backward's recomputation); null otherwise
+  int w2_kn_rows;           // mlp2 with bf16 weights: 0, or w2 is stored [E][w2_kn_rows][D] (D
+                            //   contiguous) and K index f reads stored row f mod w2_kn_rows
+                            //   (a multiple of 64); the backward's products with W2 and W1.
+                            //   With h_lo set too, A is the pair h + h_lo (bf16 each)
   int T, D, E, k, F, fmt;
 };
 
@@ -100,9 +104,7 @@ struct BwdArgs {
   int32_t* poff;            // [E+1] padded column offsets per expert, then [E] the experts by
                             //   decreasing padded row count
   int32_t* padmap;          // [ldt] routed row of each padded column, -1 for padding
-  uint16_t* dout_perm;      // [A][2D] dout rows in routed order, bf16 pairs: hi then lo
-  uint16_t* w1t;            // [E][D][2F]
-  uint16_t* w2t;            // [E][F][2D]: W2^T twice along K
+  uint16_t* dout_perm;      // [2][A][D] dout rows in routed order as bf16 pairs: hi rows, then lo rows
   float* ones;              // [A] unit gates
   uint16_t* zeros;          // [E][max(D, F)] zero biases
   uint16_t* xT;             // [D][ldt]
