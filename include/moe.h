@@ -212,7 +212,7 @@ int moe_experts(const void* x, const void* w1, const void* b1, const void* w2, c
  * the softmax over the selected logits gives dl = g (dg - sum_j g_j dg_j), then
  * d_router_w[e] += dl x[t], d_router_b[e] += dl and dx[t] += dl router_w[e].  The matrix
  * products run on the bf16 matrix cores with fp32 accumulation (the products over routed rows
- * on the forward's grouped GEMM kernels, the weights transposed once per call): dout enters
+ * on the forward's grouped GEMM kernels, the weights read as stored): dout enters
  * the product with W2 as a bf16 pair (hi + lo, about 16 significant bits), while dz, du and h
  * enter theirs rounded to bf16, which bounds the relative error of each gradient near 2^-9;
  * every sum has a fixed order, so the result is bitwise reproducible.  With
