@@ -7,10 +7,10 @@
 // softmax gates.  Per assignment a = t*k + j (expert e, gate g, row p of e's group):
 //
 //   u  = x[t] W1[e]^T + b1[e]                          (recomputed: the forward's mlp1 kernel)
-//   dh' = dout[t] W2[e]                                 (the forward's mlp2 kernel on W2^T)
+//   dh' = dout[t] W2[e]                                 (the forward's mlp2 kernel, W2 as stored)
 //   dg[a] = <dh', h(u)> + <dout[t], b2[e]>              (= <dout[t], z[a]>, z the ungated mlp2 output)
 //   du = SwiGLU'(u) * (g dh')
-//   dx[t] += du W1[e]                                   (the forward's mlp2 kernel on W1^T)
+//   dx[t] += du W1[e]                                   (the forward's mlp2 kernel, W1 as stored)
 //   dW2[e] = sum_p (g dout[t])^T h,  dW1[e] = sum_p du^T x[t]   (per-expert GEMMs, K = rows)
 //   db2[e] = sum_p g dout[t],  db1[e] = sum_p du
 //   router: dl = g (dg - sum_j g_j dg_j) on the selected experts; dWr[e] = sum dl x[t],
@@ -18,8 +18,8 @@
 //
 // The three products over routed rows are the forward's grouped GEMMs (grouped_gemm_kernel):
 // mlp1 with an epilogue that stores u instead of h, and mlp2 with unit gates and zero biases
-// for dh' and for du W1 (their weights transposed once per call; dout enters as a bf16 pair,
-// the K dimension doubled: [hi | lo] against [W2^T | W2^T]).  The weight gradients contract
+// for dh' and for du W1 (their weights read as stored, [K][N], through transposing LDS reads;
+// dout enters as a bf16 pair, hi and lo against the same weight tile).  The weight gradients contract
 // over an expert's rows, so their operands are written transposed, per expert, in a layout
 // whose expert blocks are padded to 64 rows with zeros, and multiplied by bwd_gemm_kernel.
 // Everything runs on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  No float atomics:
@@ -35,19 +35,29 @@ constexpr float BW_LIMIT = 7.0f;
 constexpr float BW_NEG_ALPHA_LOG2E = -BW_ALPHA * 1.4426950408889634f;
 
 // ------------------------------------------------------------------------------ GEMM tile
-// Weight-gradient tiles: 256 x 128 outputs per workgroup, 8 waves in a 4 x 2 grid of 64 x 64,
-// K in steps of 64 (whole 128-byte row segments per stage), two LDS stages filled through
-// registers.
-constexpr int BG_BM = 256, BG_BN = 256, BG_BK = 64, BG_CPR = BG_BK / 8;
-constexpr int BG_WAVES_M = 2, BG_WAVES_N = 4, BG_NW = BG_WAVES_M * BG_WAVES_N, BG_THREADS = 64 * BG_NW;
-constexpr int BG_WTM = BG_BM / BG_WAVES_M, BG_WTN = BG_BN / BG_WAVES_N;
-constexpr int BG_FM = BG_WTM / 32, BG_FN = BG_WTN / 32;
-constexpr int BG_A_BYTES = BG_BM * BG_BK * 2;
-constexpr int BG_B_BYTES = BG_BN * BG_BK * 2;
-constexpr int BG_STAGE = BG_A_BYTES + BG_B_BYTES;
-constexpr int BG_ALD = BG_BM * BG_CPR / BG_THREADS;   // 16-byte A chunks per thread and stage
-constexpr int BG_BLD = BG_BN * BG_CPR / BG_THREADS;   // B chunks
-static_assert(BG_ALD * BG_THREADS == BG_BM * BG_CPR && BG_BLD * BG_THREADS == BG_BN * BG_CPR, "load split");
+// Weight-gradient tiles, K in steps of 64 (whole 128-byte row segments per stage), staged to
+// LDS through registers.  Two shapes:
+//  * 256 x 256 outputs, 8 waves in a 2 x 4 grid of 128 x 64, two LDS stages and two register
+//    sets (loads two stages ahead): experts with many rows, matrix-core bound;
+//  * 256 x 128 outputs, 8 waves in a 4 x 2 grid of 64 x 64, one LDS stage and one register
+//    set, two workgroups per CU: experts with few rows (K of 64 or 128), where a tile is one
+//    or two matrix steps and then 128 KB of fp32 stores, so a second workgroup's loads and
+//    matrix work overlap the first one's stores.
+constexpr int BG_BK = 64, BG_CPR = BG_BK / 8;
+template <int BM_, int BN_, int WM_, int WN_, int SLOTS_, int WPE_>
+struct WTile {
+  static constexpr int BM = BM_, BN = BN_, WAVES_M = WM_, WAVES_N = WN_, SLOTS = SLOTS_, WPE = WPE_;
+  static constexpr int NW = WM_ * WN_, THREADS = 64 * NW;
+  static constexpr int WTM = BM / WM_, WTN = BN / WN_;
+  static constexpr int FM = WTM / 32, FN = WTN / 32;
+  static constexpr int A_BYTES = BM * BG_BK * 2, B_BYTES = BN * BG_BK * 2, STAGE = A_BYTES + B_BYTES;
+  static constexpr int ALD = BM * BG_CPR / THREADS;   // 16-byte A chunks per thread and stage
+  static constexpr int BLD = BN * BG_CPR / THREADS;   // B chunks
+  static_assert(ALD * THREADS == BM * BG_CPR && BLD * THREADS == BN * BG_CPR, "load split");
+  static_assert(SLOTS == 1 || SLOTS == 2, "LDS stages");
+};
+using WTileLarge = WTile<256, 256, 2, 4, 2, 1>;
+using WTileSmall = WTile<256, 128, 4, 2, 1, 4>;
 
 struct BwdGemmArgs {
   const int32_t* poff;      // [E+1] padded column offsets, then [E] the experts by decreasing
@@ -67,13 +77,16 @@ struct BwdGemmArgs {
 // Matrix-core mapping as in the forward's grouped GEMM: in MFMA step ks of a stage, lane l
 // feeds row l & 31 and the 8 K elements of chunk 4 (l >> 5) + ks of each operand, and output
 // register q of lane l is C[8 (q >> 2) + 4 (l >> 5) + (q & 3)][l & 31].
-__global__ __launch_bounds__(BG_THREADS, 1) void bwd_gemm_kernel(BwdGemmArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BG_STAGE];
+template <class W>
+__global__ __launch_bounds__(W::THREADS, W::WPE) void bwd_gemm_kernel(BwdGemmArgs p) {
+  constexpr int BM = W::BM, BN = W::BN, FM = W::FM, FN = W::FN, ALD = W::ALD, BLD = W::BLD;
+  constexpr int THREADS = W::THREADS, STAGE = W::STAGE, A_BYTES = W::A_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[W::SLOTS * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / BG_WAVES_N, wn = wave % BG_WAVES_N;
+  const int wm = wave / W::WAVES_N, wn = wave % W::WAVES_N;
   const int kg = lane >> 5;
 
   // ---- which tile: the tiles cost their expert's row count, so the largest experts go
@@ -94,77 +107,75 @@ __global__ __launch_bounds__(BG_THREADS, 1) void bwd_gemm_kernel(BwdGemmArgs p) 
     n_tile = (lin % gsize) / gm;
     // the expert of rank m_tile / m_tiles in decreasing padded row count
     e = p.poff[p.E + 1 + m_tile / p.m_tiles];
-    m0 = (m_tile % p.m_tiles) * BG_BM;
-    rows = min(BG_BM, p.M - m0);
+    m0 = (m_tile % p.m_tiles) * BM;
+    rows = min(BM, p.M - m0);
   }
   const int K = p.poff[e + 1] - p.poff[e];
-  const int n0 = n_tile * BG_BN;
+  const int n0 = n_tile * BN;
   const int nk = K / BG_BK;
 
   // ---- this thread's copy rows: chunk c of tile rows (tid / CPR) + (THREADS / CPR) j
   const int cch = tid % BG_CPR;
-  const uint16_t* arow[BG_ALD];
-  const uint16_t* brow[BG_BLD];
-  int ar[BG_ALD], br[BG_BLD];
+  const uint16_t* arow[ALD];
+  const uint16_t* brow[BLD];
+  int ar[ALD], br[BLD];
 #pragma unroll
-  for (int j = 0; j < BG_ALD; ++j) {
-    const int r = tid / BG_CPR + (BG_THREADS / BG_CPR) * j;
+  for (int j = 0; j < ALD; ++j) {
+    const int r = tid / BG_CPR + (THREADS / BG_CPR) * j;
     ar[j] = r;
     arow[j] = p.a + (int64_t)min(m0 + r, p.M - 1) * p.lda + p.poff[e] + cch * 8;
   }
 #pragma unroll
-  for (int j = 0; j < BG_BLD; ++j) {
-    const int r = tid / BG_CPR + (BG_THREADS / BG_CPR) * j;
+  for (int j = 0; j < BLD; ++j) {
+    const int r = tid / BG_CPR + (THREADS / BG_CPR) * j;
     br[j] = r;
     brow[j] = p.b + (int64_t)min(n0 + r, p.N - 1) * p.ldb + p.poff[e] + cch * 8;
   }
 
-  f32x16 acc[BG_FM][BG_FN];
+  f32x16 acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < BG_FM; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < BG_FN; ++j)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
   // Stage kt of this thread's rows into register set R, and register set R into LDS slot s
   // (macros, not lambdas: a call that is not inlined would leave the staging arrays in
-  // memory).  Two register sets: the loads of stage kt + 2 are issued before stage kt is
-  // multiplied and stored to LDS only after stage kt + 1 is, so two stages of matrix work
-  // cover their latency.
-  u32x4 ra0[BG_ALD], rb0[BG_BLD], ra1[BG_ALD], rb1[BG_BLD];
+  // memory).
+  u32x4 ra0[ALD], rb0[BLD];
 #define BW_GLOAD(kt, RA, RB)                                                                     \
   do {                                                                                           \
     const int ko_ = (kt) * BG_BK;                                                                \
-    _Pragma("unroll") for (int j = 0; j < BG_ALD; ++j) RA[j] = *(const u32x4*)(arow[j] + ko_);   \
-    _Pragma("unroll") for (int j = 0; j < BG_BLD; ++j) RB[j] = *(const u32x4*)(brow[j] + ko_);   \
+    _Pragma("unroll") for (int j = 0; j < ALD; ++j) RA[j] = *(const u32x4*)(arow[j] + ko_);      \
+    _Pragma("unroll") for (int j = 0; j < BLD; ++j) RB[j] = *(const u32x4*)(brow[j] + ko_);      \
   } while (0)
 #define BW_LSTORE(slot, RA, RB)                                                                  \
   do {                                                                                           \
-    uint8_t* s_ = smem + (slot) * BG_STAGE;                                                      \
-    _Pragma("unroll") for (int j = 0; j < BG_ALD; ++j)                                           \
+    uint8_t* s_ = smem + (slot) * STAGE;                                                         \
+    _Pragma("unroll") for (int j = 0; j < ALD; ++j)                                              \
       *(u32x4*)(s_ + swz<BG_CPR>(ar[j], cch)) = RA[j];                                           \
-    _Pragma("unroll") for (int j = 0; j < BG_BLD; ++j)                                           \
-      *(u32x4*)(s_ + BG_A_BYTES + swz<BG_CPR>(br[j], cch)) = RB[j];                              \
+    _Pragma("unroll") for (int j = 0; j < BLD; ++j)                                              \
+      *(u32x4*)(s_ + A_BYTES + swz<BG_CPR>(br[j], cch)) = RB[j];                                 \
   } while (0)
-  // a wave whose 64 rows are all padding skips its matrix instructions
-  const bool active = wm * BG_WTM < rows;
-  const int arow0 = wm * BG_WTM + (lane & 31);
-  const int brow0 = wn * BG_WTN + (lane & 31);
+  // a wave whose rows are all padding skips its matrix instructions
+  const bool active = wm * W::WTM < rows;
+  const int arow0 = wm * W::WTM + (lane & 31);
+  const int brow0 = wn * W::WTN + (lane & 31);
 #define BW_COMPUTE(slot)                                                                         \
   do {                                                                                           \
     if (active) {                                                                                \
-      const uint8_t* sa = smem + (slot) * BG_STAGE;                                              \
-      const uint8_t* sb = sa + BG_A_BYTES;                                                       \
+      const uint8_t* sa = smem + (slot) * STAGE;                                                 \
+      const uint8_t* sb = sa + A_BYTES;                                                          \
       _Pragma("unroll") for (int ks = 0; ks < BG_BK / 16; ++ks) {                                \
         const int cc = kg * (BG_BK / 16) + ks;                                                   \
-        bf16x8 fa[BG_FM], fb[BG_FN];                                                             \
-        _Pragma("unroll") for (int i = 0; i < BG_FM; ++i)                                        \
+        bf16x8 fa[FM], fb[FN];                                                                   \
+        _Pragma("unroll") for (int i = 0; i < FM; ++i)                                           \
           fa[i] = *(const bf16x8*)(sa + swz<BG_CPR>(arow0 + 32 * i, cc));                        \
-        _Pragma("unroll") for (int j = 0; j < BG_FN; ++j)                                        \
+        _Pragma("unroll") for (int j = 0; j < FN; ++j)                                           \
           fb[j] = *(const bf16x8*)(sb + swz<BG_CPR>(brow0 + 32 * j, cc));                        \
-        _Pragma("unroll") for (int i = 0; i < BG_FM; ++i)                                        \
-        _Pragma("unroll") for (int j = 0; j < BG_FN; ++j)                                        \
+        _Pragma("unroll") for (int i = 0; i < FM; ++i)                                           \
+        _Pragma("unroll") for (int j = 0; j < FN; ++j)                                           \
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0); \
       }                                                                                          \
     }                                                                                            \
@@ -172,21 +183,39 @@ __global__ __launch_bounds__(BG_THREADS, 1) void bwd_gemm_kernel(BwdGemmArgs p) 
   // The loads are unconditional (past the last stage they fetch the last stage again): with
   // loads under a condition the compiler's wait counts assume the newest loads may be the
   // ones a store needs, and the stores then wait for everything in flight.
-  if (nk > 0) {
-    BW_GLOAD(0, ra0, rb0);
-    BW_LSTORE(0, ra0, rb0);
-    BW_GLOAD(min(1, nk - 1), ra1, rb1);
-    for (int kt = 0; kt < nk; kt += 2) {
-      // even stage kt in slot 0; stage kt + 1 in flight in set 1
-      __syncthreads();
-      BW_GLOAD(min(kt + 2, nk - 1), ra0, rb0);
-      BW_COMPUTE(0);
-      BW_LSTORE(1, ra1, rb1);
-      // odd stage kt + 1 in slot 1; stage kt + 2 in flight in set 0
-      __syncthreads();
-      BW_GLOAD(min(kt + 3, nk - 1), ra1, rb1);
-      if (kt + 1 < nk) BW_COMPUTE(1);
+  if constexpr (W::SLOTS == 2) {
+    // two register sets: the loads of stage kt + 2 are issued before stage kt is multiplied
+    // and stored to LDS only after stage kt + 1 is, so two stages of matrix work cover their
+    // latency
+    u32x4 ra1[ALD], rb1[BLD];
+    if (nk > 0) {
+      BW_GLOAD(0, ra0, rb0);
       BW_LSTORE(0, ra0, rb0);
+      BW_GLOAD(min(1, nk - 1), ra1, rb1);
+      for (int kt = 0; kt < nk; kt += 2) {
+        // even stage kt in slot 0; stage kt + 1 in flight in set 1
+        __syncthreads();
+        BW_GLOAD(min(kt + 2, nk - 1), ra0, rb0);
+        BW_COMPUTE(0);
+        BW_LSTORE(1, ra1, rb1);
+        // odd stage kt + 1 in slot 1; stage kt + 2 in flight in set 0
+        __syncthreads();
+        BW_GLOAD(min(kt + 3, nk - 1), ra1, rb1);
+        if (kt + 1 < nk) BW_COMPUTE(1);
+        BW_LSTORE(0, ra0, rb0);
+      }
+    }
+  } else {
+    // one LDS stage: stage kt + 1 loads into the register set while stage kt is multiplied
+    if (nk > 0) {
+      BW_GLOAD(0, ra0, rb0);
+      for (int kt = 0; kt < nk; ++kt) {
+        __syncthreads();                    // the previous stage's reads are done
+        BW_LSTORE(0, ra0, rb0);
+        __syncthreads();
+        BW_GLOAD(min(kt + 1, nk - 1), ra0, rb0);
+        BW_COMPUTE(0);
+      }
     }
   }
 #undef BW_GLOAD
@@ -196,23 +225,30 @@ __global__ __launch_bounds__(BG_THREADS, 1) void bwd_gemm_kernel(BwdGemmArgs p) 
   // ---- epilogue: row rr of the tile for register q of fragment i, column for fragment j
   float* const dst = p.c + (int64_t)e * p.M * p.N;
 #pragma unroll
-  for (int j = 0; j < BG_FN; ++j) {
-    const int n = n0 + wn * BG_WTN + 32 * j + (lane & 31);
+  for (int j = 0; j < FN; ++j) {
+    const int n = n0 + wn * W::WTN + 32 * j + (lane & 31);
     if (n >= p.N) continue;
 #pragma unroll
-    for (int i = 0; i < BG_FM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const int rr = wm * BG_WTM + 32 * i + 8 * (q >> 2) + 4 * kg + (q & 3);
+        const int rr = wm * W::WTM + 32 * i + 8 * (q >> 2) + 4 * kg + (q & 3);
         if (rr < rows) dst[(int64_t)(m0 + rr) * p.N + n] = acc[i][j][q];
       }
   }
 }
 
-hipError_t launch_wgrad(BwdGemmArgs g, hipStream_t st) {
+// dst[e] = A_e B_e^T for every expert: M x N outputs per expert; `small` picks the few-rows tile
+template <class W>
+static hipError_t launch_wgrad_t(BwdGemmArgs g, hipStream_t st) {
+  g.m_tiles = (g.M + W::BM - 1) / W::BM;
+  g.n_tiles = (g.N + W::BN - 1) / W::BN;
   const int64_t tiles = (int64_t)g.E * g.m_tiles * g.n_tiles;
-  hipLaunchKernelGGL(bwd_gemm_kernel, dim3((unsigned)tiles), dim3(BG_THREADS), 0, st, g);
+  hipLaunchKernelGGL(bwd_gemm_kernel<W>, dim3((unsigned)tiles), dim3(W::THREADS), 0, st, g);
   return hipGetLastError();
+}
+hipError_t launch_wgrad(const BwdGemmArgs& g, bool small, hipStream_t st) {
+  return small ? launch_wgrad_t<WTileSmall>(g, st) : launch_wgrad_t<WTileLarge>(g, st);
 }
 
 // ------------------------------------------------------------------------------ routing helpers
@@ -633,14 +669,14 @@ hipError_t launch_backward(const BwdArgs& b, hipStream_t st) {
                      st, (const void*)b.du, G, G, b.padmap, b.perm, b.gates, k, A, ldt, b.duT);
   BW_CHECK(hipGetLastError());
   // 10. weight gradients per expert: dW2[e] = dz^T h, dW1[e] = du^T x
+  // (few rows per expert, the forward's streaming regime: tiles that are mostly stores)
+  const bool small = cfg == 0;
   BwdGemmArgs w{};
   w.poff = b.poff; w.E = E;
-  w.a = b.dzT; w.lda = ldt; w.b = b.hT; w.ldb = ldt; w.M = D; w.N = F;
-  w.m_tiles = (D + BG_BM - 1) / BG_BM; w.n_tiles = (F + BG_BN - 1) / BG_BN; w.c = b.dw2;
-  BW_CHECK(launch_wgrad(w, st));
-  w.a = b.duT; w.b = b.xT; w.M = G; w.N = D;
-  w.m_tiles = (G + BG_BM - 1) / BG_BM; w.n_tiles = (D + BG_BN - 1) / BG_BN; w.c = b.dw1;
-  BW_CHECK(launch_wgrad(w, st));
+  w.a = b.dzT; w.lda = ldt; w.b = b.hT; w.ldb = ldt; w.M = D; w.N = F; w.c = b.dw2;
+  BW_CHECK(launch_wgrad(w, small, st));
+  w.a = b.duT; w.b = b.xT; w.M = G; w.N = D; w.c = b.dw1;
+  BW_CHECK(launch_wgrad(w, small, st));
   // 11. router: dg and the softmax backward, then the per-expert sums and dx
   hipLaunchKernelGGL(router_bwd_kernel, dim3(blocks_for(T, 4)), dim3(256), 0, st, b.dgsum, b.dout, b.b2, b.idx,
                      b.gates, T, D, E, k, b.dl);
