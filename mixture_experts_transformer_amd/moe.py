@@ -235,10 +235,12 @@ def experts(x, w1, b1, w2, b2, gates, offsets, perm, k: int, fmt: str = "bf16",
     return out
 
 
-def backward(x, router_w, w1, b1, w2, b2, routing: dict, dout, k: int, fmt: str = "bf16") -> dict:
+def backward(x, router_w, w1, b1, w2, b2, routing: dict, dout, k: int, fmt: str = "bf16",
+             out: Optional[dict] = None) -> dict:
     """Gradients of the block (``moe_backward``) for the routing of a forward (``route``'s dict:
     idx, gates, offsets, perm) and the output gradient ``dout`` (fp32 [T, D]).  Returns fp32
-    dx, dwr, dbr, dw1, db1, dw2, db2 (each the shape of its input)."""
+    dx, dwr, dbr, dw1, db1, dw2, db2 (each the shape of its input), written into ``out``'s
+    tensors when given (e.g. for a captured graph)."""
     T, D = x.shape
     E = router_w.shape[0]
     F = b1.shape[-1] // 2
@@ -251,8 +253,16 @@ def backward(x, router_w, w1, b1, w2, b2, routing: dict, dout, k: int, fmt: str 
         _dev(routing[n], n, 4)
     dev = x.device
     f32 = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)
-    g = {"dx": f32(T, D), "dwr": f32(E, D), "dbr": f32(E), "dw1": f32(E, 2 * F, D), "db1": f32(E, 2 * F),
-         "dw2": f32(E, D, F), "db2": f32(E, D)}
+    shapes = {"dx": (T, D), "dwr": (E, D), "dbr": (E,), "dw1": (E, 2 * F, D), "db1": (E, 2 * F),
+              "dw2": (E, D, F), "db2": (E, D)}
+    if out is None:
+        g = {n: f32(*sh) for n, sh in shapes.items()}
+    else:
+        g = out
+        for n, sh in shapes.items():
+            _dev(g[n], n, 4)
+            if tuple(g[n].shape) != sh:
+                raise ValueError(f"out[{n!r}] must be {list(sh)}")
     _bind_stream(dev)
     _check(lib().moe_backward(_ptr(x), _ptr(router_w), _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2),
                               _ptr(routing["idx"]), _ptr(routing["gates"]), _ptr(routing["offsets"]),

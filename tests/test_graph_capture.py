@@ -103,3 +103,49 @@ def test_graph_survives_a_larger_eager_call():
     del g
     torch.cuda.synchronize()
     moe.release()
+
+
+@pytest.mark.parametrize("T", [64, 512])       # few rows per expert (streaming tiles) and many
+def test_backward_graph_replays_match_eager(T):
+    """moe_backward captured into a graph after an eager call of the same shape: every replay,
+    with eager backward calls of other inputs between the replays, equals the eager gradients
+    bit for bit (the backward clears what it accumulates with kernels, not memsets)."""
+    cfg = get_config("C2", name=f"gbwd{T}", T=T, E=4, D=256, F=256, seed=7000 + T)
+    other = get_config("C2", name=f"gbwdb{T}", T=T, E=4, D=256, F=256, seed=7100 + T)
+    d, d2 = upload(make_inputs(cfg)), upload(make_inputs(other))
+    note(f"backward graph capture T={T} E=4 D=F=256")
+    gen = torch.Generator().manual_seed(7200 + T)
+    dout = torch.randn(T, 256, generator=gen).to(DEV)
+    dout2 = torch.randn(T, 256, generator=gen).to(DEV)
+    r = moe.route(d["x"], d["router_w"], d["router_b"], cfg.k, want_logits=False)
+    r2 = moe.route(d2["x"], d2["router_w"], d2["router_b"], cfg.k, want_logits=False)
+
+    def bwd(dd, rr, g, out=None):
+        return moe.backward(dd["x"], dd["router_w"], dd["w1"], dd["b1"], dd["w2"], dd["b2"], rr, g, cfg.k, out=out)
+
+    ref = {n: t.clone() for n, t in bwd(d, r, dout).items()}
+    ref2 = {n: t.clone() for n, t in bwd(d2, r2, dout2).items()}
+    torch.cuda.synchronize()
+    out = {n: torch.empty_like(t) for n, t in ref.items()}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        bwd(d, r, dout, out)                     # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        bwd(d, r, dout, out)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in out.values():
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for n in ref:
+            assert torch.equal(out[n], ref[n]), f"replay {rep}: {n} differs from the eager backward"
+        mid = bwd(d2, r2, dout2)                 # eager work on the same workspace in between
+        torch.cuda.synchronize()
+        for n in ref2:
+            assert torch.equal(mid[n], ref2[n]), n
+    del g
