@@ -331,6 +331,52 @@ def target_summary(res):
     return out
 
 
+def mfma_calibration(iters=20000):
+    """Sustained v_mfma_f32_32x32x16_bf16 rate of this GPU on operands held in registers (the
+    calibration kernel of mixture_experts_transformer_amd/calib): random bf16 operands N(0, 1)
+    and constant ones (all 1.0), at one and two waves per SIMD on every CU.  Returns one dict
+    per case: TFLOP/s over the launch and its fraction of the 2.5 PF bf16 peak (the clock the
+    chip holds under each load, and the matrix cores' busy fraction, come from rocprofv3's
+    GRBM_GUI_ACTIVE and SQ_VALU_MFMA_BUSY_CYCLES on the same command)."""
+    import ctypes
+    import torch
+    from mixture_experts_transformer_amd import build as _b
+    lib = ctypes.CDLL(_b.CALIB_LIB)
+    lib.moe_calib_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    per_iter = lib.moe_calib_products_per_iteration()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = []
+    for operands in ("random", "constant"):
+        for wps in (1, 2):
+            blocks = cus * wps
+            waves = 4 * blocks
+            n = waves * 6 * 64 * 8
+            if operands == "random":
+                src = torch.randn(n, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16).cuda()
+            else:
+                src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+            sink = torch.empty(waves * 64, dtype=torch.float32, device="cuda")
+            cyc = torch.empty(waves, dtype=torch.int64, device="cuda")
+            st = torch.cuda.current_stream().cuda_stream
+            run = lambda: lib.moe_calib_mfma(src.data_ptr(), blocks, iters, sink.data_ptr(), cyc.data_ptr(), st)
+            if run() != 0:
+                raise RuntimeError("calibration kernel launch failed")
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(3):
+                run()
+            e1.record()
+            torch.cuda.synchronize()
+            sec = e0.elapsed_time(e1) / 3 / 1e3
+            flops = waves * iters * per_iter * 2 * 32 * 32 * 16
+            out.append({"calibration": "mfma_bf16_32x32x16", "operands": operands, "waves_per_simd": wps,
+                        "tflops": round(flops / sec / 1e12, 1), "frac_of_peak": round(flops / sec / 2.5e15, 4),
+                        "ms": round(sec * 1e3, 3)})
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -344,6 +390,8 @@ def main():
     ap.add_argument("--backward", action="store_true", help="time only moe_backward on --workload (bf16)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device copies of MIB MiB (reference for the HBM byte counters)")
+    ap.add_argument("--mfma-calibration", action="store_true",
+                    help="only measure the sustained bf16 matrix-core rate (random and constant operands)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the MoE block is built and timed on a single MI355X; "
@@ -361,6 +409,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
+        return
+    if args.mfma_calibration:
+        for line in mfma_calibration():
+            print(json.dumps(line), flush=True)
         return
     if args.backward:
         print(json.dumps(bench_backward(args.workload, args.steps, args.warmup)), flush=True)

@@ -19,6 +19,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
 SOURCES = ["route.hip", "gemm.hip", "backward.hip", "moe_api.hip"]
+# bench.py's matrix-core rate calibration (not part of the MoE block), its own small library
+CALIB_SRC = os.path.join(HERE, "calib", "mfma_rate.hip")
+CALIB_LIB = os.path.join(HERE, "calib", "libmoe_calib.so")
 ARCH = "gfx950"
 
 
@@ -90,6 +93,12 @@ def build(verbose: bool = False) -> str:
         if verbose:
             print(f"M0 check {s}: {n} copies, no other use", flush=True)
     os.replace(tmp, LIB)
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-o", CALIB_LIB + ".tmp", CALIB_SRC]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc (calibration kernel) failed ({r.returncode}):\n{r.stderr[-4000:]}")
+    os.replace(CALIB_LIB + ".tmp", CALIB_LIB)
     return LIB
 
 
