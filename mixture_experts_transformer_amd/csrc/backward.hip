@@ -35,14 +35,12 @@ constexpr float BW_LIMIT = 7.0f;
 constexpr float BW_NEG_ALPHA_LOG2E = -BW_ALPHA * 1.4426950408889634f;
 
 // ------------------------------------------------------------------------------ GEMM tile
-// Weight-gradient tiles, K in steps of 64 (whole 128-byte row segments per stage), staged to
-// LDS through registers.  Two shapes:
-//  * 256 x 256 outputs, 8 waves in a 2 x 4 grid of 128 x 64, two LDS stages and two register
-//    sets (loads two stages ahead): experts with many rows, matrix-core bound;
-//  * 256 x 128 outputs, 8 waves in a 4 x 2 grid of 64 x 64, one LDS stage and one register
-//    set, two workgroups per CU: experts with few rows (K of 64 or 128), where a tile is one
-//    or two matrix steps and then 128 KB of fp32 stores, so a second workgroup's loads and
-//    matrix work overlap the first one's stores.
+// Weight-gradient tiles for experts with few rows (K of 64 or 128), where a tile is one or two
+// matrix steps and then 128 KB of fp32 stores: 256 x 128 outputs, 8 waves in a 4 x 2 grid of
+// 64 x 64, K in steps of 64 (whole 128-byte row segments) staged to one LDS stage through
+// registers, two workgroups per CU so one tile's loads and matrix work overlap another's
+// stores.  Experts with many rows take the grouped GEMM kernel's weight-gradient mode
+// (launch_wgrad_tiles: 256 x 256 tiles fed by direct-to-LDS copies).
 constexpr int BG_BK = 64, BG_CPR = BG_BK / 8;
 template <int BM_, int BN_, int WM_, int WN_, int SLOTS_, int WPE_>
 struct WTile {
@@ -54,9 +52,8 @@ struct WTile {
   static constexpr int ALD = BM * BG_CPR / THREADS;   // 16-byte A chunks per thread and stage
   static constexpr int BLD = BN * BG_CPR / THREADS;   // B chunks
   static_assert(ALD * THREADS == BM * BG_CPR && BLD * THREADS == BN * BG_CPR, "load split");
-  static_assert(SLOTS == 1 || SLOTS == 2, "LDS stages");
+  static_assert(SLOTS == 1, "one LDS stage");
 };
-using WTileLarge = WTile<256, 256, 2, 4, 2, 1>;
 using WTileSmall = WTile<256, 128, 4, 2, 1, 4>;
 
 struct BwdGemmArgs {
@@ -183,39 +180,15 @@ __global__ __launch_bounds__(W::THREADS, W::WPE) void bwd_gemm_kernel(BwdGemmArg
   // The loads are unconditional (past the last stage they fetch the last stage again): with
   // loads under a condition the compiler's wait counts assume the newest loads may be the
   // ones a store needs, and the stores then wait for everything in flight.
-  if constexpr (W::SLOTS == 2) {
-    // two register sets: the loads of stage kt + 2 are issued before stage kt is multiplied
-    // and stored to LDS only after stage kt + 1 is, so two stages of matrix work cover their
-    // latency
-    u32x4 ra1[ALD], rb1[BLD];
-    if (nk > 0) {
-      BW_GLOAD(0, ra0, rb0);
+  // one LDS stage: stage kt + 1 loads into the register set while stage kt is multiplied
+  if (nk > 0) {
+    BW_GLOAD(0, ra0, rb0);
+    for (int kt = 0; kt < nk; ++kt) {
+      __syncthreads();                      // the previous stage's reads are done
       BW_LSTORE(0, ra0, rb0);
-      BW_GLOAD(min(1, nk - 1), ra1, rb1);
-      for (int kt = 0; kt < nk; kt += 2) {
-        // even stage kt in slot 0; stage kt + 1 in flight in set 1
-        __syncthreads();
-        BW_GLOAD(min(kt + 2, nk - 1), ra0, rb0);
-        BW_COMPUTE(0);
-        BW_LSTORE(1, ra1, rb1);
-        // odd stage kt + 1 in slot 1; stage kt + 2 in flight in set 0
-        __syncthreads();
-        BW_GLOAD(min(kt + 3, nk - 1), ra1, rb1);
-        if (kt + 1 < nk) BW_COMPUTE(1);
-        BW_LSTORE(0, ra0, rb0);
-      }
-    }
-  } else {
-    // one LDS stage: stage kt + 1 loads into the register set while stage kt is multiplied
-    if (nk > 0) {
-      BW_GLOAD(0, ra0, rb0);
-      for (int kt = 0; kt < nk; ++kt) {
-        __syncthreads();                    // the previous stage's reads are done
-        BW_LSTORE(0, ra0, rb0);
-        __syncthreads();
-        BW_GLOAD(min(kt + 1, nk - 1), ra0, rb0);
-        BW_COMPUTE(0);
-      }
+      __syncthreads();
+      BW_GLOAD(min(kt + 1, nk - 1), ra0, rb0);
+      BW_COMPUTE(0);
     }
   }
 #undef BW_GLOAD
@@ -238,7 +211,9 @@ __global__ __launch_bounds__(W::THREADS, W::WPE) void bwd_gemm_kernel(BwdGemmArg
   }
 }
 
-// dst[e] = A_e B_e^T for every expert: M x N outputs per expert; `small` picks the few-rows tile
+// dst[e] = A_e B_e^T for every expert: M x N outputs per expert.  Few rows per expert: the
+// single-stage tile above; many: the forward's grouped GEMM kernel in its weight-gradient
+// mode (direct-to-LDS copies, 256 x 256 tiles)
 template <class W>
 static hipError_t launch_wgrad_t(BwdGemmArgs g, hipStream_t st) {
   g.m_tiles = (g.M + W::BM - 1) / W::BM;
@@ -248,7 +223,8 @@ static hipError_t launch_wgrad_t(BwdGemmArgs g, hipStream_t st) {
   return hipGetLastError();
 }
 hipError_t launch_wgrad(const BwdGemmArgs& g, bool small, hipStream_t st) {
-  return small ? launch_wgrad_t<WTileSmall>(g, st) : launch_wgrad_t<WTileLarge>(g, st);
+  if (small) return launch_wgrad_t<WTileSmall>(g, st);
+  return launch_wgrad_tiles(g.a, g.b, g.lda, g.poff, g.E, g.M, g.N, g.c, st);
 }
 
 // ------------------------------------------------------------------------------ routing helpers

@@ -286,7 +286,9 @@ static __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
   }
 }
 
-// MODE 1: mlp1 (+SwiGLU), MODE 2: mlp2 (+bias, gate).  FMT 0: bf16 weights, 1: MXFP4.
+// MODE 1: mlp1 (+SwiGLU), MODE 2: mlp2 (+bias, gate), MODE 3: the backward's per-expert
+// weight gradients (bf16 operands both K-contiguous, K an expert's padded rows, fp32 out).
+// FMT 0: bf16 weights, 1: MXFP4.
 //
 // Matrix-core mapping: v_mfma_f32_32x32x16_bf16 (measured on gfx950 at about twice the
 // sustained rate of the 16x16x32 form).  In MFMA step ks of a stage, lane l feeds row
@@ -400,8 +402,9 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   constexpr int EP_S = (MODE == 1) ? (MX ? 4 * EP_P + 16 : 2 * EP_P + 8) : 4 * C::WTN + 32;
   constexpr int EP_REG = 32 * EP_S * ((MODE == 1 && DEC) ? 2 : 1);
   static_assert(!(MX && MODE == 1) || EP_P % 32 == 0, "whole 32-element blocks of h per wave and row");
+  static_assert(MODE != 3 || (FMT == 0 && !C::STREAM), "weight gradients: bf16 matrix-core tiles");
   static_assert(NW * EP_REG <= SMEM, "epilogue slices exceed the operand ring");
-  constexpr int ROWTAB = (MODE == 2) ? BM * 8 : 0;          // mlp2: assignment and gate per tile row
+  constexpr int ROWTAB = (MODE >= 2) ? BM * 8 : 0;          // mlp2: assignment and gate per tile row
   __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM + ROWTAB];
   uint8_t* const codes_lds = smem + NS * STAGE;
   uint8_t* const ascale_lds = codes_lds + CODE_BYTES;       // scaled-MFMA engine: A scales
@@ -428,9 +431,31 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   // column tiles fastest, so workgroups launched together read neighbouring rows of one
   // expert's weights.  Large tiles: in groups of GM row tiles, so the workgroups sharing an
   // XCD's L2 share operand tiles.
+  int m_tile, n_tile;
+  int e, row0, cnt;
+  if constexpr (MODE == 3) {
+    // weight gradients: per expert (in the order of decreasing K that offsets[E + 1 ..]
+    // lists) max_m_tiles row tiles of the M output rows by n_tiles column tiles, in block
+    // order, so the largest experts' tiles go first and spread over every XCD; in groups of
+    // GM row tiles so neighbouring workgroups share operand rows
+    const int mt = p.max_m_tiles;
+    const int total = p.E * mt * p.n_tiles;
+    const int lin = blockIdx.x;
+    if (lin >= total) return;
+    constexpr int GM = 4;
+    const int gsize = GM * p.n_tiles;
+    const int g = lin / gsize;
+    const int first_m = g * GM;
+    const int gm = min(p.E * mt - first_m, GM);
+    m_tile = first_m + (lin % gsize) % gm;
+    n_tile = (lin % gsize) / gm;
+    e = p.offsets[p.E + 1 + m_tile / mt];
+    if ((unsigned)e >= (unsigned)p.E) return;
+    row0 = (m_tile % mt) * BM;
+    cnt = p.A;
+  } else {
   const TileScan ts = tile_scan<BM>(p.offsets, p.E);
   const int total = ts.total * p.n_tiles;
-  int m_tile, n_tile;
   if (C::STREAM) {
     const int share = (total + 7) >> 3;
     const int xl = blockIdx.x >> 3;
@@ -452,14 +477,17 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
     n_tile = (lin % gsize) / gm;
   }
 
-  int e, row0, cnt;
   if (!tile_lookup<BM>(ts, p.offsets, m_tile, e, row0, cnt)) return;
-  const int gbase = p.offsets[e] + row0;    // routed row of tile row 0
+  }
+  // routed row of tile row 0 (weight gradients: output row)
+  const int gbase = MODE == 3 ? row0 : p.offsets[e] + row0;
   const int rows = min(BM, cnt - row0);
   // a routing passed in by the caller is trusted only this far: rows stay inside [0, A)
   if (gbase < 0 || rows <= 0 || gbase + rows > p.A) return;
-  const int K = p.K;
-  const int nk = K / BK;
+  const int K = p.K;                        // weight gradients: the operands' row stride
+  // weight gradients: K is the expert's padded row count, its columns from offsets[e]
+  const int kcol0 = MODE == 3 ? p.offsets[e] : 0;
+  const int nk = MODE == 3 ? (p.offsets[e + 1] - kcol0) / BK : K / BK;
   // mlp2: thread r < rows fetches tile row r's assignment now and its gate in the first K
   // step, for the epilogue (which then needs no dependent global loads)
   int rt_a = -1;
@@ -467,6 +495,10 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   if (MODE == 2 && tid < rows) {
     const int a = p.perm[gbase + tid];
     rt_a = ((unsigned)a < (unsigned)p.A) ? a : -1;
+  }
+  if (MODE == 3 && tid < rows) {            // output row of expert e's gradient, unit scale
+    rt_a = e * p.A + gbase + tid;
+    rt_g = 1.f;
   }
 
   // A row behind tile row r (clamped into the group): mlp1 gathers token rows, mlp2 reads
@@ -485,6 +517,8 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   size_t s_e_off = 0;                       // byte offset of expert e's scales in p.w
   if (BT) {
     w_e = p.w + (size_t)e * p.bt_rows * p.N * 2;
+  } else if (MODE == 3) {
+    w_e = p.w + (size_t)kcol0 * 2;
   } else if (WF == 0) {
     w_e = p.w + (size_t)e * p.N * K * 2;
   } else {
@@ -610,7 +644,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
         const uint32_t d_ = smem_l + (slot) * STAGE + gdst[j];                                   \
         if (i_ < NA) {                                                                           \
           const void* ab_ = MX ? (const void*)p.a8                                               \
-                                : (i_ < A_CPC ? (const void*)p.a : (const void*)p.a_lo);          \
+                                : (i_ < A_CPC ? (const void*)(p.a + kcol0) : (const void*)p.a_lo); \
           dma16((const uint8_t*)ab_ + (size_t)(kt) * A_ROWB, goff[j], d_);                       \
         } else {                                                                                 \
           const uint8_t* ws_ = BT ? w_e + (size_t)((kt) % bt_kt) * 64 * p.N * 2                  \
@@ -815,7 +849,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
       }                                                                                          \
     }                                                                                            \
     }                                                                                            \
-    MOE_MMA((KS - 1) & 1, FA, ACC);                                                              \
+    if (nk > 0) MOE_MMA((KS - 1) & 1, FA, ACC);                                                  \
   } while (0)
   // scaled-MFMA engine: the A pieces of row block i_ (this lane's row, its two chunks per
   // piece) from the stage at sa
@@ -968,7 +1002,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
 
   // ---- epilogue.  Output register q of fragment (i, j) is row 8 (q >> 2) + 4 kg + (q & 3)
   // of the fragment's 32 rows, column lane & 31.
-  if (MODE == 2 && tid < BM) {
+  if (MODE >= 2 && tid < BM) {
     tab_a[tid] = rt_a;
     tab_g[tid] = rt_g;
   }
@@ -978,7 +1012,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   wait_lgkmcnt0();
   barrier_nofence();                        // every wave is done with the operand ring
   uint8_t* const ep = smem + wave * EP_REG;
-  const uint16_t* bias = p.bias + (size_t)e * p.N;
+  const uint16_t* bias = MODE == 3 ? nullptr : p.bias + (size_t)e * p.N;
   if (MODE == 1) {
     // Lane n < 16 of a fragment holds the gate column of pair 16 j + n, lane n + 16 the
     // linear column of the same pair.  v_permlane16_swap of registers q and q + 8 exchanges
@@ -1104,7 +1138,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int o = o_wave + j * 32 + (lane & 31);
-      bo[j] = (o < p.N) ? bf16_to_f32(bias[o]) : 0.f;
+      bo[j] = (MODE == 2 && o < p.N) ? bf16_to_f32(bias[o]) : 0.f;
     }
     constexpr int CH = C::WTN / 4;                         // 16-byte chunks per slice row
 #pragma unroll
@@ -1191,6 +1225,21 @@ bool mx_engine(int fmt, int cfg) { return fmt == 1 && cfg == 1; }
 // Kernel format of a weight format (0 bf16, 1 MXFP4, 2 MXFP8) and tile configuration:
 // 0 bf16, 1 MXFP4 decoded, 2 MXFP4 on the scaled engine, 3 MXFP8 decoded.
 static int kernel_format(int fmt, int cfg) { return fmt == 2 ? 3 : (mx_engine(fmt, cfg) ? 2 : fmt); }
+
+// Weight gradients C[e] = A_e B_e^T on the matrix-core tiles: A and B bf16 [M][ld] and [N][ld]
+// (K contiguous), expert e's K the columns [poff[e], poff[e + 1]) (multiples of 64, zero
+// past its rows), poff[E + 1 + r] the expert of rank r by decreasing K; C fp32 [E][M][N].
+hipError_t launch_wgrad_tiles(const uint16_t* a, const uint16_t* b, int ld, const int32_t* poff, int E, int M,
+                              int N, float* c, hipStream_t st) {
+  using C = LargeTile<3, 0>;
+  GemmArgs g{};
+  g.a = a; g.w = (const uint8_t*)b; g.K = ld; g.offsets = poff; g.E = E; g.A = M; g.N = N; g.y = c;
+  g.max_m_tiles = (M + C::BM - 1) / C::BM;
+  g.n_tiles = (N + C::BN - 1) / C::BN;
+  const int64_t total = (int64_t)E * g.max_m_tiles * g.n_tiles;
+  hipLaunchKernelGGL((grouped_gemm_kernel<3, 0, C>), dim3((unsigned)total), dim3(C::THREADS), 0, st, g);
+  return hipGetLastError();
+}
 
 hipError_t launch_mlp1(const ExpertArgs& a, int cfg, hipStream_t st) {
   GemmArgs g{};

@@ -540,6 +540,10 @@ int moe_backward(const void* x, const void* router_w, const void* w1, const void
   // expert's weights (W1: 4 D F bytes) with 32-bit byte offsets; kept with a factor 4 margin
   if (T * k * 2 * (D > F ? D : F) >= ((int64_t)1 << 30) || 4 * D * F >= ((int64_t)1 << 30))
     return fail(MOE_EINVAL, "T*k*2*max(D, F) and 4*D*F must each be < 2^30 for the backward");
+  // the weight gradients address rows of the transposed, padded activations ([max(D, 2F)]
+  // rows of T*k + 64 E columns) with 32-bit byte offsets
+  if ((T * k + 64 * E) * 2 * (D > 2 * F ? D : 2 * F) >= ((int64_t)1 << 31))
+    return fail(MOE_EINVAL, "(T*k + 64*E)*2*max(D, 2F) must be < 2^31 for the backward");
   const BwdLayout L = bwd_layout(T, D, E, k, F);
   uint8_t* ws = nullptr;
   CHECK(ensure_workspace(L.total, &ws));

@@ -123,6 +123,10 @@ struct BwdArgs {
 };
 // Columns of the transposed, expert-padded activation layout (a multiple of 64).
 int bwd_padded_cols(int64_t A, int64_t E);
+// Per-expert weight gradients C[e] = A_e B_e^T on the grouped GEMM's matrix-core tiles (see
+// gemm.hip): A bf16 [M][ld], B bf16 [N][ld], expert e's K the columns [poff[e], poff[e+1]).
+hipError_t launch_wgrad_tiles(const uint16_t* a, const uint16_t* b, int ld, const int32_t* poff, int E, int M,
+                              int N, float* c, hipStream_t st);
 // Fixed row chunks of the per-expert sums.
 int bwd_sum_chunks();
 hipError_t launch_backward(const BwdArgs& b, hipStream_t st);
