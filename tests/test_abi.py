@@ -264,6 +264,10 @@ def test_backward_validates():
     assert bw(fmt=2) == MOE_EFMT
     assert bw(fmt=9) == MOE_EFMT
     assert lib.moe_backward(*([P] * 11), 8, 96, 4, 2, 64, 0, *([P] * 7)) == MOE_EINVAL
+    # within the forward's limits and T*k*2*max(D, F) < 2^30, but the weight gradients' padded
+    # activations (T*k + 64 E columns of max(D, 2F) rows) pass 2^31 bytes
+    assert lib.moe_backward(*([P] * 11), 8191, 64, 256, 4, 16384, 0, *([P] * 7)) == MOE_EINVAL
+    assert "64*E" in lib.moe_last_error().decode()
     for which in range(11):
         ptrs = [P] * 11
         ptrs[which] = None
