@@ -430,6 +430,10 @@ def main():
         for name in TARGETS:
             res["targets"][name] = target_summary(bench_workload(name, args.steps, args.warmup, with_cpu=False))
         res["backward"] = {name: bench_backward(name, args.steps, args.warmup) for name in ("C2", "C3")}
+        # what the matrix cores sustain on this GPU, the reference for the T = 8192 targets'
+        # matrix-core fractions (random operands: the clock drops under load)
+        res["mfma_calibration"] = {f"{c['operands']}_{c['waves_per_simd']}wps_tflops": c["tflops"]
+                                   for c in mfma_calibration()}
     print(json.dumps(res), flush=True)
 
 
