@@ -377,6 +377,37 @@ def mfma_calibration(iters=20000):
     return out
 
 
+def hbm_calibration(gib=2):
+    """Sustained HBM read rate of this GPU: a plain stream of 16-byte loads over a buffer of
+    `gib` GiB (the calibration kernel of mixture_experts_transformer_amd/calib), at one to eight
+    workgroups of 256 lanes per CU; returns the best rate in GB/s and the sweep."""
+    import ctypes
+    import torch
+    from mixture_experts_transformer_amd import build as _b
+    lib = ctypes.CDLL(_b.CALIB_LIB)
+    lib.moe_calib_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    n = gib << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    st = torch.cuda.current_stream().cuda_stream
+    sweep = {}
+    for per_cu in (1, 2, 4, 8):
+        blocks = cus * per_cu
+        sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+        run = lambda: lib.moe_calib_stream(src.data_ptr(), n, blocks, sink.data_ptr(), st)
+        if run() != 0:
+            raise RuntimeError("stream calibration launch failed")
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        sweep[per_cu] = round(n * 5 / (e0.elapsed_time(e1) / 1e3) / 1e9, 1)
+    return {"read_gbs": max(sweep.values()), "by_workgroups_per_cu": sweep}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -392,6 +423,8 @@ def main():
                     help="only run 3 plain device copies of MIB MiB (reference for the HBM byte counters)")
     ap.add_argument("--mfma-calibration", action="store_true",
                     help="only measure the sustained bf16 matrix-core rate (random and constant operands)")
+    ap.add_argument("--hbm-calibration", action="store_true",
+                    help="only measure the sustained HBM read rate (plain 16-byte load stream)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the MoE block is built and timed on a single MI355X; "
@@ -414,6 +447,9 @@ def main():
         for line in mfma_calibration():
             print(json.dumps(line), flush=True)
         return
+    if args.hbm_calibration:
+        print(json.dumps({"calibration": "hbm_read", **hbm_calibration()}), flush=True)
+        return
     if args.backward:
         print(json.dumps(bench_backward(args.workload, args.steps, args.warmup)), flush=True)
         return
@@ -434,6 +470,11 @@ def main():
         # matrix-core fractions (random operands: the clock drops under load)
         res["mfma_calibration"] = {f"{c['operands']}_{c['waves_per_simd']}wps_tflops": c["tflops"]
                                    for c in mfma_calibration()}
+        # and what HBM sustains for a plain read stream: the headline roofline also as a
+        # fraction of that measured rate
+        hbm = hbm_calibration()
+        res["hbm_calibration"] = hbm
+        res["roofline"]["frac_of_measured_peak"] = round(res["roofline"]["achieved"] / hbm["read_gbs"], 4)
     print(json.dumps(res), flush=True)
 
 

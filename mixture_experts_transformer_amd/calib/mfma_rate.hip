@@ -1,4 +1,6 @@
-// Matrix-core rate calibration for bench.py (not part of the MoE block): the sustained rate of
+// Rate calibrations for bench.py (not part of the MoE block).
+//
+// Matrix cores: the sustained rate of
 // v_mfma_f32_32x32x16_bf16 on this GPU when nothing else limits it, for the operand data a
 // GEMM really multiplies (random bf16 values) and for constant operands, at one and two waves
 // per SIMD.  It is the reference against which the grouped GEMM's matrix-core fraction is read.
@@ -67,3 +69,38 @@ extern "C" int moe_calib_mfma(const void* src, int blocks, int iters, float* sin
 }
 
 extern "C" int moe_calib_products_per_iteration(void) { return CAL_NA * CAL_NB; }
+
+// HBM: the sustained read rate of a plain stream of 16-byte loads over a buffer much larger
+// than the caches, every byte read once: grid-stride over 16-byte chunks (chunk i = thread +
+// j * threads, so each wave's load instruction reads 1 KB contiguous), eight independent loads
+// in flight per lane, folded with XOR into one word per thread so nothing is optimised away.
+// (Visiting 1 KB blocks in a scattered order instead measured ≈ 4 % slower.)
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ src, int64_t nchunks,
+                                                          uint32_t* __restrict__ sink) {
+  const int64_t threads = (int64_t)gridDim.x * 256;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  uint4 acc = {0u, 0u, 0u, 0u};
+  int64_t i = t;
+  for (; i + 7 * threads < nchunks; i += 8 * threads) {
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = src[i + u * threads];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      acc.x ^= v[u].x; acc.y ^= v[u].y; acc.z ^= v[u].z; acc.w ^= v[u].w;
+    }
+  }
+  for (; i < nchunks; i += threads) {
+    const uint4 v = src[i];
+    acc.x ^= v.x; acc.y ^= v.y; acc.z ^= v.z; acc.w ^= v.w;
+  }
+  sink[t] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
+
+// src: bytes (a multiple of 16) of device memory; sink: blocks * 256 uint32
+extern "C" int moe_calib_stream(const void* src, int64_t bytes, int blocks, uint32_t* sink, void* stream) {
+  if (blocks <= 0 || bytes < 16 || (bytes & 15) || !src || !sink) return -1;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const uint4*)src,
+                     bytes / 16, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
