@@ -42,9 +42,9 @@ constexpr float BW_NEG_ALPHA_LOG2E = -BW_ALPHA * 1.4426950408889634f;
 // stores.  Experts with many rows take the grouped GEMM kernel's weight-gradient mode
 // (launch_wgrad_tiles: 256 x 256 tiles fed by direct-to-LDS copies).
 constexpr int BG_BK = 64, BG_CPR = BG_BK / 8;
-template <int BM_, int BN_, int WM_, int WN_, int SLOTS_, int WPE_>
+template <int BM_, int BN_, int WM_, int WN_, int WPE_>
 struct WTile {
-  static constexpr int BM = BM_, BN = BN_, WAVES_M = WM_, WAVES_N = WN_, SLOTS = SLOTS_, WPE = WPE_;
+  static constexpr int BM = BM_, BN = BN_, WAVES_M = WM_, WAVES_N = WN_, WPE = WPE_;
   static constexpr int NW = WM_ * WN_, THREADS = 64 * NW;
   static constexpr int WTM = BM / WM_, WTN = BN / WN_;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -52,9 +52,8 @@ struct WTile {
   static constexpr int ALD = BM * BG_CPR / THREADS;   // 16-byte A chunks per thread and stage
   static constexpr int BLD = BN * BG_CPR / THREADS;   // B chunks
   static_assert(ALD * THREADS == BM * BG_CPR && BLD * THREADS == BN * BG_CPR, "load split");
-  static_assert(SLOTS == 1, "one LDS stage");
 };
-using WTileSmall = WTile<256, 128, 4, 2, 1, 4>;
+using WTileSmall = WTile<256, 128, 4, 2, 4>;
 
 struct BwdGemmArgs {
   const int32_t* poff;      // [E+1] padded column offsets, then [E] the experts by decreasing
@@ -78,7 +77,7 @@ template <class W>
 __global__ __launch_bounds__(W::THREADS, W::WPE) void bwd_gemm_kernel(BwdGemmArgs p) {
   constexpr int BM = W::BM, BN = W::BN, FM = W::FM, FN = W::FN, ALD = W::ALD, BLD = W::BLD;
   constexpr int THREADS = W::THREADS, STAGE = W::STAGE, A_BYTES = W::A_BYTES;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[W::SLOTS * STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
