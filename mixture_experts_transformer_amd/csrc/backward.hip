@@ -417,38 +417,63 @@ __global__ __launch_bounds__(256) void gather_transpose_kernel(const void* __res
 }
 
 // ------------------------------------------------------------------------------ router
-// One wave per token: dg_j = <dh', h> (from the SwiGLU backward) + <dout[t], b2[e_j]>, then
-// the softmax backward over the k selected logits, dl_j = g_j (dg_j - sum_i g_i dg_i).
-// Lane l keeps dg_j for the slots j = l + 64 m (k <= 256).
+// One workgroup per token: dg_j = <dh', h> (from the SwiGLU backward) + <dout[t], b2[e_j]>,
+// then the softmax backward over the k selected logits, dl_j = g_j (dg_j - sum_i g_i dg_i).
+// The dot products take the slots four at a time: thread i reads four consecutive elements
+// of dout's row (16 bytes) and of each slot's b2 row (8 bytes) at 256-element steps, the
+// workgroup's partial sums meet in LDS in a fixed order, and wave 0 finishes the token (lane
+// l keeps dg_j for the slots j = l + 64 m, k <= 256).
 __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict__ dgh,
                                                          const float* __restrict__ dout,
                                                          const uint16_t* __restrict__ b2,
                                                          const int32_t* __restrict__ idx,
                                                          const float* __restrict__ gates, int T, int D, int E,
                                                          int k, float* __restrict__ dl) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (t >= T) return;
-  const int A = T * k;
-  float mine[4] = {0.f, 0.f, 0.f, 0.f};
-  float sgd = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int a = t * k + j;
-    const int e = min(max(idx[a], 0), E - 1);
-    float v = 0.f;
-    for (int d = lane; d < D; d += 64) v += dout[(int64_t)t * D + d] * bf16_to_f32(b2[(int64_t)e * D + d]);
+  constexpr int JG = 4;                     // slots per pass over dout's row
+  __shared__ float part[JG][4];
+  __shared__ float dgs[256];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float4* const drow = (const float4*)(dout + (int64_t)t * D);
+  for (int j0 = 0; j0 < k; j0 += JG) {
+    const uint2* brow[JG];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-    const float d_g = dgh[a] + v;
+    for (int jj = 0; jj < JG; ++jj) {
+      const int j = min(j0 + jj, k - 1);
+      const int e = min(max(idx[(int64_t)t * k + j], 0), E - 1);
+      brow[jj] = (const uint2*)(b2 + (int64_t)e * D);
+    }
+    float v[JG];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-      if (j == lane + 64 * m) mine[m] = d_g;
-    sgd += gates[a] * d_g;
+    for (int jj = 0; jj < JG; ++jj) v[jj] = 0.f;
+    for (int c = tid; c < D / 4; c += 256) {    // D is a multiple of 64
+      const float4 o = drow[c];
+#pragma unroll
+      for (int jj = 0; jj < JG; ++jj) {
+        if (j0 + jj < k) {
+          const uint2 w = brow[jj][c];
+          v[jj] += o.x * __uint_as_float(w.x << 16) + o.y * __uint_as_float(w.x & 0xFFFF0000u) +
+                   o.z * __uint_as_float(w.y << 16) + o.w * __uint_as_float(w.y & 0xFFFF0000u);
+        }
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < JG; ++jj) {
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) v[jj] += __shfl_xor(v[jj], off);
+      if (lane == 0) part[jj][wave] = v[jj];
+    }
+    __syncthreads();
+    if (tid < JG && j0 + tid < k) {
+      const int a = t * k + j0 + tid;
+      dgs[j0 + tid] = dgh[a] + ((part[tid][0] + part[tid][1]) + (part[tid][2] + part[tid][3]));
+    }
+    __syncthreads();
   }
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int j = lane + 64 * m;
-    if (j < k) dl[t * k + j] = gates[t * k + j] * (mine[m] - sgd);
+  if (wave == 0) {
+    float sgd = 0.f;
+    for (int j = 0; j < k; ++j) sgd += gates[t * k + j] * dgs[j];
+    for (int j = lane; j < k; j += 64) dl[t * k + j] = gates[t * k + j] * (dgs[j] - sgd);
   }
 }
 
@@ -653,7 +678,7 @@ hipError_t launch_backward(const BwdArgs& b, hipStream_t st) {
   w.a = b.duT; w.b = b.xT; w.M = G; w.N = D; w.c = b.dw1;
   BW_CHECK(launch_wgrad(w, small, st));
   // 11. router: dg and the softmax backward, then the per-expert sums and dx
-  hipLaunchKernelGGL(router_bwd_kernel, dim3(blocks_for(T, 4)), dim3(256), 0, st, b.dgsum, b.dout, b.b2, b.idx,
+  hipLaunchKernelGGL(router_bwd_kernel, dim3((unsigned)T), dim3(256), 0, st, b.dgsum, b.dout, b.b2, b.idx,
                      b.gates, T, D, E, k, b.dl);
   BW_CHECK(hipGetLastError());
   const unsigned wblk = blocks_for(G > D ? G : D);
