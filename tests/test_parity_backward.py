@@ -69,6 +69,10 @@ CASES = {
     "ragged": dict(base="C2", name="bwd-ragged", T=1000, D=256, F=384, E=8, k=4, seed=8101, empty=5),
     # weights large enough that the SwiGLU clamps engage on both halves
     "clamped": dict(base="C2", name="bwd-clamp", T=300, D=128, F=192, E=6, k=2, seed=8102, weight_std=0.45),
+    # every expert selected by every token (k = E), a single token
+    "k_equals_E_one_token": dict(base="C2", name="bwd-kE", T=1, D=64, F=64, E=4, k=4, seed=8105),
+    # the largest expert count: most of the 256 experts get no row
+    "256_experts": dict(base="C2", name="bwd-e256", T=64, D=64, F=128, E=256, k=2, seed=8106),
 }
 
 
