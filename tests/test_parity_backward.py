@@ -134,6 +134,33 @@ def test_backward_20b_shape_sampled_experts():
     rep.done()
 
 
+def test_backward_t8192_zipf_layer():
+    """The backward at the layer bench.py times at T = 8192 (20B shape, Zipf-skewed routing:
+    the matrix-core tiles, the weight-gradient mode over long and short expert K ranges):
+    dx and the router gradients whole, the expert gradients of the most loaded expert, a
+    middle one and the least loaded live one."""
+    cfg = get_config("C3")
+    inp = make_inputs("C3")
+    dout = make_dout(cfg.T, cfg.D, seed=8107)
+    note("backward 20B shape (C3), 8192 tokens, Zipf routing")
+    _, r, _, g = gpu_backward(cfg, inp, dout)
+    idx = oracle.select_experts(oracle.router_logits(inp.x, inp.wr, inp.br), cfg.k)
+    assert np.array_equal(r["idx"].cpu().numpy(), idx)
+    counts = np.bincount(idx.reshape(-1), minlength=cfg.E)
+    live = np.flatnonzero(counts)
+    order = live[np.argsort(counts[live], kind="stable")]
+    pick = sorted({int(order[-1]), int(order[len(order) // 2]), int(order[0])})
+    ref = oracle.moe_backward_grouped(inp.x, inp.wr, inp.br, inp.w1, inp.b1, inp.w2, inp.b2, idx, dout,
+                                      cfg.k, cfg.F, "bf16", weight_experts=pick)
+    rep = Report()
+    for n in ("dx", "dwr", "dbr"):
+        rep.check(g[n].cpu().numpy(), ref[n], f"backward C3 {n}")
+    for e in pick:
+        for n in ("dw1", "db1", "dw2", "db2"):
+            rep.check(g[n][e].cpu().numpy(), ref[n][e], f"backward C3 {n}[{e}] ({counts[e]} rows)")
+    rep.done()
+
+
 def test_backward_is_deterministic():
     cfg = get_config("C2", name="bwd-det", T=700, D=256, F=256, E=8, k=4, seed=8104)
     inp = make_inputs(cfg)
