@@ -149,7 +149,7 @@ def stored_traffic(workload, kernel):
     return rec.get("bytes_per_launch")
 
 
-def bench_workload(name, steps, warmup, with_cpu):
+def bench_workload(name, steps, warmup, with_cpu, library=False):
     import torch
     import mixture_experts_transformer_amd as moe
     from synth import get_config, make_inputs
@@ -258,6 +258,9 @@ def bench_workload(name, steps, warmup, with_cpu):
         "kernel_us": {s: round(tms / max(n, 1) * 1e3, 2) for s, (tms, n) in stages.items()},
         "roofline": roof,
     }
+    if library and cfg.fmt == "bf16":
+        log(f"[bench] {name}: timing the library grouped GEMM on the same products")
+        res["library_comparison"] = library_comparison(cfg, x, w1_0, w2_0, r)
     if with_cpu:
         n_cpu = min(cfg.T, 256 if cfg.E <= 32 else 64)
         log(f"[bench] {name}: timing the CPU oracle on {n_cpu} tokens")
@@ -265,6 +268,66 @@ def bench_workload(name, steps, warmup, with_cpu):
     del w1s, w2s
     torch.cuda.empty_cache()
     return res
+
+
+def library_comparison(cfg, x, w1, w2, r, reps=20):
+    """The two expert products of one forward run by the library grouped GEMM that torchtitan's
+    GPT-OSS MoE calls (torch._grouped_mm, here PyTorch's ROCm build) on this GPU, timed for
+    context beside mlp1 and mlp2.  A = x's routed rows (mlp1) and N(0, 1) rows standing in for
+    h (mlp2); B = the layer's expert weights transposed to [E][K][N]; each expert's rows padded
+    to a multiple of 16, as torchtitan pads them.  The products alone: no gather, SwiGLU, bias,
+    gate or combine, which the library leaves to other launches.  Beside them one dense
+    torch.mm (hipBLASLt) over the same padded row count with one expert's weights: the vendor
+    GEMM's own rate at this shape.  bf16 weights only; rates are algorithmic flops (unpadded
+    rows) per second, the dense one over its padded rows."""
+    import torch
+    E, D, F, k = cfg.E, cfg.D, cfg.F, cfg.k
+    dev = x.device
+    counts = r["counts"].cpu().numpy().astype(np.int64)
+    padded = (counts + 15) // 16 * 16
+    M = int(padded.sum())
+    ends = np.cumsum(padded)
+    offs = torch.tensor(ends, dtype=torch.int32, device=dev)
+    # routed rows in the library's padded layout: expert e's rows at [ends[e] - padded[e], ...)
+    perm = r["perm"].long()
+    dst = torch.cat([torch.arange(int(e0), int(e0) + int(c), device=dev)
+                     for e0, c in zip(ends - padded, counts)]) if counts.sum() else torch.empty(0, device=dev)
+    a1 = torch.zeros((M, D), dtype=torch.bfloat16, device=dev)
+    a1[dst.long()] = x.view(torch.bfloat16)[perm // k]
+    a2 = torch.randn((M, F), dtype=torch.bfloat16, device=dev, generator=torch.Generator(device=dev).manual_seed(3))
+    b1 = w1.view(torch.bfloat16).view(E, 2 * F, D).transpose(1, 2).contiguous()
+    b2 = w2.view(torch.bfloat16).view(E, D, F).transpose(1, 2).contiguous()
+    rows = int(counts.sum())
+    alg = {"mlp1": 2.0 * rows * D * 2 * F, "mlp2": 2.0 * rows * F * D}
+    dense = {"mlp1": 2.0 * M * D * 2 * F, "mlp2": 2.0 * M * F * D}
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps / 1e3
+
+    out = {"library": f"torch {torch.__version__} torch._grouped_mm and torch.mm (bf16, fp32 accumulate)",
+           "padded_rows": M, "rows": rows}
+    try:
+        t = {"mlp1": timed(lambda: torch._grouped_mm(a1, b1, offs=offs)),
+             "mlp2": timed(lambda: torch._grouped_mm(a2, b2, offs=offs))}
+        out["grouped_mm_us"] = {s: round(v * 1e6, 1) for s, v in t.items()}
+        out["grouped_mm_tflops"] = {s: round(alg[s] / v / 1e12, 1) for s, v in t.items()}
+    except Exception as ex:  # an unsupported library path is reported, not fatal
+        out["grouped_mm_error"] = repr(ex)[:200]
+    t = {"mlp1": timed(lambda: torch.mm(a1, b1[0])), "mlp2": timed(lambda: torch.mm(a2, b2[0]))}
+    out["dense_mm_us"] = {s: round(v * 1e6, 1) for s, v in t.items()}
+    out["dense_mm_tflops"] = {s: round(dense[s] / v / 1e12, 1) for s, v in t.items()}
+    del a1, a2, b1, b2
+    torch.cuda.empty_cache()
+    return out
 
 
 def bench_backward(name, steps, warmup):
@@ -325,7 +388,8 @@ TARGETS = ("C3", "X1", "X2")     # the other target workloads: bf16 at 8192 toke
 def target_summary(res):
     """The fields of a target workload's measurement that go into the headline line."""
     keep = ("value", "unit", "ms_per_step", "steps", "warmup", "dtype", "step_tflops", "step_mfma_frac",
-            "step_fp8_peak_frac", "step_fp4_peak_frac", "step_hbm_gbs", "step_hbm_frac", "kernel_us", "roofline")
+            "step_fp8_peak_frac", "step_fp4_peak_frac", "step_hbm_gbs", "step_hbm_frac", "kernel_us", "roofline",
+            "library_comparison")
     out = {k: res[k] for k in keep if k in res}
     out["workload"] = res["config"]["workload"]
     return out
@@ -425,6 +489,9 @@ def main():
                     help="only measure the sustained bf16 matrix-core rate (random and constant operands)")
     ap.add_argument("--hbm-calibration", action="store_true",
                     help="only measure the sustained HBM read rate (plain 16-byte load stream)")
+    ap.add_argument("--library-comparison", action="store_true",
+                    help="with a bf16 --workload: also time the same expert products on torch._grouped_mm "
+                         "and a dense torch.mm (the default line does this for C2 and C3)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the MoE block is built and timed on a single MI355X; "
@@ -458,13 +525,16 @@ def main():
             res = bench_workload(name, args.steps, args.warmup, with_cpu=(not args.no_cpu) and i == 0)
             print(json.dumps(res), flush=True)
         return
-    res = bench_workload(args.workload, args.steps, args.warmup, with_cpu=not args.no_cpu)
-    if args.workload == "C2" and not args.no_targets:
+    headline = args.workload == "C2" and not args.no_targets
+    res = bench_workload(args.workload, args.steps, args.warmup, with_cpu=not args.no_cpu,
+                         library=args.library_comparison or headline)
+    if headline:
         # the headline workload's line also carries the other target workloads, each timed the
         # same way (own warm-up, K timed steps between synchronisations, then an event pass)
         res["targets"] = {}
         for name in TARGETS:
-            res["targets"][name] = target_summary(bench_workload(name, args.steps, args.warmup, with_cpu=False))
+            res["targets"][name] = target_summary(bench_workload(name, args.steps, args.warmup, with_cpu=False,
+                                                                 library=True))
         res["backward"] = {name: bench_backward(name, args.steps, args.warmup) for name in ("C2", "C3")}
         # what the matrix cores sustain on this GPU, the reference for the T = 8192 targets'
         # matrix-core fractions (random operands: the clock drops under load)
