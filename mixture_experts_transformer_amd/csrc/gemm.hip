@@ -811,6 +811,26 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
     __builtin_amdgcn_sched_group_barrier(0x008, AP * (FA) * FN, 0);                              \
   } while (0)
 
+  // Matrix-core tiles: a stage's row copies go out between the previous stage's deferred
+  // matrix instructions instead of in one burst after the barrier, so the matrix pipe works
+  // while the copies queue for the CU's memory path (each 1 KB copy holds it ~16 cycles).
+  constexpr bool ILV = !C::STREAM && NS == 2 && !DEC;
+#define MOE_COPY_SLOT(kt_, j_)                                                                   \
+  do {                                                                                           \
+    const int i_ = wave + (j_) * NW;                                                             \
+    if (i_ < NG && !(i_ < NA && (i_ % A_CPC) * 64 / A_CPR >= rows)) {                           \
+      const uint32_t d_ = smem_l + ((kt_) % NS) * STAGE + gdst[j_];                              \
+      if (i_ < NA) {                                                                             \
+        const void* ab_ = MX ? (const void*)p.a8                                                 \
+                             : (i_ < A_CPC ? (const void*)(p.a + kcol0) : (const void*)p.a_lo);  \
+        dma16((const uint8_t*)ab_ + (size_t)(kt_) * A_ROWB, goff[j_], d_);                       \
+      } else {                                                                                   \
+        const uint8_t* ws_ = BT ? w_e + (size_t)((kt_) % bt_kt) * 64 * p.N * 2                   \
+                                : w_e + (size_t)(kt_) * ROWB;                                    \
+        dma16(ws_, goff[j_], d_);                                                                \
+      }                                                                                          \
+    }                                                                                            \
+  } while (0)
 // the K loop for FA active 32-row fragment rows per wave (the rest are padding), into ACC
 #define MOE_MAIN_LOOP(FA, ACC)                                                                   \
   do {                                                                                           \
@@ -824,7 +844,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
       barrier_nofence();                                                                         \
       if (MODE == 2 && kt == 0 && rt_a >= 0) rt_g = p.gates[rt_a];                               \
       MOE_ISSUE_NEXT_WIN(kt);                                                                    \
-      if (kt + NS - 1 < nk) MOE_ISSUE(kt + NS - 1);                                              \
+      if (!ILV && kt + NS - 1 < nk) MOE_ISSUE(kt + NS - 1);                                      \
                                                                                                  \
       const uint8_t* sa = smem + slot * STAGE;                                                   \
       const uint8_t* sb = sa + AP * A_BYTES;                                                     \
@@ -839,7 +859,24 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
         }                                                                                        \
       }                                                                                          \
       MOE_LOAD_FRAGS(0, 0, sa, sb, FA);                                                          \
-      if (kt > 0) MOE_MMA((KS - 1) & 1, FA, ACC);  /* last MFMA step of the previous stage */    \
+      if (ILV) {                                                                                 \
+        /* the previous stage's last MFMA step, the next stage's copies in between */            \
+        const bool cp_ = kt + 1 < nk;                                                            \
+        _Pragma("unroll") for (int m_ = 0; m_ < AP * (FA) * FN || m_ < PW_G; ++m_) {             \
+          if (m_ < AP * (FA) * FN && kt > 0) {                                                   \
+            const int i_ = m_ / (AP * FN), pa_ = (m_ / FN) % AP, j_ = m_ % FN;                    \
+            ACC[i_][j_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                               \
+                fa[(KS - 1) & 1][pa_][i_], fb[(KS - 1) & 1][j_], ACC[i_][j_], 0, 0, 0);          \
+          }                                                                                      \
+          if (m_ < PW_G) {                                                                       \
+            __builtin_amdgcn_sched_barrier(0);                                                   \
+            if (cp_) MOE_COPY_SLOT(kt + 1, m_);                                                  \
+            __builtin_amdgcn_sched_barrier(0);                                                   \
+          }                                                                                      \
+        }                                                                                        \
+      } else if (kt > 0) {                                                                       \
+        MOE_MMA((KS - 1) & 1, FA, ACC);     /* last MFMA step of the previous stage */           \
+      }                                                                                          \
       MOE_SCHED(FA);                                                                             \
   _Pragma("unroll")                                                                              \
       for (int ks = 0; ks < KS - 1; ++ks) {                                                      \
@@ -922,7 +959,14 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
       barrier_nofence();                                                                         \
       if (MODE == 2 && kt == 0 && rt_a >= 0) rt_g = p.gates[rt_a];                               \
       MOE_ISSUE_NEXT_WIN(kt);                                                                    \
-      if (kt + NS - 1 < nk) MOE_ISSUE(kt + NS - 1);                                              \
+      if (kt + NS - 1 < nk) {                                                                    \
+        if (!ILV) {                                                                              \
+          MOE_ISSUE(kt + NS - 1);                                                                \
+        } else if ((kt + NS - 1) % SUPER == 0) {  /* the scales now, the rows below */           \
+          if (!WALIGN) MOE_ISSUE_WIN((kt + NS - 1) / SUPER);                                     \
+          MOE_ISSUE_ASC((kt + NS - 1) / SUPER);                                                  \
+        }                                                                                        \
+      }                                                                                          \
       const uint8_t* sa = smem + slot * STAGE;                                                   \
       const uint8_t* sas = ascale_lds + ((kt / SUPER) % NSB) * ASL_SLOT;                         \
       const uint8_t* sb = sa + A_BYTES;                                                          \
@@ -943,7 +987,31 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
       }                                                                                          \
       i32x8 fa[2][AP];                                                                           \
       MX_LOAD_A(fa[0], 0);                                                                       \
-      if (kt > 0) MX_MMA(ACC, (FA) - 1, fap, fbp, sap, sbp);                                     \
+      if (ILV) {                                                                                 \
+        /* the previous stage's last row block, this stage's row copies in between */            \
+        const bool cp_ = kt + NS - 1 < nk;                                                       \
+        _Pragma("unroll") for (int m_ = 0; m_ < AP * FN || m_ < PW_G; ++m_) {                    \
+          if (m_ < AP * FN && kt > 0) {                                                          \
+            const int pa = m_ / FN, j = m_ % FN;                                                 \
+            if (pa == 0)                                                                         \
+              ACC[(FA) - 1][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                \
+                  fap[pa], fbp[j], ACC[(FA) - 1][j], 0, 4, 0, (int)sap, 0, (int)sbp[j]);         \
+            else if (pa == 1)                                                                    \
+              ACC[(FA) - 1][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                \
+                  fap[pa], fbp[j], ACC[(FA) - 1][j], 0, 4, 1, (int)sap, 0, (int)sbp[j]);         \
+            else                                                                                 \
+              ACC[(FA) - 1][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                \
+                  fap[pa], fbp[j], ACC[(FA) - 1][j], 0, 4, 2, (int)sap, 0, (int)sbp[j]);         \
+          }                                                                                      \
+          if (m_ < PW_G) {                                                                       \
+            __builtin_amdgcn_sched_barrier(0);                                                   \
+            if (cp_) MOE_COPY_SLOT(kt + NS - 1, m_);                                             \
+            __builtin_amdgcn_sched_barrier(0);                                                   \
+          }                                                                                      \
+        }                                                                                        \
+      } else if (kt > 0) {                                                                       \
+        MX_MMA(ACC, (FA) - 1, fap, fbp, sap, sbp);                                               \
+      }                                                                                          \
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * FN + (FA) + 2 * AP, 0);                    \
       __builtin_amdgcn_sched_group_barrier(0x008, AP * FN, 0);                                   \
       _Pragma("unroll") for (int i = 0; i + 1 < (FA); ++i) {                                     \
@@ -984,6 +1052,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
 #undef MX_LOAD_A
 #undef MX_MMA
 #undef MOE_MAIN_LOOP
+#undef MOE_COPY_SLOT
 #undef MOE_LOAD_FRAGS
 #undef MOE_MMA
 #undef MOE_SCHED
