@@ -53,7 +53,8 @@ M0_SOURCES = ["gemm.hip"]
 def check_m0(src: str) -> int:
     """The LDS copies load M0 in inline assembly that the compiler does not preserve; that is
     sound only while nothing else in the generated code uses M0.  Raise if any use of M0 in
-    the gfx950 assembly of `src` is not 's_mov_b32 m0, sN' directly followed by 's_nop 0' and
+    the gfx950 assembly of `src` is not 's_mov_b32 m0, <scalar register>' (sN, or vcc_lo / vcc_hi
+    where the compiler puts the copy's LDS address there) directly followed by 's_nop 0' and
     a global_load_lds copy.  Returns the number of copies checked."""
     import re
     lines = [l.split(";")[0].strip() for l in device_asm(src).splitlines()]
@@ -62,7 +63,7 @@ def check_m0(src: str) -> int:
     if not uses:
         raise RuntimeError(f"{src}: expected the LDS copies to set M0")
     for i in uses:
-        if not re.fullmatch(r"s_mov_b32 m0, s\d+", lines[i]):
+        if not re.fullmatch(r"s_mov_b32 m0, (s\d+|vcc_lo|vcc_hi)", lines[i]):
             raise RuntimeError(f"{src}: M0 used other than by an LDS copy: {lines[i]!r}")
         nxt = lines[i + 1:i + 3]
         if len(nxt) < 2 or nxt[0] != "s_nop 0" or not nxt[1].startswith("global_load_lds_dword"):

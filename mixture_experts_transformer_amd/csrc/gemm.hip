@@ -814,7 +814,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   // Matrix-core tiles: a stage's row copies go out between the previous stage's deferred
   // matrix instructions instead of in one burst after the barrier, so the matrix pipe works
   // while the copies queue for the CU's memory path (each 1 KB copy holds it ~16 cycles).
-  constexpr bool ILV = !C::STREAM && NS == 2 && !DEC;
+  constexpr bool ILV = !C::STREAM && NS == 2;
 #define MOE_COPY_SLOT(kt_, j_)                                                                   \
   do {                                                                                           \
     const int i_ = wave + (j_) * NW;                                                             \
@@ -844,7 +844,14 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
       barrier_nofence();                                                                         \
       if (MODE == 2 && kt == 0 && rt_a >= 0) rt_g = p.gates[rt_a];                               \
       MOE_ISSUE_NEXT_WIN(kt);                                                                    \
-      if (!ILV && kt + NS - 1 < nk) MOE_ISSUE(kt + NS - 1);                                      \
+      if (kt + NS - 1 < nk) {                                                                    \
+        if (!ILV) {                                                                              \
+          MOE_ISSUE(kt + NS - 1);                                                                \
+        } else if (WF != 0 && (kt + NS - 1) % SUPER == 0) {  /* codes, scales; rows below */     \
+          if (!WALIGN) MOE_ISSUE_WIN((kt + NS - 1) / SUPER);                                     \
+          MOE_ISSUE_ASC((kt + NS - 1) / SUPER);                                                  \
+        }                                                                                        \
+      }                                                                                          \
                                                                                                  \
       const uint8_t* sa = smem + slot * STAGE;                                                   \
       const uint8_t* sb = sa + AP * A_BYTES;                                                     \

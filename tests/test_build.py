@@ -27,9 +27,13 @@ def test_m0_check_rejects_other_uses(monkeypatch):
     good = "s_mov_b32 m0, s4\ns_nop 0\nglobal_load_lds_dwordx4 v1, s[2:3]\n"
     monkeypatch.setattr(b, "device_asm", lambda src: good)
     assert b.check_m0("x.hip") == 1
+    vcc = "s_mov_b32 m0, vcc_lo\ns_nop 0\nglobal_load_lds_dwordx4 v1, s[2:3]\n"
+    monkeypatch.setattr(b, "device_asm", lambda src: good + vcc)
+    assert b.check_m0("x.hip") == 2
     for bad in ("s_mov_b32 m0, s4\ns_nop 0\nds_read_b32 v1, v2\n",
                 good + "s_mov_b32 m0, -1\nds_write_b32 v1, v2\n",
-                good + "v_readlane_b32 s5, v1, m0\n"):
+                good + "v_readlane_b32 s5, v1, m0\n",
+                good + "s_mov_b32 m0, v1\ns_nop 0\nglobal_load_lds_dwordx4 v1, s[2:3]\n"):
         monkeypatch.setattr(b, "device_asm", lambda src, t=bad: t)
         with pytest.raises(RuntimeError):
             b.check_m0("x.hip")
