@@ -36,12 +36,8 @@ constexpr int RT_WAVES = 4;           // waves per workgroup, each owns 16 token
 constexpr int RT_CHUNK = 32;          // K elements per MFMA group (8 steps of K=4)
 constexpr int RT_PD = 4;              // chunks whose loads are in flight (up to 64 experts)
 
-#ifndef RT_TARGET_WAVES
-#define RT_TARGET_WAVES 2048
-#endif
-#ifndef RT_MIN_CHUNKS
-#define RT_MIN_CHUNKS 3
-#endif
+constexpr int64_t RT_TARGET_WAVES = 2048;  // waves the K split aims at (measured choice)
+constexpr int64_t RT_MIN_CHUNKS = 3;        // K chunks per split at least (6 measured slower)
 int router_ksplit(int64_t T, int64_t D) {
   const int64_t chunks = D / RT_CHUNK;
   const int64_t tiles = (T + 15) / 16;
