@@ -217,7 +217,13 @@ int moe_experts(const void* x, const void* w1, const void* b1, const void* w2, c
  * enter theirs rounded to bf16, which bounds the relative error of each gradient near 2^-9;
  * every sum has a fixed order, so the result is bitwise reproducible.  With
  * T = 0 the parameter gradients are set to zero.  Uses moe_backward_workspace_bytes of
- * workspace (the same workspace rules as the forward).  Timed as stage 7 by moe_profile_*. */
+ * workspace (the same workspace rules as the forward).  Timed as stage 7 by moe_profile_*.
+ * Ordering is that of the calling thread's stream: at many routed rows per expert and
+ * outside graph capture the memory-bound side work runs on a second stream the library keeps
+ * per thread (default priority, created
+ * on first use, destroyed by moe_release), which waits for the calling stream's earlier work
+ * and which the calling stream waits for before the call's last kernel; under capture all of
+ * it runs on the calling stream. */
 int moe_backward(const void* x, const void* router_w, const void* w1, const void* b1,
                  const void* w2, const void* b2,
                  const int32_t* topk_idx, const float* gates, const int32_t* offsets, const int32_t* perm,

@@ -612,11 +612,21 @@ int bwd_padded_cols(int64_t A, int64_t E) {
 }
 int bwd_sum_chunks() { return EX_CHUNKS; }
 
-hipError_t launch_backward(const BwdArgs& b, hipStream_t st) {
+hipError_t launch_backward(const BwdArgs& b, hipStream_t st, const BwdSide* side) {
   const int T = b.T, D = b.D, E = b.E, k = b.k, F = b.F, G = 2 * F;
   const int A = T * k;
   const int ldt = bwd_padded_cols(A, E);
   const int DF = D > F ? D : F;
+  // The memory-bound side work (activation transposes, the dout pair, the router and bias
+  // gradients) goes to the side stream, when there is one, beside the grouped products on
+  // st; events order the two where one reads what the other writes.  Without a side stream
+  // everything runs on st in the same order.
+  hipStream_t sb = side ? side->stream : st;
+  auto fork = [&](hipStream_t from, hipStream_t to, int i) -> hipError_t {
+    if (!side) return hipSuccess;
+    const hipError_t e = hipEventRecord(side->ev[i], from);
+    return e != hipSuccess ? e : hipStreamWaitEvent(to, side->ev[i], 0);
+  };
   // 1. padded layout of the routed rows per expert (weight gradients)
   hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(256), 0, st, b.offsets, E, b.poff);
   BW_CHECK(hipGetLastError());
@@ -628,16 +638,17 @@ hipError_t launch_backward(const BwdArgs& b, hipStream_t st) {
   hipLaunchKernelGGL(fill_f32_kernel, dim3(blocks_for((int64_t)E * DF / 2)), dim3(256), 0, st, (float*)b.zeros,
                      (int64_t)E * DF / 2, 0.0f);
   BW_CHECK(hipGetLastError());
-  // 3. transposed, padded x and dz = g dout (operands of the weight gradients)
+  BW_CHECK(fork(st, sb, 0));
+  // 3. (side) transposed, padded x and dz = g dout (operands of the weight gradients)
   hipLaunchKernelGGL((gather_transpose_kernel<true, false, false>), dim3(ldt / 64, blocks_for(D, 64)), dim3(256), 0,
-                     st, (const void*)b.x, D, D, b.padmap, b.perm, b.gates, k, A, ldt, b.xT);
+                     sb, (const void*)b.x, D, D, b.padmap, b.perm, b.gates, k, A, ldt, b.xT);
   BW_CHECK(hipGetLastError());
   hipLaunchKernelGGL((gather_transpose_kernel<true, true, true>), dim3(ldt / 64, blocks_for(D, 64)), dim3(256), 0,
-                     st, (const void*)b.dout, D, D, b.padmap, b.perm, b.gates, k, A, ldt, b.dzT);
+                     sb, (const void*)b.dout, D, D, b.padmap, b.perm, b.gates, k, A, ldt, b.dzT);
   BW_CHECK(hipGetLastError());
-  // 4. dout rows in routed order as bf16 pairs
+  // 4. (side) dout rows in routed order as bf16 pairs
   uint16_t* const dout_lo = b.dout_perm + (int64_t)A * D;
-  hipLaunchKernelGGL(gather_dout_pair_kernel, dim3(blocks_for((int64_t)A * D / 4)), dim3(256), 0, st,
+  hipLaunchKernelGGL(gather_dout_pair_kernel, dim3(blocks_for((int64_t)A * D / 4)), dim3(256), 0, sb,
                      (const float4*)b.dout, b.perm, A, k, D / 4, (uint2*)b.dout_perm, (uint2*)dout_lo);
   BW_CHECK(hipGetLastError());
 
@@ -647,6 +658,7 @@ hipError_t launch_backward(const BwdArgs& b, hipStream_t st) {
   f.x = b.x; f.w1 = b.w1; f.b1 = b.b1; f.gates = b.gates; f.offsets = b.offsets; f.perm = b.perm;
   f.u_out = b.u; f.T = T; f.D = D; f.E = E; f.k = k; f.F = F; f.fmt = 0;
   BW_CHECK(launch_mlp1(f, cfg, st));
+  BW_CHECK(fork(sb, st, 1));                // the dout pair (and the transposes) are written
   // 6. dh' = (dout hi + lo) W2 at the slot rows: the forward's mlp2 with K = D, N = F, reading
   // W2 [E][D][F] as stored, both parts of A against each staged tile of W2
   ExpertArgs m{};
@@ -657,17 +669,35 @@ hipError_t launch_backward(const BwdArgs& b, hipStream_t st) {
   hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)A), dim3(256), 0, st, b.u, b.dxs, b.perm, b.gates, A, F, b.h,
                      b.du, b.dgsum);
   BW_CHECK(hipGetLastError());
+  BW_CHECK(fork(st, sb, 2));                // h, du and dg are written
+  // 9. (side) transposed, padded h and du
+  hipLaunchKernelGGL((gather_transpose_kernel<false, false, false>), dim3(ldt / 64, blocks_for(F, 64)), dim3(256), 0,
+                     sb, (const void*)b.h, F, F, b.padmap, b.perm, b.gates, k, A, ldt, b.hT);
+  BW_CHECK(hipGetLastError());
+  hipLaunchKernelGGL((gather_transpose_kernel<false, false, false>), dim3(ldt / 64, blocks_for(G, 64)), dim3(256), 0,
+                     sb, (const void*)b.du, G, G, b.padmap, b.perm, b.gates, k, A, ldt, b.duT);
+  BW_CHECK(hipGetLastError());
+  BW_CHECK(side ? hipEventRecord(side->ev[3], sb) : hipSuccess);
+  // 11. (side) router: dg and the softmax backward, then the per-expert sums (read h, du,
+  // dg, dout and x only)
+  hipLaunchKernelGGL(router_bwd_kernel, dim3((unsigned)T), dim3(256), 0, sb, b.dgsum, b.dout, b.b2, b.idx,
+                     b.gates, T, D, E, k, b.dl);
+  BW_CHECK(hipGetLastError());
+  const unsigned wblk = blocks_for(G > D ? G : D);
+  hipLaunchKernelGGL(expert_partial_kernel, dim3(wblk, E, EX_CHUNKS), dim3(256), 0, sb, b.offsets, b.perm, b.gates,
+                     b.dl, b.x, b.dout, b.du, D, F, k, A, E, b.part_w, b.part_b2, b.part_b1);
+  BW_CHECK(hipGetLastError());
+  hipLaunchKernelGGL(expert_reduce_kernel, dim3(wblk, E), dim3(256), 0, sb, b.part_w, b.part_b2, b.part_b1, D, F, E,
+                     b.dwr, b.db2, b.db1);
+  BW_CHECK(hipGetLastError());
+  hipLaunchKernelGGL(router_bias_grad_kernel, dim3(E), dim3(256), 0, sb, b.offsets, b.perm, b.dl, A, b.dbr);
+  BW_CHECK(hipGetLastError());
+  BW_CHECK(side ? hipEventRecord(side->ev[4], sb) : hipSuccess);
   // 8. dx contributions du W1[e] at the slot rows: the forward's mlp2 with K = 2F, N = D,
   // reading W1 [E][2F][D] as stored
   m.h = b.du; m.h_lo = nullptr; m.w2 = b.w1; m.y = b.dxs; m.D = D; m.F = G; m.w2_kn_rows = G;
   BW_CHECK(launch_mlp2(m, cfg, st));
-  // 9. transposed, padded h and du
-  hipLaunchKernelGGL((gather_transpose_kernel<false, false, false>), dim3(ldt / 64, blocks_for(F, 64)), dim3(256), 0,
-                     st, (const void*)b.h, F, F, b.padmap, b.perm, b.gates, k, A, ldt, b.hT);
-  BW_CHECK(hipGetLastError());
-  hipLaunchKernelGGL((gather_transpose_kernel<false, false, false>), dim3(ldt / 64, blocks_for(G, 64)), dim3(256), 0,
-                     st, (const void*)b.du, G, G, b.padmap, b.perm, b.gates, k, A, ldt, b.duT);
-  BW_CHECK(hipGetLastError());
+  BW_CHECK(side ? hipStreamWaitEvent(st, side->ev[3], 0) : hipSuccess);   // hT, duT (and xT, dzT)
   // 10. weight gradients per expert: dW2[e] = dz^T h, dW1[e] = du^T x
   // (few rows per expert, the forward's streaming regime: tiles that are mostly stores)
   const bool small = cfg == 0;
@@ -677,19 +707,8 @@ hipError_t launch_backward(const BwdArgs& b, hipStream_t st) {
   BW_CHECK(launch_wgrad(w, small, st));
   w.a = b.duT; w.b = b.xT; w.M = G; w.N = D; w.c = b.dw1;
   BW_CHECK(launch_wgrad(w, small, st));
-  // 11. router: dg and the softmax backward, then the per-expert sums and dx
-  hipLaunchKernelGGL(router_bwd_kernel, dim3((unsigned)T), dim3(256), 0, st, b.dgsum, b.dout, b.b2, b.idx,
-                     b.gates, T, D, E, k, b.dl);
-  BW_CHECK(hipGetLastError());
-  const unsigned wblk = blocks_for(G > D ? G : D);
-  hipLaunchKernelGGL(expert_partial_kernel, dim3(wblk, E, EX_CHUNKS), dim3(256), 0, st, b.offsets, b.perm, b.gates,
-                     b.dl, b.x, b.dout, b.du, D, F, k, A, E, b.part_w, b.part_b2, b.part_b1);
-  BW_CHECK(hipGetLastError());
-  hipLaunchKernelGGL(expert_reduce_kernel, dim3(wblk, E), dim3(256), 0, st, b.part_w, b.part_b2, b.part_b1, D, F, E,
-                     b.dwr, b.db2, b.db1);
-  BW_CHECK(hipGetLastError());
-  hipLaunchKernelGGL(router_bias_grad_kernel, dim3(E), dim3(256), 0, st, b.offsets, b.perm, b.dl, A, b.dbr);
-  BW_CHECK(hipGetLastError());
+  BW_CHECK(side ? hipStreamWaitEvent(st, side->ev[4], 0) : hipSuccess);   // dl, and the side's end
+  // 12. dx
   hipLaunchKernelGGL(dx_combine_kernel, dim3(blocks_for((int64_t)T * D / 4)), dim3(256), 0, st, b.dxs, D, b.dl,
                      b.idx, b.wr, T, D, E, k, b.dx);
   return hipGetLastError();

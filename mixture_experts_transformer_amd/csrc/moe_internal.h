@@ -129,7 +129,14 @@ hipError_t launch_wgrad_tiles(const uint16_t* a, const uint16_t* b, int ld, cons
                               int N, float* c, hipStream_t st);
 // Fixed row chunks of the per-expert sums.
 int bwd_sum_chunks();
-hipError_t launch_backward(const BwdArgs& b, hipStream_t st);
+// A second stream for the backward's memory-bound side work and the events that join it to
+// the main one (created by the caller on the current device; default priority).
+struct BwdSide {
+  hipStream_t stream;
+  hipEvent_t ev[5];
+};
+// side: null runs everything on st.
+hipError_t launch_backward(const BwdArgs& b, hipStream_t st, const BwdSide* side);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 
 }  // namespace moe
