@@ -173,6 +173,33 @@ def test_backward_is_deterministic():
         assert torch.equal(g1[n], g2[n]), n
 
 
+def test_backward_side_stream_follows_the_calling_stream():
+    """At many rows per expert the backward forks its memory-bound work onto a side stream and
+    joins it back: called on a non-default stream, and again after moe_release has destroyed
+    the side stream, it gives the default stream's gradients bit for bit."""
+    cfg = get_config("C2", name="bwd-stream", T=700, D=256, F=256, E=8, k=4, seed=8108)
+    assert cfg.T * cfg.k >= 128 * cfg.E             # the matrix-core regime, where the side stream runs
+    inp = make_inputs(cfg)
+    dout = make_dout(cfg.T, cfg.D, seed=8108)
+    note("backward on a caller stream and after release")
+    d, r, dt, ref = gpu_backward(cfg, inp, dout)
+    ref = {n: t.clone() for n, t in ref.items()}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        out = {n: torch.empty_like(t) for n, t in ref.items()}
+        moe.backward(d["x"], d["router_w"], d["w1"], d["b1"], d["w2"], d["b2"], r, dt, cfg.k, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for n in NAMES:
+        assert torch.equal(out[n], ref[n]), n
+    moe.release()
+    again = moe.backward(d["x"], d["router_w"], d["w1"], d["b1"], d["w2"], d["b2"], r, dt, cfg.k)
+    torch.cuda.synchronize()
+    for n in NAMES:
+        assert torch.equal(again[n], ref[n]), n
+
+
 def test_backward_zero_tokens_zeroes_parameter_gradients():
     cfg = get_config("C1")
     inp = make_inputs("C1")
