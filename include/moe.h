@@ -220,10 +220,10 @@ int moe_experts(const void* x, const void* w1, const void* b1, const void* w2, c
  * workspace (the same workspace rules as the forward).  Timed as stage 7 by moe_profile_*.
  * Ordering is that of the calling thread's stream: at many routed rows per expert and
  * outside graph capture the memory-bound side work runs on a second stream the library keeps
- * per thread (default priority, created
- * on first use, destroyed by moe_release), which waits for the calling stream's earlier work
- * and which the calling stream waits for before the call's last kernel; under capture all of
- * it runs on the calling stream. */
+ * per thread (default priority, created on the thread's first such call, destroyed by that
+ * thread's moe_release), which waits for the calling stream's earlier work and which the
+ * calling stream waits for before the call's last kernel; under capture all of it runs on
+ * the calling stream. */
 int moe_backward(const void* x, const void* router_w, const void* w1, const void* b1,
                  const void* w2, const void* b2,
                  const int32_t* topk_idx, const float* gates, const int32_t* offsets, const int32_t* perm,
@@ -252,9 +252,10 @@ int moe_set_workspace(void* dev_ptr, size_t bytes);
 /* Message for the calling thread's last failing call ("" if none). */
 const char* moe_last_error(void);
 
-/* Free the library-owned workspace (with the buffers kept for captured graphs) and the
- * profiling events, and return the calling thread to the library-owned workspace.  Must not
- * run while work that uses the workspace is queued or a captured graph may still replay. */
+/* Free the library-owned workspace (with the buffers kept for captured graphs), the
+ * profiling events and the calling thread's backward side stream, and return the calling
+ * thread to the library-owned workspace.  Must not run while work that uses the workspace is
+ * queued or a captured graph may still replay. */
 void moe_release(void);
 
 /* Kernel timing (tracing): while enabled, every launch is bracketed by HIP events on the
