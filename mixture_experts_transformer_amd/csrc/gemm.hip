@@ -270,6 +270,70 @@ static __device__ __forceinline__ uint32_t mx_piece4(float* v, float inv, float 
   return (uint32_t)pk;
 }
 
+// fp6 pieces (OCP E2M3: 3 mantissa bits, exponent bias 1, no infinity or NaN, largest 7.5,
+// subnormal step 1/8) of h for the scaled engine's mlp2.  The scale for a block whose largest
+// remaining magnitude is m = 1.f 2^x is the smallest power of two with m / 2^s <= 7.5:
+// s = x - 2, one more when 1.f > 1.875.  It is kept at or above 2^-119 so that the scale and
+// every decoded value stay normal fp32 (a block that small contributes nothing the output can
+// hold), and an all-zero block takes 2^0.
+typedef float f32x32 __attribute__((ext_vector_type(32)));
+typedef uint32_t u32x6 __attribute__((ext_vector_type(6)));
+static __device__ __forceinline__ int e2m3_scale_exp(float m) {
+  if (!(m > 0.f)) return 127;
+  const uint32_t mb = __float_as_uint(m);
+  const int q = (int)(mb >> 23) - 2 + ((mb & 0x7FFFFFu) > 0x700000u ? 1 : 0);
+  return min(max(q, 8), 254);
+}
+// v_cvt_scalef32_2xpk16_fp6_f32 (gfx950), measured on the GPU: code 2i is s0[i] / scale and
+// code 2i + 1 is s1[i] / scale, each rounded to the nearest E2M3 value (ties to even), packed
+// at bits 6 i of the six result dwords.  The instruction writes its result while it still
+// reads its sources, so the result must not share their registers (early clobber); as inline
+// assembly its neighbours get no hazard padding from the compiler, hence the s_nop on each side.
+static __device__ __forceinline__ u32x6 fp6_encode32(f32x16 s0, f32x16 s1, float scale) {
+  u32x6 r;
+  asm("s_nop 1\n\tv_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3\n\ts_nop 1"
+      : "=&v"(r) : "v"(s0), "v"(s1), "v"(scale));
+  return r;
+}
+// v_cvt_scalef32_pk32_f32_fp6: value i = E2M3 code i (bits 6 i) times scale, exactly.
+static __device__ __forceinline__ f32x32 fp6_decode32(u32x6 c, float scale) {
+  f32x32 r;
+  asm("s_nop 1\n\tv_cvt_scalef32_pk32_f32_fp6 %0, %1, %2\n\ts_nop 1" : "=&v"(r) : "v"(c), "v"(scale));
+  return r;
+}
+// Three E2M3 pieces of this lane's 16 values v (one half of a 32-element block whose other
+// half is in lane ^ 1): codes[pc] holds piece pc's 16 codes (value i at bits 6 i), byte pc of
+// the result its E8M0 scale; piece pc rounds what the earlier ones left.  v is consumed.
+static __device__ __forceinline__ uint32_t fp6_pieces16(float* v, uint32_t (*codes)[3]) {
+  uint32_t sc = 0;
+#pragma unroll
+  for (int pc = 0; pc < 3; ++pc) {
+    float m = 0.f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) m = fmaxf(m, fabsf(v[u]));
+    m = fmaxf(m, __shfl_xor(m, 1));
+    const int se = e2m3_scale_exp(m);
+    sc |= (uint32_t)se << (8 * pc);
+    const float scl = __uint_as_float((uint32_t)se << 23);
+    f32x16 s0, s1;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      s0[u] = u < 8 ? v[2 * u] : 0.f;
+      s1[u] = u < 8 ? v[2 * u + 1] : 0.f;
+    }
+    const u32x6 c = fp6_encode32(s0, s1, scl);
+    codes[pc][0] = c[0];
+    codes[pc][1] = c[1];
+    codes[pc][2] = c[2];
+    if (pc < 2) {
+      const f32x32 d = fp6_decode32(c, scl);
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] -= d[u];
+    }
+  }
+  return sc;
+}
+
 // ------------------------------------------------------------------------------ kernel
 // s_waitcnt needs an immediate: dispatch a wave-uniform count to the matching wait.
 static __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
@@ -329,7 +393,9 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   constexpr bool BT = FMT == 4 || FMT == 5;
   constexpr int WF = BT ? 0 : FMT;
   constexpr int FM = C::FM, FN = C::FN;
-  constexpr bool MX = FMT == 2;                             // scaled MFMA on fp8 pieces
+  constexpr bool MX = FMT == 2;                             // scaled MFMA on fp8/fp6 pieces
+  // its A operand format: E4M3 (0) for the pieces of x in mlp1, E2M3 (2) for those of h in mlp2
+  constexpr int ACB = MODE == 2 ? 2 : 0;
   constexpr bool DEC = FMT == 1 || FMT == 3;                // codes decoded to bf16 (MXFP4, MXFP8)
   constexpr int CBS = FMT == 3 ? 64 : 32;                   // code bytes per row and stage
   constexpr int KS = MX ? 1 : BK / 16;                      // MFMA K steps per stage
@@ -914,13 +980,13 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
     _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                             \
       if (pa == 0)                                                                               \
         ACC[i_][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                             \
-            (FA)[pa], (FB)[j], ACC[i_][j], 0, 4, 0, (int)(SA), 0, (int)(SB)[j]);                  \
+            (FA)[pa], (FB)[j], ACC[i_][j], ACB, 4, 0, (int)(SA), 0, (int)(SB)[j]);                  \
       else if (pa == 1)                                                                          \
         ACC[i_][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                             \
-            (FA)[pa], (FB)[j], ACC[i_][j], 0, 4, 1, (int)(SA), 0, (int)(SB)[j]);                  \
+            (FA)[pa], (FB)[j], ACC[i_][j], ACB, 4, 1, (int)(SA), 0, (int)(SB)[j]);                  \
       else                                                                                       \
         ACC[i_][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                             \
-            (FA)[pa], (FB)[j], ACC[i_][j], 0, 4, 2, (int)(SA), 0, (int)(SB)[j]);                  \
+            (FA)[pa], (FB)[j], ACC[i_][j], ACB, 4, 2, (int)(SA), 0, (int)(SB)[j]);                  \
     }                                                                                            \
   } while (0)
   if constexpr (!MX) {
@@ -1002,13 +1068,13 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
             const int pa = m_ / FN, j = m_ % FN;                                                 \
             if (pa == 0)                                                                         \
               ACC[(FA) - 1][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                \
-                  fap[pa], fbp[j], ACC[(FA) - 1][j], 0, 4, 0, (int)sap, 0, (int)sbp[j]);         \
+                  fap[pa], fbp[j], ACC[(FA) - 1][j], ACB, 4, 0, (int)sap, 0, (int)sbp[j]);         \
             else if (pa == 1)                                                                    \
               ACC[(FA) - 1][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                \
-                  fap[pa], fbp[j], ACC[(FA) - 1][j], 0, 4, 1, (int)sap, 0, (int)sbp[j]);         \
+                  fap[pa], fbp[j], ACC[(FA) - 1][j], ACB, 4, 1, (int)sap, 0, (int)sbp[j]);         \
             else                                                                                 \
               ACC[(FA) - 1][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                \
-                  fap[pa], fbp[j], ACC[(FA) - 1][j], 0, 4, 2, (int)sap, 0, (int)sbp[j]);         \
+                  fap[pa], fbp[j], ACC[(FA) - 1][j], ACB, 4, 2, (int)sap, 0, (int)sbp[j]);         \
           }                                                                                      \
           if (m_ < PW_G) {                                                                       \
             __builtin_amdgcn_sched_barrier(0);                                                   \
@@ -1157,9 +1223,10 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
         }
       }
       if constexpr (MX) {
-        // three fp8 pieces of each 32-element block of the rows, in the layout the
-        // matrix-core loop of mlp2 reads (the split kernel's): lane l takes half l & 1 of
-        // row l >> 1
+        // three fp6 (E2M3) pieces of each 32-element block of the rows: lane l takes half
+        // l & 1 of row l >> 1.  In the row's 192-byte record of a 64-wide K stage, piece pc
+        // of K block b holds its 32 codes in bytes 96 b + 32 pc .. + 23 (the bytes to + 31
+        // are not read), which is what a lane of mlp2's fragment loads for its K half
         const int r = lane >> 1, hh = lane & 1;
         const int rl = wm * C::WTM + i * 32 + r;
         const size_t row = (size_t)(gbase + rl);
@@ -1173,23 +1240,17 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
           v[4 * u] = w4[0]; v[4 * u + 1] = w4[1]; v[4 * u + 2] = w4[2]; v[4 * u + 3] = w4[3];
         }
         const bool st = rl < rows && f0 < p.F;
-        uint8_t* const dst = p.h8 + row * (size_t)(3 * p.F) + (f0 >> 6) * 192 + ((f0 >> 5) & 1) * 16 + hh * 96;
-        uint32_t sc = 0;
+        uint32_t* const dst = (uint32_t*)(p.h8 + row * (size_t)(3 * p.F) + (f0 >> 6) * 192 +
+                                          ((f0 >> 5) & 1) * 96 + hh * 12);
+        uint32_t codes[3][3];
+        const uint32_t sc = fp6_pieces16(v, codes);
+        if (st) {
 #pragma unroll
-        for (int pc = 0; pc < 3; ++pc) {
-          float m = 0.f;
-#pragma unroll
-          for (int u = 0; u < 16; ++u) m = fmaxf(m, fabsf(v[u]));
-          m = fmaxf(m, __shfl_xor(m, 1));
-          const int se = mx_scale_exp(m);
-          sc |= (uint32_t)se << (8 * pc);
-          const float inv = mx_inv_scale(se), scl = mx_scale(se);
-          uint4 o;
-          o.x = mx_piece4(v, inv, scl, pc < 2);
-          o.y = mx_piece4(v + 4, inv, scl, pc < 2);
-          o.z = mx_piece4(v + 8, inv, scl, pc < 2);
-          o.w = mx_piece4(v + 12, inv, scl, pc < 2);
-          if (st) *(uint4*)(dst + pc * 32) = o;
+          for (int pc = 0; pc < 3; ++pc) {
+            dst[8 * pc] = codes[pc][0];
+            dst[8 * pc + 1] = codes[pc][1];
+            dst[8 * pc + 2] = codes[pc][2];
+          }
         }
         if (st && hh == 0) p.h8s[row * p.h8s_stride + (f0 >> 5)] = sc;
         }
