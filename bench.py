@@ -34,7 +34,7 @@ METRIC = "MoE-layer tokens/sec + TFLOP/s (frac. of peak) at GPT-OSS-20B shape, b
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 matrix peak: the rate of the scaled fp8 x fp4 instruction
-FP4_PEAK_TFLOPS = 10100.0      # MI355X dense FP4 matrix peak (reported for MXFP4 weights only)
+FP4_PEAK_TFLOPS = 10100.0      # MI355X dense FP4/FP6 matrix peak: the rate of the scaled fp6 x fp4 instruction
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 GEMM_SRC = os.path.join(ROOT, "mixture_experts_transformer_amd", "csrc", "gemm.hip")
 
@@ -44,8 +44,9 @@ def log(msg):
 
 
 def mx_engine(cfg):
-    """True where the library runs the expert GEMMs on the scaled fp8 x fp4 instruction: MXFP4
-    weights with at least 128 routed rows per expert on average (its matrix-core tiles)."""
+    """True where the library runs the expert GEMMs on the scaled matrix instruction (fp8 pieces
+    of x times MXFP4 in mlp1, fp6 pieces of h times MXFP4 in mlp2): MXFP4 weights with at least
+    128 routed rows per expert on average (its matrix-core tiles)."""
     return cfg.fmt == "mxfp4" and cfg.T * cfg.k >= 128 * cfg.E
 
 
@@ -56,7 +57,9 @@ def algorithmic(cfg, counts):
     the router, x (bf16) and out (fp32).  Per kernel, mlp1 reads x (bf16; on the scaled
     engine its two fp8 pieces, the same two bytes per element) and writes h, mlp2 reads h
     and writes y (fp32); h is bf16 (bf16 weights), a bf16 pair (MXFP4, few rows) or three
-    fp8 pieces and one scale dword per 32 elements (scaled engine); MXFP8 weights are one
+    fp6 pieces (six bits each) and one scale dword per 32 elements (scaled engine; the
+    kernels keep each piece's 24 bytes per 32 elements in a 32-byte slot, the format's bytes
+    are what is counted); MXFP8 weights are one
     byte per element plus one scale byte per 32 and carry h as a bf16 pair.
     """
     T, D, E, k, F = cfg.T, cfg.D, cfg.E, cfg.k, cfg.F
@@ -70,7 +73,7 @@ def algorithmic(cfg, counts):
         w1_e, w2_e = 2 * F * (D // 2 + D // 32), D * (F // 2 + F // 32)
     b1_e, b2_e = 2 * F * 2, D * 2
     if mx_engine(cfg):
-        hbytes = A * (3 * F + ((F // 32 + 7) // 8 * 8) * 4)
+        hbytes = A * (3 * F * 6 // 8 + ((F // 32 + 7) // 8 * 8) * 4)
     else:
         hbytes = A * F * 2 * (1 if cfg.fmt == "bf16" else 2)
     flops = T * (2 * D * E + 6 * k * D * F)
@@ -205,10 +208,11 @@ def bench_workload(name, steps, warmup, with_cpu, library=False):
     tms, n = stages[dom]
     avg_s = tms / n / 1e3
     # the matrix instruction the kernel issues: bf16 (bf16 weights, or MXFP4 decoded to bf16
-    # at few rows per expert), or the scaled fp8 x fp4 one, which runs at the fp8 rate and
-    # issues each flop once per activation piece (x: 2, h: 3)
+    # at few rows per expert), or the scaled one, which issues each flop once per activation
+    # piece (x: 2 fp8 pieces in mlp1, at the fp8 rate; h: 3 fp6 pieces in mlp2, at the FP6/FP4
+    # rate)
     mx = mx_engine(cfg)
-    peak_t = FP8_PEAK_TFLOPS if mx else BF16_PEAK_TFLOPS
+    peak_t = (FP8_PEAK_TFLOPS if dom == "mlp1" else FP4_PEAK_TFLOPS) if mx else BF16_PEAK_TFLOPS
     pieces = (2 if dom == "mlp1" else 3) if mx else (2 if (cfg.fmt != "bf16" and dom == "mlp2") else 1)
     hbm_bound = alg[dom]["flops"] * pieces / alg[dom]["bytes"] < peak_t * 1e12 / (HBM_PEAK_GBS * 1e9)
     if hbm_bound:
@@ -220,8 +224,8 @@ def bench_workload(name, steps, warmup, with_cpu, library=False):
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_t, "unit": "TFLOP/s",
                 "frac": round(achieved / peak_t, 4)}
     roof["kernel"] = dom
-    roof["instruction"] = ("v_mfma_scale_f32_32x32x64_f8f6f4 (fp8 E4M3 activation pieces x MXFP4)" if mx
-                           else "v_mfma_f32_32x32x16_bf16")
+    roof["instruction"] = ((f"v_mfma_scale_f32_32x32x64_f8f6f4 ({'fp8 E4M3' if dom == 'mlp1' else 'fp6 E2M3'} "
+                            "activation pieces x MXFP4)") if mx else "v_mfma_f32_32x32x16_bf16")
     roof["issued_flop_per_algorithmic_flop"] = pieces
     roof["issued_frac"] = round(alg[dom]["flops"] * pieces / avg_s / 1e12 / peak_t, 4)
     roof["avg_launch_us"] = round(avg_s * 1e6, 2)
@@ -239,7 +243,7 @@ def bench_workload(name, steps, warmup, with_cpu, library=False):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8xfp4" if mx else "bf16",
+        "dtype": ("fp8xfp4" if dom == "mlp1" else "fp6xfp4") if mx else "bf16",
         "data": "synthetic",
         "config": {"workload": f"{name}: T={cfg.T} D={cfg.D} E={cfg.E} k={cfg.k} F={cfg.F} "
                                f"{cfg.fmt} expert weights ({cfg.note})",

@@ -50,10 +50,10 @@
  * Numerics: every product is accumulated in fp32 on the matrix cores except the
  * router (fp64).  The bf16 path rounds h to bf16 once.  With MXFP4 weights, small
  * token counts carry h as a bf16 pair (hi + lo, 16 significant bits) into mlp2;
- * large ones run both GEMMs on the scaled fp8 x fp4 matrix instructions, with x
- * as two and h as three fp8 pieces that share one power-of-two scale per 32
- * elements (x exactly but for values far below their block's largest; h to
- * about 12 significant bits of the block's largest).  The output is fp32
+ * large ones run both GEMMs on the scaled matrix instructions, with x as two fp8
+ * (E4M3) pieces times fp4 and h as three fp6 (E2M3) pieces times fp4, the pieces of
+ * each 32 elements sharing one power-of-two scale (x exactly but for values far below
+ * their block's largest; h to about 12 bits of the block's largest).  The output is fp32
  * and deterministic: no float atomics, fixed summation orders, bitwise equal
  * from run to run.
  *
@@ -261,7 +261,7 @@ void moe_release(void);
 /* Kernel timing (tracing): while enabled, every launch is bracketed by HIP events on the
  * call's stream, and each kernel's summed device time and launch count accumulate per
  * stage.  Stages: 0 router, 1 top-k, 2 permute, 3 mlp1, 4 mlp2, 5 combine, 6 split (the
- * fp8 pieces of the activations that the scaled matrix-core engine reads; MXFP4 weights
+ * fp8 pieces of x that the scaled matrix-core engine reads; MXFP4 weights
  * at large token counts only), 7 backward (a whole moe_backward call).  moe_profile_read
  * synchronises on the recorded events; it fills ms[8] and launches[8] (either may be NULL)
  * and resets the counters. */

@@ -65,7 +65,7 @@ static __device__ __forceinline__ bool tile_lookup(const TileScan& ts, const int
 
 // LDS layout of a bf16 operand stage: [rows][BK] with the 16-byte chunks of a row
 // XOR-swizzled by row bits, which spreads the rows one chunk index touches over the banks.
-// Rows of twelve chunks (three fp8 pieces of 64 elements) XOR the two low chunk bits with
+// Rows of twelve chunks (three 64-byte pieces of 64 elements) XOR the two low chunk bits with
 // row bits 2..3, which keeps a chunk inside its aligned group of four: the 16-byte slots
 // of sixteen consecutive rows (row stride 192 bytes) then cover all 64 banks once.
 template <int CPR>

@@ -31,9 +31,10 @@
 //   a single bf16 would cost the output its accuracy.
 //   Many rows per expert (matrix-core tiles): the scaled instruction
 //   v_mfma_scale_f32_32x32x64_f8f6f4 takes the codes as its fp4 B operand and the scale
-//   bytes as its B scales unchanged; the activations enter as fp8 E4M3 pieces with their
-//   own block scales (x: two pieces from the split kernel, h: three pieces written by
-//   mlp1's epilogue), so no weight is ever decoded.
+//   bytes as its B scales unchanged; the activations enter as pieces with their own
+//   block scales (x: two fp8 E4M3 pieces from the split kernel; h: three fp6 E2M3 pieces
+//   written by mlp1's epilogue, which the instruction multiplies at the FP6/FP4 rate), so
+//   no weight is ever decoded.
 //
 // MXFP8 weights (E4M3 elements with the same block scales; the torchtitan guide's grouped
 // GEMM section names MXFP8 converters as users of the scaled grouped-GEMM seam) are
@@ -90,8 +91,8 @@ template <int MODE, int FMT> using SmallTile =
 template <int MODE, int FMT> struct LargeTileSel {   // bf16 weights
   using type = Tile<256, 256, 2, 4, 2, 64, false>;
 };
-// the scaled-MFMA engine (fp8 activation pieces x MXFP4); mlp2 reads three pieces of h per
-// stage, so its code super-stage is halved to fit LDS
+// the scaled-MFMA engine (activation pieces x MXFP4); mlp2 reads three pieces of h per
+// stage (a 32-byte slot per piece and K half), so its code super-stage is halved to fit LDS
 template <> struct LargeTileSel<1, 2> {
   using type = Tile<256, 256, 2, 4, 2, 64, false, 4>;
 };
@@ -115,7 +116,8 @@ template <int MODE, int FMT> using LargeTile = typename LargeTileSel<MODE, FMT>:
 struct GemmArgs {
   const uint16_t* a;        // mlp1: x [T][K]; mlp2: h (hi) [A][K]
   const uint16_t* a_lo;     // mlp2 + MXFP4: h lo [A][K]
-  const uint8_t* a8;        // scaled-MFMA engine: fp8 pieces of the A rows [rows][K / 64][pieces][64]
+  const uint8_t* a8;        // scaled-MFMA engine: pieces of the A rows, 192 bytes per row and
+                            //   64-wide K stage (x: fp8 [K/64][2][64]; h: fp6 as in mlp1's epilogue)
   const uint32_t* a8s;      //   and their scales [rows][a8s_stride] (piece p in byte p)
   int a8s_stride;           //   scale dwords per row (K / 32 rounded up to a multiple of 8)
   const int32_t* perm;
@@ -127,7 +129,7 @@ struct GemmArgs {
   float* u_out;             // mlp1, bf16 weights: when set, the pre-activation u [A][2F] (fp32,
                             //   gate half then linear half) is stored instead of h
   uint16_t* h_lo;
-  uint8_t* h8;              // mlp1 output for the scaled-MFMA engine: three fp8 pieces of h
+  uint8_t* h8;              // mlp1 output for the scaled-MFMA engine: three fp6 pieces of h
   uint32_t* h8s;            //   and their scales
   int h8s_stride;
   float* y;                 // mlp2 output
@@ -399,7 +401,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   constexpr bool DEC = FMT == 1 || FMT == 3;                // codes decoded to bf16 (MXFP4, MXFP8)
   constexpr int CBS = FMT == 3 ? 64 : 32;                   // code bytes per row and stage
   constexpr int KS = MX ? 1 : BK / 16;                      // MFMA K steps per stage
-  // A parts: bf16 (1), h hi + lo (2), or fp8 pieces (x: 2, h: 3)
+  // A parts: bf16 (1), h hi + lo (2), or pieces (x: 2 fp8, h: 3 fp6)
   constexpr int AP = MX ? (MODE == 1 ? 2 : 3) : ((MODE == 2 && (DEC || FMT == 5)) ? 2 : 1);
   constexpr int ROWB = CPR * 16;                            // bytes per bf16 row segment
   constexpr int APL = MX ? 1 : AP;                          // A parts in LDS (pieces share rows)

@@ -52,9 +52,10 @@ struct ExpertArgs {
   const int32_t* perm;      // [A]
   uint16_t* h;              // [A][F] bf16 (hi part for MXFP4)
   uint16_t* h_lo;           // [A][F] bf16 low part (MXFP4 only)
-  // scaled-MFMA engine (h and h_lo unused): fp8 pieces of x (two) and of h (three), each
-  // row stored as 64-element groups of 64 bytes per piece, and their scales, one dword per
-  // row and 32-element block (piece p in byte p), mx_scale_stride(K) dwords per row
+  // scaled-MFMA engine (h and h_lo unused): fp8 pieces of x (two; each row as 64-element
+  // groups of 64 bytes per piece) and fp6 pieces of h (three; each row as 64-element groups
+  // of 192 bytes, piece p of K half b in bytes 96 b + 32 p .. + 23), and their scales, one
+  // dword per row and 32-element block (piece p in byte p), mx_scale_stride(K) dwords per row
   uint8_t* xq;              // [T][2 D]
   uint32_t* xs;             // [T][mx_scale_stride(D)]
   uint8_t* hq;              // [A][3 F]
@@ -74,7 +75,7 @@ struct ExpertArgs {
 int expert_tile_config(int64_t A, int64_t E);
 // Whether the expert GEMMs run on the scaled matrix-core engine (MXFP4 weights,
 // matrix-core tiles): mlp1 then reads x as fp8 pieces written by launch_mx_split and
-// writes h as fp8 pieces, which mlp2 reads.
+// writes h as fp6 pieces, which mlp2 reads.
 bool mx_engine(int fmt, int cfg);
 // Scale dwords per row of the pieces of a K-wide row (K / 32 rounded up to a multiple of 8).
 int mx_scale_stride(int K);
