@@ -120,6 +120,11 @@ extern "C" {
  *            fmt 2: MXFP8 buffer (codes [E][D][F], scales [E][D][F/32])
  *   b2       bf16 [E][D]
  *   out      fp32 [T][D] (written)
+ * Ordering is that of the calling thread's stream.  With MXFP4 weights at many routed rows
+ * per expert (the scaled matrix-core engine) and outside graph capture, the split of x into
+ * fp8 pieces runs beside the routing on the calling thread's second stream (the one
+ * moe_backward uses), which waits for the calling stream's earlier work and which the
+ * calling stream waits for before mlp1; under capture it runs on the calling stream.
  */
 int moe_forward(const void* x, const void* router_w, const void* router_b,
                 const void* w1, const void* b1, const void* w2, const void* b2,
@@ -253,7 +258,8 @@ int moe_set_workspace(void* dev_ptr, size_t bytes);
 const char* moe_last_error(void);
 
 /* Free the library-owned workspace (with the buffers kept for captured graphs), the
- * profiling events and the calling thread's backward side stream, and return the calling
+ * profiling events and the calling thread's second stream (forward split, backward side
+ * work), and return the calling
  * thread to the library-owned workspace.  Must not run while work that uses the workspace is
  * queued or a captured graph may still replay. */
 void moe_release(void);

@@ -47,8 +47,9 @@ struct ScratchTable {
 };
 ScratchTable g_scratch;
 
-// The backward's second stream and its join events, per thread (created on first use on the
-// thread's current device, default priority, non-blocking; destroyed by moe_release).
+// A second stream and its join events, per thread (created on first use on the thread's
+// current device, default priority, non-blocking; destroyed by moe_release): the backward's
+// side products, and the forward's split of x into fp8 pieces beside the routing.
 struct SideStream {
   moe::BwdSide side{};
   int device = -1;
@@ -260,10 +261,10 @@ int ensure_workspace(size_t bytes, uint8_t** base) {
   return MOE_OK;
 }
 
-// Launch wrapper: optional event bracketing, error translation.
+// Launch wrapper: optional event bracketing (on the stream the kernel runs on), error
+// translation.
 template <class F>
-int launch(int stage, const char* name, F&& fn) {
-  hipStream_t st = g_stream;
+int launch_on(hipStream_t st, int stage, const char* name, F&& fn) {
   hipEvent_t a = nullptr, b = nullptr;
   bool prof = false;
   {
@@ -305,6 +306,41 @@ int launch(int stage, const char* name, F&& fn) {
   }
   return MOE_OK;
 }
+template <class F>
+int launch(int stage, const char* name, F&& fn) {
+  return launch_on(g_stream, stage, name, fn);
+}
+
+// The calling thread's side stream on the current device (made on first use), or null when
+// the calling stream is capturing a graph: a capture stays on the one stream.
+int side_stream(const moe::BwdSide** out) {
+  *out = nullptr;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (g_stream && hipStreamIsCapturing(g_stream, &cs) != hipSuccess)
+    return fail(MOE_EHIP, "hipStreamIsCapturing failed");
+  if (cs != hipStreamCaptureStatusNone) return MOE_OK;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(MOE_EHIP, "hipGetDevice failed");
+  if (t_side.made && t_side.device != dev) drop_side();
+  if (!t_side.made) {
+    SideStream n;
+    bool good = hipStreamCreateWithFlags(&n.side.stream, hipStreamNonBlocking) == hipSuccess;
+    int made_ev = 0;
+    for (; good && made_ev < 5; ++made_ev)
+      good = hipEventCreateWithFlags(&n.side.ev[made_ev], hipEventDisableTiming) == hipSuccess;
+    if (!good) {
+      (void)hipGetLastError();
+      if (n.side.stream) (void)hipStreamDestroy(n.side.stream);
+      for (int i = 0; i + 1 < made_ev; ++i) (void)hipEventDestroy(n.side.ev[i]);
+      return fail(MOE_EHIP, "creating the side stream failed");
+    }
+    n.device = dev;
+    n.made = true;
+    t_side = n;
+  }
+  *out = &t_side.side;
+  return MOE_OK;
+}
 
 // router -> top-k -> grouping
 int run_route(uint8_t* ws, const Layout& L, const void* x, const void* router_w, const void* router_b,
@@ -328,7 +364,7 @@ int run_route(uint8_t* ws, const Layout& L, const void* x, const void* router_w,
 int run_experts(const uint8_t* ws, const Layout& L, const void* x, const void* w1, const void* b1,
                 const void* w2, const void* b2, const float* gates, const int32_t* offsets,
                 const int32_t* perm, int64_t T, int64_t D, int64_t E, int64_t k, int64_t F, int fmt,
-                float* out) {
+                float* out, bool split_done = false) {
   moe::ExpertArgs ea{};
   ea.x = (const uint16_t*)x;
   ea.w1 = w1;
@@ -348,7 +384,7 @@ int run_experts(const uint8_t* ws, const Layout& L, const void* x, const void* w
   ea.out = out;
   ea.T = (int)T; ea.D = (int)D; ea.E = (int)E; ea.k = (int)k; ea.F = (int)F; ea.fmt = fmt;
   const int cfg = moe::expert_tile_config(T * k, E);
-  if (moe::mx_engine(fmt, cfg))
+  if (moe::mx_engine(fmt, cfg) && !split_done)
     CHECK(launch(moe::ST_SPLIT, "split", [&](hipStream_t st) {
       return moe::launch_mx_split(ea.x, T, (int)D, ea.xq, ea.xs, st);
     }));
@@ -411,8 +447,25 @@ int forward_impl(const void* x, const void* router_w, const void* router_b, bool
   int32_t* counts = (int32_t*)(ws + L.counts);
   int32_t* offsets = (int32_t*)(ws + L.offsets);
   int32_t* perm = (int32_t*)(ws + L.perm);
+  // On the scaled engine the split of x into fp8 pieces needs only x: it runs on the side
+  // stream beside the routing, after everything queued before the call, and mlp1 waits for
+  // it (not under graph capture, nor in the allocation-free entry point: there one stream).
+  const moe::BwdSide* side = nullptr;
+  if (!noalloc && moe::mx_engine(fmt, moe::expert_tile_config(T * k, E))) CHECK(side_stream(&side));
+  if (side) {
+    if (hipEventRecord(side->ev[0], g_stream) != hipSuccess ||
+        hipStreamWaitEvent(side->stream, side->ev[0], 0) != hipSuccess)
+      return fail(MOE_EHIP, "forking the split onto the side stream failed");
+    CHECK(launch_on(side->stream, moe::ST_SPLIT, "split", [&](hipStream_t st) {
+      return moe::launch_mx_split((const uint16_t*)x, (int)T, (int)D, (uint8_t*)(ws + L.xq), (uint32_t*)(ws + L.xs), st);
+    }));
+    if (hipEventRecord(side->ev[1], side->stream) != hipSuccess)
+      return fail(MOE_EHIP, "recording the split's event failed");
+  }
   CHECK(run_route(ws, L, x, router_w, router_b, ebias, T, D, E, k, nullptr, idx, gates, counts, offsets, perm));
-  CHECK(run_experts(ws, L, x, w1, b1, w2, b2, gates, offsets, perm, T, D, E, k, F, fmt, out));
+  if (side && hipStreamWaitEvent(g_stream, side->ev[1], 0) != hipSuccess)
+    return fail(MOE_EHIP, "joining the split failed");
+  CHECK(run_experts(ws, L, x, w1, b1, w2, b2, gates, offsets, perm, T, D, E, k, F, fmt, out, side != nullptr));
   return ok();
 }
 
@@ -581,31 +634,7 @@ int moe_backward(const void* x, const void* router_w, const void* w1, const void
   // expert: measured at 8192 tokens -2.4 %; at 256 the joins cost more than the overlap
   // gains, +1.8 %), and never under graph capture (there the calling stream runs it all)
   const moe::BwdSide* side = nullptr;
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  if (g_stream && hipStreamIsCapturing(g_stream, &cs) != hipSuccess)
-    return fail(MOE_EHIP, "hipStreamIsCapturing failed");
-  if (cs == hipStreamCaptureStatusNone && moe::expert_tile_config(T * k, E) != 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return fail(MOE_EHIP, "hipGetDevice failed");
-    if (t_side.made && t_side.device != dev) drop_side();
-    if (!t_side.made) {
-      SideStream n;
-      bool good = hipStreamCreateWithFlags(&n.side.stream, hipStreamNonBlocking) == hipSuccess;
-      int made_ev = 0;
-      for (; good && made_ev < 5; ++made_ev)
-        good = hipEventCreateWithFlags(&n.side.ev[made_ev], hipEventDisableTiming) == hipSuccess;
-      if (!good) {
-        (void)hipGetLastError();
-        if (n.side.stream) (void)hipStreamDestroy(n.side.stream);
-        for (int i = 0; i + 1 < made_ev; ++i) (void)hipEventDestroy(n.side.ev[i]);
-        return fail(MOE_EHIP, "creating the backward's side stream failed");
-      }
-      n.device = dev;
-      n.made = true;
-      t_side = n;
-    }
-    side = &t_side.side;
-  }
+  if (moe::expert_tile_config(T * k, E) != 0) CHECK(side_stream(&side));
   CHECK(launch(moe::ST_BACKWARD, "backward", [&](hipStream_t st) { return moe::launch_backward(b, st, side); }));
   return ok();
 }
