@@ -71,6 +71,36 @@ def test_forward_large_sampled(name, n):
     assert_close(got[sample], ref, f"forward {name} ({sample.size} sampled tokens)")
 
 
+def test_forward_split_stream_follows_the_calling_stream():
+    """On the scaled engine the forward forks the split of x into fp8 pieces onto a second
+    stream beside the routing and joins it before mlp1.  Against the oracle on every output;
+    then on a non-default stream whose x is written by that stream just before the call (the
+    fork must wait for it), and again after moe_release has destroyed the second stream, it
+    gives the default stream's output bit for bit."""
+    cfg = get_config("C4", name="fwd-stream", T=700, D=256, F=256, E=8, k=4, seed=8109)
+    assert cfg.fmt == "mxfp4" and cfg.T * cfg.k >= 128 * cfg.E   # the scaled engine's regime
+    inp = make_inputs(cfg)
+    d = upload(inp)
+    note("forward with the split on the second stream: default stream, caller stream, after release")
+    ref = forward(inp, d).clone()
+    want = oracle.moe_forward(inp.x, inp.wr, inp.br, inp.w1, inp.b1, inp.w2, inp.b2, k=cfg.k, F=cfg.F, fmt=cfg.fmt)
+    assert_close(ref.cpu().numpy(), want, "forward, split on the second stream")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            x2 = torch.zeros_like(d["x"])
+            x2.copy_(d["x"])                         # written on the calling stream just before
+            out = moe.forward(x2, d["router_w"], d["router_b"], d["w1"], d["b1"], d["w2"], d["b2"],
+                              cfg.k, cfg.fmt)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    moe.release()
+    again = forward(inp, d)
+    assert torch.equal(again, ref)
+
+
 @pytest.mark.parametrize("name", ["C2", "C3", "C4", "C5", "X1", "X2", "Y2"])
 def test_forward_is_bitwise_deterministic(name):
     inp = make_inputs(name)
