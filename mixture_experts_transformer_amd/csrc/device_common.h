@@ -68,8 +68,12 @@ static __device__ __forceinline__ bool tile_lookup(const TileScan& ts, const int
 // Rows of twelve chunks (three 64-byte pieces of 64 elements) XOR the two low chunk bits with
 // row bits 2..3, which keeps a chunk inside its aligned group of four: the 16-byte slots
 // of sixteen consecutive rows (row stride 192 bytes) then cover all 64 banks once.
+// Rows of nine chunks (144 bytes: three fp6 pieces of 64 elements) are not swizzled: at a
+// row stride of 36 dwords the 8-byte reads of sixteen consecutive rows already fall on
+// distinct banks.
 template <int CPR>
 static __device__ __forceinline__ int swz_pos(int r, int c) {
+  if (CPR == 9) return c;
   if (CPR == 8) return c ^ (r & 7) ^ ((r >> 3) & 1);
   if (CPR == 12) return c ^ ((r >> 2) & 3);
   return c ^ ((r >> 1) & 3) ^ ((r >> 3) & 1);

@@ -92,7 +92,7 @@ template <int MODE, int FMT> struct LargeTileSel {   // bf16 weights
   using type = Tile<256, 256, 2, 4, 2, 64, false>;
 };
 // the scaled-MFMA engine (activation pieces x MXFP4); mlp2 reads three pieces of h per
-// stage (a 32-byte slot per piece and K half), so its code super-stage is halved to fit LDS
+// stage, so its code super-stage is halved to fit LDS
 template <> struct LargeTileSel<1, 2> {
   using type = Tile<256, 256, 2, 4, 2, 64, false, 4>;
 };
@@ -116,8 +116,8 @@ template <int MODE, int FMT> using LargeTile = typename LargeTileSel<MODE, FMT>:
 struct GemmArgs {
   const uint16_t* a;        // mlp1: x [T][K]; mlp2: h (hi) [A][K]
   const uint16_t* a_lo;     // mlp2 + MXFP4: h lo [A][K]
-  const uint8_t* a8;        // scaled-MFMA engine: pieces of the A rows, 192 bytes per row and
-                            //   64-wide K stage (x: fp8 [K/64][2][64]; h: fp6 as in mlp1's epilogue)
+  const uint8_t* a8;        // scaled-MFMA engine: pieces of the A rows per 64-wide K stage
+                            //   (x: fp8 [K/64][2][64], 128 bytes; h: fp6, 144 bytes as in mlp1's epilogue)
   const uint32_t* a8s;      //   and their scales [rows][a8s_stride] (piece p in byte p)
   int a8s_stride;           //   scale dwords per row (K / 32 rounded up to a multiple of 8)
   const int32_t* perm;
@@ -405,7 +405,10 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
   constexpr int AP = MX ? (MODE == 1 ? 2 : 3) : ((MODE == 2 && (DEC || FMT == 5)) ? 2 : 1);
   constexpr int ROWB = CPR * 16;                            // bytes per bf16 row segment
   constexpr int APL = MX ? 1 : AP;                          // A parts in LDS (pieces share rows)
-  constexpr int A_CPR = MX ? 4 * AP : CPR;                  // 16-byte chunks per A row per stage
+  // scaled engine, mlp2: h as three fp6 pieces packed into 144 bytes per row and stage (24
+  // bytes per piece and K half)
+  constexpr bool HC = MX && MODE == 2;
+  constexpr int A_CPR = MX ? (HC ? 9 : 4 * AP) : CPR;     // 16-byte chunks per A row per stage
   constexpr int A_ROWB = A_CPR * 16;
   constexpr int A_CPC = BM * A_CPR / 64;                    // A copies per part and stage
   constexpr int A_BYTES = BM * A_ROWB;                      // per A part per stage
@@ -642,7 +645,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
       const int r = idx / A_CPR;
       const int c = swz_pos<A_CPR>(r, idx % A_CPR);        // logical chunk at this position
       if (MX) {
-        goff[j] = (uint32_t)(a_row(r) * (size_t)(AP * K) + c * 16);
+        goff[j] = (uint32_t)(a_row(r) * (size_t)(HC ? 9 * K / 4 : AP * K) + c * 16);
       } else {
         goff[j] = (uint32_t)((a_row(r) * K + c * 8) * 2);
       }
@@ -964,14 +967,25 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
     if (nk > 0) MOE_MMA((KS - 1) & 1, FA, ACC);                                                  \
   } while (0)
   // scaled-MFMA engine: the A pieces of row block i_ (this lane's row, its two chunks per
-  // piece) from the stage at sa
+  // piece; fp6 pieces of h: the 24 bytes of the piece for this lane's K half, the operand's
+  // six dwords, in three 8-byte reads) from the stage at sa
 #define MX_LOAD_A(dst, i_)                                                                       \
   do {                                                                                           \
     _Pragma("unroll") for (int pa = 0; pa < AP; ++pa) {                                          \
       const int r_ = arow0 + 32 * (i_);                                                          \
-      const i32x4 lo_ = *(const i32x4*)(sa + swz<A_CPR>(r_, 2 * AP * kg + 2 * pa));              \
-      const i32x4 hi_ = *(const i32x4*)(sa + swz<A_CPR>(r_, 2 * AP * kg + 2 * pa + 1));          \
-      (dst)[pa] = __builtin_shufflevector(lo_, hi_, 0, 1, 2, 3, 4, 5, 6, 7);                     \
+      if (HC) {                                                                                  \
+        const uint8_t* f_ = sa + r_ * A_ROWB + 72 * kg + 24 * pa;                                \
+        const i32x2 d0_ = *(const i32x2*)(f_);                                                   \
+        const i32x2 d1_ = *(const i32x2*)(f_ + 8);                                               \
+        const i32x2 d2_ = *(const i32x2*)(f_ + 16);                                              \
+        const i32x4 d01_ = __builtin_shufflevector(d0_, d1_, 0, 1, 2, 3);                        \
+        const i32x4 d2x_ = __builtin_shufflevector(d2_, d2_, 0, 1, -1, -1);                      \
+        (dst)[pa] = __builtin_shufflevector(d01_, d2x_, 0, 1, 2, 3, 4, 5, -1, -1);               \
+      } else {                                                                                   \
+        const i32x4 lo_ = *(const i32x4*)(sa + swz<A_CPR>(r_, 2 * AP * kg + 2 * pa));            \
+        const i32x4 hi_ = *(const i32x4*)(sa + swz<A_CPR>(r_, 2 * AP * kg + 2 * pa + 1));        \
+        (dst)[pa] = __builtin_shufflevector(lo_, hi_, 0, 1, 2, 3, 4, 5, 6, 7);                   \
+      }                                                                                          \
     }                                                                                            \
   } while (0)
   // the scale dword of this lane's row and K block holds piece pa's scale in byte pa,
@@ -1226,9 +1240,9 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
       }
       if constexpr (MX) {
         // three fp6 (E2M3) pieces of each 32-element block of the rows: lane l takes half
-        // l & 1 of row l >> 1.  In the row's 192-byte record of a 64-wide K stage, piece pc
-        // of K block b holds its 32 codes in bytes 96 b + 32 pc .. + 23 (the bytes to + 31
-        // are not read), which is what a lane of mlp2's fragment loads for its K half
+        // l & 1 of row l >> 1.  In the row's 144-byte record of a 64-wide K stage, the 24
+        // bytes of piece pc of K block b (its 32 codes) are bytes 72 b + 24 pc .. + 23: what
+        // a lane of mlp2's fragment loads for its K half; a lane writes 12 of them
         const int r = lane >> 1, hh = lane & 1;
         const int rl = wm * C::WTM + i * 32 + r;
         const size_t row = (size_t)(gbase + rl);
@@ -1242,16 +1256,16 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
           v[4 * u] = w4[0]; v[4 * u + 1] = w4[1]; v[4 * u + 2] = w4[2]; v[4 * u + 3] = w4[3];
         }
         const bool st = rl < rows && f0 < p.F;
-        uint32_t* const dst = (uint32_t*)(p.h8 + row * (size_t)(3 * p.F) + (f0 >> 6) * 192 +
-                                          ((f0 >> 5) & 1) * 96 + hh * 12);
+        uint32_t* const dst = (uint32_t*)(p.h8 + row * (size_t)(9 * p.F / 4) + (f0 >> 6) * 144 +
+                                          ((f0 >> 5) & 1) * 72 + hh * 12);
         uint32_t codes[3][3];
         const uint32_t sc = fp6_pieces16(v, codes);
         if (st) {
 #pragma unroll
           for (int pc = 0; pc < 3; ++pc) {
-            dst[8 * pc] = codes[pc][0];
-            dst[8 * pc + 1] = codes[pc][1];
-            dst[8 * pc + 2] = codes[pc][2];
+            dst[6 * pc] = codes[pc][0];
+            dst[6 * pc + 1] = codes[pc][1];
+            dst[6 * pc + 2] = codes[pc][2];
           }
         }
         if (st && hh == 0) p.h8s[row * p.h8s_stride + (f0 >> 5)] = sc;

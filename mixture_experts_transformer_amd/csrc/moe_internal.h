@@ -14,6 +14,7 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 enum Stage {
   ST_ROUTER = 0, ST_TOPK = 1, ST_PERMUTE = 2, ST_MLP1 = 3, ST_MLP2 = 4, ST_COMBINE = 5, ST_SPLIT = 6,
@@ -54,7 +55,8 @@ struct ExpertArgs {
   uint16_t* h_lo;           // [A][F] bf16 low part (MXFP4 only)
   // scaled-MFMA engine (h and h_lo unused): fp8 pieces of x (two; each row as 64-element
   // groups of 64 bytes per piece) and fp6 pieces of h (three; each row as 64-element groups
-  // of 192 bytes, piece p of K half b in bytes 96 b + 32 p .. + 23), and their scales, one
+  // of 144 bytes, piece p of K half b in bytes 72 b + 24 p .. + 23;
+  // rows 9 F / 4 bytes apart, in a buffer of 3 F bytes per row), and their scales, one
   // dword per row and 32-element block (piece p in byte p), mx_scale_stride(K) dwords per row
   uint8_t* xq;              // [T][2 D]
   uint32_t* xs;             // [T][mx_scale_stride(D)]
