@@ -122,9 +122,10 @@ extern "C" {
  *   out      fp32 [T][D] (written)
  * Ordering is that of the calling thread's stream.  With MXFP4 weights at many routed rows
  * per expert (the scaled matrix-core engine) and outside graph capture, the split of x into
- * fp8 pieces runs beside the routing on the calling thread's second stream (the one
- * moe_backward uses), which waits for the calling stream's earlier work and which the
- * calling stream waits for before mlp1; under capture it runs on the calling stream.
+ * fp8 pieces runs beside the top-k and the grouping on the calling thread's second stream
+ * (the one moe_backward uses), which waits for the calling stream's earlier work (through
+ * the router) and which the calling stream waits for before mlp1; under capture it runs on
+ * the calling stream.
  */
 int moe_forward(const void* x, const void* router_w, const void* router_b,
                 const void* w1, const void* b1, const void* w2, const void* b2,

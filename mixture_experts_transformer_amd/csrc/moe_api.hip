@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <cmath>
+#include <functional>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -342,16 +343,18 @@ int side_stream(const moe::BwdSide** out) {
   return MOE_OK;
 }
 
-// router -> top-k -> grouping
+// router -> top-k -> grouping; after_router (if any) runs once the router is queued
 int run_route(uint8_t* ws, const Layout& L, const void* x, const void* router_w, const void* router_b,
               const float* ebias, int64_t T, int64_t D, int64_t E, int64_t k, float* logits, int32_t* idx,
-              float* gates, int32_t* counts, int32_t* offsets, int32_t* perm) {
+              float* gates, int32_t* counts, int32_t* offsets, int32_t* perm,
+              const std::function<int()>& after_router = nullptr) {
   double* partial = (double*)(ws + L.partial);
   const int ks = moe::router_ksplit(T, D);
   CHECK(launch(moe::ST_ROUTER, "router", [&](hipStream_t st) {
     return moe::launch_router_partial((const uint16_t*)x, (const uint16_t*)router_w, (int)T, (int)D, (int)E, ks,
                                       partial, st);
   }));
+  if (after_router) CHECK(after_router());
   CHECK(launch(moe::ST_TOPK, "topk", [&](hipStream_t st) {
     return moe::launch_topk(partial, ks, (const uint16_t*)router_b, ebias, (int)T, (int)E, (int)k, logits, idx,
                             gates, st);
@@ -448,11 +451,13 @@ int forward_impl(const void* x, const void* router_w, const void* router_b, bool
   int32_t* offsets = (int32_t*)(ws + L.offsets);
   int32_t* perm = (int32_t*)(ws + L.perm);
   // On the scaled engine the split of x into fp8 pieces needs only x: it runs on the side
-  // stream beside the routing, after everything queued before the call, and mlp1 waits for
-  // it (not under graph capture, nor in the allocation-free entry point: there one stream).
+  // stream beside the top-k and the grouping (latency-bound launches that leave most of the
+  // GPU idle; beside the router, which fills it, it slowed the router more than it saved),
+  // after everything queued before it, and mlp1 waits for it (not under graph capture, nor
+  // in the allocation-free entry point: there one stream).
   const moe::BwdSide* side = nullptr;
   if (!noalloc && moe::mx_engine(fmt, moe::expert_tile_config(T * k, E))) CHECK(side_stream(&side));
-  if (side) {
+  auto fork_split = [&]() -> int {
     if (hipEventRecord(side->ev[0], g_stream) != hipSuccess ||
         hipStreamWaitEvent(side->stream, side->ev[0], 0) != hipSuccess)
       return fail(MOE_EHIP, "forking the split onto the side stream failed");
@@ -461,8 +466,10 @@ int forward_impl(const void* x, const void* router_w, const void* router_b, bool
     }));
     if (hipEventRecord(side->ev[1], side->stream) != hipSuccess)
       return fail(MOE_EHIP, "recording the split's event failed");
-  }
-  CHECK(run_route(ws, L, x, router_w, router_b, ebias, T, D, E, k, nullptr, idx, gates, counts, offsets, perm));
+    return MOE_OK;
+  };
+  CHECK(run_route(ws, L, x, router_w, router_b, ebias, T, D, E, k, nullptr, idx, gates, counts, offsets, perm,
+                  side ? std::function<int()>(fork_split) : std::function<int()>()));
   if (side && hipStreamWaitEvent(g_stream, side->ev[1], 0) != hipSuccess)
     return fail(MOE_EHIP, "joining the split failed");
   CHECK(run_experts(ws, L, x, w1, b1, w2, b2, gates, offsets, perm, T, D, E, k, F, fmt, out, side != nullptr));
