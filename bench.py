@@ -57,9 +57,8 @@ def algorithmic(cfg, counts):
     the router, x (bf16) and out (fp32).  Per kernel, mlp1 reads x (bf16; on the scaled
     engine its two fp8 pieces, the same two bytes per element) and writes h, mlp2 reads h
     and writes y (fp32); h is bf16 (bf16 weights), a bf16 pair (MXFP4, few rows) or three
-    fp6 pieces (six bits each) and one scale dword per 32 elements (scaled engine; the
-    kernels keep each piece's 24 bytes per 32 elements in a 32-byte slot, the format's bytes
-    are what is counted); MXFP8 weights are one
+    fp6 pieces (six bits each) and one scale dword per 32 elements (scaled engine); MXFP8
+    weights are one
     byte per element plus one scale byte per 32 and carry h as a bf16 pair.
     """
     T, D, E, k, F = cfg.T, cfg.D, cfg.E, cfg.k, cfg.F
