@@ -539,12 +539,13 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void grouped_gemm_kernel(GemmAr
     const int xl = blockIdx.x >> 3;
     const int lin = (blockIdx.x & 7) * share + xl;
     if (xl >= share || lin >= total) return;
-    // row tiles per group: 1 for the forward's mlp2 (bf16 and scaled engine) and the scaled
-    // engine's mlp1, whose column tiles of one row tile then run side by side and read each
-    // stage of its A rows as one (measured: mlp2 C3 -4.5 %, X2 -2 %, C5 -1 %; scaled mlp1 X2
-    // -3.8 %, C5 -0.9 %); 8 for the bf16 mlp1 (C3 -1.3 % against 4; +3 % with 1, +1.5 %
-    // with 2, -1 % with 16); 4 elsewhere
-    constexpr int GM = ((MODE == 2 && (FMT == 0 || FMT == 2)) || (MODE == 1 && FMT == 2)) ? 1
+    // row tiles per group: 1 for the forward's mlp2 (bf16 and scaled engine), the backward's
+    // products of the same kind (formats 4, 5) and the scaled engine's mlp1, whose column
+    // tiles of one row tile then run side by side and read each stage of its A rows as one
+    // (measured: mlp2 C3 -4.5 %, X2 -2 %, C5 -1 %; scaled mlp1 X2 -3.8 %, C5 -0.9 %; C3
+    // backward -0.7 %); 8 for the bf16 mlp1 (C3 -1.3 % against 4; +3 % with 1, +1.5 % with 2,
+    // -1 % with 16); 4 elsewhere
+    constexpr int GM = ((MODE == 2 && FMT != 3) || (MODE == 1 && FMT == 2)) ? 1
                        : (MODE == 1 && FMT == 0) ? 8 : 4;
     const int gsize = GM * p.n_tiles;
     const int g = lin / gsize;
