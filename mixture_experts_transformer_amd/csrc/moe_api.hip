@@ -451,8 +451,8 @@ int forward_impl(const void* x, const void* router_w, const void* router_b, bool
   int32_t* offsets = (int32_t*)(ws + L.offsets);
   int32_t* perm = (int32_t*)(ws + L.perm);
   // On the scaled engine the split of x into fp8 pieces needs only x: it runs on the side
-  // stream beside the top-k and the grouping (latency-bound launches that leave most of the
-  // GPU idle; beside the router, which fills it, it slowed the router more than it saved),
+  // stream beside the top-k and the grouping (forked after the router, which fills the GPU;
+  // forked before it, the split slowed the router by as much as it slows the top-k here),
   // after everything queued before it, and mlp1 waits for it (not under graph capture, nor
   // in the allocation-free entry point: there one stream).
   const moe::BwdSide* side = nullptr;
