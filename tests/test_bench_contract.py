@@ -44,6 +44,28 @@ def test_algorithmic_work_of_the_20b_layer(name, fmt_bytes_per_expert):
     assert bench.algorithmic(cfg, counts2)["bytes"] == alg["bytes"] - fmt_bytes_per_expert
 
 
+@pytest.mark.parametrize("name,h_bytes_per_row", [
+    ("C2", 2880 * 2),                  # h in bf16
+    ("X1", 2880 * 4),                  # MXFP4 at few rows per expert: h as a bf16 pair
+    ("X2", 2880 * 6 * 3 // 8 + 96 * 4),  # scaled engine: three fp6 pieces, a scale dword per 32 (96 per row)
+])
+def test_per_kernel_bytes_of_the_20b_layer(name, h_bytes_per_row):
+    """The bytes each grouped GEMM's roofline divides by: its touched experts' weights and
+    biases, what it reads of the activations and what it writes (mlp1: x in bf16 and h; mlp2:
+    h and the fp32 slot rows), with h in the representation the kernels use."""
+    cfg = get_config(name)
+    counts = np.full(cfg.E, cfg.T * cfg.k // cfg.E)
+    alg = bench.algorithmic(cfg, counts)
+    assert bench.mx_engine(cfg) == (name == "X2")
+    rows = cfg.T * 4                   # routed rows, top-4
+    w1 = alg["mlp1"]["unit_bytes"]
+    w2 = alg["mlp2"]["unit_bytes"]
+    assert alg["mlp1"]["bytes"] == 32 * w1 + cfg.T * 2880 * 2 + rows * h_bytes_per_row
+    assert alg["mlp2"]["bytes"] == 32 * w2 + rows * h_bytes_per_row + rows * 2880 * 4
+    assert alg["mlp1"]["flops"] == 4 * rows * 2880 * 2880
+    assert alg["mlp2"]["flops"] == 2 * rows * 2880 * 2880
+
+
 def test_stored_traffic_goes_stale_when_the_kernel_source_changes(tmp_path, monkeypatch):
     src = tmp_path / "gemm.hip"
     src.write_text("int a; // one comment\n/* block\ncomment */\nint b;\n")
