@@ -1,8 +1,9 @@
 """GPU moe_forward end to end vs the oracle, at every workload's full size.
 
-Small workloads are compared on every output.  At the large ones the integer routing is
-compared in full (through moe_route, same kernels as moe_forward) and the fp32 output on a
-sample of tokens the oracle evaluates on its own: a token's output depends only on its
+Every workload is compared on every output (the large ones in test_forward_large_full).
+At the large ones the integer routing is also compared in full (through moe_route, same
+kernels as moe_forward) and the fp32 output on a sample of tokens the oracle evaluates on
+its own: a token's output depends only on its
 own row, so the oracle runs the block on the sampled rows alone.  The C5 sample takes, for
 every live expert, the first token routed to it, plus random tokens, so every expert's tiles
 (the Zipf head, the middle and the tail, on the scaled matrix-core engine) are compared."""
@@ -69,6 +70,19 @@ def test_forward_large_sampled(name, n):
     got = out.cpu().numpy()
     assert np.all(np.isfinite(got))
     assert_close(got[sample], ref, f"forward {name} ({sample.size} sampled tokens)")
+
+
+@pytest.mark.parametrize("name", ["C3", "C4", "X2", "C5", "Y2"])
+def test_forward_large_full(name):
+    """The large workloads on every output: the oracle runs the whole layer (float64, one
+    expert at a time), so every row tile of every expert, the Zipf head and tail, the padding
+    of each group's last tile and every column tile's edge are compared."""
+    inp = make_inputs(name)
+    cfg = inp.cfg
+    note(f"forward {name} full: T={cfg.T} E={cfg.E} fmt={cfg.fmt}")
+    out = forward(inp).cpu().numpy()
+    ref = oracle.moe_forward(inp.x, inp.wr, inp.br, inp.w1, inp.b1, inp.w2, inp.b2, k=cfg.k, F=cfg.F, fmt=cfg.fmt)
+    assert_close(out, ref, f"forward {name} (all {cfg.T} tokens)")
 
 
 def test_forward_split_stream_follows_the_calling_stream():
