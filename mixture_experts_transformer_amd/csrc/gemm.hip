@@ -1520,12 +1520,36 @@ __global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__
   }
   out[i] = s;
 }
+// the same sum for a fixed slot count: every slot's load is issued before the first add
+template <int K>
+__global__ __launch_bounds__(256) void combine_k_kernel(const float4* __restrict__ y, int T, int D4,
+                                                        float4* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)T * D4) return;
+  const int64_t t = i / D4;
+  const int64_t c = i - t * D4;
+  const float4* src = y + (t * K) * D4 + c;
+  float4 v[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) v[j] = src[(int64_t)j * D4];
+  float4 s = v[0];
+#pragma unroll
+  for (int j = 1; j < K; ++j) {
+    s.x += v[j].x; s.y += v[j].y; s.z += v[j].z; s.w += v[j].w;
+  }
+  out[i] = s;
+}
 
 hipError_t launch_combine(const float* y, int T, int D, int k, float* out, hipStream_t st) {
   const int D4 = D / 4;
   const int64_t n = (int64_t)T * D4;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                     (const float4*)y, T, D4, k, (float4*)out);
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (k == 4)
+    hipLaunchKernelGGL(combine_k_kernel<4>, grid, dim3(256), 0, st, (const float4*)y, T, D4, (float4*)out);
+  else if (k == 2)
+    hipLaunchKernelGGL(combine_k_kernel<2>, grid, dim3(256), 0, st, (const float4*)y, T, D4, (float4*)out);
+  else
+    hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, st, (const float4*)y, T, D4, k, (float4*)out);
   return hipGetLastError();
 }
 
